@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Benchmark of the collective datapath on one MI355X.
+
+One step = the bandwidth-sweep workload: R = 8 rank buffers of bf16 N(0,1) at
+1, 4, 16, 64 and 256 MiB per rank, each size run as All-Reduce, then
+Reduce-Scatter into 8 contiguous chunks, then All-Gather of those chunks;
+plus the same three at fp32, 64 MiB.  Inputs are resident in HBM before the
+timed region.  ``value`` = algorithmic bytes of the whole step (every input
+byte read once, every output byte written once) / step time.
+
+Also reported on the same line:
+* ``roofline``: the dominant kernel (the 256 MiB All-Reduce reduce kernel):
+  algorithmic bytes per launch / its mean duration from HIP events on the
+  launch stream, against the 8 TB/s HBM peak;
+* ``decode``: the batch-1 decode All-Reduce (8 ranks x 4096 bf16), kernel
+  time from events and back-to-back time per call, next to an empty kernel;
+* ``cpu_baseline``: the CPU oracle on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "achieved HBM GB/s (% of peak) for 8-rank reduce/copy; µs per batch-1 All-Reduce"
+PEAK_GBS = 8000.0
+R = 8
+SIZES_MIB = [1, 4, 16, 64, 256]
+FP32_MIB = 64
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-iters", type=int, default=2000)
+    return ap.parse_args()
+
+
+def alg_bytes(S_bytes):
+    """(AR, RS, AG) algorithmic bytes for S bytes per rank (full tensor)."""
+    return 2 * R * S_bytes, (R + 1) * S_bytes, (R + 1) * S_bytes
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: the R ranks are buffers in one GPU's HBM; "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import reduce_rank_buffers_amd as rrb
+    from reduce_rank_buffers_amd import inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda", 0)
+    rrb.lib()  # loud failure if the library is missing
+
+    # ---- resident inputs and outputs --------------------------------------
+    cases = []  # (label, dtype, S_bytes, ins, ar_out, rs_out, ag_out)
+    t0 = time.perf_counter()
+    for S in SIZES_MIB + ["fp32"]:
+        dtype = "f32" if S == "fp32" else "bf16"
+        smib = FP32_MIB if S == "fp32" else S
+        host = inputs.sweep(smib, dtype=dtype)
+        tdt = torch.float32 if dtype == "f32" else torch.int16
+        ins = [torch.from_numpy(h.view(np.int16) if dtype == "bf16" else h).to(dev) for h in host]
+        del host
+        n = ins[0].numel()
+        ar = [torch.empty(n, dtype=tdt, device=dev) for _ in range(R)]
+        rs = [torch.empty(n // R, dtype=tdt, device=dev) for _ in range(R)]
+        ag = [torch.empty(n, dtype=tdt, device=dev) for _ in range(R)]
+        cases.append((f"{smib}MiB-{dtype}", dtype, smib << 20, ins, ar, rs, ag))
+    torch.cuda.synchronize()
+    log(f"inputs resident ({time.perf_counter() - t0:.1f} s)")
+
+    step_bytes = sum(sum(alg_bytes(c[2])) for c in cases)
+    big = next(c for c in cases if c[0] == "256MiB-bf16")
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    roof_events = []
+    per_case_events = {c[0]: [] for c in cases}
+
+    def step(record):
+        for label, dtype, Sb, ins, ar, rs, ag in cases:
+            if record:
+                e = [ev() for _ in range(4)]
+                e[0].record()
+            rrb.all_reduce(ins, ar)
+            if record:
+                e[1].record()
+            rrb.reduce_scatter(ins, rs)
+            if record:
+                e[2].record()
+            rrb.all_gather(rs, ag)
+            if record:
+                e[3].record()
+                per_case_events[label].append(e)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    value = step_bytes / (wall / args.steps) / 1e9
+
+    sweep = {}
+    for label, dtype, Sb, *_ in cases:
+        ab = alg_bytes(Sb)
+        times = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)]
+                          for e in per_case_events[label]])  # ms
+        mean = times.mean(axis=0)
+        sweep[label] = {
+            k: {"us": round(float(m) * 1e3, 2), "GBps": round(b / (m * 1e-3) / 1e9, 1),
+                "frac": round(b / (m * 1e-3) / 1e9 / PEAK_GBS, 4)}
+            for k, m, b in zip(("all_reduce", "reduce_scatter", "all_gather"), mean, ab)
+        }
+        sweep[label]["cache_note"] = "fits in the 256 MB Infinity Cache" if Sb * R * 2 <= (256 << 20) else "above the Infinity Cache"
+    ar_bytes = alg_bytes(big[2])[0]
+    ar_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in per_case_events[big[0]]]))
+    achieved = ar_bytes / (ar_ms * 1e-3) / 1e9
+
+    # ---- decode All-Reduce latency (8 x 4096 bf16) -------------------------
+    dec_host = inputs.decode_allreduce()
+    dins = [torch.from_numpy(h.view(np.int16)).to(dev) for h in dec_host]
+    douts = [torch.empty(4096, dtype=torch.int16, device=dev) for _ in range(R)]
+    for _ in range(50):
+        rrb.all_reduce(dins, douts)
+        rrb.empty_kernel()
+    torch.cuda.synchronize()
+
+    def per_launch_us(fn, iters):
+        es = [(ev(), ev()) for _ in range(iters)]
+        for a, b in es:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) * 1e3 for a, b in es])
+
+    def back_to_back_us(fn, iters):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(iters):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) * 1e6 / iters
+
+    it = args.decode_iters
+    ar_ev = per_launch_us(lambda: rrb.all_reduce(dins, douts), it)
+    em_ev = per_launch_us(rrb.empty_kernel, it)
+    decode = {
+        "workload": "All-Reduce, 8 ranks x 4096 bf16 (TP=8 batch-1 decode, hidden 4096)",
+        "allreduce_event_us_p50": round(float(np.median(ar_ev)), 2),
+        "allreduce_event_us_p10": round(float(np.percentile(ar_ev, 10)), 2),
+        "allreduce_event_us_p90": round(float(np.percentile(ar_ev, 90)), 2),
+        "empty_kernel_event_us_p50": round(float(np.median(em_ev)), 2),
+        "allreduce_back_to_back_us": round(back_to_back_us(lambda: rrb.all_reduce(dins, douts), it), 2),
+        "empty_back_to_back_us": round(back_to_back_us(rrb.empty_kernel, it), 2),
+    }
+
+    # ---- CPU oracle on a bounded sample ------------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline()
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "io_dtype": "bf16 (one fp32 leg at 64 MiB)",
+        "data": "synthetic",
+        "config": {
+            "workload": "bandwidth sweep: 8 rank buffers x {1,4,16,64,256} MiB bf16 N(0,1), "
+                        "All-Reduce -> Reduce-Scatter (8 contiguous chunks) -> All-Gather of "
+                        "those chunks, plus fp32 at 64 MiB",
+            "ranks": R,
+            "step_algorithmic_bytes": step_bytes,
+            "parallelism": "single GPU (ranks are HBM buffers)",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "reduce_vec_kernel<8,2,bf16> (All-Reduce, 256 MiB per rank)",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBS, 4),
+            "traffic": None,
+            "alg_bytes_per_launch": ar_bytes,
+            "mean_launch_us": round(ar_ms * 1e3, 2),
+        },
+        "decode": decode,
+        "sweep": sweep,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline():
+    """The oracle, untuned, on a bounded sample: All-Reduce -> Reduce-Scatter ->
+    All-Gather of 8 ranks x 16 MiB bf16 (the sweep's 16 MiB size)."""
+    from oracle import collectives as C
+    from reduce_rank_buffers_amd import inputs
+    S = 16
+    ins = inputs.sweep(S)
+    t0 = time.perf_counter()
+    C.all_reduce(ins)
+    rs = C.reduce_scatter(ins)
+    C.all_gather(rs)
+    dt = time.perf_counter() - t0
+    b = sum(alg_bytes(S << 20))
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {"value": round(b / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "host_cores_visible": cores,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": "All-Reduce -> Reduce-Scatter -> All-Gather, 8 ranks x 16 MiB bf16 "
+                      "(numpy, single thread)"}
+
+
+if __name__ == "__main__":
+    main()

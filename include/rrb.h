@@ -1,0 +1,283 @@
+/*
+ * rrb.h -- C ABI of librrb, an MI355X (gfx950) collective datapath on one GPU.
+ *
+ * The R "ranks" are R buffers in one GPU's HBM.  The library follows the
+ * three-way split of Purlin: Separating Orchestration from the Datapath of
+ * Collectives ("The Purlin PDF describes a three-layer design"):
+ *
+ *   collective spec  -- a naming of an input layout and an output layout plus
+ *                       a copy or a reduce            -> rrb_plan_create
+ *   SNAC             -- stage / notify / consume orchestration, here as epoch
+ *                       flags between workgroups      -> rrb_snac_*
+ *   Atom             -- the copy and reduce datapath  -> rrb_copy, rrb_reduce
+ *
+ * Conventions for every function:
+ *   - Return value: RRB_OK (0) or a negative rrb_status.  Nothing throws
+ *     across the ABI.  rrb_last_error() returns a thread-local text for the
+ *     last failure on the calling thread (including HIP's error string).
+ *   - Ownership: the caller owns every device buffer and every stream.  The
+ *     library never allocates, frees or reallocates device memory; it owns
+ *     only the host-side plan / SNAC objects it creates.
+ *   - Streams: an rrb_stream_t is a hipStream_t (NULL = the null stream).
+ *     Entry points that launch work are asynchronous on that stream and never
+ *     synchronise it.
+ *   - Pointers named d_* are device pointers; all others are host pointers.
+ *   - Element types: RRB_BF16 (IEEE binary32's upper 16 bits) and RRB_F32.
+ */
+#ifndef RRB_H
+#define RRB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RRB_ABI_VERSION 1
+#define RRB_MAX_RANKS 16
+
+typedef int32_t rrb_status;
+#define RRB_OK            0
+#define RRB_EINVAL       (-1) /* bad argument or an invalid layout naming          */
+#define RRB_EUNSUPPORTED (-2) /* well formed, but outside what this build runs     */
+#define RRB_EHIP         (-3) /* a HIP runtime call failed; see rrb_last_error()    */
+#define RRB_ETIMEOUT     (-4) /* a bounded wait in a SNAC kernel expired            */
+#define RRB_ENOMEM       (-5) /* a host allocation failed                           */
+
+typedef void *rrb_stream_t; /* hipStream_t */
+
+typedef enum { RRB_BF16 = 0, RRB_F32 = 1 } rrb_dtype;
+typedef enum { RRB_COPY = 0, RRB_REDUCE_SUM = 1 } rrb_op;
+
+/*
+ * Layout names.  The pages say only that a collective names an input and an
+ * output layout (Purlin news page, "The Purlin PDF describes a three-layer
+ * design"); this is the naming this library reads into that.  A logical
+ * tensor X has `count` elements; layouts that name blocks split it into R
+ * contiguous blocks of count / R elements.
+ *
+ *   PARTIAL     rank q holds a full-length partial of X (X = sum over ranks)
+ *   REPLICATED  every rank holds all of X
+ *   SHARD       rank q holds block q of X
+ *   ROOT        rank `root` holds all of X; other ranks hold nothing
+ *   BLOCK_ROW   X is an R x R matrix of blocks M[r][q]; rank r holds row r
+ *   BLOCK_COL   rank q holds column q (its local block r is M[r][q])
+ *
+ * copy:   each output element receives the input element carrying the same
+ *         name (the lowest rank's copy if several ranks hold it).
+ * reduce: input must be PARTIAL; output element X[j] receives
+ *         RNE_bf16(((P_0[j] + P_1[j]) + ...) + P_{R-1}[j]) accumulated in fp32
+ *         in rank order 0..R-1 (fp32 data: the fp32 sum itself).
+ * The seven collectives are: All-Reduce PARTIAL->REPLICATED reduce;
+ * Reduce-Scatter PARTIAL->SHARD reduce; All-Gather SHARD->REPLICATED copy;
+ * All-to-All BLOCK_ROW->BLOCK_COL copy; Broadcast ROOT(r)->REPLICATED copy;
+ * Reduce ROOT: PARTIAL->ROOT(r) reduce; Gather SHARD->ROOT(r) copy.
+ */
+typedef enum {
+  RRB_PARTIAL = 0,
+  RRB_REPLICATED = 1,
+  RRB_SHARD = 2,
+  RRB_ROOT = 3,
+  RRB_BLOCK_ROW = 4,
+  RRB_BLOCK_COL = 5
+} rrb_layout_kind;
+
+typedef struct {
+  int32_t kind; /* rrb_layout_kind */
+  int32_t root; /* used by RRB_ROOT only */
+} rrb_layout;
+
+typedef struct {
+  int32_t nranks; /* R, 1..RRB_MAX_RANKS */
+  int32_t dtype;  /* rrb_dtype */
+  int64_t count;  /* elements of the logical tensor X (per-rank buffer length
+                     for BLOCK_ROW / BLOCK_COL); >= 0 */
+  rrb_layout in;
+  rrb_layout out;
+  int32_t op;     /* rrb_op */
+  int32_t reserved; /* must be 0 */
+} rrb_spec;
+
+/* One entry of a plan's index map, as returned by rrb_plan_segments: `len`
+ * elements move from rank src_rank at element offset src_off (or, for a
+ * reduce, from every rank 0..R-1 at src_off, folded in rank order) to every
+ * rank set in dst_mask at element offset dst_off. */
+typedef struct {
+  int64_t src_off;
+  int64_t dst_off;
+  int64_t len;
+  int32_t src_rank; /* -1: all ranks, folded in order (reduce) */
+  uint32_t dst_mask;
+} rrb_segment;
+
+typedef struct rrb_plan_s *rrb_plan_t;
+
+/* ---- errors --------------------------------------------------------------- */
+
+/* Static text for a status code. */
+const char *rrb_status_string(rrb_status s);
+/* Thread-local text describing the last failure on this thread ("" if none). */
+const char *rrb_last_error(void);
+/* RRB_ABI_VERSION of the loaded library. */
+int32_t rrb_abi_version(void);
+
+/* ---- plans: layout naming -> index map (host only) ------------------------ */
+
+/*
+ * Validate `spec` and build its index map (Purlin news page, "The Purlin PDF
+ * describes a three-layer design": a collective is a naming of input and
+ * output layouts plus copy or reduce).  Rules: reduce iff the input layout is
+ * PARTIAL; a reduce output must name elements of X (REPLICATED, SHARD, ROOT);
+ * a copy output's every name must be held by the input; BLOCK_ROW/BLOCK_COL
+ * only pair with each other; block-naming layouts need count % nranks == 0.
+ * On success *out receives a new plan (free with rrb_plan_destroy).
+ * Errors: RRB_EINVAL (message in rrb_last_error), RRB_ENOMEM.
+ */
+rrb_status rrb_plan_create(const rrb_spec *spec, rrb_plan_t *out);
+
+/*
+ * Row-map plan for expert-parallel MoE.  `tokens` rows of `hidden` elements
+ * (dtype bf16) are sharded over `nranks` source ranks, tokens/nranks
+ * consecutive rows each; `experts` experts live on the ranks in contiguous
+ * groups of experts/nranks.  topk_idx[tokens][topk] (int32, distinct experts
+ * per row) and topk_w[tokens][topk] (float32) are host arrays, copied.
+ *   dir = RRB_MOE_DISPATCH: copy each token's row to every selected expert.
+ *     Rank r's receive buffer is expert-major over its experts in ascending
+ *     id, tokens ascending within an expert (in = token shards [tokens/R][h],
+ *     out = receive buffers [rows_r][h]).
+ *   dir = RRB_MOE_COMBINE: y[t] = RNE_bf16 of the fp32 fold, over t's experts
+ *     in ascending id, of fl32(w * z[slot]) with one multiply then one add per
+ *     step (no fused multiply-add) (in = expert outputs in the dispatch
+ *     layout, out = token shards).
+ * The maps are uploaded by rrb_plan_bind into caller-owned workspace.
+ * Errors: RRB_EINVAL (shapes, indices out of range, repeated expert in a row).
+ */
+#define RRB_MOE_DISPATCH 0
+#define RRB_MOE_COMBINE 1
+rrb_status rrb_plan_create_rows(int32_t nranks, int64_t tokens, int64_t hidden,
+                                int32_t experts, int32_t topk,
+                                const int32_t *topk_idx, const float *topk_w,
+                                int32_t dir, rrb_plan_t *out);
+
+/*
+ * Sizes a plan needs.  *workspace_bytes: device workspace to pass to
+ * rrb_plan_bind (0 if none).  in_count[R], out_count[R] (host arrays of
+ * nranks entries, either may be NULL): elements each rank's input / output
+ * buffer must hold (0: that rank's buffer is not read / not written and may
+ * be NULL).
+ */
+rrb_status rrb_plan_query(rrb_plan_t plan, size_t *workspace_bytes,
+                          int64_t *in_count, int64_t *out_count);
+
+/*
+ * Upload the plan's device-side map (row plans) into d_workspace (caller-owned,
+ * >= workspace_bytes, 256-byte aligned) with an async copy on `stream`.  The
+ * plan keeps d_workspace; it must stay allocated while the plan is used.
+ * Plans with workspace_bytes == 0 accept NULL and do nothing.
+ */
+rrb_status rrb_plan_bind(rrb_plan_t plan, void *d_workspace, size_t bytes,
+                         rrb_stream_t stream);
+
+/* Copy up to `cap` index-map segments into out[]; *n receives the total. */
+rrb_status rrb_plan_segments(rrb_plan_t plan, rrb_segment *out, int32_t cap,
+                             int32_t *n);
+
+void rrb_plan_destroy(rrb_plan_t plan);
+
+/* ---- Atom: the datapath --------------------------------------------------- */
+
+/*
+ * Atom copy (Purlin news page, "The Purlin PDF describes a three-layer
+ * design": copy is one of the two datapath primitives).  d_in[R] and d_out[R]
+ * are host arrays of device pointers, sized per rrb_plan_query; entries for
+ * ranks with a zero count may be NULL.  Outputs of ranks the plan does not
+ * write are left untouched.  Input and output buffers must not overlap.
+ * Requires a copy plan (RRB_EINVAL otherwise) that is bound if it needs a
+ * workspace.  Asynchronous on `stream`.
+ */
+rrb_status rrb_copy(rrb_plan_t plan, const void *const *d_in,
+                    void *const *d_out, rrb_stream_t stream);
+
+/*
+ * Atom reduce (same passage: reduce is the other primitive).  Same argument
+ * rules as rrb_copy; requires a reduce plan.  Elementwise fold in fixed rank
+ * order with fp32 accumulation and one round-to-nearest-even to bf16 (the
+ * result is bit-identical in every output that receives it).
+ */
+rrb_status rrb_reduce(rrb_plan_t plan, const void *const *d_in,
+                      void *const *d_out, rrb_stream_t stream);
+
+/* Launch an empty kernel (one workgroup) on `stream`: the launch floor that
+ * decode-size collectives are measured against. */
+rrb_status rrb_empty_kernel(rrb_stream_t stream);
+
+/* ---- SNAC: stage / notify / consume chain --------------------------------- */
+
+/*
+ * A chain of back-to-back All-Reduces over R ranks of `count` elements, run
+ * as one persistent kernel in which each rank is a group of `slices`
+ * workgroups and the ranks coordinate only through epoch flags in device
+ * memory (Purlin news page: Stage, Notify, And Consume; SiFAR:
+ * Synchronization-Free All-Reduce for Low-Latency LLM Inference, abstract:
+ * top and bottom barriers, dual buffering, speculative reduction).
+ * flags:
+ *   0                          top barrier + bottom barrier, one buffer
+ *   RRB_SNAC_DUAL_BUFFER       two staging buffers by epoch parity; the
+ *                              bottom barrier is dropped
+ *   | RRB_SNAC_SPECULATIVE     (with DUAL_BUFFER) no top barrier: read first,
+ *                              then check the reduced validation flag
+ *                              (sum of the R flags == R * epoch) and retry on
+ *                              mismatch (SiFAR review, Fig. 14)
+ * slices: workgroups per rank (1..64; 0 = choose from count).
+ */
+#define RRB_SNAC_DUAL_BUFFER 1u
+#define RRB_SNAC_SPECULATIVE 2u
+typedef struct rrb_snac_s *rrb_snac_t;
+
+/* Device-side counters a chain call may accumulate into (zeroed by the
+ * caller).  misspec: validations that failed; retries: slice re-reads;
+ * timeouts: bounded waits that expired; epochs: epochs completed (per rank
+ * and slice, summed). */
+typedef struct {
+  unsigned long long misspec;
+  unsigned long long retries;
+  unsigned long long timeouts;
+  unsigned long long epochs;
+} rrb_snac_stats;
+
+rrb_status rrb_snac_create(int32_t nranks, int64_t count, int32_t dtype,
+                           uint32_t flags, int32_t slices, rrb_snac_t *out);
+/* Device workspace the handle needs: two staging buffers of R x count
+ * elements, flags and status words. */
+rrb_status rrb_snac_workspace(rrb_snac_t h, size_t *bytes);
+/* Attach caller-owned workspace (256-byte aligned) and clear its flags with a
+ * fill kernel on `stream`; resets the handle's epoch counter. */
+rrb_status rrb_snac_bind(rrb_snac_t h, void *d_workspace, size_t bytes,
+                         rrb_stream_t stream);
+/*
+ * Run `epochs` All-Reduces.  d_in: [epochs][R][count] payloads; d_out:
+ * [epochs][R][count], every rank's copy of each epoch's result.  d_stats
+ * (nullable) accumulates counters.  d_stagger (nullable test hook, R uint32):
+ * rank r sleeps about d_stagger[r] x 64 cycles before every stage.
+ * spin_limit: polls before a wait gives up (0 = default, about 2 s); on
+ * expiry every workgroup leaves, stats.timeouts counts it and
+ * rrb_snac_check reports RRB_ETIMEOUT.  The epoch counter carries across
+ * calls, so flags never need clearing between calls.  Calls on one handle
+ * must be serialised on one stream.
+ */
+rrb_status rrb_snac_allreduce_chain(rrb_snac_t h, int32_t epochs,
+                                    const void *d_in, void *d_out,
+                                    rrb_snac_stats *d_stats,
+                                    const uint32_t *d_stagger,
+                                    uint32_t spin_limit, rrb_stream_t stream);
+/* Synchronise `stream` and report RRB_ETIMEOUT if any chain call on this
+ * handle since bind timed out (the handle is unusable until rebound). */
+rrb_status rrb_snac_check(rrb_snac_t h, rrb_stream_t stream);
+void rrb_snac_destroy(rrb_snac_t h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RRB_H */

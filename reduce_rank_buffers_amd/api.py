@@ -1,0 +1,248 @@
+"""Torch-facing binding of librrb: plans, Atom copy / reduce, MoE, SNAC chain.
+
+PyTorch supplies device memory and the current stream; every step of the
+datapath runs in librrb's HIP kernels.  Tensors are passed by pointer; bf16
+data may be any 2-byte tensor (torch.bfloat16, int16, uint16 views), fp32 data
+any 4-byte tensor.
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib as L
+
+# layout kinds, for collective()
+PARTIAL = L.RRB_PARTIAL
+REPLICATED = L.RRB_REPLICATED
+SHARD = L.RRB_SHARD
+BLOCK_ROW = L.RRB_BLOCK_ROW
+BLOCK_COL = L.RRB_BLOCK_COL
+
+
+def ROOT(rho):
+    return (L.RRB_ROOT, int(rho))
+
+
+def _layout(x):
+    if isinstance(x, tuple):
+        return L.Layout(int(x[0]), int(x[1]))
+    return L.Layout(int(x), 0)
+
+
+def _dtype_code(dtype):
+    if dtype in ("bf16", torch.bfloat16, L.RRB_BF16):
+        return L.RRB_BF16
+    if dtype in ("f32", torch.float32, L.RRB_F32):
+        return L.RRB_F32
+    raise ValueError(f"unsupported dtype {dtype!r}")
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptrs(tensors, R):
+    out = []
+    for r in range(R):
+        t = tensors[r] if r < len(tensors) else None
+        out.append(None if t is None else t.data_ptr())
+    return L.ptr_array(out)
+
+
+class Plan:
+    """A layout-naming spec compiled to an index map (rrb_plan_create)."""
+
+    def __init__(self, nranks, count, dtype, in_layout, out_layout, op):
+        spec = L.Spec()
+        spec.nranks = int(nranks)
+        spec.dtype = _dtype_code(dtype)
+        spec.count = int(count)
+        spec.in_ = _layout(in_layout)
+        spec.out = _layout(out_layout)
+        spec.op = L.RRB_REDUCE_SUM if op in ("reduce", L.RRB_REDUCE_SUM) else L.RRB_COPY
+        spec.reserved = 0
+        self._lib = L.lib()
+        h = ctypes.c_void_p()
+        L.check(self._lib.rrb_plan_create(ctypes.byref(spec), ctypes.byref(h)), "rrb_plan_create")
+        self.handle = h
+        self.nranks = int(nranks)
+        self.op = spec.op
+        self.dtype = spec.dtype
+        self._ws = None
+        self._query()
+
+    def _query(self):
+        R = self.nranks
+        ws = ctypes.c_size_t()
+        inc = (ctypes.c_int64 * R)()
+        outc = (ctypes.c_int64 * R)()
+        L.check(self._lib.rrb_plan_query(self.handle, ctypes.byref(ws), inc, outc), "rrb_plan_query")
+        self.workspace_bytes = ws.value
+        self.in_count = list(inc)
+        self.out_count = list(outc)
+
+    def segments(self):
+        n = ctypes.c_int32()
+        L.check(self._lib.rrb_plan_segments(self.handle, None, 0, ctypes.byref(n)), "rrb_plan_segments")
+        arr = (L.Segment * max(1, n.value))()
+        L.check(self._lib.rrb_plan_segments(self.handle, arr, n.value, ctypes.byref(n)),
+                "rrb_plan_segments")
+        return [(s.src_rank, s.src_off, s.dst_off, s.len, s.dst_mask) for s in arr[:n.value]]
+
+    def bind(self, device=None, stream=None):
+        """Allocate (torch) and upload the device-side map if the plan has one."""
+        if self.workspace_bytes:
+            dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+            self._ws = torch.empty(self.workspace_bytes + 256, dtype=torch.uint8, device=dev)
+            base = self._ws.data_ptr()
+            aligned = (base + 255) // 256 * 256
+            L.check(self._lib.rrb_plan_bind(self.handle, ctypes.c_void_p(aligned),
+                                            self.workspace_bytes, _stream(stream)), "rrb_plan_bind")
+        return self
+
+    def run(self, ins, outs, stream=None):
+        """Atom copy or reduce, whichever the plan names, on torch's stream."""
+        fn = self._lib.rrb_reduce if self.op == L.RRB_REDUCE_SUM else self._lib.rrb_copy
+        L.check(fn(self.handle, _ptrs(ins, self.nranks), _ptrs(outs, self.nranks), _stream(stream)),
+                "rrb_reduce" if self.op == L.RRB_REDUCE_SUM else "rrb_copy")
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            self._lib.rrb_plan_destroy(h)
+            self.handle = None
+
+
+_PLANS = {}
+
+
+def plan(nranks, count, dtype, in_layout, out_layout, op):
+    key = (int(nranks), int(count), _dtype_code(dtype), in_layout, out_layout, op)
+    p = _PLANS.get(key)
+    if p is None:
+        p = Plan(nranks, count, dtype, in_layout, out_layout, op)
+        _PLANS[key] = p
+    return p
+
+
+def _dtype_of(t):
+    return L.RRB_F32 if t.element_size() == 4 else L.RRB_BF16
+
+
+def collective(in_layout, out_layout, op, ins, outs, count, stream=None):
+    """Any layout-named collective: the plan is cached per (R, n, dtype, naming, op)."""
+    t = next(x for x in ins if x is not None)
+    p = plan(len(ins), count, _dtype_of(t), in_layout, out_layout, op)
+    p.run(ins, outs, stream)
+    return outs
+
+
+# The seven collectives (count = elements of the logical tensor X).
+def all_reduce(ins, outs, stream=None):
+    return collective(PARTIAL, REPLICATED, "reduce", ins, outs, ins[0].numel(), stream)
+
+
+def reduce_scatter(ins, outs, stream=None):
+    return collective(PARTIAL, SHARD, "reduce", ins, outs, ins[0].numel(), stream)
+
+
+def all_gather(ins, outs, stream=None):
+    return collective(SHARD, REPLICATED, "copy", ins, outs, ins[0].numel() * len(ins), stream)
+
+
+def all_to_all(ins, outs, stream=None):
+    return collective(BLOCK_ROW, BLOCK_COL, "copy", ins, outs, ins[0].numel(), stream)
+
+
+def broadcast(ins, outs, root, stream=None):
+    return collective(ROOT(root), REPLICATED, "copy", ins, outs, ins[root].numel(), stream)
+
+
+def reduce(ins, outs, root, stream=None):
+    return collective(PARTIAL, ROOT(root), "reduce", ins, outs, ins[0].numel(), stream)
+
+
+def gather(ins, outs, root, stream=None):
+    return collective(SHARD, ROOT(root), "copy", ins, outs, ins[0].numel() * len(ins), stream)
+
+
+def empty_kernel(stream=None):
+    L.check(L.lib().rrb_empty_kernel(_stream(stream)), "rrb_empty_kernel")
+
+
+# ---- MoE --------------------------------------------------------------------
+
+class MoePlan(Plan):
+    """Row-map plan for expert-parallel dispatch (copy) or combine (reduce)."""
+
+    def __init__(self, nranks, hidden, experts, topk_idx, topk_w, direction, device=None):
+        import numpy as np
+        idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+        w = np.ascontiguousarray(topk_w, dtype=np.float32)
+        T, k = idx.shape
+        self._lib = L.lib()
+        h = ctypes.c_void_p()
+        d = L.RRB_MOE_DISPATCH if direction == "dispatch" else L.RRB_MOE_COMBINE
+        L.check(self._lib.rrb_plan_create_rows(int(nranks), int(T), int(hidden), int(experts), int(k),
+                                               idx.ctypes.data, w.ctypes.data, d, ctypes.byref(h)),
+                "rrb_plan_create_rows")
+        self.handle = h
+        self.nranks = int(nranks)
+        self.op = L.RRB_COPY if d == L.RRB_MOE_DISPATCH else L.RRB_REDUCE_SUM
+        self.dtype = L.RRB_BF16
+        self.hidden = int(hidden)
+        self._ws = None
+        self._query()
+        self.rows_per_rank = [(c if d == L.RRB_MOE_DISPATCH else i) // self.hidden
+                              for i, c in zip(self.in_count, self.out_count)]
+        self.bind(device)
+
+
+# ---- SNAC chain -------------------------------------------------------------
+
+VARIANTS = {"barrier": 0, "dual": L.RRB_SNAC_DUAL_BUFFER,
+            "speculative": L.RRB_SNAC_DUAL_BUFFER | L.RRB_SNAC_SPECULATIVE}
+
+
+class SnacChain:
+    """A bound SNAC handle: back-to-back All-Reduces in one persistent kernel."""
+
+    def __init__(self, nranks, count, dtype="bf16", variant="dual", slices=0, device=None,
+                 stream=None):
+        self._lib = L.lib()
+        h = ctypes.c_void_p()
+        L.check(self._lib.rrb_snac_create(int(nranks), int(count), _dtype_code(dtype),
+                                          VARIANTS[variant], int(slices), ctypes.byref(h)),
+                "rrb_snac_create")
+        self.handle = h
+        self.nranks = int(nranks)
+        self.count = int(count)
+        self.variant = variant
+        ws = ctypes.c_size_t()
+        L.check(self._lib.rrb_snac_workspace(h, ctypes.byref(ws)), "rrb_snac_workspace")
+        dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self._ws = torch.empty(ws.value + 256, dtype=torch.uint8, device=dev)
+        base = (self._ws.data_ptr() + 255) // 256 * 256
+        L.check(self._lib.rrb_snac_bind(h, ctypes.c_void_p(base), ws.value, _stream(stream)),
+                "rrb_snac_bind")
+
+    def run(self, inp, out, stats=None, stagger=None, spin_limit=0, stream=None):
+        """inp, out: [epochs, R, count] device tensors; stats: int64[4] device tensor."""
+        E = inp.shape[0]
+        L.check(self._lib.rrb_snac_allreduce_chain(
+            self.handle, int(E), ctypes.c_void_p(inp.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+            ctypes.c_void_p(stats.data_ptr() if stats is not None else 0),
+            ctypes.c_void_p(stagger.data_ptr() if stagger is not None else 0),
+            int(spin_limit), _stream(stream)), "rrb_snac_allreduce_chain")
+        return out
+
+    def check(self, stream=None):
+        L.check(self._lib.rrb_snac_check(self.handle, _stream(stream)), "rrb_snac_check")
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            self._lib.rrb_snac_destroy(h)
+            self.handle = None

@@ -1,0 +1,325 @@
+// Atom: the copy and reduce datapath on gfx950 (MI355X).
+//
+// Purlin: Separating Orchestration from the Datapath of Collectives ("The
+// Purlin PDF describes a three-layer design"): below the orchestration sits a
+// hardware-specific datapath with two primitives, copy and reduce.  On one
+// MI355X both are HBM-streaming kernels: every source byte is read once with
+// 128-bit loads, the reduce accumulates in fp32 registers in rank order
+// 0..R-1 and rounds once to bf16 (round-to-nearest-even), and a fan-out
+// segment writes its result to every destination rank from registers.  There
+// is no contraction here, so no MFMA and no LDS: the work is bounded by HBM
+// bandwidth (large payloads) or by launch and memory latency (decode sizes).
+//
+// A plan's segments ride in the kernel arguments (at most kMaxItems per
+// launch), so a decode-size All-Reduce issues its loads without first
+// fetching a table from memory.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+
+#include "rrb_internal.h"
+#include "rrb_kernels.h"
+
+namespace rrb {
+
+constexpr int kMaxItems = 64;
+
+struct KItem {
+  int64_t src_off;  // bytes
+  int64_t dst_off;  // bytes
+  int32_t src_rank; // copy: source rank; reduce: unused (all ranks)
+  uint32_t dst_mask;
+};
+
+struct UniArgs {
+  const unsigned char *in[RRB_MAX_RANKS];
+  unsigned char *out[RRB_MAX_RANKS];
+  KItem items[kMaxItems];
+  int64_t nvec;   // whole 16-byte vectors per item (vector path)
+  int64_t tail;   // elements per item after those vectors (vector path)
+  int64_t nelem;  // elements per item (element path)
+  int32_t tiles;  // workgroups per item
+  int32_t nranks;
+};
+
+// ---- kernels ---------------------------------------------------------------
+
+template <int R, int U, bool BF16>
+__global__ void __launch_bounds__(256) reduce_vec_kernel(UniArgs a) {
+  const int bs = blockDim.x;
+  const int item = blockIdx.x / a.tiles;
+  const int tile = blockIdx.x - item * a.tiles;
+  const KItem it = a.items[item];
+  const int64_t base = static_cast<int64_t>(tile) * bs * U + threadIdx.x;
+
+  uint4 v[U][R];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t i = base + static_cast<int64_t>(u) * bs;
+    if (i < a.nvec) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        v[u][r] = *reinterpret_cast<const uint4 *>(a.in[r] + it.src_off + i * 16);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t i = base + static_cast<int64_t>(u) * bs;
+    if (i < a.nvec) {
+      const uint4 res = BF16 ? fold_bf16x8<R>(v[u]) : fold_f32x4<R>(v[u]);
+      for (uint32_t m = it.dst_mask; m; m &= m - 1) {
+        const int q = __builtin_ctz(m);
+        *reinterpret_cast<uint4 *>(a.out[q] + it.dst_off + i * 16) = res;
+      }
+    }
+  }
+  // Elements after the last whole vector of the item (single-segment plans
+  // whose length is not a multiple of the vector width).
+  if (a.tail && tile == a.tiles - 1 && threadIdx.x < a.tail) {
+    const int64_t e = a.nvec * (BF16 ? 8 : 4) + threadIdx.x;
+    const int esz = BF16 ? 2 : 4;
+    if (BF16) {
+      float acc = bf16_to_f32(*reinterpret_cast<const uint16_t *>(a.in[0] + it.src_off + e * esz));
+#pragma unroll
+      for (int r = 1; r < R; ++r)
+        acc = acc + bf16_to_f32(*reinterpret_cast<const uint16_t *>(a.in[r] + it.src_off + e * esz));
+      const uint16_t b = f32_to_bf16_rne(acc);
+      for (uint32_t m = it.dst_mask; m; m &= m - 1) {
+        const int q = __builtin_ctz(m);
+        *reinterpret_cast<uint16_t *>(a.out[q] + it.dst_off + e * esz) = b;
+      }
+    } else {
+      float acc = *reinterpret_cast<const float *>(a.in[0] + it.src_off + e * esz);
+#pragma unroll
+      for (int r = 1; r < R; ++r)
+        acc = acc + *reinterpret_cast<const float *>(a.in[r] + it.src_off + e * esz);
+      for (uint32_t m = it.dst_mask; m; m &= m - 1) {
+        const int q = __builtin_ctz(m);
+        *reinterpret_cast<float *>(a.out[q] + it.dst_off + e * esz) = acc;
+      }
+    }
+  }
+}
+
+// Element-at-a-time reduce for buffers or offsets that are not 16-byte
+// aligned: correct for any layout, not tuned.
+template <bool BF16>
+__global__ void __launch_bounds__(256) reduce_elem_kernel(UniArgs a) {
+  const int item = blockIdx.x / a.tiles;
+  const int tile = blockIdx.x - item * a.tiles;
+  const KItem it = a.items[item];
+  const int64_t e = static_cast<int64_t>(tile) * blockDim.x + threadIdx.x;
+  if (e >= a.nelem) return;
+  if (BF16) {
+    float acc = bf16_to_f32(*reinterpret_cast<const uint16_t *>(a.in[0] + it.src_off + e * 2));
+    for (int r = 1; r < a.nranks; ++r)
+      acc = acc + bf16_to_f32(*reinterpret_cast<const uint16_t *>(a.in[r] + it.src_off + e * 2));
+    const uint16_t b = f32_to_bf16_rne(acc);
+    for (uint32_t m = it.dst_mask; m; m &= m - 1)
+      *reinterpret_cast<uint16_t *>(a.out[__builtin_ctz(m)] + it.dst_off + e * 2) = b;
+  } else {
+    float acc = *reinterpret_cast<const float *>(a.in[0] + it.src_off + e * 4);
+    for (int r = 1; r < a.nranks; ++r)
+      acc = acc + *reinterpret_cast<const float *>(a.in[r] + it.src_off + e * 4);
+    for (uint32_t m = it.dst_mask; m; m &= m - 1)
+      *reinterpret_cast<float *>(a.out[__builtin_ctz(m)] + it.dst_off + e * 4) = acc;
+  }
+}
+
+template <int U>
+__global__ void __launch_bounds__(256) copy_vec_kernel(UniArgs a) {
+  const int bs = blockDim.x;
+  const int item = blockIdx.x / a.tiles;
+  const int tile = blockIdx.x - item * a.tiles;
+  const KItem it = a.items[item];
+  const unsigned char *src = a.in[it.src_rank] + it.src_off;
+  const int64_t base = static_cast<int64_t>(tile) * bs * U + threadIdx.x;
+  uint4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t i = base + static_cast<int64_t>(u) * bs;
+    if (i < a.nvec) v[u] = *reinterpret_cast<const uint4 *>(src + i * 16);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t i = base + static_cast<int64_t>(u) * bs;
+    if (i < a.nvec)
+      for (uint32_t m = it.dst_mask; m; m &= m - 1)
+        *reinterpret_cast<uint4 *>(a.out[__builtin_ctz(m)] + it.dst_off + i * 16) = v[u];
+  }
+  // Tail in 2-byte units (every element type is a multiple of 2 bytes).
+  if (a.tail && tile == a.tiles - 1 && threadIdx.x < a.tail) {
+    const int64_t off = a.nvec * 16 + static_cast<int64_t>(threadIdx.x) * 2;
+    const uint16_t x = *reinterpret_cast<const uint16_t *>(src + off);
+    for (uint32_t m = it.dst_mask; m; m &= m - 1)
+      *reinterpret_cast<uint16_t *>(a.out[__builtin_ctz(m)] + it.dst_off + off) = x;
+  }
+}
+
+// 2-byte-unit copy for unaligned layouts.
+__global__ void __launch_bounds__(256) copy_elem_kernel(UniArgs a) {
+  const int item = blockIdx.x / a.tiles;
+  const int tile = blockIdx.x - item * a.tiles;
+  const KItem it = a.items[item];
+  const int64_t e = static_cast<int64_t>(tile) * blockDim.x + threadIdx.x;
+  if (e >= a.nelem) return;
+  const uint16_t x = *reinterpret_cast<const uint16_t *>(a.in[it.src_rank] + it.src_off + e * 2);
+  for (uint32_t m = it.dst_mask; m; m &= m - 1)
+    *reinterpret_cast<uint16_t *>(a.out[__builtin_ctz(m)] + it.dst_off + e * 2) = x;
+}
+
+__global__ void empty_kernel() {}
+
+// ---- launchers -------------------------------------------------------------
+
+namespace {
+
+using ReduceFn = void (*)(UniArgs);
+
+template <int U, bool BF16>
+ReduceFn reduce_vec_for(int R) {
+  switch (R) {
+#define RRB_CASE(n) \
+  case n:           \
+    return reduce_vec_kernel<n, U, BF16>;
+    RRB_CASE(1) RRB_CASE(2) RRB_CASE(3) RRB_CASE(4) RRB_CASE(5) RRB_CASE(6) RRB_CASE(7)
+    RRB_CASE(8) RRB_CASE(9) RRB_CASE(10) RRB_CASE(11) RRB_CASE(12) RRB_CASE(13)
+    RRB_CASE(14) RRB_CASE(15) RRB_CASE(16)
+#undef RRB_CASE
+  }
+  return nullptr;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+rrb_status check_launch(const char *what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(RRB_EHIP, "%s launch: %s", what, hipGetErrorString(e));
+  return RRB_OK;
+}
+
+// Checks the caller's pointer arrays against the plan's per-rank counts.
+rrb_status check_buffers(const Plan &p, const void *const *in, void *const *out) {
+  if (!in || !out) return fail(RRB_EINVAL, "NULL pointer array");
+  for (int32_t r = 0; r < p.nranks; ++r) {
+    if (p.in_count[r] > 0 && !in[r]) return fail(RRB_EINVAL, "input of rank %d is NULL", r);
+    if (p.out_count[r] > 0 && !out[r]) return fail(RRB_EINVAL, "output of rank %d is NULL", r);
+  }
+  return RRB_OK;
+}
+
+rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out,
+                          hipStream_t stream) {
+  const int esz = elem_size(p.dtype);
+  if (p.segs.empty() || p.segs[0].len == 0) return RRB_OK;
+  const int64_t len = p.segs[0].len;
+
+  bool vec = true;
+  for (int32_t r = 0; r < p.nranks; ++r) {
+    if (p.in_count[r] > 0 && !aligned16(in[r])) vec = false;
+    if (p.out_count[r] > 0 && !aligned16(out[r])) vec = false;
+  }
+  for (const Segment &s : p.segs)
+    if ((s.src_off * esz) % 16 || (s.dst_off * esz) % 16) vec = false;
+
+  UniArgs a;
+  std::memset(&a, 0, sizeof a);
+  for (int32_t r = 0; r < p.nranks; ++r) {
+    a.in[r] = static_cast<const unsigned char *>(in[r]);
+    a.out[r] = static_cast<unsigned char *>(out[r]);
+  }
+  a.nranks = p.nranks;
+  a.nelem = len;
+  const bool reduce = p.op == RRB_REDUCE_SUM;
+  const bool bf16 = p.dtype == RRB_BF16;
+
+  int bs;
+  int U;
+  void (*kern)(UniArgs) = nullptr;
+  if (vec) {
+    a.nvec = (len * esz) / 16;
+    a.tail = reduce ? (len - a.nvec * (16 / esz)) : ((len * esz - a.nvec * 16) / 2);
+    // Decode-size items spread over more, smaller workgroups; large items
+    // keep several 16-byte loads per source in flight per lane.
+    const bool small = a.nvec <= 4096;
+    bs = small ? 64 : 256;
+    if (reduce) {
+      U = (small || p.nranks > 8) ? 1 : 2;
+      kern = U == 1 ? (bf16 ? reduce_vec_for<1, true>(p.nranks) : reduce_vec_for<1, false>(p.nranks))
+                    : (bf16 ? reduce_vec_for<2, true>(p.nranks) : reduce_vec_for<2, false>(p.nranks));
+    } else {
+      U = small ? 1 : 4;
+      kern = U == 1 ? copy_vec_kernel<1> : copy_vec_kernel<4>;
+    }
+    const int64_t per_tile = static_cast<int64_t>(bs) * U;
+    int64_t tiles = (a.nvec + per_tile - 1) / per_tile;
+    if (tiles == 0) tiles = 1;  // tail-only item
+    if (a.tail > bs) return fail(RRB_EUNSUPPORTED, "tail longer than a workgroup");
+    a.tiles = static_cast<int32_t>(tiles);
+  } else {
+    bs = 256;
+    U = 1;
+    kern = reduce ? (bf16 ? reduce_elem_kernel<true> : reduce_elem_kernel<false>) : copy_elem_kernel;
+    // the element copy moves 2-byte units
+    if (!reduce) a.nelem = len * esz / 2;
+    a.tiles = static_cast<int32_t>((a.nelem + bs - 1) / bs);
+  }
+  if (static_cast<int64_t>(a.tiles) * kMaxItems > 0x7fffffffLL)
+    return fail(RRB_EUNSUPPORTED, "segment too long for one launch");
+
+  const size_t nseg = p.segs.size();
+  for (size_t first = 0; first < nseg; first += kMaxItems) {
+    const int cnt = static_cast<int>(std::min<size_t>(kMaxItems, nseg - first));
+    for (int i = 0; i < cnt; ++i) {
+      const Segment &s = p.segs[first + i];
+      a.items[i].src_off = s.src_off * esz;
+      a.items[i].dst_off = s.dst_off * esz;
+      a.items[i].src_rank = s.src_rank < 0 ? 0 : s.src_rank;
+      a.items[i].dst_mask = s.dst_mask;
+    }
+    const unsigned grid = static_cast<unsigned>(cnt) * static_cast<unsigned>(a.tiles);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(bs), 0, stream, a);
+    const rrb_status st = check_launch(reduce ? "reduce" : "copy");
+    if (st != RRB_OK) return st;
+  }
+  return RRB_OK;
+}
+
+}  // namespace
+}  // namespace rrb
+
+using namespace rrb;
+
+extern "C" {
+
+rrb_status rrb_copy(rrb_plan_t plan, const void *const *d_in, void *const *d_out,
+                    rrb_stream_t stream) {
+  clear_error();
+  if (!plan) return fail(RRB_EINVAL, "NULL plan");
+  const Plan &p = plan->p;
+  if (p.op != RRB_COPY) return fail(RRB_EINVAL, "rrb_copy needs a copy plan");
+  rrb_status s = check_buffers(p, d_in, d_out);
+  if (s != RRB_OK) return s;
+  if (p.kind == PlanKind::Rows) return launch_rows(p, d_in, d_out, stream);
+  return launch_uniform(p, d_in, d_out, static_cast<hipStream_t>(stream));
+}
+
+rrb_status rrb_reduce(rrb_plan_t plan, const void *const *d_in, void *const *d_out,
+                      rrb_stream_t stream) {
+  clear_error();
+  if (!plan) return fail(RRB_EINVAL, "NULL plan");
+  const Plan &p = plan->p;
+  if (p.op != RRB_REDUCE_SUM) return fail(RRB_EINVAL, "rrb_reduce needs a reduce plan");
+  rrb_status s = check_buffers(p, d_in, d_out);
+  if (s != RRB_OK) return s;
+  if (p.kind == PlanKind::Rows) return launch_rows(p, d_in, d_out, stream);
+  return launch_uniform(p, d_in, d_out, static_cast<hipStream_t>(stream));
+}
+
+rrb_status rrb_empty_kernel(rrb_stream_t stream) {
+  clear_error();
+  hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream));
+  return check_launch("empty");
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Internal declarations shared by the host-side plan builder, the C ABI and
+// the HIP launchers of librrb.  Not installed; the public ABI is include/rrb.h.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/rrb.h"
+
+namespace rrb {
+
+// Records a failure message for rrb_last_error() and returns `s`.
+rrb_status fail(rrb_status s, const char *fmt, ...);
+// Clears the thread's last-error text.
+void clear_error();
+
+inline int elem_size(int32_t dtype) { return dtype == RRB_F32 ? 4 : 2; }
+
+// An index-map entry at element granularity (the same fields rrb_segment
+// exposes).  src_rank == -1 means "every rank 0..R-1, folded in rank order".
+struct Segment {
+  int64_t src_off;
+  int64_t dst_off;
+  int64_t len;
+  int32_t src_rank;
+  uint32_t dst_mask;
+};
+
+enum class PlanKind { Uniform, Rows };
+
+// Row maps of an expert-parallel plan, as uploaded to the device.
+// Entry (t, i), i < topk, is token t's i-th expert in ascending expert id:
+//   slot_rank[t*k+i], slot_row[t*k+i]  where the row sits in the dispatch
+//   layout; weight[t*k+i] its combine weight.
+struct RowMaps {
+  int64_t tokens = 0, hidden = 0;
+  int32_t experts = 0, topk = 0, dir = 0;
+  std::vector<int32_t> slot;    // [T*k] packed (rank << 26) | row
+  std::vector<float> weight;    // [T*k]
+  std::vector<int64_t> rows_per_rank;
+};
+
+struct Plan {
+  PlanKind kind = PlanKind::Uniform;
+  int32_t nranks = 0;
+  int32_t dtype = RRB_BF16;
+  int32_t op = RRB_COPY;
+  int64_t count = 0;
+  std::vector<Segment> segs;  // all of equal length for uniform plans
+  std::vector<int64_t> in_count, out_count;
+  RowMaps rows;
+  void *d_ws = nullptr;       // bound device workspace (row plans)
+  size_t ws_bytes = 0;
+};
+
+// Builds a uniform plan from a layout-naming spec (rrb_plan.cpp).
+rrb_status build_uniform_plan(const rrb_spec &spec, Plan &plan);
+// Builds a MoE row plan (rrb_plan.cpp).
+rrb_status build_row_plan(int32_t nranks, int64_t tokens, int64_t hidden,
+                          int32_t experts, int32_t topk, const int32_t *idx,
+                          const float *w, int32_t dir, Plan &plan);
+
+// Launches a MoE row plan (rrb_moe.hip).  `stream` is a hipStream_t.
+rrb_status launch_rows(const Plan &plan, const void *const *in, void *const *out,
+                       void *stream);
+
+constexpr int kSlotRankShift = 26;
+constexpr int32_t kSlotRowMask = (1 << kSlotRankShift) - 1;
+
+}  // namespace rrb
+
+struct rrb_plan_s {
+  rrb::Plan p;
+};

@@ -1,0 +1,76 @@
+// Device helpers shared by the Atom, SNAC and MoE kernels of librrb.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace rrb {
+
+// bf16 -> fp32 is exact: the bf16 pattern is the upper half of the binary32.
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest, ties to even, on the bit pattern: adding
+// 0x7fff plus the lowest kept bit carries into bit 16 exactly when the
+// dropped half is above the midpoint, or at the midpoint with an odd kept
+// part.  Infinities stay infinite, finite overflow carries into the infinity
+// pattern, subnormals and -0 are kept; every NaN becomes 0x7fc0.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16_rne(lo)) |
+         (static_cast<uint32_t>(f32_to_bf16_rne(hi)) << 16);
+}
+
+// Fixed rank-order fold of 8 bf16 lanes from R sources: fp32 accumulation,
+// one rounding at the end.  The adds are written one per step so the
+// compiler cannot reassociate them (no fast-math anywhere in this library).
+template <int R>
+__device__ __forceinline__ uint4 fold_bf16x8(const uint4 (&v)[R]) {
+  float a[8];
+  a[0] = bf16_lo(v[0].x); a[1] = bf16_hi(v[0].x);
+  a[2] = bf16_lo(v[0].y); a[3] = bf16_hi(v[0].y);
+  a[4] = bf16_lo(v[0].z); a[5] = bf16_hi(v[0].z);
+  a[6] = bf16_lo(v[0].w); a[7] = bf16_hi(v[0].w);
+#pragma unroll
+  for (int r = 1; r < R; ++r) {
+    a[0] = a[0] + bf16_lo(v[r].x); a[1] = a[1] + bf16_hi(v[r].x);
+    a[2] = a[2] + bf16_lo(v[r].y); a[3] = a[3] + bf16_hi(v[r].y);
+    a[4] = a[4] + bf16_lo(v[r].z); a[5] = a[5] + bf16_hi(v[r].z);
+    a[6] = a[6] + bf16_lo(v[r].w); a[7] = a[7] + bf16_hi(v[r].w);
+  }
+  uint4 o;
+  o.x = pack_bf16x2(a[0], a[1]);
+  o.y = pack_bf16x2(a[2], a[3]);
+  o.z = pack_bf16x2(a[4], a[5]);
+  o.w = pack_bf16x2(a[6], a[7]);
+  return o;
+}
+
+template <int R>
+__device__ __forceinline__ uint4 fold_f32x4(const uint4 (&v)[R]) {
+  float a0 = __uint_as_float(v[0].x), a1 = __uint_as_float(v[0].y);
+  float a2 = __uint_as_float(v[0].z), a3 = __uint_as_float(v[0].w);
+#pragma unroll
+  for (int r = 1; r < R; ++r) {
+    a0 = a0 + __uint_as_float(v[r].x);
+    a1 = a1 + __uint_as_float(v[r].y);
+    a2 = a2 + __uint_as_float(v[r].z);
+    a3 = a3 + __uint_as_float(v[r].w);
+  }
+  uint4 o;
+  o.x = __float_as_uint(a0);
+  o.y = __float_as_uint(a1);
+  o.z = __float_as_uint(a2);
+  o.w = __float_as_uint(a3);
+  return o;
+}
+
+}  // namespace rrb

@@ -1,0 +1,455 @@
+// SNAC: stage / notify / consume orchestration of a decode All-Reduce chain.
+//
+// Purlin: Separating Orchestration from the Datapath of Collectives ("The
+// Purlin PDF describes a three-layer design") names the orchestration layer
+// Stage, Notify, And Consume.  SiFAR: Synchronization-Free All-Reduce for
+// Low-Latency LLM Inference (review page: abstract; Fig. 1, Fig. 8, Fig. 14;
+// the "Load-bearing premise"; referee report on §8.1) gives the protocol
+// variants run here, over R simulated ranks in one GPU:
+//
+//   barrier      one staging buffer; top barrier (every source's flag) before
+//                consuming, bottom barrier (every reader done) before the
+//                next stage -- the write-after-read guard of Fig. 8.
+//   dual         two staging buffers by epoch parity; the next epoch's top
+//                barrier already proves the readers of this buffer finished,
+//                so the bottom barrier goes.
+//   speculative  dual buffers and no top barrier: the consume loads start at
+//                once and a reduced validation flag (sum of the R sources'
+//                flags == R * epoch, per workgroup slice) decides whether the
+//                result stands; on mismatch the slice waits for the flags and
+//                is read again.
+//
+// One persistent kernel runs the whole chain.  Rank r is a group of S
+// workgroups; workgroup (r, s) stages slice s of rank r's payload, publishes
+// flag[buf][r][s] = epoch, then reduces slice s of all R staged payloads in
+// rank order 0..R-1 (fp32, one bf16 rounding) into rank r's output -- the
+// oneshot All-Reduce of SiFAR's Fig. 5, every rank reducing the full payload.
+//
+// Speculation order.  The pages read the payload first and the flags after,
+// and rely on no rank overtaking the reader between those two loads.  Here
+// the flag loads are issued first and the payload loads right after them,
+// with no wait in between: a flag equal to the epoch then means the source
+// finished staging before the payload loads were issued, and a stale read
+// needs a later-issued load to be served before an earlier one by more than
+// the writer's stage-to-flag gap.  The speculative loads are device-coherent
+// (the same cache policy as agent-scope atomic loads), so a line cached from
+// an earlier epoch is never returned.
+//
+// Every wait is bounded: a wait that exceeds its poll budget raises a status
+// word that every other wait also watches, so the whole grid drains and the
+// host sees RRB_ETIMEOUT.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+
+#include "rrb_internal.h"
+#include "rrb_kernels.h"
+
+namespace rrb {
+namespace {
+
+constexpr int kFlagStride = 32;          // u32 words: one 128-byte line per flag
+constexpr uint32_t kDefaultSpin = 1u << 21;  // polls (about 1 us each)
+constexpr int kMaxSlices = 64;
+
+enum Variant : int32_t { kBarrier = 0, kDual = 1, kSpeculative = 2 };
+
+struct SnacArgs {
+  const unsigned char *in;   // [E][R][count]
+  unsigned char *out;        // [E][R][count]
+  unsigned char *staging;    // [2][R][count]
+  uint32_t *flag;            // [2][R][S] x kFlagStride
+  uint32_t *done;            // [R][S] x kFlagStride
+  uint32_t *status;          // [0]: nonzero once any wait timed out
+  rrb_snac_stats *stats;
+  const uint32_t *stagger;
+  int64_t count;             // elements per rank payload
+  int64_t rank_bytes;        // count * elem size
+  int64_t nvec;              // 16-byte vectors per rank payload
+  int64_t slice_vec;         // vectors per slice (the last slice may be short)
+  uint32_t epoch0;           // global number of this call's first epoch (>= 1)
+  int32_t epochs;
+  int32_t S;
+  uint32_t spin_limit;
+};
+
+struct Layout {
+  int64_t staging_off, flag_off, done_off, status_off, total;
+};
+
+Layout layout_for(int32_t R, int64_t count, int32_t dtype, int32_t S) {
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  Layout l;
+  l.staging_off = 0;
+  const int64_t staging = up(2LL * R * count * elem_size(dtype));
+  l.flag_off = staging;
+  const int64_t flags = up(2LL * R * S * kFlagStride * 4);
+  l.done_off = l.flag_off + flags;
+  const int64_t done = up(1LL * R * S * kFlagStride * 4);
+  l.status_off = l.done_off + done;
+  l.total = l.status_off + 256;
+  return l;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// Device-coherent 16-byte load (cache policy sc1, as for agent-scope atomic
+// loads): never served from a line another epoch left in this CU's caches.
+__device__ __forceinline__ uint4 load_coherent(__amdgpu_buffer_rsrc_t r, int32_t off) {
+  const v4u x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16);
+  uint4 o;
+  o.x = x[0];
+  o.y = x[1];
+  o.z = x[2];
+  o.w = x[3];
+  return o;
+}
+
+__device__ __forceinline__ uint32_t load_flag_relaxed(const uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Polls *p until it reaches `want`; false if the budget ran out or another
+// wait already timed out (then the status word is set).
+__device__ bool wait_at_least(const uint32_t *p, uint32_t want, uint32_t *status,
+                              uint32_t limit) {
+  uint32_t spins = 0;
+  // Relaxed (device-coherent) polls; the caller's acquire fence orders what
+  // follows a successful wait.
+  while (load_flag_relaxed(p) < want) {
+    if ((spins & 63) == 0 && load_flag_relaxed(status) != 0) return false;
+    if (++spins >= limit) {
+      __hip_atomic_store(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return true;
+}
+
+// Threads 0..R-1 each wait for one rank's word at `base + t * stride_words`;
+// returns, in every thread of the workgroup, whether all waits succeeded.
+template <int R>
+__device__ bool wait_all(const uint32_t *base, int64_t stride_words, uint32_t want,
+                         uint32_t *status, uint32_t limit, int *lds_ok) {
+  if (threadIdx.x == 0) *lds_ok = 1;
+  __syncthreads();
+  if (threadIdx.x < R) {
+    if (!wait_at_least(base + threadIdx.x * stride_words, want, status, limit))
+      *lds_ok = 0;
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return *lds_ok != 0;
+}
+
+// Reduce one pass of this workgroup's slice: R loads in flight per lane, fold
+// in rank order, store to this rank's output.
+template <int R, bool BF16>
+__device__ __forceinline__ void reduce_pass(const uint4 (&v)[R], unsigned char *dst) {
+  const uint4 res = BF16 ? fold_bf16x8<R>(v) : fold_f32x4<R>(v);
+  *reinterpret_cast<uint4 *>(dst) = res;
+}
+
+template <int R, bool BF16, int VAR>
+__global__ void __launch_bounds__(256) snac_chain_kernel(SnacArgs a) {
+  __shared__ int lds_ok;
+  __shared__ int lds_valid;
+  const int r = blockIdx.x / a.S;
+  const int s = blockIdx.x - r * a.S;
+  const int bs = blockDim.x;
+  const int64_t v0 = static_cast<int64_t>(s) * a.slice_vec;
+  const int64_t v1 = min(a.nvec, v0 + a.slice_vec);
+  const int64_t stride_rs = static_cast<int64_t>(a.S) * kFlagStride;  // words per rank
+  unsigned long long misspec = 0, retries = 0, timeouts = 0, done_epochs = 0;
+
+  for (int k = 0; k < a.epochs; ++k) {
+    const uint32_t ep = a.epoch0 + static_cast<uint32_t>(k);
+    const int b = VAR == kBarrier ? 0 : static_cast<int>(ep & 1u);
+    unsigned char *stage_base = a.staging + static_cast<int64_t>(b) * R * a.rank_bytes;
+    uint32_t *flags_b = a.flag + static_cast<int64_t>(b) * R * stride_rs;
+
+    // Test hook: a late rank.
+    if (a.stagger) {
+      const uint32_t d = a.stagger[r];
+      for (uint32_t i = 0; i < d; ++i) __builtin_amdgcn_s_sleep(1);
+    }
+
+    // Stage: this rank's slice lands in its staged buffer.
+    const unsigned char *src = a.in + (static_cast<int64_t>(k) * R + r) * a.rank_bytes;
+    unsigned char *mine = stage_base + static_cast<int64_t>(r) * a.rank_bytes;
+    for (int64_t i = v0 + threadIdx.x; i < v1; i += bs)
+      *reinterpret_cast<uint4 *>(mine + i * 16) = *reinterpret_cast<const uint4 *>(src + i * 16);
+
+    // Notify: every wave's stores reach device scope, then one flag store.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_store(flags_b + r * stride_rs + s * kFlagStride, ep, __ATOMIC_RELEASE,
+                         __HIP_MEMORY_SCOPE_AGENT);
+
+    unsigned char *dst_base = a.out + (static_cast<int64_t>(k) * R + r) * a.rank_bytes;
+    bool ok = true;
+    int64_t first_pass_end = v0;  // vectors already reduced speculatively
+
+    if (VAR == kSpeculative) {
+      // Consume without a top barrier: flag loads first, payload right after.
+      uint32_t f = 0;
+      if (threadIdx.x < R) f = load_flag_relaxed(flags_b + threadIdx.x * stride_rs + s * kFlagStride);
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      const int64_t i = v0 + threadIdx.x;
+      uint4 v[R];
+      if (i < v1) {
+#pragma unroll
+        for (int q = 0; q < R; ++q)
+          v[q] = load_coherent(rsrc(stage_base + static_cast<int64_t>(q) * a.rank_bytes, a.rank_bytes),
+                               static_cast<int32_t>(i * 16));
+      }
+      // Reduced validation flag: the sum over the R sources must be R * epoch.
+      if (threadIdx.x < 64) {
+        uint32_t sum = threadIdx.x < R ? f : 0u;
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) sum += __shfl_xor(sum, m);
+        if (threadIdx.x == 0) lds_valid = (sum == static_cast<uint32_t>(R) * ep) ? 1 : 0;
+      }
+      __syncthreads();
+      const bool valid = lds_valid != 0;
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      if (valid) {
+        if (i < v1) reduce_pass<R, BF16>(v, dst_base + i * 16);
+        first_pass_end = min(v1, v0 + bs);
+      } else {
+        ++misspec;
+        ++retries;
+        ok = wait_all<R>(flags_b + s * kFlagStride, stride_rs, ep, a.status, a.spin_limit, &lds_ok);
+      }
+    } else {
+      ok = wait_all<R>(flags_b + s * kFlagStride, stride_rs, ep, a.status, a.spin_limit, &lds_ok);
+    }
+    if (!ok) {
+      ++timeouts;
+      break;
+    }
+
+    // Consume: fold the R staged slices in rank order.
+    for (int64_t i = first_pass_end + threadIdx.x; i < v1; i += bs) {
+      uint4 v[R];
+#pragma unroll
+      for (int q = 0; q < R; ++q)
+        v[q] = load_coherent(rsrc(stage_base + static_cast<int64_t>(q) * a.rank_bytes, a.rank_bytes),
+                             static_cast<int32_t>(i * 16));
+      reduce_pass<R, BF16>(v, dst_base + i * 16);
+    }
+
+    if (VAR == kBarrier) {
+      // Bottom barrier: every reader of this rank's slice is done before the
+      // next stage overwrites it.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __syncthreads();
+      if (threadIdx.x == 0)
+        __hip_atomic_store(a.done + (static_cast<int64_t>(r) * a.S + s) * kFlagStride, ep,
+                           __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      if (!wait_all<R>(a.done + static_cast<int64_t>(s) * kFlagStride, stride_rs, ep, a.status,
+                       a.spin_limit, &lds_ok)) {
+        ++timeouts;
+        break;
+      }
+    }
+    ++done_epochs;
+  }
+
+  if (a.stats && threadIdx.x == 0) {
+    if (misspec) atomicAdd(&a.stats->misspec, misspec);
+    if (retries) atomicAdd(&a.stats->retries, retries);
+    if (timeouts) atomicAdd(&a.stats->timeouts, timeouts);
+    atomicAdd(&a.stats->epochs, done_epochs);
+  }
+}
+
+__global__ void fill_u32_kernel(uint32_t *p, int64_t n, uint32_t v) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = v;
+}
+
+using SnacFn = void (*)(SnacArgs);
+
+template <bool BF16, int VAR>
+SnacFn snac_for(int R) {
+  switch (R) {
+#define RRB_CASE(n) \
+  case n:           \
+    return snac_chain_kernel<n, BF16, VAR>;
+    RRB_CASE(1) RRB_CASE(2) RRB_CASE(3) RRB_CASE(4) RRB_CASE(5) RRB_CASE(6) RRB_CASE(7)
+    RRB_CASE(8) RRB_CASE(9) RRB_CASE(10) RRB_CASE(11) RRB_CASE(12) RRB_CASE(13)
+    RRB_CASE(14) RRB_CASE(15) RRB_CASE(16)
+#undef RRB_CASE
+  }
+  return nullptr;
+}
+
+}  // namespace
+}  // namespace rrb
+
+struct rrb_snac_s {
+  int32_t R = 0;
+  int64_t count = 0;
+  int32_t dtype = RRB_BF16;
+  uint32_t flags = 0;
+  int32_t S = 1;
+  int bs = 64;
+  rrb::Layout lay{};
+  unsigned char *ws = nullptr;
+  uint32_t next_epoch = 1;
+};
+
+using namespace rrb;
+
+extern "C" {
+
+rrb_status rrb_snac_create(int32_t nranks, int64_t count, int32_t dtype, uint32_t flags,
+                           int32_t slices, rrb_snac_t *out) {
+  clear_error();
+  if (!out) return fail(RRB_EINVAL, "NULL out");
+  *out = nullptr;
+  if (nranks < 1 || nranks > RRB_MAX_RANKS)
+    return fail(RRB_EINVAL, "nranks %d outside 1..%d", nranks, RRB_MAX_RANKS);
+  if (dtype != RRB_BF16 && dtype != RRB_F32) return fail(RRB_EINVAL, "unknown dtype %d", dtype);
+  if (flags & ~(RRB_SNAC_DUAL_BUFFER | RRB_SNAC_SPECULATIVE))
+    return fail(RRB_EINVAL, "unknown SNAC flags 0x%x", flags);
+  if ((flags & RRB_SNAC_SPECULATIVE) && !(flags & RRB_SNAC_DUAL_BUFFER))
+    return fail(RRB_EINVAL, "speculative reduction needs dual buffering");
+  const int esz = elem_size(dtype);
+  if (count <= 0 || (count * esz) % 16)
+    return fail(RRB_EUNSUPPORTED, "chain payloads must be a positive multiple of 16 bytes");
+  if (2LL * nranks * count * esz > 0x7fffffffLL)
+    return fail(RRB_EUNSUPPORTED, "staging above 2 GiB");
+  if (slices < 0 || slices > kMaxSlices)
+    return fail(RRB_EINVAL, "slices %d outside 0..%d", slices, kMaxSlices);
+  const int64_t nvec = count * esz / 16;
+  int bs = nvec <= 64 * 8 ? 64 : 256;
+  int32_t S = slices;
+  if (S == 0) {
+    // One pass per workgroup where possible, within the co-resident budget.
+    S = static_cast<int32_t>(std::min<int64_t>(kMaxSlices, (nvec + bs - 1) / bs));
+    if (S < 1) S = 1;
+  }
+  if (S > nvec) S = static_cast<int32_t>(nvec);
+  rrb_snac_s *h = new (std::nothrow) rrb_snac_s;
+  if (!h) return fail(RRB_ENOMEM, "handle allocation failed");
+  h->R = nranks;
+  h->count = count;
+  h->dtype = dtype;
+  h->flags = flags;
+  h->S = S;
+  h->bs = bs;
+  h->lay = layout_for(nranks, count, dtype, S);
+  *out = h;
+  return RRB_OK;
+}
+
+rrb_status rrb_snac_workspace(rrb_snac_t h, size_t *bytes) {
+  clear_error();
+  if (!h || !bytes) return fail(RRB_EINVAL, "NULL handle or bytes");
+  *bytes = static_cast<size_t>(h->lay.total);
+  return RRB_OK;
+}
+
+rrb_status rrb_snac_bind(rrb_snac_t h, void *d_ws, size_t bytes, rrb_stream_t stream) {
+  clear_error();
+  if (!h) return fail(RRB_EINVAL, "NULL handle");
+  if (!d_ws || bytes < static_cast<size_t>(h->lay.total))
+    return fail(RRB_EINVAL, "workspace of %lld bytes needed", (long long)h->lay.total);
+  if (reinterpret_cast<uintptr_t>(d_ws) % 256) return fail(RRB_EINVAL, "workspace must be 256-byte aligned");
+  h->ws = static_cast<unsigned char *>(d_ws);
+  h->next_epoch = 1;
+  // Clear flags, done words and status with a fill kernel (graph-safe).
+  uint32_t *p = reinterpret_cast<uint32_t *>(h->ws + h->lay.flag_off);
+  const int64_t n = (h->lay.total - h->lay.flag_off) / 4;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(64), dim3(256), 0, static_cast<hipStream_t>(stream), p, n,
+                     0u);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(RRB_EHIP, "flag clear: %s", hipGetErrorString(e));
+  return RRB_OK;
+}
+
+rrb_status rrb_snac_allreduce_chain(rrb_snac_t h, int32_t epochs, const void *d_in, void *d_out,
+                                    rrb_snac_stats *d_stats, const uint32_t *d_stagger,
+                                    uint32_t spin_limit, rrb_stream_t stream) {
+  clear_error();
+  if (!h) return fail(RRB_EINVAL, "NULL handle");
+  if (!h->ws) return fail(RRB_EINVAL, "handle is not bound to a workspace");
+  if (epochs < 0) return fail(RRB_EINVAL, "negative epoch count");
+  if (epochs == 0) return RRB_OK;
+  if (!d_in || !d_out) return fail(RRB_EINVAL, "NULL payload pointer");
+  if ((reinterpret_cast<uintptr_t>(d_in) | reinterpret_cast<uintptr_t>(d_out)) & 15)
+    return fail(RRB_EINVAL, "payloads must be 16-byte aligned");
+  if (h->next_epoch > 0xffffffffu - static_cast<uint32_t>(epochs) - 2)
+    return fail(RRB_EUNSUPPORTED, "epoch counter exhausted; rebind the handle");
+  const int esz = elem_size(h->dtype);
+  SnacArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.in = static_cast<const unsigned char *>(d_in);
+  a.out = static_cast<unsigned char *>(d_out);
+  a.staging = h->ws + h->lay.staging_off;
+  a.flag = reinterpret_cast<uint32_t *>(h->ws + h->lay.flag_off);
+  a.done = reinterpret_cast<uint32_t *>(h->ws + h->lay.done_off);
+  a.status = reinterpret_cast<uint32_t *>(h->ws + h->lay.status_off);
+  a.stats = d_stats;
+  a.stagger = d_stagger;
+  a.count = h->count;
+  a.rank_bytes = h->count * esz;
+  a.nvec = a.rank_bytes / 16;
+  a.slice_vec = (a.nvec + h->S - 1) / h->S;
+  a.epoch0 = h->next_epoch;
+  a.epochs = epochs;
+  a.S = h->S;
+  a.spin_limit = spin_limit ? spin_limit : kDefaultSpin;
+
+  const bool bf16 = h->dtype == RRB_BF16;
+  const int var = (h->flags & RRB_SNAC_SPECULATIVE) ? kSpeculative
+                  : (h->flags & RRB_SNAC_DUAL_BUFFER) ? kDual : kBarrier;
+  SnacFn fn = nullptr;
+  if (bf16) {
+    fn = var == kBarrier ? snac_for<true, kBarrier>(h->R)
+         : var == kDual  ? snac_for<true, kDual>(h->R)
+                         : snac_for<true, kSpeculative>(h->R);
+  } else {
+    fn = var == kBarrier ? snac_for<false, kBarrier>(h->R)
+         : var == kDual  ? snac_for<false, kDual>(h->R)
+                         : snac_for<false, kSpeculative>(h->R);
+  }
+  // Every workgroup waits on others: the grid must be co-resident, which a
+  // cooperative launch guarantees (or refuses).
+  void *args[] = {&a};
+  const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(fn),
+                                                  dim3(h->R * h->S), dim3(h->bs), args, 0,
+                                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RRB_EHIP, "chain launch: %s", hipGetErrorString(e));
+  h->next_epoch += static_cast<uint32_t>(epochs);
+  return RRB_OK;
+}
+
+rrb_status rrb_snac_check(rrb_snac_t h, rrb_stream_t stream) {
+  clear_error();
+  if (!h || !h->ws) return fail(RRB_EINVAL, "NULL or unbound handle");
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  uint32_t st = 0;
+  if (e == hipSuccess)
+    e = hipMemcpy(&st, h->ws + h->lay.status_off, 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(RRB_EHIP, "status read: %s", hipGetErrorString(e));
+  if (st) return fail(RRB_ETIMEOUT, "a SNAC wait exceeded its poll budget");
+  return RRB_OK;
+}
+
+void rrb_snac_destroy(rrb_snac_t h) { delete h; }
+
+}  // extern "C"

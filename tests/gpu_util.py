@@ -1,0 +1,50 @@
+"""Helpers for the GPU parity tests: numpy <-> device, sampling, sentinels."""
+
+import numpy as np
+import torch
+
+DEV = torch.device("cuda", 0)
+
+
+def require_gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X; run them with -m gpu on the GPU box"
+
+
+def to_dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(DEV)
+    return torch.from_numpy(a).to(DEV)
+
+
+def from_dev(t):
+    a = t.detach().cpu().numpy()
+    if a.dtype == np.int16:
+        return a.view(np.uint16)
+    return a
+
+
+def empty_like_np(n, dtype, fill=None):
+    tdt = torch.int16 if dtype in ("bf16", np.uint16) else torch.float32
+    t = torch.empty(int(n), dtype=tdt, device=DEV)
+    if fill is not None:
+        t.fill_(fill)
+    return t
+
+
+def sentinel(dtype):
+    return -21555 if dtype == "bf16" else -12345.0  # 0xABCD as int16
+
+
+def assert_bits_equal(got, want, what=""):
+    got = np.asarray(got)
+    want = np.asarray(want)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    g = got.view(np.uint8)
+    w = want.view(np.uint8)
+    if not np.array_equal(g, w):
+        gi = got.view(np.uint16 if got.dtype.itemsize == 2 else np.uint32)
+        wi = want.view(np.uint16 if want.dtype.itemsize == 2 else np.uint32)
+        bad = np.nonzero(gi != wi)[0]
+        raise AssertionError(f"{what}: {len(bad)} mismatches, first at {bad[:5]}: "
+                             f"got {gi[bad[:5]]} want {wi[bad[:5]]}")

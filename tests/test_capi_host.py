@@ -1,0 +1,198 @@
+"""C ABI on the host (no GPU): the library loads, exports every symbol the
+header declares, and its plan builder produces index maps that, applied to
+buffers by a plain Python interpreter of rrb_segment, give exactly the
+oracle's collectives."""
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import collectives as C, fold, moe as OM
+from reduce_rank_buffers_amd import _lib as L
+from reduce_rank_buffers_amd import api
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "rrb.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rrb_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(librrb):
+    names = _declared()
+    assert len(names) >= 18
+    for n in names:
+        assert hasattr(librrb, n), n
+    assert set(names) == set(L.EXPORTS)
+    assert librrb.rrb_abi_version() == 1
+
+
+def _apply(segments, ins, in_count, out_count, R, dtype):
+    """Interpret a plan's index map on numpy buffers (sentinel-filled outputs)."""
+    dt = np.uint16 if dtype == "bf16" else np.float32
+    sentinel = dt(0xABCD) if dtype == "bf16" else np.float32(-12345.0)
+    outs = [np.full(int(c), sentinel, dtype=dt) for c in out_count]
+    for src_rank, so, do, ln, mask in segments:
+        if src_rank < 0:
+            val = fold.reduce([ins[r][so:so + ln] for r in range(R)], dtype)
+        else:
+            val = ins[src_rank][so:so + ln]
+        for q in range(R):
+            if mask >> q & 1:
+                outs[q][do:do + ln] = val
+    return [o if c else None for o, c in zip(outs, out_count)]
+
+
+def _payloads(R, n, dtype, seed):
+    rng = np.random.default_rng(seed)
+    if dtype == "f32":
+        return [rng.standard_normal(n).astype(np.float32) for _ in range(R)]
+    from oracle import bf16
+    return [bf16.rne(rng.standard_normal(n).astype(np.float32)) for _ in range(R)]
+
+
+ROOTS = {"broadcast": 3, "reduce": 0, "gather": 5}
+
+
+@pytest.mark.parametrize("name", list(C.SEVEN))
+@pytest.mark.parametrize("R,n", [(8, 64), (8, 8 * 37), (4, 32), (3, 12), (1, 8), (5, 40)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_plan_map_equals_oracle(librrb, name, R, n, dtype):
+    inl, outl, op = C.SEVEN[name]
+    root = ROOTS.get(name, 0) % R
+    kind = lambda l: api.ROOT(root) if isinstance(l, tuple) else getattr(api, l)
+    p = api.Plan(R, n, dtype, kind(inl), kind(outl), op)
+    segs = p.segments()
+    c = n // R
+    if name in ("all_gather", "gather"):
+        ins = _payloads(R, c, dtype, 1)
+    else:
+        ins = _payloads(R, n, dtype, 1)
+    got = _apply(segs, ins, p.in_count, p.out_count, R, dtype)
+    want = C.named(name, ins, dtype, root=root)
+    for g, w in zip(got, want):
+        if w is None:
+            assert g is None
+        else:
+            assert np.array_equal(g.view(np.uint8), np.asarray(w).view(np.uint8))
+    # sizes the plan asks for match the layouts
+    for r in range(R):
+        assert p.in_count[r] == (0 if (name == "broadcast" and r != root) else len(ins[r]))
+
+
+def test_fan_out_and_fusion_shapes(librrb):
+    R, n = 8, 8 * 1024
+    ar = api.Plan(R, n, "bf16", api.PARTIAL, api.REPLICATED, "reduce").segments()
+    assert ar == [(-1, 0, 0, n, 0xFF)]  # one segment, read once, written 8 times
+    rs = api.Plan(R, n, "bf16", api.PARTIAL, api.SHARD, "reduce").segments()
+    assert sorted(rs) == sorted((-1, q * 1024, 0, 1024, 1 << q) for q in range(R))
+    ag = api.Plan(R, n, "bf16", api.SHARD, api.REPLICATED, "copy").segments()
+    assert sorted(ag) == sorted((r, 0, r * 1024, 1024, 0xFF) for r in range(R))
+    a2a = api.Plan(R, n, "bf16", api.BLOCK_ROW, api.BLOCK_COL, "copy").segments()
+    assert len(a2a) == 64
+    bc = api.Plan(R, n, "bf16", api.ROOT(3), api.REPLICATED, "copy").segments()
+    assert bc == [(3, 0, 0, n, 0xFF)]
+
+
+def test_other_namings(librrb):
+    R, n = 4, 32
+    ins = _payloads(R, n, "bf16", 2)
+    for inl, outl, op, ol in [
+        (api.ROOT(2), api.SHARD, "copy", (C.ROOT(2), C.SHARD)),
+        (api.REPLICATED, api.SHARD, "copy", (C.REPLICATED, C.SHARD)),
+        (api.SHARD, api.SHARD, "copy", (C.SHARD, C.SHARD)),
+        (api.REPLICATED, api.ROOT(1), "copy", (C.REPLICATED, C.ROOT(1))),
+        (api.BLOCK_COL, api.BLOCK_ROW, "copy", (C.BLOCK_COL, C.BLOCK_ROW)),
+    ]:
+        p = api.Plan(R, n, "bf16", inl, outl, op)
+        src = [x if p.in_count[r] else None for r, x in enumerate(ins)]
+        src = [x[:p.in_count[r]] if x is not None else None for r, x in enumerate(src)]
+        got = _apply(p.segments(), src, p.in_count, p.out_count, R, "bf16")
+        want = C.collective(ol[0], ol[1], op, src, R, n)
+        for g, w in zip(got, want):
+            assert (g is None) == (w is None)
+            if w is not None:
+                assert np.array_equal(g, w)
+
+
+@pytest.mark.parametrize("spec,msg", [
+    ((8, 64, api.SHARD, api.REPLICATED, "reduce"), "PARTIAL input"),
+    ((8, 64, api.PARTIAL, api.REPLICATED, "copy"), "reduce op"),
+    ((8, 60, api.PARTIAL, api.SHARD, "reduce"), "count % nranks"),
+    ((8, 64, api.SHARD, api.BLOCK_COL, "copy"), "only pair"),
+    ((8, 64, api.PARTIAL, api.ROOT(9), "reduce"), "root"),
+    ((17, 64, api.PARTIAL, api.REPLICATED, "reduce"), "nranks"),
+    ((8, 64, api.REPLICATED, api.PARTIAL, "copy"), "cannot be an output"),
+    ((8, 64, api.ROOT(1), api.BLOCK_COL, "copy"), "only pair"),
+])
+def test_invalid_specs(librrb, spec, msg):
+    R, n, i, o, op = spec
+    with pytest.raises(L.RrbError) as e:
+        api.Plan(R, n, "bf16", i, o, op)
+    assert e.value.status == L.RRB_EINVAL
+    assert msg in str(e.value)
+
+
+def test_zero_count_plan(librrb):
+    p = api.Plan(8, 0, "bf16", api.PARTIAL, api.REPLICATED, "reduce")
+    assert p.in_count == [0] * 8 and p.out_count == [0] * 8
+
+
+@pytest.mark.parametrize("T,E,k,R", [(64, 32, 4, 8), (4096, 256, 8, 8), (32, 8, 8, 4)])
+def test_row_plan_sizes_match_oracle(librrb, T, E, k, R):
+    rng = np.random.default_rng(T)
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    h = 16
+    _, counts, offsets, rows = OM.layout(idx, E, R)
+    import ctypes
+    lib = L.lib()
+    for d, name in ((L.RRB_MOE_DISPATCH, "dispatch"), (L.RRB_MOE_COMBINE, "combine")):
+        hdl = ctypes.c_void_p()
+        L.check(lib.rrb_plan_create_rows(R, T, h, E, k, idx.ctypes.data, w.ctypes.data, d,
+                                         ctypes.byref(hdl)), "rows")
+        ws = ctypes.c_size_t()
+        inc = (ctypes.c_int64 * R)()
+        outc = (ctypes.c_int64 * R)()
+        L.check(lib.rrb_plan_query(hdl, ctypes.byref(ws), inc, outc), "query")
+        recv = [int(x) * h for x in rows]
+        tok = [T // R * h] * R
+        if name == "dispatch":
+            assert list(inc) == tok and list(outc) == recv
+        else:
+            assert list(inc) == recv and list(outc) == tok
+        assert ws.value >= 2 * T * k * 4
+        lib.rrb_plan_destroy(hdl)
+
+
+def test_row_plan_rejects_bad_routing(librrb):
+    import ctypes
+    lib = L.lib()
+    idx = np.array([[0, 0], [1, 2]], dtype=np.int32)
+    w = np.ones((2, 2), dtype=np.float32)
+    hdl = ctypes.c_void_p()
+    st = lib.rrb_plan_create_rows(2, 2, 8, 4, 2, idx.ctypes.data, w.ctypes.data, 0, ctypes.byref(hdl))
+    assert st == L.RRB_EINVAL and b"twice" in lib.rrb_last_error()
+    idx = np.array([[0, 7], [1, 2]], dtype=np.int32)
+    st = lib.rrb_plan_create_rows(2, 2, 8, 4, 2, idx.ctypes.data, w.ctypes.data, 0, ctypes.byref(hdl))
+    assert st == L.RRB_EINVAL and b"expert 7" in lib.rrb_last_error()
+
+
+def test_snac_create_validation(librrb):
+    import ctypes
+    lib = L.lib()
+    h = ctypes.c_void_p()
+    assert lib.rrb_snac_create(8, 4096, 0, 2, 0, ctypes.byref(h)) == L.RRB_EINVAL  # spec w/o dual
+    assert lib.rrb_snac_create(8, 4095, 0, 1, 0, ctypes.byref(h)) == L.RRB_EUNSUPPORTED
+    assert lib.rrb_snac_create(0, 4096, 0, 1, 0, ctypes.byref(h)) == L.RRB_EINVAL
+    assert lib.rrb_snac_create(8, 4096, 0, 3, 0, ctypes.byref(h)) == L.RRB_OK
+    ws = ctypes.c_size_t()
+    assert lib.rrb_snac_workspace(h, ctypes.byref(ws)) == L.RRB_OK
+    assert ws.value >= 2 * 8 * 4096 * 2
+    # unbound handle refuses to run
+    assert lib.rrb_snac_allreduce_chain(h, 1, None, None, None, None, 0, None) == L.RRB_EINVAL
+    lib.rrb_snac_destroy(h)

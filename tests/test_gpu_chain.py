@@ -1,0 +1,191 @@
+"""GPU parity of the SNAC decode chain against the oracle, through the C ABI.
+
+Each of the 64 epochs (32 layers x 2 All-Reduces) must give every rank the
+exact oracle All-Reduce of that epoch's payloads, for the barrier, dual-buffer
+and speculative variants, at every payload of the decode chain workload
+(b in 1..64 tokens x h in {4096, 8192} bf16, N(0, 0.02)).  Protocol stress:
+staggered ranks (a test hook delays rank r before every stage), the pages'
+own 100k-iteration exact-match check for the speculative variant, and a
+bounded wait forced to expire from the host (tiny poll budget), which must
+end the kernel and report RRB_ETIMEOUT rather than hang."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import chain as OC
+from reduce_rank_buffers_amd import api, inputs
+from reduce_rank_buffers_amd import _lib as L
+from tests.gpu_util import DEV, assert_bits_equal, from_dev, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = ["barrier", "dual", "speculative"]
+R = 8
+EPOCHS = 64
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _check_chain(out_dev, want, what):
+    got = from_dev(out_dev.reshape(out_dev.shape[0], R, -1))
+    for e in range(len(want)):
+        for r in range(R):
+            assert_bits_equal(got[e, r], want[e], f"{what} epoch {e} rank {r}")
+
+
+@pytest.mark.parametrize("h", [4096, 8192])
+@pytest.mark.parametrize("b", [1, 2, 4, 8, 16, 32, 64])
+def test_chain_all_variants_bit_exact(b, h):
+    require_gpu()
+    n = b * h
+    ins_np = inputs.chain(EPOCHS, R, n)
+    want = OC.allreduce_chain(ins_np)
+    inp = to_dev(ins_np)
+    for v in VARIANTS:
+        _say(f"chain b={b} h={h} variant={v}")
+        ch = api.SnacChain(R, n, "bf16", v)
+        stats = torch.zeros(4, dtype=torch.int64, device=DEV)
+        out = torch.empty_like(inp)
+        ch.run(inp, out, stats=stats)
+        ch.check()
+        _check_chain(out, want, f"{v} b={b} h={h}")
+        st = stats.cpu().tolist()
+        assert st[2] == 0  # no timeouts
+        assert st[3] == EPOCHS * R * _slices_of(ch)
+        # a second call continues the epoch counter on the same flags
+        out2 = torch.empty_like(inp)
+        ch.run(inp, out2)
+        ch.check()
+        assert torch.equal(out2, out)
+
+
+def _slices_of(ch):
+    # the stats epochs field divided by EPOCHS * R after one call gives S; the
+    # library picks S from the payload size: min(64, ceil(vectors / block))
+    nvec = ch.count * 2 // 16
+    bs = 64 if nvec <= 512 else 256
+    return min(64, (nvec + bs - 1) // bs)
+
+
+@pytest.mark.parametrize("v", VARIANTS)
+def test_chain_staggered_ranks(v):
+    """Late ranks (rank r sleeps about r x 4k cycles before each stage)."""
+    require_gpu()
+    n = 4096
+    ins_np = inputs.chain(EPOCHS, R, n, kind=77)
+    want = OC.allreduce_chain(ins_np)
+    inp = to_dev(ins_np)
+    for pattern in ("ramp", "reverse", "one_slow"):
+        if pattern == "ramp":
+            st = [r * 64 for r in range(R)]
+        elif pattern == "reverse":
+            st = [(R - 1 - r) * 64 for r in range(R)]
+        else:
+            st = [0] * R
+            st[5] = 400
+        _say(f"stagger {v} {pattern}")
+        stagger = torch.tensor(st, dtype=torch.int32, device=DEV)
+        ch = api.SnacChain(R, n, "bf16", v)
+        stats = torch.zeros(4, dtype=torch.int64, device=DEV)
+        out = torch.empty_like(inp)
+        ch.run(inp, out, stats=stats, stagger=stagger)
+        ch.check()
+        _check_chain(out, want, f"stagger {v} {pattern}")
+        s = stats.cpu().tolist()
+        if v == "speculative":
+            _say(f"  misspec {s[0]} retries {s[1]}")
+            assert s[0] > 0  # late ranks force the retry path
+
+
+@pytest.mark.parametrize("slices", [1, 3, 8])
+def test_chain_slice_counts(slices):
+    require_gpu()
+    n = 8192
+    ins_np = inputs.chain(16, R, n, kind=78)
+    want = OC.allreduce_chain(ins_np)
+    inp = to_dev(ins_np)
+    for v in VARIANTS:
+        ch = api.SnacChain(R, n, "bf16", v, slices=slices)
+        out = torch.empty_like(inp)
+        ch.run(inp, out)
+        ch.check()
+        _check_chain(out, want, f"slices={slices} {v}")
+
+
+def test_chain_other_rank_counts_and_fp32():
+    require_gpu()
+    for Rx, n, dt in [(2, 4096, "bf16"), (3, 1024, "bf16"), (16, 2048, "bf16"), (8, 2048, "f32")]:
+        E = 8
+        rng = np.random.default_rng(Rx * n)
+        if dt == "bf16":
+            ins_np = inputs.chain(E, Rx, n, kind=79)
+        else:
+            ins_np = rng.standard_normal((E, Rx, n)).astype(np.float32)
+        want = OC.allreduce_chain(ins_np, dt)
+        inp = to_dev(ins_np)
+        for v in VARIANTS:
+            _say(f"chain R={Rx} n={n} {dt} {v}")
+            ch = api.SnacChain(Rx, n, dt, v)
+            out = torch.empty_like(inp)
+            ch.run(inp, out)
+            ch.check()
+            got = from_dev(out)
+            for e in range(E):
+                for r in range(Rx):
+                    assert_bits_equal(got[e, r], want[e], f"R={Rx} {dt} {v} e={e} r={r}")
+
+
+def test_speculative_100k_iterations_exact():
+    """The pages' correctness check for speculative reduction: 100k chained
+    All-Reduces, every result bit-exact (here against precomputed oracle
+    results; payloads cycle through 256 seeded input sets)."""
+    require_gpu()
+    n, pool, per_call, total = 4096, 256, 256, 100_000
+    ins_np = inputs.chain(pool, R, n, kind=80)
+    want = np.stack(OC.allreduce_chain(ins_np))  # [pool, n]
+    inp = to_dev(ins_np)
+    want_dev = to_dev(np.repeat(want[:, None, :], R, axis=1))  # [pool, R, n]
+    ch = api.SnacChain(R, n, "bf16", "speculative")
+    stats = torch.zeros(4, dtype=torch.int64, device=DEV)
+    out = torch.empty_like(inp)
+    done = 0
+    calls = 0
+    while done < total:
+        ch.run(inp, out, stats=stats)
+        if not torch.equal(out, want_dev):
+            ch.check()
+            bad = (out != want_dev).nonzero()
+            raise AssertionError(f"speculative mismatch after {done} epochs at {bad[:5].tolist()}")
+        done += per_call
+        calls += 1
+        if calls % 100 == 0:
+            _say(f"  {done} epochs exact")
+    ch.check()
+    s = stats.cpu().tolist()
+    _say(f"100k: misspec {s[0]} retries {s[1]} epochs {done}")
+
+
+def test_bounded_wait_times_out_cleanly():
+    """A poll budget of 1 with one rank delayed: waits expire, every
+    workgroup leaves, and the host gets RRB_ETIMEOUT (no hang)."""
+    require_gpu()
+    n = 4096
+    ins_np = inputs.chain(4, R, n, kind=81)
+    inp = to_dev(ins_np)
+    st = [0] * R
+    st[7] = 20000
+    stagger = torch.tensor(st, dtype=torch.int32, device=DEV)
+    for v in ("barrier", "dual"):
+        ch = api.SnacChain(R, n, "bf16", v)
+        stats = torch.zeros(4, dtype=torch.int64, device=DEV)
+        out = torch.empty_like(inp)
+        ch.run(inp, out, stats=stats, stagger=stagger, spin_limit=1)
+        with pytest.raises(L.RrbError) as e:
+            ch.check()
+        assert e.value.status == L.RRB_ETIMEOUT
+        assert stats.cpu().tolist()[2] > 0

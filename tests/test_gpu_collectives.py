@@ -1,0 +1,208 @@
+"""GPU parity of the Atom copy / reduce kernels against the oracle, through the
+C ABI.  Bit-exact: the fixed-order reduce and every copy have exactly one
+correct bit pattern.  Workloads: the decode All-Reduce (8 x 4096 bf16), the
+bandwidth sweep (1..256 MiB per rank, All-Reduce -> Reduce-Scatter ->
+All-Gather, plus fp32 at 64 MiB), the seven layout-named collectives at 16 MiB
+per rank, and edge cases (empty, ragged tails, unaligned layouts and
+pointers, R from 1 to 16)."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import collectives as C, fold
+from reduce_rank_buffers_amd import api, inputs
+from tests.gpu_util import (DEV, assert_bits_equal, empty_like_np, from_dev, require_gpu,
+                            sentinel, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _run_and_check(name, ins_np, dtype, root=None):
+    R = len(ins_np)
+    n_in = len(ins_np[0])
+    want = C.named(name, ins_np, dtype, root=root)
+    ins = [to_dev(x) for x in ins_np]
+    outs = []
+    for w in want:
+        n_out = len(want[0]) if w is None else len(w)
+        if w is None:
+            n_out = next(len(x) for x in want if x is not None)
+        outs.append(empty_like_np(n_out, dtype, sentinel(dtype)))
+    fn = getattr(api, name if name != "reduce" else "reduce")
+    if name in ("broadcast", "reduce", "gather"):
+        fn(ins, outs, root)
+    else:
+        fn(ins, outs)
+    torch.cuda.synchronize()
+    for q, (o, w) in enumerate(zip(outs, want)):
+        g = from_dev(o)
+        if w is None:  # not written: still the sentinel
+            assert np.all(g == (np.uint16(0xABCD) if dtype == "bf16" else np.float32(-12345.0))), \
+                f"{name}: rank {q} output was written"
+        else:
+            assert_bits_equal(g, w, f"{name} rank {q}")
+
+
+def test_decode_allreduce_bit_exact():
+    require_gpu()
+    ins = inputs.decode_allreduce()
+    _say("decode all-reduce 8 x 4096 bf16")
+    _run_and_check("all_reduce", ins, "bf16")
+
+
+@pytest.mark.parametrize("S", [1, 4, 16])
+def test_sweep_small_full_compare(S):
+    require_gpu()
+    _say(f"sweep S={S} MiB: AR, RS, AG full compare")
+    ins = inputs.sweep(S)
+    _run_and_check("all_reduce", ins, "bf16")
+    _run_and_check("reduce_scatter", ins, "bf16")
+    rs = C.reduce_scatter(ins)
+    _run_and_check("all_gather", rs, "bf16")
+
+
+def _sampled_sweep(S, dtype):
+    """Full-size AR -> RS -> AG on the GPU, as the bench runs them; outputs
+    checked on sampled elements against the oracle fold of those elements,
+    plus the invariants AG(RS) == AR and identical replicas, on all bytes."""
+    R = 8
+    ins_np = inputs.sweep(S, dtype=dtype)
+    n = len(ins_np[0])
+    c = n // R
+    ins = [to_dev(x) for x in ins_np]
+    ar = [empty_like_np(n, dtype) for _ in range(R)]
+    rs = [empty_like_np(c, dtype) for _ in range(R)]
+    ag = [empty_like_np(n, dtype) for _ in range(R)]
+    api.all_reduce(ins, ar)
+    api.reduce_scatter(ins, rs)
+    api.all_gather(rs, ag)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(S)
+    idx = np.unique(np.concatenate([rng.integers(0, n, size=1 << 18), np.arange(64),
+                                    np.arange(n - 64, n), np.arange(c - 8, c + 8)]))
+    want = fold.reduce([x[idx] for x in ins_np], dtype)
+    tidx = torch.from_numpy(idx).to(DEV)
+    for q in range(R):
+        assert_bits_equal(from_dev(ar[q][tidx]), want, f"AR rank {q} sampled")
+    for q in range(R):
+        sel = (idx >= q * c) & (idx < (q + 1) * c)
+        got = from_dev(rs[q][torch.from_numpy(idx[sel] - q * c).to(DEV)])
+        assert_bits_equal(got, want[sel], f"RS rank {q} sampled")
+    for q in range(R):
+        assert torch.equal(ar[q], ar[0]), f"AR replica {q} differs"
+        assert torch.equal(ag[q], ar[0]), f"AG(RS) rank {q} differs from AR"
+
+
+@pytest.mark.parametrize("S", [64, 256])
+def test_sweep_large_sampled(S):
+    require_gpu()
+    _say(f"sweep S={S} MiB bf16 sampled")
+    _sampled_sweep(S, "bf16")
+
+
+def test_sweep_fp32_64mib():
+    require_gpu()
+    _say("sweep fp32 64 MiB sampled")
+    _sampled_sweep(64, "f32")
+
+
+ROOTS = {"broadcast": 3, "reduce": 0, "gather": 5}
+
+
+@pytest.mark.parametrize("name", list(C.SEVEN))
+def test_seven_collectives_16mib(name):
+    require_gpu()
+    _say(f"seven: {name} 16 MiB")
+    R = 8
+    n = (16 << 20) // 2
+    kind = list(C.SEVEN).index(name)
+    if name in ("all_gather", "gather"):
+        ins = inputs.rank_payloads(n // R, R, "bf16", 1.0, inputs.WL_SEVEN, kind)
+    else:
+        ins = inputs.rank_payloads(n, R, "bf16", 1.0, inputs.WL_SEVEN, kind)
+    _run_and_check(name, ins, "bf16", ROOTS.get(name))
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 16])
+@pytest.mark.parametrize("n", [0, 1, 7, 8, 37, 8 * 513 + 3, 4096])
+def test_edge_all_reduce(R, n):
+    require_gpu()
+    rng = np.random.default_rng(R * 1000 + n)
+    from oracle import bf16
+    ins = [bf16.rne(rng.standard_normal(n).astype(np.float32)) for _ in range(R)]
+    if n == 0:
+        outs = [empty_like_np(0, "bf16") for _ in range(R)]
+        api.all_reduce([to_dev(x) for x in ins], outs)
+        torch.cuda.synchronize()
+        return
+    _run_and_check("all_reduce", ins, "bf16")
+
+
+@pytest.mark.parametrize("name", list(C.SEVEN))
+@pytest.mark.parametrize("R,c", [(8, 3), (8, 129), (3, 8), (16, 16), (4, 1)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_edge_block_layouts(name, R, c, dtype):
+    """Block sizes not a multiple of 16 bytes take the element path."""
+    require_gpu()
+    root = ROOTS.get(name, 0) % R
+    n = R * c
+    rng = np.random.default_rng(R * 7 + c)
+    from oracle import bf16
+    gen = (lambda m: bf16.rne(rng.standard_normal(m).astype(np.float32))) if dtype == "bf16" \
+        else (lambda m: rng.standard_normal(m).astype(np.float32))
+    ins = [gen(c if name in ("all_gather", "gather") else n) for _ in range(R)]
+    _run_and_check(name, ins, dtype, root if name in ROOTS else None)
+
+
+def test_unaligned_pointers():
+    """Views that start one element into an allocation are not 16-byte
+    aligned; the library must still produce the exact result."""
+    require_gpu()
+    R, n = 8, 4096 + 5
+    rng = np.random.default_rng(3)
+    from oracle import bf16
+    ins_np = [bf16.rne(rng.standard_normal(n).astype(np.float32)) for _ in range(R)]
+    bases = [to_dev(np.concatenate([np.zeros(1, np.uint16), x])) for x in ins_np]
+    ins = [b[1:] for b in bases]
+    obases = [empty_like_np(n + 1, "bf16") for _ in range(R)]
+    outs = [b[1:] for b in obases]
+    api.all_reduce(ins, outs)
+    torch.cuda.synchronize()
+    want = C.all_reduce(ins_np)
+    for q in range(R):
+        assert_bits_equal(from_dev(outs[q]), want[q], f"unaligned AR rank {q}")
+
+
+def test_special_values_and_denormals():
+    require_gpu()
+    R = 8
+    vals = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x3F80, 0xBF80, 0x7F7F,
+                     0xFF7F, 0x7F00, 0x4000, 0xC000, 0x3F81, 0xBF81, 0x0100, 0x7F80, 0xFF80,
+                     0x7FC0], dtype=np.uint16)
+    rng = np.random.default_rng(4)
+    n = 8 * 4096
+    ins = [vals[rng.integers(0, len(vals), size=n)] for _ in range(R)]
+    _run_and_check("all_reduce", ins, "bf16")
+    _run_and_check("reduce_scatter", ins, "bf16")
+
+
+def test_invalid_call_arguments():
+    require_gpu()
+    p = api.Plan(8, 64, "bf16", api.PARTIAL, api.REPLICATED, "reduce")
+    from reduce_rank_buffers_amd import _lib as L
+    ins = [empty_like_np(64, "bf16") for _ in range(8)]
+    outs = [empty_like_np(64, "bf16") for _ in range(7)] + [None]
+    with pytest.raises(L.RrbError) as e:
+        p.run(ins, outs)
+    assert e.value.status == L.RRB_EINVAL
+    cp = api.Plan(8, 64, "bf16", api.SHARD, api.REPLICATED, "copy")
+    with pytest.raises(L.RrbError):
+        L.check(L.lib().rrb_reduce(cp.handle, api._ptrs(ins, 8), api._ptrs(ins, 8),
+                                   api._stream()), "rrb_reduce")
