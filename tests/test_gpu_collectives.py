@@ -25,17 +25,11 @@ def _say(*a):
 
 
 def _run_and_check(name, ins_np, dtype, root=None):
-    R = len(ins_np)
-    n_in = len(ins_np[0])
     want = C.named(name, ins_np, dtype, root=root)
     ins = [to_dev(x) for x in ins_np]
-    outs = []
-    for w in want:
-        n_out = len(want[0]) if w is None else len(w)
-        if w is None:
-            n_out = next(len(x) for x in want if x is not None)
-        outs.append(empty_like_np(n_out, dtype, sentinel(dtype)))
-    fn = getattr(api, name if name != "reduce" else "reduce")
+    n_full = next(len(x) for x in want if x is not None)
+    outs = [empty_like_np(n_full if w is None else len(w), dtype, sentinel(dtype)) for w in want]
+    fn = getattr(api, name)
     if name in ("broadcast", "reduce", "gather"):
         fn(ins, outs, root)
     else:
