@@ -175,6 +175,19 @@ def main():
         "empty_back_to_back_us": round(back_to_back_us(rrb.empty_kernel, it), 2),
     }
 
+    # ---- copy calibration: a plain 192 MiB copy through the library -------
+    # (one rank, SHARD -> SHARD): the known-size kernel that scales the HBM
+    # traffic counters, and the practical streaming ceiling next to peak.
+    cal_bytes = 192 << 20
+    cal_in = torch.empty(cal_bytes // 2, dtype=torch.int16, device=dev).fill_(7)
+    cal_out = torch.empty_like(cal_in)
+    cal_plan = rrb.Plan(1, cal_bytes // 2, "bf16", rrb.SHARD, rrb.SHARD, "copy")
+    for _ in range(3):
+        cal_plan.run([cal_in], [cal_out])
+    cal_ev = per_launch_us(lambda: cal_plan.run([cal_in], [cal_out]), 10)
+    copy_cal = {"bytes": 2 * cal_bytes, "us": round(float(np.median(cal_ev)), 2),
+                "GBps": round(2 * cal_bytes / (float(np.median(cal_ev)) * 1e-6) / 1e9, 1)}
+
     # ---- CPU oracle on a bounded sample ------------------------------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -209,15 +222,43 @@ def main():
             "peak": PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic_bytes(),
             "alg_bytes_per_launch": ar_bytes,
             "mean_launch_us": round(ar_ms * 1e3, 2),
         },
         "decode": decode,
+        "copy_calibration": copy_cal,
         "sweep": sweep,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def kernel_source_digest():
+    """sha256 over the sources that define the Atom kernels."""
+    import hashlib
+    h = hashlib.sha256()
+    base = os.path.join(os.path.dirname(os.path.abspath(__file__)), "reduce_rank_buffers_amd", "csrc")
+    for f in ("rrb_atom.hip", "rrb_kernels.h"):
+        with open(os.path.join(base, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_bytes():
+    """Counter-measured HBM bytes per launch of the roofline kernel, from the
+    committed rocprofv3 --pmc summary -- or None if the kernel sources changed
+    since those counters were taken."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        "hbm_traffic_allreduce_256mib.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return rec.get("traffic_bytes_per_launch")
 
 
 def cpu_baseline():
