@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-iters", type=int, default=2000)
+    ap.add_argument("--workload", default="sweep", choices=["sweep", "chain", "moe", "seven"],
+                    help="sweep (default) is the headline line; the others print "
+                         "their own line for the decode chain, MoE and the seven collectives")
     return ap.parse_args()
 
 
@@ -67,6 +70,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda", 0)
     rrb.lib()  # loud failure if the library is missing
+    if args.workload != "sweep":
+        {"chain": bench_chain, "moe": bench_moe, "seven": bench_seven}[args.workload](args, dev)
+        return
 
     # ---- resident inputs and outputs --------------------------------------
     cases = []  # (label, dtype, S_bytes, ins, ar_out, rs_out, ag_out)
@@ -232,6 +238,119 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def _events_ms(torch, fn, iters):
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev])
+
+
+def bench_chain(args, dev):
+    """Decode chain: 64 back-to-back All-Reduces (32 layers x 2) per call, for
+    each payload b x h and variant; reports us per All-Reduce (kernel time /
+    64) next to 64 separate Atom All-Reduce launches."""
+    import torch
+    import reduce_rank_buffers_amd as rrb
+    from reduce_rank_buffers_amd import inputs
+    E = 64
+    rows = []
+    for h in (4096, 8192):
+        for b in (1, 2, 4, 8, 16, 32, 64):
+            n = b * h
+            inp = torch.from_numpy(inputs.chain(E, R, n).view(np.int16)).to(dev)
+            out = torch.empty_like(inp)
+            res = {"b": b, "h": h, "payload_bytes": n * 2}
+            for v in ("barrier", "dual", "speculative"):
+                ch = rrb.SnacChain(R, n, "bf16", v)
+                stats = torch.zeros(4, dtype=torch.int64, device=dev)
+                for _ in range(3):
+                    ch.run(inp, out)
+                ms = _events_ms(torch, lambda: ch.run(inp, out, stats=stats), max(5, args.steps))
+                ch.check()
+                st = stats.cpu().tolist()
+                res[v] = {"us_per_allreduce": round(float(np.median(ms)) * 1e3 / E, 3),
+                          "misspec_per_call": round(st[0] / max(5, args.steps), 2)}
+            ins = [[inp[e, r] for r in range(R)] for e in range(E)]
+            outs = [[out[e, r] for r in range(R)] for e in range(E)]
+
+            def separate():
+                for e in range(E):
+                    rrb.all_reduce(ins[e], outs[e])
+            for _ in range(3):
+                separate()
+            ms = _events_ms(torch, separate, max(5, args.steps))
+            res["separate_launches"] = {"us_per_allreduce": round(float(np.median(ms)) * 1e3 / E, 3)}
+            rows.append(res)
+            log(json.dumps(res))
+    print(json.dumps({"metric": "us per All-Reduce in a 64-deep decode chain", "unit": "us",
+                      "higher_is_better": False, "workload": "decode chain, 8 ranks, b x h bf16 N(0,0.02)",
+                      "rows": rows}), flush=True)
+
+
+def bench_moe(args, dev):
+    """MoE dispatch / combine: 4096 tokens x 7168 bf16, 256 experts over 8
+    ranks, top-8."""
+    import torch
+    import reduce_rank_buffers_amd as rrb
+    from reduce_rank_buffers_amd import inputs
+    T, h, E, k = 4096, 7168, 256, 8
+    idx, w = inputs.moe_routing(T, E, k)
+    shards = inputs.moe_tokens(T, h, R)
+    xs = [torch.from_numpy(s.reshape(-1).view(np.int16)).to(dev) for s in shards]
+    disp = rrb.MoePlan(R, h, E, idx, w, "dispatch")
+    comb = rrb.MoePlan(R, h, E, idx, w, "combine")
+    recv = [torch.empty(r * h, dtype=torch.int16, device=dev) for r in disp.rows_per_rank]
+    y = [torch.empty(T // R * h, dtype=torch.int16, device=dev) for _ in range(R)]
+    for _ in range(3):
+        disp.run(xs, recv)
+        comb.run(recv, y)
+    d_ms = float(np.median(_events_ms(torch, lambda: disp.run(xs, recv), max(10, args.steps))))
+    c_ms = float(np.median(_events_ms(torch, lambda: comb.run(recv, y), max(10, args.steps))))
+    d_bytes = T * h * 2 * (1 + k)
+    c_bytes = T * h * 2 * (k + 1) + T * k * 8
+    print(json.dumps({"metric": "achieved HBM GB/s, MoE dispatch / combine", "unit": "GB/s",
+                      "workload": "MoE 4096 tokens x 7168 bf16, 256 experts over 8 ranks, top-8",
+                      "dispatch": {"us": round(d_ms * 1e3, 2), "GBps": round(d_bytes / (d_ms * 1e-3) / 1e9, 1),
+                                   "frac": round(d_bytes / (d_ms * 1e-3) / 1e9 / PEAK_GBS, 4), "bytes": d_bytes},
+                      "combine": {"us": round(c_ms * 1e3, 2), "GBps": round(c_bytes / (c_ms * 1e-3) / 1e9, 1),
+                                  "frac": round(c_bytes / (c_ms * 1e-3) / 1e9 / PEAK_GBS, 4), "bytes": c_bytes},
+                      "rows_per_rank": disp.rows_per_rank}), flush=True)
+
+
+def bench_seven(args, dev):
+    """The seven layout-named collectives at 16 MiB bf16 per rank."""
+    import torch
+    import reduce_rank_buffers_amd as rrb
+    from reduce_rank_buffers_amd import inputs
+    S = 16 << 20
+    n = S // 2
+    c = n // R
+    full = [torch.from_numpy(x.view(np.int16)).to(dev) for x in inputs.sweep(16)]
+    shards = [x[:c].clone() for x in full]
+    outs = [torch.empty(n, dtype=torch.int16, device=dev) for _ in range(R)]
+    souts = [torch.empty(c, dtype=torch.int16, device=dev) for _ in range(R)]
+    cases = {
+        "all_reduce": (lambda: rrb.all_reduce(full, outs), 2 * R * S),
+        "reduce_scatter": (lambda: rrb.reduce_scatter(full, souts), (R + 1) * S),
+        "all_gather": (lambda: rrb.all_gather(shards, outs), (R + 1) * S),
+        "all_to_all": (lambda: rrb.all_to_all(full, outs), 2 * R * S),
+        "broadcast": (lambda: rrb.broadcast(full, outs, 3), (R + 1) * S),
+        "reduce": (lambda: rrb.reduce(full, outs, 0), (R + 1) * S),
+        "gather": (lambda: rrb.gather(shards, outs, 5), 2 * S),
+    }
+    res = {}
+    for name, (fn, b) in cases.items():
+        for _ in range(3):
+            fn()
+        ms = float(np.median(_events_ms(torch, fn, max(10, args.steps))))
+        res[name] = {"us": round(ms * 1e3, 2), "GBps": round(b / (ms * 1e-3) / 1e9, 1), "bytes": b}
+    print(json.dumps({"metric": "achieved GB/s, seven collectives, 8 ranks x 16 MiB bf16 (cache-resident sizes)",
+                      "unit": "GB/s", "results": res}), flush=True)
 
 
 def kernel_source_digest():

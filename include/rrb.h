@@ -229,7 +229,10 @@ rrb_status rrb_empty_kernel(rrb_stream_t stream);
  *                              then check the reduced validation flag
  *                              (sum of the R flags == R * epoch) and retry on
  *                              mismatch (SiFAR review, Fig. 14)
- * slices: workgroups per rank (1..64; 0 = choose from count).
+ * slices: single-wave workgroups per rank (1..256; 0 = choose from count:
+ *         8 up to 64 KiB payloads, then about 16 KiB per workgroup up to 32).
+ *         The grid (nranks x slices) must be co-resident: the launch is
+ *         cooperative and fails with RRB_EHIP if it cannot be.
  */
 #define RRB_SNAC_DUAL_BUFFER 1u
 #define RRB_SNAC_SPECULATIVE 2u

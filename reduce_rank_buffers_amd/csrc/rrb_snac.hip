@@ -52,7 +52,8 @@ namespace {
 
 constexpr int kFlagStride = 32;          // u32 words: one 128-byte line per flag
 constexpr uint32_t kDefaultSpin = 1u << 21;  // polls (about 1 us each)
-constexpr int kMaxSlices = 64;
+constexpr int kMaxSlices = 256;
+constexpr int kStageU = 8;  // vectors in flight per lane in the stage copy
 
 enum Variant : int32_t { kBarrier = 0, kDual = 1, kSpeculative = 2 };
 
@@ -135,19 +136,31 @@ __device__ bool wait_at_least(const uint32_t *p, uint32_t want, uint32_t *status
 }
 
 // Threads 0..R-1 each wait for one rank's word at `base + t * stride_words`;
-// returns, in every thread of the workgroup, whether all waits succeeded.
+// then every wave takes its own agent-scope acquire (a fence in one wave does
+// not order another wave's loads: measured, sharing one fence per workgroup
+// returned stale staging data).  Returns, in every thread, whether all R
+// waits succeeded.  `ok` is an LDS array of R flags.
 template <int R>
 __device__ bool wait_all(const uint32_t *base, int64_t stride_words, uint32_t want,
-                         uint32_t *status, uint32_t limit, int *lds_ok) {
-  if (threadIdx.x == 0) *lds_ok = 1;
-  __syncthreads();
-  if (threadIdx.x < R) {
-    if (!wait_at_least(base + threadIdx.x * stride_words, want, status, limit))
-      *lds_ok = 0;
-  }
+                         uint32_t *status, uint32_t limit, int *ok) {
+  if (threadIdx.x < R)
+    ok[threadIdx.x] = wait_at_least(base + threadIdx.x * stride_words, want, status, limit) ? 1 : 0;
   __syncthreads();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return *lds_ok != 0;
+  bool all = true;
+#pragma unroll
+  for (int t = 0; t < R; ++t) all = all && ok[t] != 0;
+  return all;
+}
+
+// Publishes `ep` in *flag after every wave's earlier stores: each wave
+// releases its own stores at agent scope (write-back of L2 plus a wait for
+// its stores), then thread 0 stores the flag after the workgroup barrier.
+// Chain workgroups are a single wave, so this is one release per workgroup.
+__device__ __forceinline__ void notify(uint32_t *flag, uint32_t ep) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(flag, ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Reduce one pass of this workgroup's slice: R loads in flight per lane, fold
@@ -159,8 +172,8 @@ __device__ __forceinline__ void reduce_pass(const uint4 (&v)[R], unsigned char *
 }
 
 template <int R, bool BF16, int VAR>
-__global__ void __launch_bounds__(256) snac_chain_kernel(SnacArgs a) {
-  __shared__ int lds_ok;
+__global__ void __launch_bounds__(64) snac_chain_kernel(SnacArgs a) {
+  __shared__ int lds_ok[R];
   __shared__ int lds_valid;
   const int r = blockIdx.x / a.S;
   const int s = blockIdx.x - r * a.S;
@@ -185,15 +198,23 @@ __global__ void __launch_bounds__(256) snac_chain_kernel(SnacArgs a) {
     // Stage: this rank's slice lands in its staged buffer.
     const unsigned char *src = a.in + (static_cast<int64_t>(k) * R + r) * a.rank_bytes;
     unsigned char *mine = stage_base + static_cast<int64_t>(r) * a.rank_bytes;
-    for (int64_t i = v0 + threadIdx.x; i < v1; i += bs)
-      *reinterpret_cast<uint4 *>(mine + i * 16) = *reinterpret_cast<const uint4 *>(src + i * 16);
+    {
+      int64_t i = v0 + threadIdx.x;
+      for (; i + static_cast<int64_t>(kStageU - 1) * bs < v1; i += static_cast<int64_t>(bs) * kStageU) {
+        v4u x[kStageU];  // (HIP's uint4 struct here would be placed in scratch)
+#pragma unroll
+        for (int u = 0; u < kStageU; ++u)
+          x[u] = *reinterpret_cast<const v4u *>(src + (i + static_cast<int64_t>(u) * bs) * 16);
+#pragma unroll
+        for (int u = 0; u < kStageU; ++u)
+          *reinterpret_cast<v4u *>(mine + (i + static_cast<int64_t>(u) * bs) * 16) = x[u];
+      }
+      for (; i < v1; i += bs)
+        *reinterpret_cast<uint4 *>(mine + i * 16) = *reinterpret_cast<const uint4 *>(src + i * 16);
+    }
 
-    // Notify: every wave's stores reach device scope, then one flag store.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __syncthreads();
-    if (threadIdx.x == 0)
-      __hip_atomic_store(flags_b + r * stride_rs + s * kFlagStride, ep, __ATOMIC_RELEASE,
-                         __HIP_MEMORY_SCOPE_AGENT);
+    // Notify.
+    notify(flags_b + r * stride_rs + s * kFlagStride, ep);
 
     unsigned char *dst_base = a.out + (static_cast<int64_t>(k) * R + r) * a.rank_bytes;
     bool ok = true;
@@ -214,51 +235,63 @@ __global__ void __launch_bounds__(256) snac_chain_kernel(SnacArgs a) {
                                static_cast<int32_t>(i * 16));
       }
       // Reduced validation flag: the sum over the R sources must be R * epoch.
+      // Wave 0 holds the flags; a valid result takes the acquire there (it
+      // orders this rank's next stage after every source's earlier reads).
       if (threadIdx.x < 64) {
         uint32_t sum = threadIdx.x < R ? f : 0u;
 #pragma unroll
         for (int m = 1; m < 64; m <<= 1) sum += __shfl_xor(sum, m);
-        if (threadIdx.x == 0) lds_valid = (sum == static_cast<uint32_t>(R) * ep) ? 1 : 0;
+        if (threadIdx.x == 0) lds_valid = sum == static_cast<uint32_t>(R) * ep ? 1 : 0;
       }
       __syncthreads();
       const bool valid = lds_valid != 0;
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      // Orders this rank's next stage after every source's earlier reads.
+      if (valid) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       if (valid) {
         if (i < v1) reduce_pass<R, BF16>(v, dst_base + i * 16);
         first_pass_end = min(v1, v0 + bs);
       } else {
         ++misspec;
         ++retries;
-        ok = wait_all<R>(flags_b + s * kFlagStride, stride_rs, ep, a.status, a.spin_limit, &lds_ok);
+        ok = wait_all<R>(flags_b + s * kFlagStride, stride_rs, ep, a.status, a.spin_limit, lds_ok);
       }
     } else {
-      ok = wait_all<R>(flags_b + s * kFlagStride, stride_rs, ep, a.status, a.spin_limit, &lds_ok);
+      ok = wait_all<R>(flags_b + s * kFlagStride, stride_rs, ep, a.status, a.spin_limit, lds_ok);
     }
     if (!ok) {
       ++timeouts;
       break;
     }
 
-    // Consume: fold the R staged slices in rank order.
-    for (int64_t i = first_pass_end + threadIdx.x; i < v1; i += bs) {
-      uint4 v[R];
+    // Consume: fold the R staged slices in rank order, CU vectors x R
+    // sources in flight per lane.
+    constexpr int CU = R <= 8 ? 4 : 2;
+    for (int64_t i0 = first_pass_end + threadIdx.x; i0 < v1; i0 += static_cast<int64_t>(bs) * CU) {
+      uint4 v[CU][R];
 #pragma unroll
-      for (int q = 0; q < R; ++q)
-        v[q] = load_coherent(rsrc(stage_base + static_cast<int64_t>(q) * a.rank_bytes, a.rank_bytes),
-                             static_cast<int32_t>(i * 16));
-      reduce_pass<R, BF16>(v, dst_base + i * 16);
+      for (int u = 0; u < CU; ++u) {
+        const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+        if (i < v1) {
+#pragma unroll
+          for (int q = 0; q < R; ++q)
+            v[u][q] = load_coherent(rsrc(stage_base + static_cast<int64_t>(q) * a.rank_bytes,
+                                         a.rank_bytes),
+                                    static_cast<int32_t>(i * 16));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < CU; ++u) {
+        const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+        if (i < v1) reduce_pass<R, BF16>(v[u], dst_base + i * 16);
+      }
     }
 
     if (VAR == kBarrier) {
       // Bottom barrier: every reader of this rank's slice is done before the
       // next stage overwrites it.
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __syncthreads();
-      if (threadIdx.x == 0)
-        __hip_atomic_store(a.done + (static_cast<int64_t>(r) * a.S + s) * kFlagStride, ep,
-                           __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      notify(a.done + (static_cast<int64_t>(r) * a.S + s) * kFlagStride, ep);
       if (!wait_all<R>(a.done + static_cast<int64_t>(s) * kFlagStride, stride_rs, ep, a.status,
-                       a.spin_limit, &lds_ok)) {
+                       a.spin_limit, lds_ok)) {
         ++timeouts;
         break;
       }
@@ -335,12 +368,21 @@ rrb_status rrb_snac_create(int32_t nranks, int64_t count, int32_t dtype, uint32_
   if (slices < 0 || slices > kMaxSlices)
     return fail(RRB_EINVAL, "slices %d outside 0..%d", slices, kMaxSlices);
   const int64_t nvec = count * esz / 16;
-  int bs = nvec <= 64 * 8 ? 64 : 256;
+  // Single-wave workgroups: each wave's own release / acquire covers exactly
+  // its own accesses.  One pass (64 vectors) per workgroup where possible,
+  // up to kMaxSlices workgroups per rank.
+  const int bs = 64;
   int32_t S = slices;
   if (S == 0) {
-    // One pass per workgroup where possible, within the co-resident budget.
-    S = static_cast<int32_t>(std::min<int64_t>(kMaxSlices, (nvec + bs - 1) / bs));
-    if (S < 1) S = 1;
+    // Measured on MI355X (8 ranks): decode payloads up to 64 KiB per rank are
+    // fastest with 8 workgroups per rank (each workgroup's agent-scope fences
+    // serialise, so more of them cost more than they parallelise); larger
+    // payloads with about 1024 vectors per workgroup, up to 32 per rank.
+    if (nvec <= 4096)
+      S = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(8, nvec / 64)));
+    else
+      S = static_cast<int32_t>(std::min<int64_t>(32, std::max<int64_t>(8, nvec / 1024)));
+    S = std::min<int32_t>(S, 2048 / nranks);
   }
   if (S > nvec) S = static_cast<int32_t>(nvec);
   rrb_snac_s *h = new (std::nothrow) rrb_snac_s;

@@ -65,11 +65,10 @@ def test_chain_all_variants_bit_exact(b, h):
 
 
 def _slices_of(ch):
-    # the stats epochs field divided by EPOCHS * R after one call gives S; the
-    # library picks S from the payload size: min(64, ceil(vectors / block))
+    # the library's default slices per rank for a payload of nvec vectors
     nvec = ch.count * 2 // 16
-    bs = 64 if nvec <= 512 else 256
-    return min(64, (nvec + bs - 1) // bs)
+    S = max(1, min(8, nvec // 64)) if nvec <= 4096 else min(32, max(8, nvec // 1024))
+    return min(S, 2048 // R, nvec)
 
 
 @pytest.mark.parametrize("v", VARIANTS)
