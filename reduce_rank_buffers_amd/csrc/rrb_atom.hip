@@ -65,7 +65,18 @@ struct UniArgs {
   int64_t nelem;  // elements per item (element path)
   int32_t tiles;  // workgroups per item
   int32_t nranks;
+  int32_t xcd_chunk;  // 0, or C: XCD-chunked tile order (tiles % (8 * C) == 0)
 };
+
+// Workgroups are dealt to the 8 XCDs round-robin in blockIdx order.  With a
+// chunk C, XCD x takes runs of C consecutive tiles in turn, so each XCD
+// streams contiguous stretches of every buffer (a bijection on the item's
+// tiles when tiles % (8 * C) == 0).
+__device__ __forceinline__ int xcd_tile(int local, int C) {
+  if (C == 0) return local;
+  const int x = local & 7, k = local >> 3;
+  return (k / C) * (8 * C) + x * C + (k % C);
+}
 
 // ---- kernels ---------------------------------------------------------------
 
@@ -73,7 +84,7 @@ template <int R, int U, bool BF16, bool NTL, bool NTS>
 __global__ void __launch_bounds__(256) reduce_vec_kernel(UniArgs a) {
   const int bs = blockDim.x;
   const int item = blockIdx.x / a.tiles;
-  const int tile = blockIdx.x - item * a.tiles;
+  const int tile = xcd_tile(blockIdx.x - item * a.tiles, a.xcd_chunk);
   const KItem it = a.items[item];
   const int64_t base = static_cast<int64_t>(tile) * bs * U + threadIdx.x;
 
@@ -155,7 +166,7 @@ template <int U, bool NTS>
 __global__ void __launch_bounds__(256) copy_vec_kernel(UniArgs a) {
   const int bs = blockDim.x;
   const int item = blockIdx.x / a.tiles;
-  const int tile = blockIdx.x - item * a.tiles;
+  const int tile = xcd_tile(blockIdx.x - item * a.tiles, a.xcd_chunk);
   const KItem it = a.items[item];
   const unsigned char *src = a.in[it.src_rank] + it.src_off;
   const int64_t base = static_cast<int64_t>(tile) * bs * U + threadIdx.x;
@@ -215,8 +226,17 @@ ReduceFn reduce_vec_for(int R) {
   return nullptr;
 }
 
-// Total bytes a launch moves above which it streams past the caches.
-constexpr int64_t kStreamBytes = 512LL << 20;
+// Total bytes a launch moves above which it streams past the caches
+// (non-temporal hints).  Measured on the bandwidth sweep on MI355X: reduces
+// gain from 64 MiB up; copies only from 512 MiB up (below that, plain stores
+// leave the outputs in the Infinity Cache, which the next collective of the
+// sweep reads).
+constexpr int64_t kStreamBytesReduce = 64LL << 20;
+constexpr int64_t kStreamBytesCopy = 512LL << 20;
+// Tiles per XCD run in the chunked order of streaming launches.
+constexpr int kXcdChunk = 16;
+// Vectors per launch above which a lane handles more than one vector.
+constexpr int64_t kBigVectors = 2LL << 20;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
@@ -274,11 +294,14 @@ rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out
     const bool small = a.nvec <= 4096;
     const int64_t traffic = static_cast<int64_t>(p.segs.size()) * len * esz *
                             (reduce ? p.nranks : 1) * 2;
-    const bool stream = traffic >= kStreamBytes;
+    const bool stream = traffic >= (reduce ? kStreamBytesReduce : kStreamBytesCopy);
+    // Mid-size launches keep one vector per lane so the grid still covers
+    // every CU several times over; only very large ones unroll.
+    const bool big = static_cast<int64_t>(p.segs.size()) * a.nvec >= kBigVectors;
     bs = small ? 64 : 256;
     if (reduce) {
       const bool fan = __builtin_popcount(p.segs[0].dst_mask) > 1;
-      U = (small || p.nranks > 8) ? 1 : 2;
+      U = (small || !big || p.nranks > 8) ? 1 : 2;
       if (U == 1) {
         kern = stream ? (fan ? (bf16 ? reduce_vec_for<1, true, true, true>(p.nranks)
                                      : reduce_vec_for<1, false, true, true>(p.nranks))
@@ -295,7 +318,7 @@ rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out
                               : reduce_vec_for<2, false, false, false>(p.nranks));
       }
     } else {
-      U = (small || stream) ? 1 : 4;
+      U = (small || stream || !big) ? 1 : 4;
       kern = stream ? copy_vec_kernel<1, true> : (U == 1 ? copy_vec_kernel<1, false>
                                                           : copy_vec_kernel<4, false>);
     }
@@ -304,6 +327,7 @@ rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out
     if (tiles == 0) tiles = 1;  // tail-only item
     if (a.tail > bs) return fail(RRB_EUNSUPPORTED, "tail longer than a workgroup");
     a.tiles = static_cast<int32_t>(tiles);
+    a.xcd_chunk = (stream && tiles % (8 * kXcdChunk) == 0) ? kXcdChunk : 0;
   } else {
     bs = 256;
     U = 1;
