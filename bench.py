@@ -76,6 +76,7 @@ def main():
 
     # ---- resident inputs and outputs --------------------------------------
     cases = []  # (label, dtype, S_bytes, ins, ar_out, rs_out, ag_out)
+    host_inputs = {}  # kept for the CPU oracle leg
     t0 = time.perf_counter()
     for S in SIZES_MIB + ["fp32"]:
         dtype = "f32" if S == "fp32" else "bf16"
@@ -83,6 +84,8 @@ def main():
         host = inputs.sweep(smib, dtype=dtype)
         tdt = torch.float32 if dtype == "f32" else torch.int16
         ins = [torch.from_numpy(h.view(np.int16) if dtype == "bf16" else h).to(dev) for h in host]
+        if not args.no_cpu_baseline:
+            host_inputs[(smib, dtype)] = host
         del host
         n = ins[0].numel()
         ar = [torch.empty(n, dtype=tdt, device=dev) for _ in range(R)]
@@ -197,7 +200,7 @@ def main():
     # ---- CPU oracle on a bounded sample ------------------------------------
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline()
+        cpu = cpu_baseline(host_inputs)
 
     out = {
         "metric": METRIC,
@@ -380,27 +383,27 @@ def traffic_bytes():
     return rec.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline():
-    """The oracle, untuned, on a bounded sample: All-Reduce -> Reduce-Scatter ->
-    All-Gather of 8 ranks x 16 MiB bf16 (the sweep's 16 MiB size)."""
+def cpu_baseline(host_inputs):
+    """The oracle, untuned, on one whole step of the same workload: All-Reduce
+    -> Reduce-Scatter -> All-Gather at every sweep size (bf16 1..256 MiB and
+    fp32 64 MiB per rank), on the same host arrays the GPU received."""
     from oracle import collectives as C
-    from reduce_rank_buffers_amd import inputs
-    S = 16
-    ins = inputs.sweep(S)
     t0 = time.perf_counter()
-    C.all_reduce(ins)
-    rs = C.reduce_scatter(ins)
-    C.all_gather(rs)
+    total = 0
+    for (smib, dtype), ins in host_inputs.items():
+        C.all_reduce(ins, dtype)
+        rs = C.reduce_scatter(ins, dtype)
+        C.all_gather(rs)
+        total += sum(alg_bytes(smib << 20))
     dt = time.perf_counter() - t0
-    b = sum(alg_bytes(S << 20))
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
-    return {"value": round(b / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "host_cores_visible": cores,
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": "All-Reduce -> Reduce-Scatter -> All-Gather, 8 ranks x 16 MiB bf16 "
-                      "(numpy, single thread)"}
+    return {"value": round(total / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "host_cores_visible": cores, "kind": "oracle", "seconds": round(dt, 2),
+            "sample": "one full step: All-Reduce -> Reduce-Scatter -> All-Gather, 8 ranks x "
+                      "{1,4,16,64,256} MiB bf16 + 64 MiB fp32 (numpy, single thread)"}
 
 
 if __name__ == "__main__":

@@ -204,6 +204,73 @@ __global__ void __launch_bounds__(256) copy_elem_kernel(UniArgs a) {
     *reinterpret_cast<uint16_t *>(a.out[__builtin_ctz(m)] + it.dst_off + e * 2) = x;
 }
 
+// Decode-size single-segment launches (All-Reduce, Reduce, Broadcast of a few
+// KiB per rank): the pointers arrive already offset and the destinations as
+// a compact list, so the wave issues its loads without a table lookup or an
+// integer division first (measured 2.5 us vs 3.5 us per 8 x 8 KiB All-Reduce
+// on MI355X, against a 1.3 us empty kernel).
+struct OneArgs {
+  int32_t nvec;   // whole 16-byte vectors (>= 1)
+  int32_t ndst;   // >= 1
+  int32_t tail;   // elements (reduce) or 2-byte units (copy) after the vectors
+  int32_t pad;
+  const unsigned char *in[RRB_MAX_RANKS];  // reduce: rank r's source; copy: [0]
+  unsigned char *out[RRB_MAX_RANKS];       // the ndst destinations
+};
+
+constexpr int kOneBlock = 64;
+
+// The lane index is clamped instead of branched on, and the first store is
+// unconditional, so the compiler issues every source load as soon as the
+// kernel arguments arrive (one scalar round trip instead of three).  Lanes
+// past the end repeat the last vector's work and store the same bits.
+// ALL: every rank is a destination (ndst == R), so the stores unroll with
+// all destination pointers fetched up front.
+template <int R, bool BF16, bool ALL>
+__global__ void __launch_bounds__(kOneBlock) reduce_one_kernel(OneArgs a) {
+  const int i = min(static_cast<int>(blockIdx.x) * kOneBlock + static_cast<int>(threadIdx.x),
+                    a.nvec - 1);
+  uint4 v[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) v[r] = *reinterpret_cast<const uint4 *>(a.in[r] + static_cast<int64_t>(i) * 16);
+  const uint4 res = BF16 ? fold_bf16x8<R>(v) : fold_f32x4<R>(v);
+  if (ALL) {
+#pragma unroll
+    for (int q = 0; q < R; ++q) *reinterpret_cast<uint4 *>(a.out[q] + static_cast<int64_t>(i) * 16) = res;
+  } else {
+    *reinterpret_cast<uint4 *>(a.out[0] + static_cast<int64_t>(i) * 16) = res;
+    for (int q = 1; q < a.ndst; ++q) *reinterpret_cast<uint4 *>(a.out[q] + static_cast<int64_t>(i) * 16) = res;
+  }
+  if (a.tail && blockIdx.x == gridDim.x - 1 && static_cast<int>(threadIdx.x) < a.tail) {
+    const int64_t e = static_cast<int64_t>(a.nvec) * (BF16 ? 8 : 4) + threadIdx.x;
+    if (BF16) {
+      float acc = bf16_to_f32(*reinterpret_cast<const uint16_t *>(a.in[0] + e * 2));
+#pragma unroll
+      for (int r = 1; r < R; ++r) acc = acc + bf16_to_f32(*reinterpret_cast<const uint16_t *>(a.in[r] + e * 2));
+      const uint16_t b = f32_to_bf16_rne(acc);
+      for (int q = 0; q < a.ndst; ++q) *reinterpret_cast<uint16_t *>(a.out[q] + e * 2) = b;
+    } else {
+      float acc = *reinterpret_cast<const float *>(a.in[0] + e * 4);
+#pragma unroll
+      for (int r = 1; r < R; ++r) acc = acc + *reinterpret_cast<const float *>(a.in[r] + e * 4);
+      for (int q = 0; q < a.ndst; ++q) *reinterpret_cast<float *>(a.out[q] + e * 4) = acc;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kOneBlock) copy_one_kernel(OneArgs a) {
+  const int i = min(static_cast<int>(blockIdx.x) * kOneBlock + static_cast<int>(threadIdx.x),
+                    a.nvec - 1);
+  const uint4 x = *reinterpret_cast<const uint4 *>(a.in[0] + static_cast<int64_t>(i) * 16);
+  *reinterpret_cast<uint4 *>(a.out[0] + static_cast<int64_t>(i) * 16) = x;
+  for (int q = 1; q < a.ndst; ++q) *reinterpret_cast<uint4 *>(a.out[q] + static_cast<int64_t>(i) * 16) = x;
+  if (a.tail && blockIdx.x == gridDim.x - 1 && static_cast<int>(threadIdx.x) < a.tail) {
+    const int64_t off = static_cast<int64_t>(a.nvec) * 16 + threadIdx.x * 2;
+    const uint16_t y = *reinterpret_cast<const uint16_t *>(a.in[0] + off);
+    for (int q = 0; q < a.ndst; ++q) *reinterpret_cast<uint16_t *>(a.out[q] + off) = y;
+  }
+}
+
 __global__ void empty_kernel() {}
 
 // ---- launchers -------------------------------------------------------------
@@ -256,6 +323,54 @@ rrb_status check_buffers(const Plan &p, const void *const *in, void *const *out)
   return RRB_OK;
 }
 
+using OneFn = void (*)(OneArgs);
+
+template <bool BF16, bool ALL>
+OneFn reduce_one_for(int R) {
+  switch (R) {
+#define RRB_CASE(n) \
+  case n:           \
+    return reduce_one_kernel<n, BF16, ALL>;
+    RRB_CASE(1) RRB_CASE(2) RRB_CASE(3) RRB_CASE(4) RRB_CASE(5) RRB_CASE(6) RRB_CASE(7)
+    RRB_CASE(8) RRB_CASE(9) RRB_CASE(10) RRB_CASE(11) RRB_CASE(12) RRB_CASE(13)
+    RRB_CASE(14) RRB_CASE(15) RRB_CASE(16)
+#undef RRB_CASE
+  }
+  return nullptr;
+}
+
+// Single aligned segment of at most kOneMaxVectors vectors: the decode path.
+constexpr int64_t kOneMaxVectors = 4096;
+
+rrb_status launch_one(const Plan &p, const void *const *in, void *const *out, hipStream_t stream) {
+  const int esz = elem_size(p.dtype);
+  const Segment &sg = p.segs[0];
+  const bool reduce = p.op == RRB_REDUCE_SUM;
+  OneArgs a;
+  std::memset(&a, 0, sizeof a);
+  if (reduce) {
+    for (int32_t r = 0; r < p.nranks; ++r)
+      a.in[r] = static_cast<const unsigned char *>(in[r]) + sg.src_off * esz;
+  } else {
+    a.in[0] = static_cast<const unsigned char *>(in[sg.src_rank]) + sg.src_off * esz;
+  }
+  for (int32_t q = 0; q < p.nranks; ++q)
+    if (sg.dst_mask >> q & 1u) a.out[a.ndst++] = static_cast<unsigned char *>(out[q]) + sg.dst_off * esz;
+  a.nvec = static_cast<int32_t>(sg.len * esz / 16);
+  a.tail = reduce ? static_cast<int32_t>(sg.len - static_cast<int64_t>(a.nvec) * (16 / esz))
+                  : static_cast<int32_t>((sg.len * esz - static_cast<int64_t>(a.nvec) * 16) / 2);
+  const unsigned grid = static_cast<unsigned>((a.nvec + kOneBlock - 1) / kOneBlock);
+  const bool all = a.ndst == p.nranks;
+  const bool bf16 = p.dtype == RRB_BF16;
+  OneFn kern = reduce ? (all ? (bf16 ? reduce_one_for<true, true>(p.nranks)
+                                     : reduce_one_for<false, true>(p.nranks))
+                             : (bf16 ? reduce_one_for<true, false>(p.nranks)
+                                     : reduce_one_for<false, false>(p.nranks)))
+                      : copy_one_kernel;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kOneBlock), 0, stream, a);
+  return check_launch(reduce ? "reduce" : "copy");
+}
+
 rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out,
                           hipStream_t stream) {
   const int esz = elem_size(p.dtype);
@@ -269,6 +384,9 @@ rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out
   }
   for (const Segment &s : p.segs)
     if ((s.src_off * esz) % 16 || (s.dst_off * esz) % 16) vec = false;
+  if (vec && p.segs.size() == 1 && (len * esz) / 16 >= 1 && (len * esz) / 16 <= kOneMaxVectors &&
+      p.segs[0].dst_mask != 0)
+    return launch_one(p, in, out, stream);
 
   UniArgs a;
   std::memset(&a, 0, sizeof a);
