@@ -174,7 +174,12 @@ def main():
     it = args.decode_iters
     ar_ev = per_launch_us(lambda: rrb.all_reduce(dins, douts), it)
     em_ev = per_launch_us(rrb.empty_kernel, it)
+    g_ar = graph_us_per_launch(torch, lambda: rrb.all_reduce(dins, douts))
+    g_em = graph_us_per_launch(torch, rrb.empty_kernel)
     decode = {
+        "allreduce_graph_us": round(g_ar, 3),
+        "empty_kernel_graph_us": round(g_em, 3),
+        "graph_note": "64 launches captured in one HIP graph, replayed; us per launch",
         "workload": "All-Reduce, 8 ranks x 4096 bf16 (TP=8 batch-1 decode, hidden 4096)",
         "allreduce_event_us_p50": round(float(np.median(ar_ev)), 2),
         "allreduce_event_us_p10": round(float(np.percentile(ar_ev, 10)), 2),
@@ -243,6 +248,33 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def graph_us_per_launch(torch, fn, per_graph=64, replays=50):
+    """Capture `per_graph` back-to-back launches of fn in one HIP graph (on a
+    side stream, as torch requires), replay it, and return us per launch."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            fn()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (replays * per_graph)
+
+
 def _events_ms(torch, fn, iters):
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
     for a, b in ev:
@@ -288,6 +320,8 @@ def bench_chain(args, dev):
                 separate()
             ms = _events_ms(torch, separate, max(5, args.steps))
             res["separate_launches"] = {"us_per_allreduce": round(float(np.median(ms)) * 1e3 / E, 3)}
+            res["separate_launches_graph"] = {
+                "us_per_allreduce": round(graph_us_per_launch(torch, separate, per_graph=1, replays=20) / E, 3)}
             rows.append(res)
             log(json.dumps(res))
     print(json.dumps({"metric": "us per All-Reduce in a 64-deep decode chain", "unit": "us",

@@ -200,3 +200,37 @@ def test_invalid_call_arguments():
     with pytest.raises(L.RrbError):
         L.check(L.lib().rrb_reduce(cp.handle, api._ptrs(ins, 8), api._ptrs(ins, 8),
                                    api._stream()), "rrb_reduce")
+
+
+def test_graph_capture_replays_match_eager():
+    """Atom launches captured in a HIP graph (torch.cuda.CUDAGraph over the
+    library's stream argument) replay correctly several times, with eager
+    input updates and synchronisations between replays."""
+    require_gpu()
+    R, n = 8, 4096
+    sets = [inputs.rank_payloads(n, R, "bf16", 1.0, inputs.WL_DECODE, 10 + k) for k in range(3)]
+    ins = [to_dev(x) for x in sets[0]]
+    outs = [empty_like_np(n, "bf16") for _ in range(R)]
+    rs = [empty_like_np(n // R, "bf16") for _ in range(R)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        api.all_reduce(ins, outs)
+        api.reduce_scatter(ins, rs)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        api.all_reduce(ins, outs)
+        api.reduce_scatter(ins, rs)
+    for k in range(3):
+        for r in range(R):
+            ins[r].copy_(to_dev(sets[k][r]))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = C.all_reduce(sets[k])
+        want_rs = C.reduce_scatter(sets[k])
+        for q in range(R):
+            assert_bits_equal(from_dev(outs[q]), want[q], f"graph replay {k} AR rank {q}")
+            assert_bits_equal(from_dev(rs[q]), want_rs[q], f"graph replay {k} RS rank {q}")
