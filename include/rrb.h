@@ -161,6 +161,38 @@ rrb_status rrb_plan_create_rows(int32_t nranks, int64_t tokens, int64_t hidden,
                                 int32_t dir, rrb_plan_t *out);
 
 /*
+ * Row-map plan whose maps are built on the device from device routing arrays
+ * (per step, with no host round trip): same layout rules as
+ * rrb_plan_create_rows, except that the receive side is ONE arena of exactly
+ * tokens*topk rows -- rank r's rows (its experts in ascending id, tokens
+ * ascending within an expert) start at arena row rank_offsets[r] -- passed as
+ * pointer 0 of the receive-side array (dispatch: d_out[0]; combine: d_in[0];
+ * other ranks' entries are unused).  Limits: experts <= 1024, topk <= 16,
+ * tokens*topk < 2^26 (RRB_EUNSUPPORTED otherwise).  Bind a workspace with
+ * rrb_plan_bind (it clears the maps: every slot is arena row 0 until routed);
+ * a dispatch and a combine plan of the same shape may share one workspace.
+ */
+rrb_status rrb_plan_create_rows_device(int32_t nranks, int64_t tokens, int64_t hidden,
+                                       int32_t experts, int32_t topk, int32_t dir,
+                                       rrb_plan_t *out);
+
+/*
+ * Build a device row plan's maps on `stream` from d_topk_idx[tokens][topk]
+ * (int32) and d_topk_w[tokens][topk] (float32), device arrays: expert
+ * histogram, prefix offsets and the per-token slot list in ascending expert
+ * id.  d_rank_offsets (nullable, nranks+1 int32, device) receives the arena
+ * row where each rank's region starts, then tokens*topk.  Out-of-range or
+ * repeated experts are skipped (their slots point at arena row 0, weight 0)
+ * and recorded for rrb_moe_route_check.  Asynchronous; deterministic.
+ */
+rrb_status rrb_moe_route(rrb_plan_t plan, const int32_t *d_topk_idx, const float *d_topk_w,
+                         int32_t *d_rank_offsets, rrb_stream_t stream);
+
+/* Synchronise `stream` and report RRB_EINVAL if the last rrb_moe_route on
+ * this plan's workspace saw an out-of-range or repeated expert. */
+rrb_status rrb_moe_route_check(rrb_plan_t plan, rrb_stream_t stream);
+
+/*
  * Sizes a plan needs.  *workspace_bytes: device workspace to pass to
  * rrb_plan_bind (0 if none).  in_count[R], out_count[R] (host arrays of
  * nranks entries, either may be NULL): elements each rank's input / output

@@ -36,7 +36,8 @@ RRB_MAX_RANKS = 16
 # Every symbol include/rrb.h declares.
 EXPORTS = (
     "rrb_status_string", "rrb_last_error", "rrb_abi_version",
-    "rrb_plan_create", "rrb_plan_create_rows", "rrb_plan_query", "rrb_plan_bind",
+    "rrb_plan_create", "rrb_plan_create_rows", "rrb_plan_create_rows_device", "rrb_moe_route",
+    "rrb_moe_route_check", "rrb_plan_query", "rrb_plan_bind",
     "rrb_plan_segments", "rrb_plan_destroy",
     "rrb_copy", "rrb_reduce", "rrb_empty_kernel",
     "rrb_snac_create", "rrb_snac_workspace", "rrb_snac_bind", "rrb_snac_allreduce_chain",
@@ -84,6 +85,9 @@ _SIGS = {
     "rrb_abi_version": (_I32, []),
     "rrb_plan_create": (_I32, [ctypes.POINTER(Spec), ctypes.POINTER(_P)]),
     "rrb_plan_create_rows": (_I32, [_I32, _I64, _I64, _I32, _I32, _P, _P, _I32, ctypes.POINTER(_P)]),
+    "rrb_plan_create_rows_device": (_I32, [_I32, _I64, _I64, _I32, _I32, _I32, ctypes.POINTER(_P)]),
+    "rrb_moe_route": (_I32, [_P, _P, _P, _P, _P]),
+    "rrb_moe_route_check": (_I32, [_P, _P]),
     "rrb_plan_query": (_I32, [_P, ctypes.POINTER(_SZ), _P, _P]),
     "rrb_plan_bind": (_I32, [_P, _P, _SZ, _P]),
     "rrb_plan_segments": (_I32, [_P, ctypes.POINTER(Segment), _I32, ctypes.POINTER(_I32)]),

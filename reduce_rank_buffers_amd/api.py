@@ -200,6 +200,48 @@ class MoePlan(Plan):
         self.bind(device)
 
 
+class MoeDevicePlan(Plan):
+    """Row-map plan whose maps are built on the GPU by route() each step.
+
+    The receive side is one arena of tokens*topk rows (rank regions back to
+    back); pass it as element 0 of the receive-side tensor list.  A combine
+    plan can share the dispatch plan's workspace (share=dispatch_plan), so one
+    route() serves both.
+    """
+
+    def __init__(self, nranks, tokens, hidden, experts, topk, direction, share=None, device=None):
+        self._lib = L.lib()
+        h = ctypes.c_void_p()
+        d = L.RRB_MOE_DISPATCH if direction == "dispatch" else L.RRB_MOE_COMBINE
+        L.check(self._lib.rrb_plan_create_rows_device(int(nranks), int(tokens), int(hidden),
+                                                      int(experts), int(topk), d, ctypes.byref(h)),
+                "rrb_plan_create_rows_device")
+        self.handle = h
+        self.nranks = int(nranks)
+        self.op = L.RRB_COPY if d == L.RRB_MOE_DISPATCH else L.RRB_REDUCE_SUM
+        self.dtype = L.RRB_BF16
+        self.tokens, self.hidden, self.experts, self.topk = int(tokens), int(hidden), int(experts), int(topk)
+        self._ws = None
+        self._query()
+        if share is not None:
+            self._ws = share._ws
+            base = (self._ws.data_ptr() + 255) // 256 * 256
+            L.check(self._lib.rrb_plan_bind(self.handle, ctypes.c_void_p(base), self.workspace_bytes,
+                                            _stream()), "rrb_plan_bind")
+        else:
+            self.bind(device)
+
+    def route(self, topk_idx, topk_w, rank_offsets=None, stream=None):
+        """topk_idx int32 [T, k], topk_w float32 [T, k]: device tensors."""
+        L.check(self._lib.rrb_moe_route(
+            self.handle, ctypes.c_void_p(topk_idx.data_ptr()), ctypes.c_void_p(topk_w.data_ptr()),
+            ctypes.c_void_p(rank_offsets.data_ptr() if rank_offsets is not None else 0),
+            _stream(stream)), "rrb_moe_route")
+
+    def check(self, stream=None):
+        L.check(self._lib.rrb_moe_route_check(self.handle, _stream(stream)), "rrb_moe_route_check")
+
+
 # ---- SNAC chain -------------------------------------------------------------
 
 VARIANTS = {"barrier": 0, "dual": L.RRB_SNAC_DUAL_BUFFER,

@@ -490,7 +490,7 @@ rrb_status rrb_copy(rrb_plan_t plan, const void *const *d_in, void *const *d_out
   if (p.op != RRB_COPY) return fail(RRB_EINVAL, "rrb_copy needs a copy plan");
   rrb_status s = check_buffers(p, d_in, d_out);
   if (s != RRB_OK) return s;
-  if (p.kind == PlanKind::Rows) return launch_rows(p, d_in, d_out, stream);
+  if (p.kind != PlanKind::Uniform) return launch_rows(p, d_in, d_out, stream);
   return launch_uniform(p, d_in, d_out, static_cast<hipStream_t>(stream));
 }
 
@@ -502,7 +502,7 @@ rrb_status rrb_reduce(rrb_plan_t plan, const void *const *d_in, void *const *d_o
   if (p.op != RRB_REDUCE_SUM) return fail(RRB_EINVAL, "rrb_reduce needs a reduce plan");
   rrb_status s = check_buffers(p, d_in, d_out);
   if (s != RRB_OK) return s;
-  if (p.kind == PlanKind::Rows) return launch_rows(p, d_in, d_out, stream);
+  if (p.kind != PlanKind::Uniform) return launch_rows(p, d_in, d_out, stream);
   return launch_uniform(p, d_in, d_out, static_cast<hipStream_t>(stream));
 }
 

@@ -87,6 +87,49 @@ rrb_status rrb_plan_create_rows(int32_t nranks, int64_t tokens, int64_t hidden,
   return RRB_OK;
 }
 
+rrb_status rrb_plan_create_rows_device(int32_t nranks, int64_t tokens, int64_t hidden,
+                                       int32_t experts, int32_t topk, int32_t dir,
+                                       rrb_plan_t *out) {
+  clear_error();
+  if (!out) return fail(RRB_EINVAL, "NULL out");
+  *out = nullptr;
+  rrb_plan_s *p = new (std::nothrow) rrb_plan_s;
+  if (!p) return fail(RRB_ENOMEM, "plan allocation failed");
+  const rrb_status s = build_row_plan_device(nranks, tokens, hidden, experts, topk, dir, p->p);
+  if (s != RRB_OK) {
+    delete p;
+    return s;
+  }
+  *out = p;
+  return RRB_OK;
+}
+
+rrb_status rrb_moe_route(rrb_plan_t plan, const int32_t *d_topk_idx, const float *d_topk_w,
+                         int32_t *d_rank_offsets, rrb_stream_t stream) {
+  clear_error();
+  if (!plan) return fail(RRB_EINVAL, "NULL plan");
+  Plan &p = plan->p;
+  if (p.kind != PlanKind::RowsDevice) return fail(RRB_EINVAL, "rrb_moe_route needs a device row plan");
+  if (!p.d_ws) return fail(RRB_EINVAL, "plan is not bound to a workspace");
+  if (p.rows.tokens > 0 && (!d_topk_idx || !d_topk_w)) return fail(RRB_EINVAL, "NULL routing arrays");
+  return launch_route(p, d_topk_idx, d_topk_w, d_rank_offsets, stream);
+}
+
+rrb_status rrb_moe_route_check(rrb_plan_t plan, rrb_stream_t stream) {
+  clear_error();
+  if (!plan) return fail(RRB_EINVAL, "NULL plan");
+  const Plan &p = plan->p;
+  if (p.kind != PlanKind::RowsDevice || !p.d_ws) return fail(RRB_EINVAL, "not a bound device row plan");
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  int32_t st = 0;
+  if (e == hipSuccess)
+    e = hipMemcpy(&st, static_cast<const char *>(p.d_ws) + p.rows.off_status, 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(RRB_EHIP, "route status read: %s", hipGetErrorString(e));
+  if (st & 1) return fail(RRB_EINVAL, "routing names an expert outside 0..experts-1");
+  if (st & 2) return fail(RRB_EINVAL, "routing selects an expert twice for one token");
+  return RRB_OK;
+}
+
 rrb_status rrb_plan_query(rrb_plan_t plan, size_t *workspace_bytes, int64_t *in_count,
                           int64_t *out_count) {
   clear_error();
@@ -109,6 +152,12 @@ rrb_status rrb_plan_bind(rrb_plan_t plan, void *d_workspace, size_t bytes, rrb_s
     return fail(RRB_EINVAL, "workspace of %zu bytes needed", p.ws_bytes);
   if (reinterpret_cast<uintptr_t>(d_workspace) % 256)
     return fail(RRB_EINVAL, "workspace must be 256-byte aligned");
+  if (p.kind == PlanKind::RowsDevice) {
+    // Maps are written by rrb_moe_route on the device; until then every slot
+    // is row 0 of the arena (in bounds).
+    p.d_ws = d_workspace;
+    return clear_route_maps(p, stream);
+  }
   const RowMaps &m = p.rows;
   const size_t n = m.slot.size();
   const size_t slot_bytes = ((n * 4 + 255) / 256) * 256;

@@ -27,7 +27,7 @@ struct Segment {
   uint32_t dst_mask;
 };
 
-enum class PlanKind { Uniform, Rows };
+enum class PlanKind { Uniform, Rows, RowsDevice };
 
 // Row maps of an expert-parallel plan, as uploaded to the device.
 // Entry (t, i), i < topk, is token t's i-th expert in ascending expert id:
@@ -39,7 +39,19 @@ struct RowMaps {
   std::vector<int32_t> slot;    // [T*k] packed (rank << 26) | row
   std::vector<float> weight;    // [T*k]
   std::vector<int64_t> rows_per_rank;
+  // Device-routed plans: byte offsets of the maps inside the workspace.
+  int64_t nblk = 0;             // token blocks of kRouteBlock tokens
+  size_t off_slot = 0, off_weight = 0, off_counts = 0, off_expert = 0, off_rank = 0,
+         off_bcounts = 0, off_bbase = 0, off_status = 0;
 };
+
+// Tokens per block of the device-side routing kernels.
+constexpr int kRouteBlock = 256;
+// Largest expert count the device-side routing supports (one 256-bit token
+// mask per expert in LDS).
+constexpr int kRouteMaxExperts = 1024;
+// Largest top-k the device-side routing supports.
+constexpr int kRouteMaxTopk = 16;
 
 struct Plan {
   PlanKind kind = PlanKind::Uniform;
@@ -60,6 +72,17 @@ rrb_status build_uniform_plan(const rrb_spec &spec, Plan &plan);
 rrb_status build_row_plan(int32_t nranks, int64_t tokens, int64_t hidden,
                           int32_t experts, int32_t topk, const int32_t *idx,
                           const float *w, int32_t dir, Plan &plan);
+
+// Builds a MoE row plan whose maps are computed on the device (rrb_plan.cpp).
+rrb_status build_row_plan_device(int32_t nranks, int64_t tokens, int64_t hidden,
+                                 int32_t experts, int32_t topk, int32_t dir, Plan &plan);
+// Enqueues the device-side routing kernels of a device row plan (rrb_moe.hip).
+rrb_status launch_route(Plan &plan, const int32_t *d_idx, const float *d_w,
+                        int32_t *d_rank_offsets, void *stream);
+
+// Zero-fills a device row plan's slot map and status word on `stream`, so a
+// copy or reduce before the first rrb_moe_route stays in bounds (rrb_moe.hip).
+rrb_status clear_route_maps(const Plan &plan, void *stream);
 
 // Launches a MoE row plan (rrb_moe.hip).  `stream` is a hipStream_t.
 rrb_status launch_rows(const Plan &plan, const void *const *in, void *const *out,

@@ -183,6 +183,234 @@ __global__ void __launch_bounds__(256) moe_combine_elem_kernel(RowArgs a) {
   }
 }
 
+
+// ---- device-side routing maps ----------------------------------------------
+//
+// Builds, on the GPU, the same maps rrb_plan_create_rows builds on the host:
+// per-expert token counts, expert offsets in the expert-major receive arena,
+// and for every (token, i) the arena row of the token's i-th expert in
+// ascending id (tokens ascending within an expert) plus its weight.  Three
+// kernels, all deterministic:
+//   count: per block of kRouteBlock tokens, an LDS histogram of experts;
+//   scan:  per expert, exclusive prefix over blocks; exclusive prefix of the
+//          totals over experts; rank offsets (ranks hold contiguous experts);
+//   slot:  per block, a kRouteBlock-bit token mask per expert in LDS; a
+//          token's position within its expert is the block base plus the
+//          popcount of the mask bits below it.
+
+struct RouteArgs {
+  const int32_t *idx;     // [T][k]
+  const float *w;         // [T][k]
+  int32_t *slot;          // [T][k] arena row, ascending expert per token
+  float *weight;          // [T][k]
+  int32_t *rank_off;      // [R + 1]
+  int32_t *bcounts;       // [nblk][E]
+  int32_t *bbase;         // [nblk][E]
+  int32_t *status;        // bit 0: expert out of range, bit 1: repeated expert
+  int32_t *user_rank_off; // optional copy of rank_off
+  int32_t *expert_off;    // [E]
+  int32_t *counts;        // [E]
+  int64_t T;
+  int32_t E, k, R, per, nblk;
+};
+
+__global__ void moe_fill_kernel(int32_t *p, int64_t n, int32_t v) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = v;
+}
+
+__global__ void __launch_bounds__(kRouteBlock) moe_route_count_kernel(RouteArgs a) {
+  __shared__ int32_t hist[kRouteMaxExperts];
+  for (int e = threadIdx.x; e < a.E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kRouteBlock + threadIdx.x;
+  if (t < a.T) {
+    const int32_t *row = a.idx + t * a.k;
+    for (int j = 0; j < a.k; ++j) {
+      const int32_t e = row[j];
+      if (e < 0 || e >= a.E) {
+        atomicOr(a.status, 1);
+        continue;
+      }
+      bool dup = false;
+      for (int j2 = 0; j2 < j; ++j2) dup = dup || row[j2] == e;
+      if (dup) {
+        atomicOr(a.status, 2);
+        continue;
+      }
+      atomicAdd(&hist[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < a.E; e += blockDim.x)
+    a.bcounts[static_cast<int64_t>(blockIdx.x) * a.E + e] = hist[e];
+}
+
+constexpr int kScanThreads = 1024;
+
+__global__ void __launch_bounds__(kScanThreads) moe_route_scan_kernel(RouteArgs a) {
+  __shared__ int32_t tot[kScanThreads];
+  const int e = threadIdx.x;
+  int32_t run = 0;
+  if (e < a.E) {
+    for (int b = 0; b < a.nblk; ++b) {
+      const int64_t o = static_cast<int64_t>(b) * a.E + e;
+      a.bbase[o] = run;
+      run += a.bcounts[o];
+    }
+    a.counts[e] = run;
+  }
+  tot[e] = e < a.E ? run : 0;
+  __syncthreads();
+  // Inclusive scan over experts (Hillis-Steele), then shift to exclusive.
+  for (int d = 1; d < kScanThreads; d <<= 1) {
+    const int32_t add = e >= d ? tot[e - d] : 0;
+    __syncthreads();
+    tot[e] += add;
+    __syncthreads();
+  }
+  if (e < a.E) a.expert_off[e] = tot[e] - run;
+  __syncthreads();
+  if (e <= a.R) {
+    const int32_t v = e < a.R ? (e * a.per == 0 ? 0 : tot[e * a.per - 1]) : tot[a.E - 1];
+    a.rank_off[e] = v;
+    if (a.user_rank_off) a.user_rank_off[e] = v;
+  }
+}
+
+template <int K>
+__global__ void __launch_bounds__(kRouteBlock) moe_route_slot_kernel(RouteArgs a) {
+  constexpr int W = kRouteBlock / 32;
+  __shared__ uint32_t mask[kRouteMaxExperts * W];
+  for (int i = threadIdx.x; i < a.E * W; i += blockDim.x) mask[i] = 0;
+  __syncthreads();
+  const int local = threadIdx.x;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kRouteBlock + local;
+  int32_t e[K];
+  float w[K];
+  bool ok[K];
+  const bool live = t < a.T;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    e[j] = live ? a.idx[t * K + j] : 0;
+    w[j] = live ? a.w[t * K + j] : 0.f;
+    ok[j] = live && e[j] >= 0 && e[j] < a.E;
+#pragma unroll
+    for (int j2 = 0; j2 < j; ++j2) ok[j] = ok[j] && e[j2] != e[j];
+    if (ok[j]) atomicOr(&mask[e[j] * W + (local >> 5)], 1u << (local & 31));
+  }
+  __syncthreads();
+  if (!live) return;
+  // Ascending expert id (bubble sort over registers; K is small and static).
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+#pragma unroll
+    for (int j = 0; j + 1 < K - i; ++j) {
+      if (e[j] > e[j + 1]) {
+        const int32_t te = e[j]; e[j] = e[j + 1]; e[j + 1] = te;
+        const float tw = w[j]; w[j] = w[j + 1]; w[j + 1] = tw;
+        const bool to = ok[j]; ok[j] = ok[j + 1]; ok[j + 1] = to;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    int32_t row = 0;
+    float wt = 0.f;
+    if (ok[j]) {
+      const uint32_t *m = mask + e[j] * W;
+      int pos = 0;
+      for (int q = 0; q < (local >> 5); ++q) pos += __popc(m[q]);
+      pos += __popc(m[local >> 5] & ((1u << (local & 31)) - 1u));
+      row = a.expert_off[e[j]] + a.bbase[static_cast<int64_t>(blockIdx.x) * a.E + e[j]] + pos;
+      wt = w[j];
+    }
+    a.slot[t * K + j] = row;
+    a.weight[t * K + j] = wt;
+  }
+}
+
+namespace {
+
+using RouteFn = void (*)(RouteArgs);
+
+RouteFn route_slot_for(int k) {
+  switch (k) {
+#define RRB_CASE(n) \
+  case n:           \
+    return moe_route_slot_kernel<n>;
+    RRB_CASE(1) RRB_CASE(2) RRB_CASE(3) RRB_CASE(4) RRB_CASE(5) RRB_CASE(6) RRB_CASE(7)
+    RRB_CASE(8) RRB_CASE(9) RRB_CASE(10) RRB_CASE(11) RRB_CASE(12) RRB_CASE(13)
+    RRB_CASE(14) RRB_CASE(15) RRB_CASE(16)
+#undef RRB_CASE
+  }
+  return nullptr;
+}
+
+rrb_status route_launch_check(const char *what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(RRB_EHIP, "%s launch: %s", what, hipGetErrorString(e));
+  return RRB_OK;
+}
+
+}  // namespace
+
+rrb_status clear_route_maps(const Plan &p, void *stream) {
+  const RowMaps &m = p.rows;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *ws = static_cast<char *>(p.d_ws);
+  const int64_t n = m.tokens * m.topk;
+  if (n > 0)
+    hipLaunchKernelGGL(moe_fill_kernel, dim3(64), dim3(256), 0, s,
+                       reinterpret_cast<int32_t *>(ws + m.off_slot), n, 0);
+  hipLaunchKernelGGL(moe_fill_kernel, dim3(1), dim3(64), 0, s,
+                     reinterpret_cast<int32_t *>(ws + m.off_status), static_cast<int64_t>(1), 0);
+  return route_launch_check("route clear");
+}
+
+rrb_status launch_route(Plan &p, const int32_t *d_idx, const float *d_w, int32_t *d_rank_offsets,
+                        void *stream) {
+  const RowMaps &m = p.rows;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *ws = static_cast<char *>(p.d_ws);
+  RouteArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.idx = d_idx;
+  a.w = d_w;
+  a.slot = reinterpret_cast<int32_t *>(ws + m.off_slot);
+  a.weight = reinterpret_cast<float *>(ws + m.off_weight);
+  a.counts = reinterpret_cast<int32_t *>(ws + m.off_counts);
+  a.expert_off = reinterpret_cast<int32_t *>(ws + m.off_expert);
+  a.rank_off = reinterpret_cast<int32_t *>(ws + m.off_rank);
+  a.bcounts = reinterpret_cast<int32_t *>(ws + m.off_bcounts);
+  a.bbase = reinterpret_cast<int32_t *>(ws + m.off_bbase);
+  a.status = reinterpret_cast<int32_t *>(ws + m.off_status);
+  a.user_rank_off = d_rank_offsets;
+  a.T = m.tokens;
+  a.E = m.experts;
+  a.k = m.topk;
+  a.R = p.nranks;
+  a.per = m.experts / p.nranks;
+  a.nblk = static_cast<int32_t>(m.nblk);
+  hipLaunchKernelGGL(moe_fill_kernel, dim3(1), dim3(64), 0, s, a.status, static_cast<int64_t>(1), 0);
+  rrb_status st = route_launch_check("route status clear");
+  if (st != RRB_OK) return st;
+  if (m.tokens > 0) {
+    hipLaunchKernelGGL(moe_route_count_kernel, dim3(static_cast<unsigned>(m.nblk)), dim3(kRouteBlock),
+                       0, s, a);
+    if ((st = route_launch_check("route count")) != RRB_OK) return st;
+  }
+  hipLaunchKernelGGL(moe_route_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a);
+  if ((st = route_launch_check("route scan")) != RRB_OK) return st;
+  if (m.tokens > 0) {
+    hipLaunchKernelGGL(route_slot_for(m.topk), dim3(static_cast<unsigned>(m.nblk)), dim3(kRouteBlock),
+                       0, s, a);
+    if ((st = route_launch_check("route slot")) != RRB_OK) return st;
+  }
+  return RRB_OK;
+}
+
 namespace {
 
 using RowFn = void (*)(RowArgs);
@@ -215,10 +443,16 @@ rrb_status launch_rows(const Plan &p, const void *const *in, void *const *out, v
         (p.out_count[r] && (reinterpret_cast<uintptr_t>(out[r]) & 15)))
       vec = false;
   }
-  const size_t n = m.slot.size();
-  const size_t slot_bytes = ((n * 4 + 255) / 256) * 256;
-  a.slot = static_cast<const int32_t *>(p.d_ws);
-  a.weight = reinterpret_cast<const float *>(static_cast<const char *>(p.d_ws) + slot_bytes);
+  if (p.kind == PlanKind::RowsDevice) {
+    // Slots are arena rows (rank bits 0): the arena is pointer 0.
+    a.slot = reinterpret_cast<const int32_t *>(static_cast<const char *>(p.d_ws) + m.off_slot);
+    a.weight = reinterpret_cast<const float *>(static_cast<const char *>(p.d_ws) + m.off_weight);
+  } else {
+    const size_t n = m.slot.size();
+    const size_t slot_bytes = ((n * 4 + 255) / 256) * 256;
+    a.slot = static_cast<const int32_t *>(p.d_ws);
+    a.weight = reinterpret_cast<const float *>(static_cast<const char *>(p.d_ws) + slot_bytes);
+  }
   a.tokens_per_rank = m.tokens / p.nranks;
   a.row_bytes = m.hidden * 2;
   a.nvec = a.row_bytes / 16;

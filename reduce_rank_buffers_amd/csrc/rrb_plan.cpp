@@ -260,4 +260,62 @@ rrb_status build_row_plan(int32_t R, int64_t T, int64_t h, int32_t E, int32_t k,
   return RRB_OK;
 }
 
+rrb_status build_row_plan_device(int32_t R, int64_t T, int64_t h, int32_t E, int32_t k,
+                                 int32_t dir, Plan &plan) {
+  if (R < 1 || R > RRB_MAX_RANKS)
+    return fail(RRB_EINVAL, "nranks %d outside 1..%d", R, RRB_MAX_RANKS);
+  if (T < 0 || h <= 0 || E < 1 || k < 1 || k > E)
+    return fail(RRB_EINVAL, "bad MoE shape: tokens %lld hidden %lld experts %d topk %d",
+                (long long)T, (long long)h, E, k);
+  if (T % R != 0) return fail(RRB_EINVAL, "tokens must divide evenly over the ranks");
+  if (E % R != 0) return fail(RRB_EINVAL, "experts must divide evenly over the ranks");
+  if (dir != RRB_MOE_DISPATCH && dir != RRB_MOE_COMBINE)
+    return fail(RRB_EINVAL, "unknown MoE direction %d", dir);
+  if (E > kRouteMaxExperts)
+    return fail(RRB_EUNSUPPORTED, "device routing supports at most %d experts", kRouteMaxExperts);
+  if (k > kRouteMaxTopk)
+    return fail(RRB_EUNSUPPORTED, "device routing supports top-k up to %d", kRouteMaxTopk);
+  if (T * k >= (int64_t(1) << kSlotRankShift) || T * k > 0x7fffffffLL)
+    return fail(RRB_EUNSUPPORTED, "more than 2^26 routed rows");
+  RowMaps &m = plan.rows;
+  m = RowMaps();
+  m.tokens = T;
+  m.hidden = h;
+  m.experts = E;
+  m.topk = k;
+  m.dir = dir;
+  m.nblk = (T + kRouteBlock - 1) / kRouteBlock;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  size_t off = 0;
+  const size_t tk = static_cast<size_t>(T * k);
+  m.off_slot = off;    off += up(tk * 4);
+  m.off_weight = off;  off += up(tk * 4);
+  m.off_counts = off;  off += up(static_cast<size_t>(E) * 4);
+  m.off_expert = off;  off += up(static_cast<size_t>(E) * 4);
+  m.off_rank = off;    off += up(static_cast<size_t>(R + 1) * 4);
+  m.off_bcounts = off; off += up(static_cast<size_t>(m.nblk) * E * 4);
+  m.off_bbase = off;   off += up(static_cast<size_t>(m.nblk) * E * 4);
+  m.off_status = off;  off += 256;
+  plan.ws_bytes = off;
+  plan.kind = PlanKind::RowsDevice;
+  plan.nranks = R;
+  plan.dtype = RRB_BF16;
+  plan.op = dir == RRB_MOE_DISPATCH ? RRB_COPY : RRB_REDUCE_SUM;
+  plan.count = T * h;
+  plan.segs.clear();
+  const int64_t Tr = T / R;
+  plan.in_count.assign(R, 0);
+  plan.out_count.assign(R, 0);
+  // The receive side is one arena of exactly T*k rows: rank r's rows (its
+  // experts in ascending id, tokens ascending within an expert) start at
+  // rank_offsets[r].  It is rank 0's buffer in the pointer arrays.
+  for (int32_t r = 0; r < R; ++r) {
+    if (dir == RRB_MOE_DISPATCH) plan.in_count[r] = Tr * h;
+    else plan.out_count[r] = Tr * h;
+  }
+  if (dir == RRB_MOE_DISPATCH) plan.out_count[0] = T * k * h;
+  else plan.in_count[0] = T * k * h;
+  return RRB_OK;
+}
+
 }  // namespace rrb

@@ -196,3 +196,30 @@ def test_snac_create_validation(librrb):
     # unbound handle refuses to run
     assert lib.rrb_snac_allreduce_chain(h, 1, None, None, None, None, 0, None) == L.RRB_EINVAL
     lib.rrb_snac_destroy(h)
+
+
+def test_device_row_plan_sizes_and_limits(librrb):
+    import ctypes
+    lib = L.lib()
+    R, T, h, E, k = 8, 4096, 7168, 256, 8
+    for d in (L.RRB_MOE_DISPATCH, L.RRB_MOE_COMBINE):
+        hdl = ctypes.c_void_p()
+        L.check(lib.rrb_plan_create_rows_device(R, T, h, E, k, d, ctypes.byref(hdl)), "dev rows")
+        ws = ctypes.c_size_t()
+        inc = (ctypes.c_int64 * R)()
+        outc = (ctypes.c_int64 * R)()
+        L.check(lib.rrb_plan_query(hdl, ctypes.byref(ws), inc, outc), "query")
+        arena = [T * k * h] + [0] * (R - 1)
+        tok = [T // R * h] * R
+        if d == L.RRB_MOE_DISPATCH:
+            assert list(inc) == tok and list(outc) == arena
+        else:
+            assert list(inc) == arena and list(outc) == tok
+        assert ws.value >= 2 * T * k * 4
+        # routing before binding is refused
+        assert lib.rrb_moe_route(hdl, None, None, None, None) == L.RRB_EINVAL
+        lib.rrb_plan_destroy(hdl)
+    hdl = ctypes.c_void_p()
+    assert lib.rrb_plan_create_rows_device(R, T, h, 2048, k, 0, ctypes.byref(hdl)) == L.RRB_EUNSUPPORTED
+    assert lib.rrb_plan_create_rows_device(R, T, h, E, 17, 0, ctypes.byref(hdl)) == L.RRB_EUNSUPPORTED
+    assert lib.rrb_plan_create_rows_device(R, T + 1, h, E, k, 0, ctypes.byref(hdl)) == L.RRB_EINVAL

@@ -1,0 +1,137 @@
+"""GPU parity of device-side MoE routing (maps built on the GPU from device
+routing arrays) against the oracle, through the C ABI: the receive arena is
+the concatenation of the oracle's per-rank receive buffers, rank offsets are
+the running sums of its per-rank row counts, combine is bit-exact.  Also:
+re-routing with new routing, bad routing reported and kept in bounds, and
+agreement with the host-built row plan."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import bf16, moe as OM
+from reduce_rank_buffers_amd import _lib as L, api, inputs
+from tests.gpu_util import DEV, assert_bits_equal, empty_like_np, from_dev, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _run(T, h, E, k, R, idx, w, x_shards, z_np=None):
+    disp = api.MoeDevicePlan(R, T, h, E, k, "dispatch")
+    comb = api.MoeDevicePlan(R, T, h, E, k, "combine", share=disp)
+    d_idx = torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).to(DEV)
+    d_w = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).to(DEV)
+    offs = torch.zeros(R + 1, dtype=torch.int32, device=DEV)
+    disp.route(d_idx, d_w, offs)
+    xs = [to_dev(s.reshape(-1)) for s in x_shards]
+    arena = empty_like_np(T * k * h, "bf16", -21555)
+    disp.run(xs, [arena] + [None] * (R - 1))
+    disp.check()
+    want_recv = OM.dispatch(x_shards, idx, E)
+    _, counts, offsets, rows = OM.layout(idx, E, R)
+    want_offs = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    assert np.array_equal(offs.cpu().numpy(), want_offs)
+    got = from_dev(arena).reshape(T * k, h)
+    assert_bits_equal(got, np.concatenate(want_recv, axis=0), "device-routed dispatch arena")
+    if z_np is None:
+        z_np, z_arena = want_recv, arena
+    else:
+        z_arena = to_dev(np.concatenate(z_np, axis=0).reshape(-1))
+    y = [empty_like_np(T // R * h, "bf16", -21555) for _ in range(R)]
+    comb.run([z_arena] + [None] * (R - 1), y)
+    torch.cuda.synchronize()
+    want_y = OM.combine(z_np, idx, w, E, T // R)
+    for r in range(R):
+        assert_bits_equal(from_dev(y[r]).reshape(-1, h), want_y[r], f"device-routed combine rank {r}")
+    return disp, comb
+
+
+def test_device_routing_full_workload():
+    require_gpu()
+    _say("device routing: 4096 x 7168, 256 experts, top-8")
+    T, h, E, k, R = 4096, 7168, 256, 8, 8
+    idx, w = inputs.moe_routing(T, E, k)
+    x = inputs.moe_tokens(T, h, R)
+    _run(T, h, E, k, R, idx, w, x)
+
+
+@pytest.mark.parametrize("T,h,E,k,R", [(104, 24, 16, 3, 8), (512, 16, 1024, 16, 8), (40, 8, 8, 1, 4),
+                                       (8, 13, 4, 2, 2), (1000, 64, 64, 8, 8)])
+def test_device_routing_shapes(T, h, E, k, R):
+    require_gpu()
+    rng = np.random.default_rng(T + E + k)
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    xa = bf16.rne(rng.standard_normal((T, h)).astype(np.float32))
+    shards = [xa[r * (T // R):(r + 1) * (T // R)] for r in range(R)]
+    _, counts, offsets, rows = OM.layout(idx, E, R)
+    z = [bf16.rne(rng.standard_normal((int(n), h)).astype(np.float32)) for n in rows]
+    _run(T, h, E, k, R, idx, w, shards, z)
+
+
+def test_device_rerouting_and_host_plan_agree():
+    require_gpu()
+    T, h, E, k, R = 1024, 128, 64, 4, 8
+    rng = np.random.default_rng(5)
+    xa = bf16.rne(rng.standard_normal((T, h)).astype(np.float32))
+    shards = [xa[r * (T // R):(r + 1) * (T // R)] for r in range(R)]
+    disp = api.MoeDevicePlan(R, T, h, E, k, "dispatch")
+    xs = [to_dev(s.reshape(-1)) for s in shards]
+    for step in range(3):
+        idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+        if step == 2:
+            idx[:, 0] = 7  # skewed: every token picks expert 7
+            for t in range(T):
+                row = [e for e in idx[t, 1:] if e != 7]
+                while len(row) < k - 1:
+                    c = int(rng.integers(E))
+                    if c != 7 and c not in row:
+                        row.append(c)
+                idx[t, 1:] = row
+        w = rng.random((T, k)).astype(np.float32)
+        disp.route(torch.from_numpy(idx).to(DEV), torch.from_numpy(w).to(DEV))
+        arena = empty_like_np(T * k * h, "bf16")
+        disp.run(xs, [arena] + [None] * (R - 1))
+        disp.check()
+        host = api.MoePlan(R, h, E, idx, w, "dispatch")
+        recv = [empty_like_np(r * h, "bf16") for r in host.rows_per_rank]
+        host.run(xs, recv)
+        torch.cuda.synchronize()
+        cat = np.concatenate([from_dev(t) for t in recv])
+        assert_bits_equal(from_dev(arena), cat, f"step {step}: device vs host row plan")
+
+
+def test_device_routing_rejects_bad_routing_in_bounds():
+    require_gpu()
+    T, h, E, k, R = 64, 16, 16, 2, 4
+    idx = np.tile(np.array([[1, 2]], dtype=np.int32), (T, 1))
+    idx[3] = [5, 5]    # repeated expert
+    idx[9] = [1, 99]   # out of range
+    w = np.ones((T, k), dtype=np.float32)
+    disp = api.MoeDevicePlan(R, T, h, E, k, "dispatch")
+    disp.route(torch.from_numpy(idx).to(DEV), torch.from_numpy(w).to(DEV))
+    arena = empty_like_np(T * k * h, "bf16")
+    xs = [empty_like_np(T // R * h, "bf16", 1) for _ in range(R)]
+    disp.run(xs, [arena] + [None] * (R - 1))
+    with pytest.raises(L.RrbError) as e:
+        disp.check()
+    assert e.value.status == L.RRB_EINVAL
+
+
+def test_device_plan_unrouted_is_in_bounds():
+    """Before the first route every slot is arena row 0: a copy is harmless."""
+    require_gpu()
+    T, h, E, k, R = 32, 8, 8, 2, 2
+    disp = api.MoeDevicePlan(R, T, h, E, k, "dispatch")
+    arena = empty_like_np(T * k * h, "bf16", 0)
+    xs = [empty_like_np(T // R * h, "bf16", 3) for _ in range(R)]
+    disp.run(xs, [arena] + [None] * (R - 1))
+    torch.cuda.synchronize()
+    a = from_dev(arena).reshape(T * k, h)
+    assert np.all(a[1:] == 0) and np.all(a[0] == 3)
