@@ -261,6 +261,12 @@ rrb_status rrb_empty_kernel(rrb_stream_t stream);
  *                              then check the reduced validation flag
  *                              (sum of the R flags == R * epoch) and retry on
  *                              mismatch (SiFAR review, Fig. 14)
+ *   RRB_SNAC_GRAPH             (alone) orchestration by kernel boundaries on
+ *                              one GPU: one Atom All-Reduce kernel per epoch,
+ *                              reading d_in[e] in place and chained in a HIP
+ *                              graph cached for the last (d_in, d_out,
+ *                              epochs); no staging, no flags.  d_stats is not
+ *                              written and d_stagger must be NULL.
  * slices: single-wave workgroups per rank (1..256; 0 = choose from count:
  *         8 up to 64 KiB payloads, then about 16 KiB per workgroup up to 32).
  *         The grid (nranks x slices) must be co-resident: the launch is
@@ -268,6 +274,7 @@ rrb_status rrb_empty_kernel(rrb_stream_t stream);
  */
 #define RRB_SNAC_DUAL_BUFFER 1u
 #define RRB_SNAC_SPECULATIVE 2u
+#define RRB_SNAC_GRAPH 4u
 typedef struct rrb_snac_s *rrb_snac_t;
 
 /* Device-side counters a chain call may accumulate into (zeroed by the

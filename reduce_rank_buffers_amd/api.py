@@ -245,7 +245,8 @@ class MoeDevicePlan(Plan):
 # ---- SNAC chain -------------------------------------------------------------
 
 VARIANTS = {"barrier": 0, "dual": L.RRB_SNAC_DUAL_BUFFER,
-            "speculative": L.RRB_SNAC_DUAL_BUFFER | L.RRB_SNAC_SPECULATIVE}
+            "speculative": L.RRB_SNAC_DUAL_BUFFER | L.RRB_SNAC_SPECULATIVE,
+            "graph": L.RRB_SNAC_GRAPH}
 
 
 class SnacChain:

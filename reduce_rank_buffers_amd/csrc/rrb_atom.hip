@@ -339,10 +339,31 @@ OneFn reduce_one_for(int R) {
   return nullptr;
 }
 
+// Issues a launch on a stream, or records it when `descs` is set.
+struct Emitter {
+  hipStream_t stream = nullptr;
+  std::vector<LaunchDesc> *descs = nullptr;
+  template <class Args>
+  rrb_status operator()(void (*kern)(Args), dim3 grid, dim3 block, const Args &a, const char *what) {
+    if (descs) {
+      LaunchDesc d;
+      d.func = reinterpret_cast<const void *>(kern);
+      d.grid = grid;
+      d.block = block;
+      d.args.assign(reinterpret_cast<const unsigned char *>(&a),
+                    reinterpret_cast<const unsigned char *>(&a) + sizeof a);
+      descs->push_back(std::move(d));
+      return RRB_OK;
+    }
+    hipLaunchKernelGGL(kern, grid, block, 0, stream, a);
+    return check_launch(what);
+  }
+};
+
 // Single aligned segment of at most kOneMaxVectors vectors: the decode path.
 constexpr int64_t kOneMaxVectors = 4096;
 
-rrb_status launch_one(const Plan &p, const void *const *in, void *const *out, hipStream_t stream) {
+rrb_status launch_one(const Plan &p, const void *const *in, void *const *out, Emitter &emit) {
   const int esz = elem_size(p.dtype);
   const Segment &sg = p.segs[0];
   const bool reduce = p.op == RRB_REDUCE_SUM;
@@ -367,12 +388,11 @@ rrb_status launch_one(const Plan &p, const void *const *in, void *const *out, hi
                              : (bf16 ? reduce_one_for<true, false>(p.nranks)
                                      : reduce_one_for<false, false>(p.nranks)))
                       : copy_one_kernel;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kOneBlock), 0, stream, a);
-  return check_launch(reduce ? "reduce" : "copy");
+  return emit(kern, dim3(grid), dim3(kOneBlock), a, reduce ? "reduce" : "copy");
 }
 
 rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out,
-                          hipStream_t stream) {
+                          Emitter &emit) {
   const int esz = elem_size(p.dtype);
   if (p.segs.empty() || p.segs[0].len == 0) return RRB_OK;
   const int64_t len = p.segs[0].len;
@@ -386,7 +406,7 @@ rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out
     if ((s.src_off * esz) % 16 || (s.dst_off * esz) % 16) vec = false;
   if (vec && p.segs.size() == 1 && (len * esz) / 16 >= 1 && (len * esz) / 16 <= kOneMaxVectors &&
       p.segs[0].dst_mask != 0)
-    return launch_one(p, in, out, stream);
+    return launch_one(p, in, out, emit);
 
   UniArgs a;
   std::memset(&a, 0, sizeof a);
@@ -468,14 +488,28 @@ rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out
       a.items[i].dst_mask = s.dst_mask;
     }
     const unsigned grid = static_cast<unsigned>(cnt) * static_cast<unsigned>(a.tiles);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(bs), 0, stream, a);
-    const rrb_status st = check_launch(reduce ? "reduce" : "copy");
+    const rrb_status st = emit(kern, dim3(grid), dim3(bs), a, reduce ? "reduce" : "copy");
     if (st != RRB_OK) return st;
   }
   return RRB_OK;
 }
 
+rrb_status launch_uniform_on(const Plan &p, const void *const *in, void *const *out,
+                             hipStream_t stream) {
+  Emitter e;
+  e.stream = stream;
+  return launch_uniform(p, in, out, e);
+}
+
 }  // namespace
+
+rrb_status describe_uniform(const Plan &p, const void *const *in, void *const *out,
+                            std::vector<LaunchDesc> &descs) {
+  Emitter e;
+  e.descs = &descs;
+  return launch_uniform(p, in, out, e);
+}
+
 }  // namespace rrb
 
 using namespace rrb;
@@ -491,7 +525,7 @@ rrb_status rrb_copy(rrb_plan_t plan, const void *const *d_in, void *const *d_out
   rrb_status s = check_buffers(p, d_in, d_out);
   if (s != RRB_OK) return s;
   if (p.kind != PlanKind::Uniform) return launch_rows(p, d_in, d_out, stream);
-  return launch_uniform(p, d_in, d_out, static_cast<hipStream_t>(stream));
+  return launch_uniform_on(p, d_in, d_out, static_cast<hipStream_t>(stream));
 }
 
 rrb_status rrb_reduce(rrb_plan_t plan, const void *const *d_in, void *const *d_out,
@@ -503,7 +537,7 @@ rrb_status rrb_reduce(rrb_plan_t plan, const void *const *d_in, void *const *d_o
   rrb_status s = check_buffers(p, d_in, d_out);
   if (s != RRB_OK) return s;
   if (p.kind != PlanKind::Uniform) return launch_rows(p, d_in, d_out, stream);
-  return launch_uniform(p, d_in, d_out, static_cast<hipStream_t>(stream));
+  return launch_uniform_on(p, d_in, d_out, static_cast<hipStream_t>(stream));
 }
 
 rrb_status rrb_empty_kernel(rrb_stream_t stream) {

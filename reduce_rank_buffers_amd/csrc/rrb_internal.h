@@ -2,6 +2,8 @@
 // the HIP launchers of librrb.  Not installed; the public ABI is include/rrb.h.
 #pragma once
 
+#include <hip/hip_runtime.h>
+
 #include <cstdint>
 #include <string>
 #include <vector>
@@ -65,6 +67,19 @@ struct Plan {
   void *d_ws = nullptr;       // bound device workspace (row plans)
   size_t ws_bytes = 0;
 };
+
+// One kernel launch, described rather than issued: kernel, grid, block and
+// the kernel's single by-value argument struct.
+struct LaunchDesc {
+  const void *func = nullptr;
+  dim3 grid, block;
+  std::vector<unsigned char> args;
+};
+
+// The launches rrb_copy / rrb_reduce would issue for a uniform plan with
+// these buffers, appended to `out` (rrb_atom.hip).
+rrb_status describe_uniform(const struct Plan &plan, const void *const *in, void *const *out,
+                            std::vector<LaunchDesc> &descs);
 
 // Builds a uniform plan from a layout-naming spec (rrb_plan.cpp).
 rrb_status build_uniform_plan(const rrb_spec &spec, Plan &plan);

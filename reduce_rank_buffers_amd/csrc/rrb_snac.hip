@@ -342,7 +342,85 @@ struct rrb_snac_s {
   rrb::Layout lay{};
   unsigned char *ws = nullptr;
   uint32_t next_epoch = 1;
+  // RRB_SNAC_GRAPH: one Atom All-Reduce kernel node per epoch, chained in a
+  // HIP graph that is cached for the last (in, out, epochs).
+  rrb::Plan ar_plan;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  const void *g_in = nullptr;
+  void *g_out = nullptr;
+  int32_t g_epochs = 0;
+  std::vector<rrb::LaunchDesc> g_descs;
+
+  void drop_graph() {
+    if (exec) (void)hipGraphExecDestroy(exec);
+    if (graph) (void)hipGraphDestroy(graph);
+    exec = nullptr;
+    graph = nullptr;
+    g_in = nullptr;
+    g_out = nullptr;
+    g_epochs = 0;
+    g_descs.clear();
+  }
+  ~rrb_snac_s() { drop_graph(); }
 };
+
+namespace rrb {
+namespace {
+
+// Builds the chain's graph: epoch e's All-Reduce reads in[e][0..R-1] and
+// writes out[e][0..R-1]; each epoch's kernels depend on the previous ones,
+// as a decode step's All-Reduces do.
+rrb_status build_chain_graph(rrb_snac_s *h, int32_t epochs, const void *d_in, void *d_out) {
+  h->drop_graph();
+  const int64_t rank_bytes = h->count * elem_size(h->dtype);
+  hipError_t e = hipGraphCreate(&h->graph, 0);
+  if (e != hipSuccess) return fail(RRB_EHIP, "graph create: %s", hipGetErrorString(e));
+  std::vector<const void *> in(h->R);
+  std::vector<void *> out(h->R);
+  for (int32_t k = 0; k < epochs; ++k) {
+    for (int32_t r = 0; r < h->R; ++r) {
+      in[r] = static_cast<const unsigned char *>(d_in) + (static_cast<int64_t>(k) * h->R + r) * rank_bytes;
+      out[r] = static_cast<unsigned char *>(d_out) + (static_cast<int64_t>(k) * h->R + r) * rank_bytes;
+    }
+    const rrb_status st = describe_uniform(h->ar_plan, in.data(), out.data(), h->g_descs);
+    if (st != RRB_OK) {
+      h->drop_graph();
+      return st;
+    }
+  }
+  hipGraphNode_t prev = nullptr;
+  for (LaunchDesc &d : h->g_descs) {
+    hipKernelNodeParams np;
+    std::memset(&np, 0, sizeof np);
+    void *params[1] = {d.args.data()};
+    np.func = const_cast<void *>(d.func);
+    np.gridDim = d.grid;
+    np.blockDim = d.block;
+    np.sharedMemBytes = 0;
+    np.kernelParams = params;
+    np.extra = nullptr;
+    hipGraphNode_t node = nullptr;
+    e = hipGraphAddKernelNode(&node, h->graph, prev ? &prev : nullptr, prev ? 1 : 0, &np);
+    if (e != hipSuccess) {
+      h->drop_graph();
+      return fail(RRB_EHIP, "graph kernel node: %s", hipGetErrorString(e));
+    }
+    prev = node;
+  }
+  e = hipGraphInstantiate(&h->exec, h->graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    h->drop_graph();
+    return fail(RRB_EHIP, "graph instantiate: %s", hipGetErrorString(e));
+  }
+  h->g_in = d_in;
+  h->g_out = d_out;
+  h->g_epochs = epochs;
+  return RRB_OK;
+}
+
+}  // namespace
+}  // namespace rrb
 
 using namespace rrb;
 
@@ -356,8 +434,10 @@ rrb_status rrb_snac_create(int32_t nranks, int64_t count, int32_t dtype, uint32_
   if (nranks < 1 || nranks > RRB_MAX_RANKS)
     return fail(RRB_EINVAL, "nranks %d outside 1..%d", nranks, RRB_MAX_RANKS);
   if (dtype != RRB_BF16 && dtype != RRB_F32) return fail(RRB_EINVAL, "unknown dtype %d", dtype);
-  if (flags & ~(RRB_SNAC_DUAL_BUFFER | RRB_SNAC_SPECULATIVE))
+  if (flags & ~(RRB_SNAC_DUAL_BUFFER | RRB_SNAC_SPECULATIVE | RRB_SNAC_GRAPH))
     return fail(RRB_EINVAL, "unknown SNAC flags 0x%x", flags);
+  if ((flags & RRB_SNAC_GRAPH) && flags != RRB_SNAC_GRAPH)
+    return fail(RRB_EINVAL, "RRB_SNAC_GRAPH takes no other flag");
   if ((flags & RRB_SNAC_SPECULATIVE) && !(flags & RRB_SNAC_DUAL_BUFFER))
     return fail(RRB_EINVAL, "speculative reduction needs dual buffering");
   const int esz = elem_size(dtype);
@@ -394,6 +474,21 @@ rrb_status rrb_snac_create(int32_t nranks, int64_t count, int32_t dtype, uint32_
   h->S = S;
   h->bs = bs;
   h->lay = layout_for(nranks, count, dtype, S);
+  if (flags & RRB_SNAC_GRAPH) {
+    rrb_spec sp;
+    std::memset(&sp, 0, sizeof sp);
+    sp.nranks = nranks;
+    sp.dtype = dtype;
+    sp.count = count;
+    sp.in.kind = RRB_PARTIAL;
+    sp.out.kind = RRB_REPLICATED;
+    sp.op = RRB_REDUCE_SUM;
+    const rrb_status st = build_uniform_plan(sp, h->ar_plan);
+    if (st != RRB_OK) {
+      delete h;
+      return st;
+    }
+  }
   *out = h;
   return RRB_OK;
 }
@@ -413,6 +508,7 @@ rrb_status rrb_snac_bind(rrb_snac_t h, void *d_ws, size_t bytes, rrb_stream_t st
   if (reinterpret_cast<uintptr_t>(d_ws) % 256) return fail(RRB_EINVAL, "workspace must be 256-byte aligned");
   h->ws = static_cast<unsigned char *>(d_ws);
   h->next_epoch = 1;
+  h->drop_graph();
   // Clear flags, done words and status with a fill kernel (graph-safe).
   uint32_t *p = reinterpret_cast<uint32_t *>(h->ws + h->lay.flag_off);
   const int64_t n = (h->lay.total - h->lay.flag_off) / 4;
@@ -434,6 +530,16 @@ rrb_status rrb_snac_allreduce_chain(rrb_snac_t h, int32_t epochs, const void *d_
   if (!d_in || !d_out) return fail(RRB_EINVAL, "NULL payload pointer");
   if ((reinterpret_cast<uintptr_t>(d_in) | reinterpret_cast<uintptr_t>(d_out)) & 15)
     return fail(RRB_EINVAL, "payloads must be 16-byte aligned");
+  if (h->flags & RRB_SNAC_GRAPH) {
+    if (d_stagger) return fail(RRB_EINVAL, "the stagger hook applies to the flag protocol only");
+    if (!(h->exec && h->g_in == d_in && h->g_out == d_out && h->g_epochs == epochs)) {
+      const rrb_status st = build_chain_graph(h, epochs, d_in, d_out);
+      if (st != RRB_OK) return st;
+    }
+    const hipError_t e = hipGraphLaunch(h->exec, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(RRB_EHIP, "graph launch: %s", hipGetErrorString(e));
+    return RRB_OK;
+  }
   if (h->next_epoch > 0xffffffffu - static_cast<uint32_t>(epochs) - 2)
     return fail(RRB_EUNSUPPORTED, "epoch counter exhausted; rebind the handle");
   const int esz = elem_size(h->dtype);

@@ -189,6 +189,9 @@ def test_snac_create_validation(librrb):
     assert lib.rrb_snac_create(8, 4096, 0, 2, 0, ctypes.byref(h)) == L.RRB_EINVAL  # spec w/o dual
     assert lib.rrb_snac_create(8, 4095, 0, 1, 0, ctypes.byref(h)) == L.RRB_EUNSUPPORTED
     assert lib.rrb_snac_create(0, 4096, 0, 1, 0, ctypes.byref(h)) == L.RRB_EINVAL
+    assert lib.rrb_snac_create(8, 4096, 0, 5, 0, ctypes.byref(h)) == L.RRB_EINVAL  # graph + dual
+    assert lib.rrb_snac_create(8, 4096, 0, 4, 0, ctypes.byref(h)) == L.RRB_OK
+    lib.rrb_snac_destroy(h)
     assert lib.rrb_snac_create(8, 4096, 0, 3, 0, ctypes.byref(h)) == L.RRB_OK
     ws = ctypes.c_size_t()
     assert lib.rrb_snac_workspace(h, ctypes.byref(ws)) == L.RRB_OK

@@ -22,7 +22,8 @@ from tests.gpu_util import DEV, assert_bits_equal, from_dev, require_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = ["barrier", "dual", "speculative"]
+VARIANTS = ["barrier", "dual", "speculative", "graph"]
+FLAG_VARIANTS = ["barrier", "dual", "speculative"]
 R = 8
 EPOCHS = 64
 
@@ -56,7 +57,8 @@ def test_chain_all_variants_bit_exact(b, h):
         _check_chain(out, want, f"{v} b={b} h={h}")
         st = stats.cpu().tolist()
         assert st[2] == 0  # no timeouts
-        assert st[3] == EPOCHS * R * _slices_of(ch)
+        if v != "graph":
+            assert st[3] == EPOCHS * R * _slices_of(ch)
         # a second call continues the epoch counter on the same flags
         out2 = torch.empty_like(inp)
         ch.run(inp, out2)
@@ -71,7 +73,7 @@ def _slices_of(ch):
     return min(S, 2048 // R, nvec)
 
 
-@pytest.mark.parametrize("v", VARIANTS)
+@pytest.mark.parametrize("v", FLAG_VARIANTS)
 def test_chain_staggered_ranks(v):
     """Late ranks (rank r sleeps about r x 4k cycles before each stage)."""
     require_gpu()
@@ -188,3 +190,28 @@ def test_bounded_wait_times_out_cleanly():
             ch.check()
         assert e.value.status == L.RRB_ETIMEOUT
         assert stats.cpu().tolist()[2] > 0
+
+
+def test_graph_chain_replays_and_rebuilds():
+    """The graph variant caches its HIP graph per (in, out, epochs): replays
+    with new input contents (eager copies and synchronisations between the
+    replays) and a rebuild for new buffers all stay bit-exact."""
+    require_gpu()
+    n, E = 4096, 16
+    ch = api.SnacChain(R, n, "bf16", "graph")
+    inp = torch.empty((E, R, n), dtype=torch.int16, device=DEV)
+    out = torch.empty_like(inp)
+    for k in range(3):
+        host = inputs.chain(E, R, n, kind=90 + k)
+        inp.copy_(to_dev(host))
+        torch.cuda.synchronize()
+        ch.run(inp, out)
+        ch.check()
+        _check_chain(out, OC.allreduce_chain(host), f"graph replay {k}")
+    inp2 = to_dev(inputs.chain(8, R, n, kind=95))
+    out2 = torch.empty_like(inp2)
+    ch.run(inp2, out2)
+    ch.check()
+    _check_chain(out2, OC.allreduce_chain(inputs.chain(8, R, n, kind=95)), "graph rebuild")
+    with pytest.raises(L.RrbError):
+        ch.run(inp, out, stagger=torch.zeros(R, dtype=torch.int32, device=DEV))
