@@ -300,7 +300,7 @@ def bench_chain(args, dev):
             inp = torch.from_numpy(inputs.chain(E, R, n).view(np.int16)).to(dev)
             out = torch.empty_like(inp)
             res = {"b": b, "h": h, "payload_bytes": n * 2}
-            for v in ("barrier", "dual", "speculative", "graph"):
+            for v in ("barrier", "dual", "speculative", "twoshot", "graph"):
                 ch = rrb.SnacChain(R, n, "bf16", v)
                 stats = torch.zeros(4, dtype=torch.int64, device=dev)
                 for _ in range(3):

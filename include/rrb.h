@@ -261,6 +261,11 @@ rrb_status rrb_empty_kernel(rrb_stream_t stream);
  *                              then check the reduced validation flag
  *                              (sum of the R flags == R * epoch) and retry on
  *                              mismatch (SiFAR review, Fig. 14)
+ *   RRB_SNAC_TWOSHOT | DUAL    twoshot (SiFAR review, Fig. 6): stage, then each
+ *                              rank reduces chunk r of the payload over all
+ *                              ranks, then every rank gathers the R reduced
+ *                              chunks; two flag rounds per epoch, each rank
+ *                              reads 2x its payload instead of R x
  *   RRB_SNAC_GRAPH             (alone) orchestration by kernel boundaries on
  *                              one GPU: one Atom All-Reduce kernel per epoch,
  *                              reading d_in[e] in place and chained in a HIP
@@ -275,6 +280,7 @@ rrb_status rrb_empty_kernel(rrb_stream_t stream);
 #define RRB_SNAC_DUAL_BUFFER 1u
 #define RRB_SNAC_SPECULATIVE 2u
 #define RRB_SNAC_GRAPH 4u
+#define RRB_SNAC_TWOSHOT 8u
 typedef struct rrb_snac_s *rrb_snac_t;
 
 /* Device-side counters a chain call may accumulate into (zeroed by the
@@ -291,7 +297,7 @@ typedef struct {
 rrb_status rrb_snac_create(int32_t nranks, int64_t count, int32_t dtype,
                            uint32_t flags, int32_t slices, rrb_snac_t *out);
 /* Device workspace the handle needs: two staging buffers of R x count
- * elements, flags and status words. */
+ * elements, two reduced buffers of count elements, flags and status words. */
 rrb_status rrb_snac_workspace(rrb_snac_t h, size_t *bytes);
 /* Attach caller-owned workspace (256-byte aligned) and clear its flags with a
  * fill kernel on `stream`; resets the handle's epoch counter. */

@@ -31,6 +31,7 @@ RRB_MOE_COMBINE = 1
 RRB_SNAC_DUAL_BUFFER = 1
 RRB_SNAC_SPECULATIVE = 2
 RRB_SNAC_GRAPH = 4
+RRB_SNAC_TWOSHOT = 8
 
 RRB_MAX_RANKS = 16
 

@@ -55,7 +55,7 @@ constexpr uint32_t kDefaultSpin = 1u << 21;  // polls (about 1 us each)
 constexpr int kMaxSlices = 256;
 constexpr int kStageU = 8;  // vectors in flight per lane in the stage copy
 
-enum Variant : int32_t { kBarrier = 0, kDual = 1, kSpeculative = 2 };
+enum Variant : int32_t { kBarrier = 0, kDual = 1, kSpeculative = 2, kTwoshot = 3 };
 
 struct SnacArgs {
   const unsigned char *in;   // [E][R][count]
@@ -70,6 +70,10 @@ struct SnacArgs {
   int64_t rank_bytes;        // count * elem size
   int64_t nvec;              // 16-byte vectors per rank payload
   int64_t slice_vec;         // vectors per slice (the last slice may be short)
+  unsigned char *reduced;    // twoshot: [2][count], chunk q owned by rank q
+  uint32_t *flag2;           // twoshot: [2][R][S] x kFlagStride, chunk reduced
+  int64_t chunk_vec;         // twoshot: vectors per chunk (ceil(nvec / R))
+  int64_t piece_vec;         // twoshot: vectors per piece (ceil(chunk_vec / S))
   uint32_t epoch0;           // global number of this call's first epoch (>= 1)
   int32_t epochs;
   int32_t S;
@@ -77,17 +81,22 @@ struct SnacArgs {
 };
 
 struct Layout {
-  int64_t staging_off, flag_off, done_off, status_off, total;
+  int64_t staging_off, reduced_off, flag_off, flag2_off, done_off, status_off, total;
 };
 
+// staging [2][R][count] | reduced [2][count] | flags [2][R][S] | flags2 [2][R][S]
+// | done [R][S] | status; everything from flag_off on is cleared at bind.
 Layout layout_for(int32_t R, int64_t count, int32_t dtype, int32_t S) {
   auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
   Layout l;
   l.staging_off = 0;
   const int64_t staging = up(2LL * R * count * elem_size(dtype));
-  l.flag_off = staging;
+  l.reduced_off = staging;
+  const int64_t reduced = up(2LL * count * elem_size(dtype));
+  l.flag_off = l.reduced_off + reduced;
   const int64_t flags = up(2LL * R * S * kFlagStride * 4);
-  l.done_off = l.flag_off + flags;
+  l.flag2_off = l.flag_off + flags;
+  l.done_off = l.flag2_off + flags;
   const int64_t done = up(1LL * R * S * kFlagStride * 4);
   l.status_off = l.done_off + done;
   l.total = l.status_off + 256;
@@ -171,6 +180,112 @@ __device__ __forceinline__ void reduce_pass(const uint4 (&v)[R], unsigned char *
   *reinterpret_cast<uint4 *>(dst) = res;
 }
 
+// Twoshot piece (q, s): slice s of chunk q, as a vector range [lo, hi).
+__device__ __forceinline__ void piece_range(const SnacArgs &a, int q, int s, int64_t &lo,
+                                            int64_t &hi) {
+  const int64_t c0 = min(a.nvec, static_cast<int64_t>(q) * a.chunk_vec);
+  const int64_t c1 = min(a.nvec, c0 + a.chunk_vec);
+  lo = min(c1, c0 + static_cast<int64_t>(s) * a.piece_vec);
+  hi = min(c1, lo + a.piece_vec);
+}
+
+// Copies pieces (q, s), q = 0..R-1, from `from` to `to` (both payload-shaped):
+// per pass, 2 vectors of every piece per lane in flight (2 R loads, no index
+// division).  COHERENT reads with the device-coherent policy (data another
+// workgroup wrote this epoch).
+template <int R, bool COHERENT>
+__device__ __forceinline__ void copy_pieces(const SnacArgs &a, int s, const unsigned char *from,
+                                            unsigned char *to, int64_t bytes) {
+  const int bs = blockDim.x;
+  int64_t lo[R], hi[R];
+#pragma unroll
+  for (int q = 0; q < R; ++q) piece_range(a, q, s, lo[q], hi[q]);
+  for (int64_t base = threadIdx.x; base < a.piece_vec; base += 2LL * bs) {
+    v4u x[R][2];
+    int64_t at[R][2];
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int64_t i = lo[q] + base + static_cast<int64_t>(u) * bs;
+        at[q][u] = i < hi[q] ? i * 16 : -1;
+        if (at[q][u] >= 0) {
+          if (COHERENT) {
+            const uint4 y = load_coherent(rsrc(from, bytes), static_cast<int32_t>(at[q][u]));
+            x[q][u] = v4u{y.x, y.y, y.z, y.w};
+          } else {
+            x[q][u] = *reinterpret_cast<const v4u *>(from + at[q][u]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < R; ++q)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        if (at[q][u] >= 0) *reinterpret_cast<v4u *>(to + at[q][u]) = x[q][u];
+  }
+}
+
+// One twoshot epoch of workgroup (r, s) (SiFAR review, Fig. 6: reduce-scatter
+// then all-gather): stage slice s of every chunk of rank r's payload; once
+// every rank has, reduce piece (r, s) -- slice s of chunk r -- over the R
+// ranks into the reduced buffer; once every rank's piece s is reduced, copy
+// pieces (q, s) of the reduced payload into rank r's output.  Two flag
+// rounds per epoch, but each rank reads 2x its payload instead of R x.
+template <int R, bool BF16>
+__device__ bool twoshot_epoch(const SnacArgs &a, int r, int s, int k, uint32_t ep, int *lds_ok) {
+  const int bs = blockDim.x;
+  const int b = static_cast<int>(ep & 1u);
+  const int64_t stride_rs = static_cast<int64_t>(a.S) * kFlagStride;
+  unsigned char *stage_base = a.staging + static_cast<int64_t>(b) * R * a.rank_bytes;
+  unsigned char *red = a.reduced + static_cast<int64_t>(b) * a.rank_bytes;
+  uint32_t *flags_b = a.flag + static_cast<int64_t>(b) * R * stride_rs;
+  uint32_t *flags2_b = a.flag2 + static_cast<int64_t>(b) * R * stride_rs;
+  const unsigned char *src = a.in + (static_cast<int64_t>(k) * R + r) * a.rank_bytes;
+  unsigned char *mine = stage_base + static_cast<int64_t>(r) * a.rank_bytes;
+  unsigned char *dst = a.out + (static_cast<int64_t>(k) * R + r) * a.rank_bytes;
+
+  // Stage pieces (q, s) of this rank's payload.
+  copy_pieces<R, false>(a, s, src, mine, a.rank_bytes);
+  notify(flags_b + r * stride_rs + s * kFlagStride, ep);
+  if (!wait_all<R>(flags_b + s * kFlagStride, stride_rs, ep, a.status, a.spin_limit, lds_ok))
+    return false;
+
+  // Reduce-scatter: piece (r, s) over all ranks, into the reduced payload.
+  {
+    int64_t lo, hi;
+    piece_range(a, r, s, lo, hi);
+    constexpr int CU = R <= 8 ? 4 : 2;
+    for (int64_t i0 = lo + threadIdx.x; i0 < hi; i0 += static_cast<int64_t>(bs) * CU) {
+      uint4 v[CU][R];
+#pragma unroll
+      for (int u = 0; u < CU; ++u) {
+        const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+        if (i < hi) {
+#pragma unroll
+          for (int q = 0; q < R; ++q)
+            v[u][q] = load_coherent(rsrc(stage_base + static_cast<int64_t>(q) * a.rank_bytes,
+                                         a.rank_bytes),
+                                    static_cast<int32_t>(i * 16));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < CU; ++u) {
+        const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+        if (i < hi) reduce_pass<R, BF16>(v[u], red + i * 16);
+      }
+    }
+  }
+  notify(flags2_b + r * stride_rs + s * kFlagStride, ep);
+  if (!wait_all<R>(flags2_b + s * kFlagStride, stride_rs, ep, a.status, a.spin_limit, lds_ok))
+    return false;
+
+  // All-gather: pieces (q, s) of the reduced payload into this rank's output.
+  copy_pieces<R, true>(a, s, red, dst, a.rank_bytes);
+  return true;
+}
+
 template <int R, bool BF16, int VAR>
 __global__ void __launch_bounds__(64) snac_chain_kernel(SnacArgs a) {
   __shared__ int lds_ok[R];
@@ -185,6 +300,18 @@ __global__ void __launch_bounds__(64) snac_chain_kernel(SnacArgs a) {
 
   for (int k = 0; k < a.epochs; ++k) {
     const uint32_t ep = a.epoch0 + static_cast<uint32_t>(k);
+    if constexpr (VAR == kTwoshot) {
+      if (a.stagger) {
+        const uint32_t d = a.stagger[r];
+        for (uint32_t i = 0; i < d; ++i) __builtin_amdgcn_s_sleep(1);
+      }
+      if (!twoshot_epoch<R, BF16>(a, r, s, k, ep, lds_ok)) {
+        ++timeouts;
+        break;
+      }
+      ++done_epochs;
+      continue;
+    }
     const int b = VAR == kBarrier ? 0 : static_cast<int>(ep & 1u);
     unsigned char *stage_base = a.staging + static_cast<int64_t>(b) * R * a.rank_bytes;
     uint32_t *flags_b = a.flag + static_cast<int64_t>(b) * R * stride_rs;
@@ -434,8 +561,10 @@ rrb_status rrb_snac_create(int32_t nranks, int64_t count, int32_t dtype, uint32_
   if (nranks < 1 || nranks > RRB_MAX_RANKS)
     return fail(RRB_EINVAL, "nranks %d outside 1..%d", nranks, RRB_MAX_RANKS);
   if (dtype != RRB_BF16 && dtype != RRB_F32) return fail(RRB_EINVAL, "unknown dtype %d", dtype);
-  if (flags & ~(RRB_SNAC_DUAL_BUFFER | RRB_SNAC_SPECULATIVE | RRB_SNAC_GRAPH))
+  if (flags & ~(RRB_SNAC_DUAL_BUFFER | RRB_SNAC_SPECULATIVE | RRB_SNAC_GRAPH | RRB_SNAC_TWOSHOT))
     return fail(RRB_EINVAL, "unknown SNAC flags 0x%x", flags);
+  if ((flags & RRB_SNAC_TWOSHOT) && flags != (RRB_SNAC_TWOSHOT | RRB_SNAC_DUAL_BUFFER))
+    return fail(RRB_EINVAL, "RRB_SNAC_TWOSHOT goes with RRB_SNAC_DUAL_BUFFER only");
   if ((flags & RRB_SNAC_GRAPH) && flags != RRB_SNAC_GRAPH)
     return fail(RRB_EINVAL, "RRB_SNAC_GRAPH takes no other flag");
   if ((flags & RRB_SNAC_SPECULATIVE) && !(flags & RRB_SNAC_DUAL_BUFFER))
@@ -458,10 +587,11 @@ rrb_status rrb_snac_create(int32_t nranks, int64_t count, int32_t dtype, uint32_
     // fastest with 8 workgroups per rank (each workgroup's agent-scope fences
     // serialise, so more of them cost more than they parallelise); larger
     // payloads with about 1024 vectors per workgroup, up to 32 per rank.
-    if (nvec <= 4096)
+    if (nvec <= 4096) {
       S = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(8, nvec / 64)));
-    else
+    } else {
       S = static_cast<int32_t>(std::min<int64_t>(32, std::max<int64_t>(8, nvec / 1024)));
+    }
     S = std::min<int32_t>(S, 2048 / nranks);
   }
   if (S > nvec) S = static_cast<int32_t>(nvec);
@@ -557,23 +687,30 @@ rrb_status rrb_snac_allreduce_chain(rrb_snac_t h, int32_t epochs, const void *d_
   a.rank_bytes = h->count * esz;
   a.nvec = a.rank_bytes / 16;
   a.slice_vec = (a.nvec + h->S - 1) / h->S;
+  a.reduced = h->ws + h->lay.reduced_off;
+  a.flag2 = reinterpret_cast<uint32_t *>(h->ws + h->lay.flag2_off);
+  a.chunk_vec = (a.nvec + h->R - 1) / h->R;
+  a.piece_vec = (a.chunk_vec + h->S - 1) / h->S;
   a.epoch0 = h->next_epoch;
   a.epochs = epochs;
   a.S = h->S;
   a.spin_limit = spin_limit ? spin_limit : kDefaultSpin;
 
   const bool bf16 = h->dtype == RRB_BF16;
-  const int var = (h->flags & RRB_SNAC_SPECULATIVE) ? kSpeculative
+  const int var = (h->flags & RRB_SNAC_TWOSHOT) ? kTwoshot
+                  : (h->flags & RRB_SNAC_SPECULATIVE) ? kSpeculative
                   : (h->flags & RRB_SNAC_DUAL_BUFFER) ? kDual : kBarrier;
   SnacFn fn = nullptr;
   if (bf16) {
     fn = var == kBarrier ? snac_for<true, kBarrier>(h->R)
          : var == kDual  ? snac_for<true, kDual>(h->R)
-                         : snac_for<true, kSpeculative>(h->R);
+         : var == kTwoshot ? snac_for<true, kTwoshot>(h->R)
+                           : snac_for<true, kSpeculative>(h->R);
   } else {
     fn = var == kBarrier ? snac_for<false, kBarrier>(h->R)
          : var == kDual  ? snac_for<false, kDual>(h->R)
-                         : snac_for<false, kSpeculative>(h->R);
+         : var == kTwoshot ? snac_for<false, kTwoshot>(h->R)
+                           : snac_for<false, kSpeculative>(h->R);
   }
   // Every workgroup waits on others: the grid must be co-resident, which a
   // cooperative launch guarantees (or refuses).

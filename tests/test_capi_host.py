@@ -190,6 +190,10 @@ def test_snac_create_validation(librrb):
     assert lib.rrb_snac_create(8, 4095, 0, 1, 0, ctypes.byref(h)) == L.RRB_EUNSUPPORTED
     assert lib.rrb_snac_create(0, 4096, 0, 1, 0, ctypes.byref(h)) == L.RRB_EINVAL
     assert lib.rrb_snac_create(8, 4096, 0, 5, 0, ctypes.byref(h)) == L.RRB_EINVAL  # graph + dual
+    assert lib.rrb_snac_create(8, 4096, 0, 8, 0, ctypes.byref(h)) == L.RRB_EINVAL  # twoshot alone
+    assert lib.rrb_snac_create(8, 4096, 0, 11, 0, ctypes.byref(h)) == L.RRB_EINVAL  # + speculative
+    assert lib.rrb_snac_create(8, 4096, 0, 9, 0, ctypes.byref(h)) == L.RRB_OK
+    lib.rrb_snac_destroy(h)
     assert lib.rrb_snac_create(8, 4096, 0, 4, 0, ctypes.byref(h)) == L.RRB_OK
     lib.rrb_snac_destroy(h)
     assert lib.rrb_snac_create(8, 4096, 0, 3, 0, ctypes.byref(h)) == L.RRB_OK

@@ -22,8 +22,8 @@ from tests.gpu_util import DEV, assert_bits_equal, from_dev, require_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = ["barrier", "dual", "speculative", "graph"]
-FLAG_VARIANTS = ["barrier", "dual", "speculative"]
+VARIANTS = ["barrier", "dual", "speculative", "twoshot", "graph"]
+FLAG_VARIANTS = ["barrier", "dual", "speculative", "twoshot"]
 R = 8
 EPOCHS = 64
 
@@ -120,7 +120,8 @@ def test_chain_slice_counts(slices):
 
 def test_chain_other_rank_counts_and_fp32():
     require_gpu()
-    for Rx, n, dt in [(2, 4096, "bf16"), (3, 1024, "bf16"), (16, 2048, "bf16"), (8, 2048, "f32")]:
+    for Rx, n, dt in [(2, 4096, "bf16"), (3, 1024, "bf16"), (16, 2048, "bf16"), (8, 2048, "f32"),
+                      (8, 800, "bf16"), (5, 4000, "bf16")]:
         E = 8
         rng = np.random.default_rng(Rx * n)
         if dt == "bf16":
@@ -181,7 +182,7 @@ def test_bounded_wait_times_out_cleanly():
     st = [0] * R
     st[7] = 20000
     stagger = torch.tensor(st, dtype=torch.int32, device=DEV)
-    for v in ("barrier", "dual"):
+    for v in ("barrier", "dual", "twoshot"):
         ch = api.SnacChain(R, n, "bf16", v)
         stats = torch.zeros(4, dtype=torch.int64, device=DEV)
         out = torch.empty_like(inp)
