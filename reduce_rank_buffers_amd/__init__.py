@@ -12,6 +12,6 @@ from .api import (  # noqa: F401
     PARTIAL, REPLICATED, SHARD, BLOCK_ROW, BLOCK_COL, ROOT,
     Plan, MoePlan, MoeDevicePlan, SnacChain, plan, collective,
     all_reduce, reduce_scatter, all_gather, all_to_all, broadcast, reduce, gather,
-    empty_kernel,
+    empty_kernel, bound, Bound,
 )
 from ._lib import RrbError, lib  # noqa: F401

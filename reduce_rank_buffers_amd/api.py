@@ -139,6 +139,47 @@ def collective(in_layout, out_layout, op, ins, outs, count, stream=None):
     return outs
 
 
+class Bound:
+    """A collective with its plan, pointer arrays and entry point resolved
+    once; calling it issues the launch on torch's current stream with a
+    single ctypes call (for launch-bound loops)."""
+
+    __slots__ = ("_fn", "_h", "_in", "_out", "_keep", "_name")
+
+    def __init__(self, p, ins, outs):
+        self._fn = p._lib.rrb_reduce if p.op == L.RRB_REDUCE_SUM else p._lib.rrb_copy
+        self._name = "rrb_reduce" if p.op == L.RRB_REDUCE_SUM else "rrb_copy"
+        self._h = p.handle
+        self._in = _ptrs(ins, p.nranks)
+        self._out = _ptrs(outs, p.nranks)
+        self._keep = (p, list(ins), list(outs))  # tensors and plan stay alive
+
+    def __call__(self, stream=None):
+        st = self._fn(self._h, self._in, self._out,
+                      torch.cuda.current_stream().cuda_stream if stream is None else stream.cuda_stream)
+        if st:
+            L.check(st, self._name)
+
+
+def bound(name, ins, outs, root=None):
+    """Pre-bind one of the seven collectives (or 'collective' via a Plan):
+    bound('all_reduce', ins, outs)() launches it."""
+    t = next(x for x in ins if x is not None)
+    R = len(ins)
+    dt = _dtype_of(t)
+    n = {"all_gather": t.numel() * R, "gather": t.numel() * R}.get(name, t.numel())
+    spec = {
+        "all_reduce": (PARTIAL, REPLICATED, "reduce"),
+        "reduce_scatter": (PARTIAL, SHARD, "reduce"),
+        "all_gather": (SHARD, REPLICATED, "copy"),
+        "all_to_all": (BLOCK_ROW, BLOCK_COL, "copy"),
+        "broadcast": (ROOT(root if root is not None else 0), REPLICATED, "copy"),
+        "reduce": (PARTIAL, ROOT(root if root is not None else 0), "reduce"),
+        "gather": (SHARD, ROOT(root if root is not None else 0), "copy"),
+    }[name]
+    return Bound(plan(R, n, dt, *spec), ins, outs)
+
+
 # The seven collectives (count = elements of the logical tensor X).
 def all_reduce(ins, outs, stream=None):
     return collective(PARTIAL, REPLICATED, "reduce", ins, outs, ins[0].numel(), stream)
