@@ -50,28 +50,24 @@ __global__ void __launch_bounds__(128) moe_dispatch_kernel(RowArgs a) {
       a.in[src_rank] + (t - src_rank * a.tokens_per_rank) * a.row_bytes;
   const int32_t *slots = a.slot + t * a.k;
   const int bs = blockDim.x;
-  int64_t i = threadIdx.x;
-  for (; i + static_cast<int64_t>(DU - 1) * bs < a.nvec; i += static_cast<int64_t>(bs) * DU) {
+  // Predicated passes of DU vectors per lane (one pass covers a 7168-wide
+  // bf16 row with 128 lanes), so every load of the row is in flight at once.
+  for (int64_t i0 = threadIdx.x; i0 < a.nvec; i0 += static_cast<int64_t>(bs) * DU) {
     v4u x[DU];
 #pragma unroll
-    for (int u = 0; u < DU; ++u)
-      x[u] = *reinterpret_cast<const v4u *>(src + (i + static_cast<int64_t>(u) * bs) * 16);
+    for (int u = 0; u < DU; ++u) {
+      const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+      if (i < a.nvec) x[u] = *reinterpret_cast<const v4u *>(src + i * 16);
+    }
     for (int j = 0; j < a.k; ++j) {
       const int32_t s = slots[j];
       unsigned char *dst = a.out[s >> kSlotRankShift] +
                            static_cast<int64_t>(s & kSlotRowMask) * a.row_bytes;
 #pragma unroll
-      for (int u = 0; u < DU; ++u)
-        __builtin_nontemporal_store(x[u], reinterpret_cast<v4u *>(dst + (i + static_cast<int64_t>(u) * bs) * 16));
-    }
-  }
-  for (; i < a.nvec; i += bs) {
-    const v4u x = *reinterpret_cast<const v4u *>(src + i * 16);
-    for (int j = 0; j < a.k; ++j) {
-      const int32_t s = slots[j];
-      unsigned char *dst = a.out[s >> kSlotRankShift] +
-                           static_cast<int64_t>(s & kSlotRowMask) * a.row_bytes;
-      __builtin_nontemporal_store(x, reinterpret_cast<v4u *>(dst + i * 16));
+      for (int u = 0; u < DU; ++u) {
+        const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+        if (i < a.nvec) __builtin_nontemporal_store(x[u], reinterpret_cast<v4u *>(dst + i * 16));
+      }
     }
   }
 }
@@ -123,10 +119,11 @@ __device__ __forceinline__ v4u combine_vec(const v4u (&z)[K], const float (&w)[K
   return o;
 }
 
-// One token per workgroup: CU vectors x K rows in flight per lane, with
-// non-temporal loads (each expert row is read once).
+// One token per workgroup of 256 lanes: CU vectors x K rows in flight per
+// lane, non-temporal loads and stores (every expert row is read once and the
+// combined row is not read again here).
 template <int K, int CU>
-__global__ void __launch_bounds__(128) moe_combine_kernel(RowArgs a) {
+__global__ void __launch_bounds__(256) moe_combine_kernel(RowArgs a) {
   const int64_t t = blockIdx.x;
   const int64_t dst_rank = t / a.tokens_per_rank;
   unsigned char *dst = a.out[dst_rank] + (t - dst_rank * a.tokens_per_rank) * a.row_bytes;
@@ -141,25 +138,23 @@ __global__ void __launch_bounds__(128) moe_combine_kernel(RowArgs a) {
     w[j] = ws[j];
   }
   const int bs = blockDim.x;
-  int64_t i = threadIdx.x;
-  for (; i + static_cast<int64_t>(CU - 1) * bs < a.nvec; i += static_cast<int64_t>(bs) * CU) {
+  for (int64_t i0 = threadIdx.x; i0 < a.nvec; i0 += static_cast<int64_t>(bs) * CU) {
     v4u z[CU][K];
 #pragma unroll
-    for (int u = 0; u < CU; ++u)
+    for (int u = 0; u < CU; ++u) {
+      const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+      if (i < a.nvec) {
 #pragma unroll
-      for (int j = 0; j < K; ++j)
-        z[u][j] = __builtin_nontemporal_load(
-            reinterpret_cast<const v4u *>(rows[j] + (i + static_cast<int64_t>(u) * bs) * 16));
+        for (int j = 0; j < K; ++j)
+          z[u][j] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(rows[j] + i * 16));
+      }
+    }
 #pragma unroll
-    for (int u = 0; u < CU; ++u)
-      *reinterpret_cast<v4u *>(dst + (i + static_cast<int64_t>(u) * bs) * 16) = combine_vec<K>(z[u], w);
-  }
-  for (; i < a.nvec; i += bs) {
-    v4u z[K];
-#pragma unroll
-    for (int j = 0; j < K; ++j)
-      z[j] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(rows[j] + i * 16));
-    *reinterpret_cast<v4u *>(dst + i * 16) = combine_vec<K>(z, w);
+    for (int u = 0; u < CU; ++u) {
+      const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+      if (i < a.nvec)
+        __builtin_nontemporal_store(combine_vec<K>(z[u], w), reinterpret_cast<v4u *>(dst + i * 16));
+    }
   }
 }
 
@@ -417,12 +412,12 @@ using RowFn = void (*)(RowArgs);
 
 RowFn combine_for(int k) {
   switch (k) {
-    case 1: return moe_combine_kernel<1, 4>;
-    case 2: return moe_combine_kernel<2, 4>;
+    case 1: return moe_combine_kernel<1, 8>;
+    case 2: return moe_combine_kernel<2, 8>;
     case 4: return moe_combine_kernel<4, 4>;
-    case 6: return moe_combine_kernel<6, 2>;
-    case 8: return moe_combine_kernel<8, 2>;
-    case 16: return moe_combine_kernel<16, 1>;
+    case 6: return moe_combine_kernel<6, 4>;
+    case 8: return moe_combine_kernel<8, 4>;
+    case 16: return moe_combine_kernel<16, 2>;
     default: return nullptr;
   }
 }
@@ -461,12 +456,12 @@ rrb_status launch_rows(const Plan &p, const void *const *in, void *const *out, v
   RowFn kern;
   int bs = 256;
   if (m.dir == RRB_MOE_DISPATCH) {
-    kern = vec ? moe_dispatch_kernel<4> : moe_dispatch_elem_kernel;
+    kern = vec ? moe_dispatch_kernel<8> : moe_dispatch_elem_kernel;
   } else {
     kern = vec ? combine_for(m.topk) : nullptr;
     if (!kern) kern = moe_combine_elem_kernel;
   }
-  if (vec && kern != moe_combine_elem_kernel) bs = 128;
+  if (vec && m.dir == RRB_MOE_DISPATCH) bs = 128;
   if (m.tokens > 0x7fffffffLL) return fail(RRB_EUNSUPPORTED, "too many tokens for one launch");
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(m.tokens)), dim3(bs), 0,
                      static_cast<hipStream_t>(stream), a);
