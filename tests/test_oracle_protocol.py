@@ -69,3 +69,44 @@ def test_payload_first_speculation_fails_only_by_overtaking(b):
     assert unexplained == 0   # ... and only that way
     assert overrun == 0
     assert misspec > 0
+
+
+def _sweep_tagged(variant, R, E, L, seeds, bias=None, tag_mod=1 << 16):
+    """(wrong results, deadlocked schedules) over seeded schedules."""
+    rng = random.Random(77 * R + E + L)
+    wrong = deadlocks = 0
+    for seed in range(seeds):
+        inp = [[[rng.randint(-9, 9) for _ in range(L)] for _ in range(R)] for _ in range(E)]
+        try:
+            out, _ = P.run(variant, inp, seed=seed, bias=bias, tag_mod=tag_mod)
+        except RuntimeError:
+            deadlocks += 1
+            continue
+        exp = P.expected(inp)
+        wrong += sum(out[e][r] != exp[e] for e in range(E) for r in range(R))
+    return wrong, deadlocks
+
+
+@pytest.mark.parametrize("R", [2, 3])
+@pytest.mark.parametrize("b", BIASES)
+@pytest.mark.parametrize("tag_mod", [3, 1 << 16])
+def test_flag_in_data_dual_buffer_always_exact(R, b, tag_mod):
+    """Tagged words, no flags, no ordering between words: exact and live."""
+    wrong, deadlocks = _sweep_tagged("lamport", R, 6, 3, 200, _bias(b, R), tag_mod)
+    assert (wrong, deadlocks) == (0, 0)
+
+
+def test_flag_in_data_needs_tags_that_tell_e_from_e_minus_2():
+    """With the tag taken modulo 2 a stale word of epoch e - 2 in the same
+    buffer carries the tag of epoch e and is accepted."""
+    wrong, deadlocks = _sweep_tagged("lamport", 3, 6, 3, 200, [1.0, 1.0, 0.15], tag_mod=2)
+    assert deadlocks == 0
+    assert wrong > 0
+
+
+def test_flag_in_data_single_buffer_exhibits_hazard():
+    """One tagged buffer: a fast rank's next epoch overwrites words a slow
+    reader still wants, which ends in a wrong result or a wait that never
+    ends."""
+    wrong, deadlocks = _sweep_tagged("lamport_single", 3, 6, 3, 200, [1.0, 1.0, 0.15])
+    assert wrong + deadlocks > 0
