@@ -305,7 +305,7 @@ def bench_chain(args, dev):
             inp = torch.from_numpy(inputs.chain(E, R, n).view(np.int16)).to(dev)
             out = torch.empty_like(inp)
             res = {"b": b, "h": h, "payload_bytes": n * 2}
-            for v in ("barrier", "dual", "speculative", "twoshot", "graph"):
+            for v in ("barrier", "dual", "speculative", "twoshot", "lamport", "graph"):
                 ch = rrb.SnacChain(R, n, "bf16", v)
                 stats = torch.zeros(4, dtype=torch.int64, device=dev)
                 for _ in range(3):
@@ -314,7 +314,8 @@ def bench_chain(args, dev):
                 ch.check()
                 st = stats.cpu().tolist()
                 res[v] = {"us_per_allreduce": round(float(np.median(ms)) * 1e3 / E, 3),
-                          "misspec_per_call": round(st[0] / max(5, args.steps), 2)}
+                          "misspec_per_call": round(st[0] / max(5, args.steps), 2),
+                          "retries_per_call": round(st[1] / max(5, args.steps), 2)}
             ins = [[inp[e, r] for r in range(R)] for e in range(E)]
             outs = [[out[e, r] for r in range(R)] for e in range(E)]
 

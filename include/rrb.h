@@ -266,6 +266,14 @@ rrb_status rrb_empty_kernel(rrb_stream_t stream);
  *                              ranks, then every rank gathers the R reduced
  *                              chunks; two flag rounds per epoch, each rank
  *                              reads 2x its payload instead of R x
+ *   RRB_SNAC_LAMPORT | DUAL    flag-in-data, the Lamport-style All-Reduce
+ *                              (SiFAR review, Fig. 20): no flags and no
+ *                              fences; each 16-bit half of the payload is
+ *                              staged in a 32-bit word under a 16-bit epoch
+ *                              tag and readers poll the words themselves
+ *                              (staged bytes are 2x the payload);
+ *                              stats.retries counts poll rounds that found an
+ *                              untagged word
  *   RRB_SNAC_GRAPH             (alone) orchestration by kernel boundaries on
  *                              one GPU: one Atom All-Reduce kernel per epoch,
  *                              reading d_in[e] in place and chained in a HIP
@@ -273,7 +281,9 @@ rrb_status rrb_empty_kernel(rrb_stream_t stream);
  *                              epochs); no staging, no flags.  d_stats is not
  *                              written and d_stagger must be NULL.
  * slices: single-wave workgroups per rank (1..256; 0 = choose from count:
- *         8 up to 64 KiB payloads, then about 16 KiB per workgroup up to 32).
+ *         8 up to 64 KiB payloads, then about 16 KiB per workgroup up to 32;
+ *         RRB_SNAC_LAMPORT: 1 KiB per workgroup below 64 KiB, then 512 B per
+ *         workgroup up to 256, and 128 above 256 KiB; at most 2048 / nranks).
  *         The grid (nranks x slices) must be co-resident: the launch is
  *         cooperative and fails with RRB_EHIP if it cannot be.
  */
@@ -281,6 +291,7 @@ rrb_status rrb_empty_kernel(rrb_stream_t stream);
 #define RRB_SNAC_SPECULATIVE 2u
 #define RRB_SNAC_GRAPH 4u
 #define RRB_SNAC_TWOSHOT 8u
+#define RRB_SNAC_LAMPORT 16u
 typedef struct rrb_snac_s *rrb_snac_t;
 
 /* Device-side counters a chain call may accumulate into (zeroed by the
@@ -297,7 +308,9 @@ typedef struct {
 rrb_status rrb_snac_create(int32_t nranks, int64_t count, int32_t dtype,
                            uint32_t flags, int32_t slices, rrb_snac_t *out);
 /* Device workspace the handle needs: two staging buffers of R x count
- * elements, two reduced buffers of count elements, flags and status words. */
+ * elements, two reduced buffers of count elements, flags and status words
+ * (RRB_SNAC_LAMPORT: two tagged buffers of R x 2 x count elements and the
+ * status word). */
 rrb_status rrb_snac_workspace(rrb_snac_t h, size_t *bytes);
 /* Attach caller-owned workspace (256-byte aligned) and clear its flags with a
  * fill kernel on `stream`; resets the handle's epoch counter. */

@@ -32,6 +32,7 @@ RRB_SNAC_DUAL_BUFFER = 1
 RRB_SNAC_SPECULATIVE = 2
 RRB_SNAC_GRAPH = 4
 RRB_SNAC_TWOSHOT = 8
+RRB_SNAC_LAMPORT = 16
 
 RRB_MAX_RANKS = 16
 

@@ -288,7 +288,8 @@ class MoeDevicePlan(Plan):
 VARIANTS = {"barrier": 0, "dual": L.RRB_SNAC_DUAL_BUFFER,
             "speculative": L.RRB_SNAC_DUAL_BUFFER | L.RRB_SNAC_SPECULATIVE,
             "graph": L.RRB_SNAC_GRAPH,
-            "twoshot": L.RRB_SNAC_TWOSHOT | L.RRB_SNAC_DUAL_BUFFER}
+            "twoshot": L.RRB_SNAC_TWOSHOT | L.RRB_SNAC_DUAL_BUFFER,
+            "lamport": L.RRB_SNAC_LAMPORT | L.RRB_SNAC_DUAL_BUFFER}
 
 
 class SnacChain:

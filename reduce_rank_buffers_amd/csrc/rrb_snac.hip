@@ -18,6 +18,11 @@
 //                flags == R * epoch, per workgroup slice) decides whether the
 //                result stands; on mismatch the slice waits for the flags and
 //                is read again.
+//   lamport      flag-in-data, the Lamport-style All-Reduce SiFAR compares
+//                against (review page, Fig. 20): no flags, no fences.  Each
+//                16-bit half of the payload is staged in a 32-bit word under
+//                a 16-bit epoch tag; a reader polls every word it needs until
+//                all carry this epoch's tag (lamport_chain_kernel below).
 //
 // One persistent kernel runs the whole chain.  Rank r is a group of S
 // workgroups; workgroup (r, s) stages slice s of rank r's payload, publishes
@@ -55,7 +60,7 @@ constexpr uint32_t kDefaultSpin = 1u << 21;  // polls (about 1 us each)
 constexpr int kMaxSlices = 256;
 constexpr int kStageU = 8;  // vectors in flight per lane in the stage copy
 
-enum Variant : int32_t { kBarrier = 0, kDual = 1, kSpeculative = 2, kTwoshot = 3 };
+enum Variant : int32_t { kBarrier = 0, kDual = 1, kSpeculative = 2, kTwoshot = 3, kLamport = 4 };
 
 struct SnacArgs {
   const unsigned char *in;   // [E][R][count]
@@ -74,6 +79,7 @@ struct SnacArgs {
   uint32_t *flag2;           // twoshot: [2][R][S] x kFlagStride, chunk reduced
   int64_t chunk_vec;         // twoshot: vectors per chunk (ceil(nvec / R))
   int64_t piece_vec;         // twoshot: vectors per piece (ceil(chunk_vec / S))
+  unsigned char *tagged;     // lamport: [2][R][2 * count * elem size] tagged words
   uint32_t epoch0;           // global number of this call's first epoch (>= 1)
   int32_t epochs;
   int32_t S;
@@ -81,24 +87,30 @@ struct SnacArgs {
 };
 
 struct Layout {
-  int64_t staging_off, reduced_off, flag_off, flag2_off, done_off, status_off, total;
+  int64_t staging_off, reduced_off, flag_off, flag2_off, done_off, tagged_off, status_off, total;
 };
 
 // staging [2][R][count] | reduced [2][count] | flags [2][R][S] | flags2 [2][R][S]
-// | done [R][S] | status; everything from flag_off on is cleared at bind.
-Layout layout_for(int32_t R, int64_t count, int32_t dtype, int32_t S) {
+// | done [R][S] | tagged [2][R][2 count] | status; everything from flag_off
+// on is cleared at bind.  The flag-in-data variant has only the tagged
+// buffers (tag 0 after the clear, which no epoch uses before overwriting),
+// the others have none.
+Layout layout_for(int32_t R, int64_t count, int32_t dtype, int32_t S, bool lamport) {
   auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  const int64_t rank_bytes = count * elem_size(dtype);
   Layout l;
   l.staging_off = 0;
-  const int64_t staging = up(2LL * R * count * elem_size(dtype));
+  const int64_t staging = lamport ? 0 : up(2LL * R * rank_bytes);
   l.reduced_off = staging;
-  const int64_t reduced = up(2LL * count * elem_size(dtype));
+  const int64_t reduced = lamport ? 0 : up(2LL * rank_bytes);
   l.flag_off = l.reduced_off + reduced;
-  const int64_t flags = up(2LL * R * S * kFlagStride * 4);
+  const int64_t flags = lamport ? 0 : up(2LL * R * S * kFlagStride * 4);
   l.flag2_off = l.flag_off + flags;
   l.done_off = l.flag2_off + flags;
-  const int64_t done = up(1LL * R * S * kFlagStride * 4);
-  l.status_off = l.done_off + done;
+  const int64_t done = lamport ? 0 : up(1LL * R * S * kFlagStride * 4);
+  l.tagged_off = l.done_off + done;
+  const int64_t tagged = lamport ? up(2LL * R * 2 * rank_bytes) : 0;
+  l.status_off = l.tagged_off + tagged;
   l.total = l.status_off + 256;
   return l;
 }
@@ -434,6 +446,169 @@ __global__ void __launch_bounds__(64) snac_chain_kernel(SnacArgs a) {
   }
 }
 
+// ---- flag-in-data (Lamport-style) chain ----------------------------------
+//
+// The payload is viewed as 16-bit halves; half j of a rank's payload is
+// staged as the 32-bit word (tag << 16) | half, tag = epoch mod 2^16, so 16
+// payload bytes become 32 staged bytes.  Words are stored and polled with
+// the agent-scope relaxed-atomic cache policy (sc1).  A 32-bit access is
+// single-copy atomic, so a word that shows this epoch's tag holds this
+// epoch's half, whatever became visible before or after it: nothing orders
+// one word against another and nothing needs to, so the variant has no flag,
+// no release and no acquire.  Two tagged buffers alternate by epoch parity.
+// A rank stores into buffer e&1 at epoch e + 2 only after it has read every
+// rank's epoch e + 1 words, and each rank stored those after its own epoch-e
+// polls had returned (their tags decide when its consume ends), so no reader
+// of epoch e is still waiting on that buffer.  The tags of e and e - 2
+// differ, and the tag 0 left by bind is met only by epochs that already
+// overwrote it.
+
+__device__ __forceinline__ void store_tagged(__amdgpu_buffer_rsrc_t r, int32_t off, v4u w) {
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 16);
+}
+
+__device__ __forceinline__ v4u load_tagged(__amdgpu_buffer_rsrc_t r, int32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16);
+}
+
+// 8 halves of a payload vector -> two vectors of tagged words (T = tag << 16).
+__device__ __forceinline__ void tag_halves(v4u x, uint32_t T, v4u &lo, v4u &hi) {
+  lo = v4u{T | (x[0] & 0xffffu), T | (x[0] >> 16), T | (x[1] & 0xffffu), T | (x[1] >> 16)};
+  hi = v4u{T | (x[2] & 0xffffu), T | (x[2] >> 16), T | (x[3] & 0xffffu), T | (x[3] >> 16)};
+}
+
+__device__ __forceinline__ bool tagged_with(v4u w, uint32_t T) {
+  return (((w[0] ^ T) | (w[1] ^ T) | (w[2] ^ T) | (w[3] ^ T)) >> 16) == 0;
+}
+
+__device__ __forceinline__ uint4 untag(v4u lo, v4u hi) {
+  uint4 x;
+  x.x = (lo[0] & 0xffffu) | (lo[1] << 16);
+  x.y = (lo[2] & 0xffffu) | (lo[3] << 16);
+  x.z = (hi[0] & 0xffffu) | (hi[1] << 16);
+  x.w = (hi[2] & 0xffffu) | (hi[3] << 16);
+  return x;
+}
+
+// Workgroup (r, s): stage slice s of rank r's payload as tagged words, then
+// poll slice s of all R ranks' tagged payloads and fold it in rank order into
+// rank r's output.  stats.retries counts poll rounds that found a word not yet
+// tagged (lane 0 of each workgroup).
+template <int R, bool BF16>
+__global__ void __launch_bounds__(64) lamport_chain_kernel(SnacArgs a) {
+  const int r = blockIdx.x / a.S;
+  const int s = blockIdx.x - r * a.S;
+  const int bs = blockDim.x;
+  const int64_t v0 = static_cast<int64_t>(s) * a.slice_vec;
+  const int64_t v1 = min(a.nvec, v0 + a.slice_vec);
+  const int64_t tbytes = 2 * a.rank_bytes;  // tagged bytes per rank
+  constexpr int CU = R <= 8 ? 2 : 1;        // payload vectors per lane per pass
+  constexpr int kLU = 4;                    // payload vectors per lane per stage pass
+  unsigned long long polls = 0, timeouts = 0, done_epochs = 0;
+
+  for (int k = 0; k < a.epochs; ++k) {
+    const uint32_t ep = a.epoch0 + static_cast<uint32_t>(k);
+    const uint32_t T = (ep & 0xffffu) << 16;
+    unsigned char *tb = a.tagged + static_cast<int64_t>(ep & 1u) * R * tbytes;
+
+    // Test hook: a late rank.
+    if (a.stagger) {
+      const uint32_t d = a.stagger[r];
+      for (uint32_t i = 0; i < d; ++i) __builtin_amdgcn_s_sleep(1);
+    }
+
+    // Stage: the store is the notification.
+    const unsigned char *src = a.in + (static_cast<int64_t>(k) * R + r) * a.rank_bytes;
+    const __amdgpu_buffer_rsrc_t mine = rsrc(tb + static_cast<int64_t>(r) * tbytes, tbytes);
+    for (int64_t i0 = v0 + threadIdx.x; i0 < v1; i0 += static_cast<int64_t>(bs) * kLU) {
+      v4u x[kLU];
+#pragma unroll
+      for (int u = 0; u < kLU; ++u) {
+        const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+        if (i < v1) x[u] = *reinterpret_cast<const v4u *>(src + i * 16);
+      }
+#pragma unroll
+      for (int u = 0; u < kLU; ++u) {
+        const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+        if (i < v1) {
+          v4u lo, hi;
+          tag_halves(x[u], T, lo, hi);
+          store_tagged(mine, static_cast<int32_t>(i * 32), lo);
+          store_tagged(mine, static_cast<int32_t>(i * 32 + 16), hi);
+        }
+      }
+    }
+
+    // Consume: poll until every word this lane needs carries the tag, then
+    // fold in rank order.
+    unsigned char *dst = a.out + (static_cast<int64_t>(k) * R + r) * a.rank_bytes;
+    bool ok = true;
+    for (int64_t i0 = v0 + threadIdx.x; i0 < v1; i0 += static_cast<int64_t>(bs) * CU) {
+      v4u lo[CU][R], hi[CU][R];
+      uint32_t spins = 0;
+      while (true) {
+        bool ready = true;
+#pragma unroll
+        for (int u = 0; u < CU; ++u) {
+          const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+          if (i < v1) {
+#pragma unroll
+            for (int q = 0; q < R; ++q) {
+              const __amdgpu_buffer_rsrc_t src_q = rsrc(tb + static_cast<int64_t>(q) * tbytes, tbytes);
+              lo[u][q] = load_tagged(src_q, static_cast<int32_t>(i * 32));
+              hi[u][q] = load_tagged(src_q, static_cast<int32_t>(i * 32 + 16));
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < CU; ++u) {
+          const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+          if (i < v1) {
+#pragma unroll
+            for (int q = 0; q < R; ++q)
+              ready = ready && tagged_with(lo[u][q], T) && tagged_with(hi[u][q], T);
+          }
+        }
+        if (ready) break;
+        ++polls;
+        if ((spins & 63) == 0 && load_flag_relaxed(a.status) != 0) {
+          ok = false;
+          break;
+        }
+        if (++spins >= a.spin_limit) {
+          __hip_atomic_store(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ok = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (!ok) break;
+#pragma unroll
+      for (int u = 0; u < CU; ++u) {
+        const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+        if (i < v1) {
+          uint4 v[R];
+#pragma unroll
+          for (int q = 0; q < R; ++q) v[q] = untag(lo[u][q], hi[u][q]);
+          reduce_pass<R, BF16>(v, dst + i * 16);
+        }
+      }
+    }
+    // Every lane leaves together once any lane gave up.
+    if (__any(!ok)) {
+      ++timeouts;
+      break;
+    }
+    ++done_epochs;
+  }
+
+  if (a.stats && threadIdx.x == 0) {
+    if (polls) atomicAdd(&a.stats->retries, polls);
+    if (timeouts) atomicAdd(&a.stats->timeouts, timeouts);
+    atomicAdd(&a.stats->epochs, done_epochs);
+  }
+}
+
 __global__ void fill_u32_kernel(uint32_t *p, int64_t n, uint32_t v) {
   for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x)
@@ -447,7 +622,8 @@ SnacFn snac_for(int R) {
   switch (R) {
 #define RRB_CASE(n) \
   case n:           \
-    return snac_chain_kernel<n, BF16, VAR>;
+    if constexpr (VAR == kLamport) return lamport_chain_kernel<n, BF16>; \
+    else return snac_chain_kernel<n, BF16, VAR>;
     RRB_CASE(1) RRB_CASE(2) RRB_CASE(3) RRB_CASE(4) RRB_CASE(5) RRB_CASE(6) RRB_CASE(7)
     RRB_CASE(8) RRB_CASE(9) RRB_CASE(10) RRB_CASE(11) RRB_CASE(12) RRB_CASE(13)
     RRB_CASE(14) RRB_CASE(15) RRB_CASE(16)
@@ -561,8 +737,11 @@ rrb_status rrb_snac_create(int32_t nranks, int64_t count, int32_t dtype, uint32_
   if (nranks < 1 || nranks > RRB_MAX_RANKS)
     return fail(RRB_EINVAL, "nranks %d outside 1..%d", nranks, RRB_MAX_RANKS);
   if (dtype != RRB_BF16 && dtype != RRB_F32) return fail(RRB_EINVAL, "unknown dtype %d", dtype);
-  if (flags & ~(RRB_SNAC_DUAL_BUFFER | RRB_SNAC_SPECULATIVE | RRB_SNAC_GRAPH | RRB_SNAC_TWOSHOT))
+  if (flags & ~(RRB_SNAC_DUAL_BUFFER | RRB_SNAC_SPECULATIVE | RRB_SNAC_GRAPH | RRB_SNAC_TWOSHOT |
+                RRB_SNAC_LAMPORT))
     return fail(RRB_EINVAL, "unknown SNAC flags 0x%x", flags);
+  if ((flags & RRB_SNAC_LAMPORT) && flags != (RRB_SNAC_LAMPORT | RRB_SNAC_DUAL_BUFFER))
+    return fail(RRB_EINVAL, "RRB_SNAC_LAMPORT goes with RRB_SNAC_DUAL_BUFFER only");
   if ((flags & RRB_SNAC_TWOSHOT) && flags != (RRB_SNAC_TWOSHOT | RRB_SNAC_DUAL_BUFFER))
     return fail(RRB_EINVAL, "RRB_SNAC_TWOSHOT goes with RRB_SNAC_DUAL_BUFFER only");
   if ((flags & RRB_SNAC_GRAPH) && flags != RRB_SNAC_GRAPH)
@@ -572,7 +751,7 @@ rrb_status rrb_snac_create(int32_t nranks, int64_t count, int32_t dtype, uint32_
   const int esz = elem_size(dtype);
   if (count <= 0 || (count * esz) % 16)
     return fail(RRB_EUNSUPPORTED, "chain payloads must be a positive multiple of 16 bytes");
-  if (2LL * nranks * count * esz > 0x7fffffffLL)
+  if (2LL * nranks * count * esz * ((flags & RRB_SNAC_LAMPORT) ? 2 : 1) > 0x7fffffffLL)
     return fail(RRB_EUNSUPPORTED, "staging above 2 GiB");
   if (slices < 0 || slices > kMaxSlices)
     return fail(RRB_EINVAL, "slices %d outside 0..%d", slices, kMaxSlices);
@@ -587,7 +766,19 @@ rrb_status rrb_snac_create(int32_t nranks, int64_t count, int32_t dtype, uint32_
     // fastest with 8 workgroups per rank (each workgroup's agent-scope fences
     // serialise, so more of them cost more than they parallelise); larger
     // payloads with about 1024 vectors per workgroup, up to 32 per rank.
-    if (nvec <= 4096) {
+    if (flags & RRB_SNAC_LAMPORT) {
+      // Flag-in-data has no fences; its time follows the coherent loads per
+      // lane, so small payloads take one vector per lane (64 per workgroup),
+      // then 32 per workgroup; above 256 KiB, 128 workgroups per rank (more
+      // of them only add poll traffic).  Measured on MI355X, 8 ranks.
+      if (nvec < 4096) {
+        S = static_cast<int32_t>(std::max<int64_t>(1, nvec / 64));
+      } else if (nvec <= 16384) {
+        S = static_cast<int32_t>(std::min<int64_t>(256, nvec / 32));
+      } else {
+        S = 128;
+      }
+    } else if (nvec <= 4096) {
       S = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(8, nvec / 64)));
     } else {
       S = static_cast<int32_t>(std::min<int64_t>(32, std::max<int64_t>(8, nvec / 1024)));
@@ -603,7 +794,7 @@ rrb_status rrb_snac_create(int32_t nranks, int64_t count, int32_t dtype, uint32_
   h->flags = flags;
   h->S = S;
   h->bs = bs;
-  h->lay = layout_for(nranks, count, dtype, S);
+  h->lay = layout_for(nranks, count, dtype, S, (flags & RRB_SNAC_LAMPORT) != 0);
   if (flags & RRB_SNAC_GRAPH) {
     rrb_spec sp;
     std::memset(&sp, 0, sizeof sp);
@@ -691,13 +882,15 @@ rrb_status rrb_snac_allreduce_chain(rrb_snac_t h, int32_t epochs, const void *d_
   a.flag2 = reinterpret_cast<uint32_t *>(h->ws + h->lay.flag2_off);
   a.chunk_vec = (a.nvec + h->R - 1) / h->R;
   a.piece_vec = (a.chunk_vec + h->S - 1) / h->S;
+  a.tagged = h->ws + h->lay.tagged_off;
   a.epoch0 = h->next_epoch;
   a.epochs = epochs;
   a.S = h->S;
   a.spin_limit = spin_limit ? spin_limit : kDefaultSpin;
 
   const bool bf16 = h->dtype == RRB_BF16;
-  const int var = (h->flags & RRB_SNAC_TWOSHOT) ? kTwoshot
+  const int var = (h->flags & RRB_SNAC_LAMPORT) ? kLamport
+                  : (h->flags & RRB_SNAC_TWOSHOT) ? kTwoshot
                   : (h->flags & RRB_SNAC_SPECULATIVE) ? kSpeculative
                   : (h->flags & RRB_SNAC_DUAL_BUFFER) ? kDual : kBarrier;
   SnacFn fn = nullptr;
@@ -705,11 +898,13 @@ rrb_status rrb_snac_allreduce_chain(rrb_snac_t h, int32_t epochs, const void *d_
     fn = var == kBarrier ? snac_for<true, kBarrier>(h->R)
          : var == kDual  ? snac_for<true, kDual>(h->R)
          : var == kTwoshot ? snac_for<true, kTwoshot>(h->R)
+         : var == kLamport ? snac_for<true, kLamport>(h->R)
                            : snac_for<true, kSpeculative>(h->R);
   } else {
     fn = var == kBarrier ? snac_for<false, kBarrier>(h->R)
          : var == kDual  ? snac_for<false, kDual>(h->R)
          : var == kTwoshot ? snac_for<false, kTwoshot>(h->R)
+         : var == kLamport ? snac_for<false, kLamport>(h->R)
                            : snac_for<false, kSpeculative>(h->R);
   }
   // Every workgroup waits on others: the grid must be co-resident, which a

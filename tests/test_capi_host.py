@@ -194,6 +194,15 @@ def test_snac_create_validation(librrb):
     assert lib.rrb_snac_create(8, 4096, 0, 11, 0, ctypes.byref(h)) == L.RRB_EINVAL  # + speculative
     assert lib.rrb_snac_create(8, 4096, 0, 9, 0, ctypes.byref(h)) == L.RRB_OK
     lib.rrb_snac_destroy(h)
+    assert lib.rrb_snac_create(8, 4096, 0, 16, 0, ctypes.byref(h)) == L.RRB_EINVAL  # lamport alone
+    assert lib.rrb_snac_create(8, 4096, 0, 19, 0, ctypes.byref(h)) == L.RRB_EINVAL  # + speculative
+    assert lib.rrb_snac_create(8, 4096, 0, 25, 0, ctypes.byref(h)) == L.RRB_EINVAL  # + twoshot
+    assert lib.rrb_snac_create(8, 4096, 0, 17, 0, ctypes.byref(h)) == L.RRB_OK
+    ws = ctypes.c_size_t()
+    assert lib.rrb_snac_workspace(h, ctypes.byref(ws)) == L.RRB_OK
+    # two tagged buffers of 8 ranks x 4096 bf16 halves, 4 bytes each, + status
+    assert ws.value == 2 * 8 * 4096 * 4 + 256
+    lib.rrb_snac_destroy(h)
     assert lib.rrb_snac_create(8, 4096, 0, 4, 0, ctypes.byref(h)) == L.RRB_OK
     lib.rrb_snac_destroy(h)
     assert lib.rrb_snac_create(8, 4096, 0, 3, 0, ctypes.byref(h)) == L.RRB_OK

@@ -5,7 +5,8 @@ exact oracle All-Reduce of that epoch's payloads, for the barrier, dual-buffer
 and speculative variants, at every payload of the decode chain workload
 (b in 1..64 tokens x h in {4096, 8192} bf16, N(0, 0.02)).  Protocol stress:
 staggered ranks (a test hook delays rank r before every stage), the pages'
-own 100k-iteration exact-match check for the speculative variant, and a
+own 100k-iteration exact-match check for the speculative and flag-in-data
+variants, and a
 bounded wait forced to expire from the host (tiny poll budget), which must
 end the kernel and report RRB_ETIMEOUT rather than hang."""
 
@@ -22,8 +23,8 @@ from tests.gpu_util import DEV, assert_bits_equal, from_dev, require_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = ["barrier", "dual", "speculative", "twoshot", "graph"]
-FLAG_VARIANTS = ["barrier", "dual", "speculative", "twoshot"]
+VARIANTS = ["barrier", "dual", "speculative", "twoshot", "lamport", "graph"]
+FLAG_VARIANTS = ["barrier", "dual", "speculative", "twoshot", "lamport"]
 R = 8
 EPOCHS = 64
 
@@ -69,7 +70,10 @@ def test_chain_all_variants_bit_exact(b, h):
 def _slices_of(ch):
     # the library's default slices per rank for a payload of nvec vectors
     nvec = ch.count * 2 // 16
-    S = max(1, min(8, nvec // 64)) if nvec <= 4096 else min(32, max(8, nvec // 1024))
+    if ch.variant == "lamport":
+        S = max(1, nvec // 64) if nvec < 4096 else min(256, nvec // 32) if nvec <= 16384 else 128
+    else:
+        S = max(1, min(8, nvec // 64)) if nvec <= 4096 else min(32, max(8, nvec // 1024))
     return min(S, 2048 // R, nvec)
 
 
@@ -101,6 +105,9 @@ def test_chain_staggered_ranks(v):
         if v == "speculative":
             _say(f"  misspec {s[0]} retries {s[1]}")
             assert s[0] > 0  # late ranks force the retry path
+        if v == "lamport":
+            _say(f"  poll rounds {s[1]}")
+            assert s[1] > 0  # late ranks leave untagged words to poll again
 
 
 @pytest.mark.parametrize("slices", [1, 3, 8])
@@ -142,17 +149,19 @@ def test_chain_other_rank_counts_and_fp32():
                     assert_bits_equal(got[e, r], want[e], f"R={Rx} {dt} {v} e={e} r={r}")
 
 
-def test_speculative_100k_iterations_exact():
+@pytest.mark.parametrize("v", ["speculative", "lamport"])
+def test_100k_iterations_exact(v):
     """The pages' correctness check for speculative reduction: 100k chained
     All-Reduces, every result bit-exact (here against precomputed oracle
-    results; payloads cycle through 256 seeded input sets)."""
+    results; payloads cycle through 256 seeded input sets).  Run for the
+    flag-in-data variant as well."""
     require_gpu()
     n, pool, per_call, total = 4096, 256, 256, 100_000
     ins_np = inputs.chain(pool, R, n, kind=80)
     want = np.stack(OC.allreduce_chain(ins_np))  # [pool, n]
     inp = to_dev(ins_np)
     want_dev = to_dev(np.repeat(want[:, None, :], R, axis=1))  # [pool, R, n]
-    ch = api.SnacChain(R, n, "bf16", "speculative")
+    ch = api.SnacChain(R, n, "bf16", v)
     stats = torch.zeros(4, dtype=torch.int64, device=DEV)
     out = torch.empty_like(inp)
     done = 0
@@ -162,14 +171,14 @@ def test_speculative_100k_iterations_exact():
         if not torch.equal(out, want_dev):
             ch.check()
             bad = (out != want_dev).nonzero()
-            raise AssertionError(f"speculative mismatch after {done} epochs at {bad[:5].tolist()}")
+            raise AssertionError(f"{v} mismatch after {done} epochs at {bad[:5].tolist()}")
         done += per_call
         calls += 1
         if calls % 100 == 0:
             _say(f"  {done} epochs exact")
     ch.check()
     s = stats.cpu().tolist()
-    _say(f"100k: misspec {s[0]} retries {s[1]} epochs {done}")
+    _say(f"100k {v}: misspec {s[0]} retries {s[1]} epochs {done}")
 
 
 def test_bounded_wait_times_out_cleanly():
@@ -182,7 +191,7 @@ def test_bounded_wait_times_out_cleanly():
     st = [0] * R
     st[7] = 20000
     stagger = torch.tensor(st, dtype=torch.int32, device=DEV)
-    for v in ("barrier", "dual", "twoshot"):
+    for v in ("barrier", "dual", "twoshot", "lamport"):
         ch = api.SnacChain(R, n, "bf16", v)
         stats = torch.zeros(4, dtype=torch.int64, device=DEV)
         out = torch.empty_like(inp)
