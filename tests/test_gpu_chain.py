@@ -1,14 +1,14 @@
 """GPU parity of the SNAC decode chain against the oracle, through the C ABI.
 
 Each of the 64 epochs (32 layers x 2 All-Reduces) must give every rank the
-exact oracle All-Reduce of that epoch's payloads, for the barrier, dual-buffer
-and speculative variants, at every payload of the decode chain workload
-(b in 1..64 tokens x h in {4096, 8192} bf16, N(0, 0.02)).  Protocol stress:
-staggered ranks (a test hook delays rank r before every stage), the pages'
-own 100k-iteration exact-match check for the speculative and flag-in-data
-variants, and a
-bounded wait forced to expire from the host (tiny poll budget), which must
-end the kernel and report RRB_ETIMEOUT rather than hang."""
+exact oracle All-Reduce of that epoch's payloads, for the barrier,
+dual-buffer, speculative, twoshot, flag-in-data and graph variants, at every
+payload of the decode chain workload (b in 1..64 tokens x h in {4096, 8192}
+bf16, N(0, 0.02)).  Protocol stress: staggered ranks (a test hook delays rank
+r before every stage), the pages' own 100k-iteration exact-match check for
+the speculative and flag-in-data variants, and a bounded wait forced to
+expire from the host (tiny poll budget), which must end the kernel and report
+RRB_ETIMEOUT rather than hang."""
 
 import sys
 
