@@ -25,6 +25,7 @@ plainest reading:
   meaning all copies are equal).
 * ``reduce``: the input must be ``PARTIAL``; the output element named X[j]
   receives the fixed-order fold over ranks 0..R-1 of P_r[j] (``fold.py``).
+  ``reduce_tree`` is the same with the tree-order fold.
 
 ``collective`` below applies that definition element by element (slow; for
 small cases).  The seven named collectives are then written out directly from
@@ -100,7 +101,7 @@ def collective(in_layout, out_layout, op, ins, R, n, dtype="bf16"):
                 o[i] = ins[r][k]
             outs.append(o)
         return outs
-    if op == "reduce":
+    if op in ("reduce", "reduce_tree"):
         if _kind(in_layout) != PARTIAL:
             raise ValueError("reduce needs a PARTIAL input layout")
         for q in range(R):
@@ -113,7 +114,8 @@ def collective(in_layout, out_layout, op, ins, R, n, dtype="bf16"):
                     raise ValueError("reduce output must name elements of X")
                 idx.append(nm[1])
             idx = np.asarray(idx, dtype=np.int64)
-            outs.append(fold.reduce([np.asarray(ins[r])[idx] for r in range(R)], dtype))
+            cols = [np.asarray(ins[r])[idx] for r in range(R)]
+            outs.append(fold.reduce(cols, dtype) if op == "reduce" else fold.reduce_tree(cols, dtype))
         return outs
     raise ValueError(f"unknown op {op!r}")
 

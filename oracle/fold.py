@@ -20,6 +20,17 @@ when every term is -0, where starting at x_0 keeps -0).
 Parity pinned by: an exact rational emulation of binary32 addition on tiny
 inputs (tests/test_oracle_fold.py), closed forms and the recursive-summation
 error bound.
+
+Tree order (an optional, flagged variant; a reading -- the pages fix no tree).
+Pairwise summation level by level: adjacent items (0, 1), (2, 3), ... are
+added with one binary32 addition each, an odd last item passes up unchanged,
+until one item is left; for R = 8 that is
+((x0 + x1) + (x2 + x3)) + ((x4 + x5) + (x6 + x7)).  For R <= 3 it coincides
+with the fixed order.  Its result may differ from the fixed-order fold by
+rounding; the bound it must meet against that fold is
+|d| <= max(1 ulp_bf16(y), 2 (R - 1) 2^-24 sum |x_r|).  Pinned by hand-worked
+cases where the association changes the result, the exact emulation of the
+same tree, and that bound.
 """
 
 import numpy as np
@@ -47,6 +58,30 @@ def reduce_bf16(ins):
 def reduce_f32(ins):
     """R float32 payloads -> float32 fixed-order sum (no final rounding)."""
     return fold_f32(ins)
+
+
+def fold_tree_f32(xs):
+    """Tree-order fp32 sum of R float32 arrays (see the module docstring)."""
+    items = [np.asarray(x, dtype=np.float32) for x in xs]
+    if not items:
+        raise ValueError("fold needs at least one rank")
+    with np.errstate(over="ignore", invalid="ignore"):
+        while len(items) > 1:
+            nxt = [(items[i] + items[i + 1]).astype(np.float32)
+                   for i in range(0, len(items) - 1, 2)]
+            if len(items) % 2:
+                nxt.append(items[-1])
+            items = nxt
+    return items[0].copy()
+
+
+def reduce_tree(ins, dtype):
+    """Tree-order reduce: bf16 payloads round once at the end, f32 do not."""
+    if dtype == "bf16":
+        return bf16.rne(fold_tree_f32([bf16.widen(x) for x in ins]))
+    if dtype == "f32":
+        return fold_tree_f32(ins)
+    raise ValueError(f"unknown dtype {dtype!r}")
 
 
 def reduce(ins, dtype):
