@@ -405,6 +405,7 @@ def bench_seven(args, dev):
     souts = [torch.empty(c, dtype=torch.int16, device=dev) for _ in range(R)]
     cases = {
         "all_reduce": (lambda: rrb.all_reduce(full, outs), 2 * R * S),
+        "all_reduce_tree_order": (lambda: rrb.all_reduce(full, outs, order="tree"), 2 * R * S),
         "reduce_scatter": (lambda: rrb.reduce_scatter(full, souts), (R + 1) * S),
         "all_gather": (lambda: rrb.all_gather(shards, outs), (R + 1) * S),
         "all_to_all": (lambda: rrb.all_to_all(full, outs), 2 * R * S),

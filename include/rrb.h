@@ -48,7 +48,14 @@ typedef int32_t rrb_status;
 typedef void *rrb_stream_t; /* hipStream_t */
 
 typedef enum { RRB_BF16 = 0, RRB_F32 = 1 } rrb_dtype;
-typedef enum { RRB_COPY = 0, RRB_REDUCE_SUM = 1 } rrb_op;
+/* RRB_REDUCE_SUM folds in fixed rank order 0..R-1.  RRB_REDUCE_SUM_TREE is an
+ * opt-in variant that folds pairwise, level by level (adjacent ranks pair up,
+ * an odd last partial sum passes up unchanged: ((0+1)+(2+3))+((4+5)+(6+7))
+ * for R = 8), still in fp32 with one final rounding; it may differ from the
+ * fixed order by rounding, within max(1 bf16 ulp, 2 (R-1) 2^-24 sum |x|).
+ * The tree is this library's reading: the pages name no order other than
+ * the fixed one. */
+typedef enum { RRB_COPY = 0, RRB_REDUCE_SUM = 1, RRB_REDUCE_SUM_TREE = 2 } rrb_op;
 
 /*
  * Layout names.  The pages say only that a collective names an input and an
@@ -233,9 +240,10 @@ rrb_status rrb_copy(rrb_plan_t plan, const void *const *d_in,
 
 /*
  * Atom reduce (same passage: reduce is the other primitive).  Same argument
- * rules as rrb_copy; requires a reduce plan.  Elementwise fold in fixed rank
- * order with fp32 accumulation and one round-to-nearest-even to bf16 (the
- * result is bit-identical in every output that receives it).
+ * rules as rrb_copy; requires a reduce plan (RRB_REDUCE_SUM or
+ * RRB_REDUCE_SUM_TREE).  Elementwise fold in the plan's order with fp32
+ * accumulation and one round-to-nearest-even to bf16 (the result is
+ * bit-identical in every output that receives it).
  */
 rrb_status rrb_reduce(rrb_plan_t plan, const void *const *d_in,
                       void *const *d_out, rrb_stream_t stream);

@@ -17,6 +17,7 @@ RRB_BF16 = 0
 RRB_F32 = 1
 RRB_COPY = 0
 RRB_REDUCE_SUM = 1
+RRB_REDUCE_SUM_TREE = 2
 
 RRB_PARTIAL = 0
 RRB_REPLICATED = 1

@@ -51,6 +51,18 @@ def _ptrs(tensors, R):
     return L.ptr_array(out)
 
 
+_OPS = {"copy": L.RRB_COPY, "reduce": L.RRB_REDUCE_SUM, "reduce_tree": L.RRB_REDUCE_SUM_TREE}
+
+
+def _op_code(op):
+    """'copy', 'reduce' (fixed rank order) or 'reduce_tree' (tree order)."""
+    if isinstance(op, int):
+        return op  # passed through; the library validates it
+    if op not in _OPS:
+        raise ValueError(f"unknown op {op!r}")
+    return _OPS[op]
+
+
 class Plan:
     """A layout-naming spec compiled to an index map (rrb_plan_create)."""
 
@@ -61,7 +73,7 @@ class Plan:
         spec.count = int(count)
         spec.in_ = _layout(in_layout)
         spec.out = _layout(out_layout)
-        spec.op = L.RRB_REDUCE_SUM if op in ("reduce", L.RRB_REDUCE_SUM) else L.RRB_COPY
+        spec.op = _op_code(op)
         spec.reserved = 0
         self._lib = L.lib()
         h = ctypes.c_void_p()
@@ -104,9 +116,9 @@ class Plan:
 
     def run(self, ins, outs, stream=None):
         """Atom copy or reduce, whichever the plan names, on torch's stream."""
-        fn = self._lib.rrb_reduce if self.op == L.RRB_REDUCE_SUM else self._lib.rrb_copy
+        fn = self._lib.rrb_copy if self.op == L.RRB_COPY else self._lib.rrb_reduce
         L.check(fn(self.handle, _ptrs(ins, self.nranks), _ptrs(outs, self.nranks), _stream(stream)),
-                "rrb_reduce" if self.op == L.RRB_REDUCE_SUM else "rrb_copy")
+                "rrb_copy" if self.op == L.RRB_COPY else "rrb_reduce")
 
     def __del__(self):
         h = getattr(self, "handle", None)
@@ -147,8 +159,8 @@ class Bound:
     __slots__ = ("_fn", "_h", "_in", "_out", "_keep", "_name")
 
     def __init__(self, p, ins, outs):
-        self._fn = p._lib.rrb_reduce if p.op == L.RRB_REDUCE_SUM else p._lib.rrb_copy
-        self._name = "rrb_reduce" if p.op == L.RRB_REDUCE_SUM else "rrb_copy"
+        self._fn = p._lib.rrb_copy if p.op == L.RRB_COPY else p._lib.rrb_reduce
+        self._name = "rrb_copy" if p.op == L.RRB_COPY else "rrb_reduce"
         self._h = p.handle
         self._in = _ptrs(ins, p.nranks)
         self._out = _ptrs(outs, p.nranks)
@@ -181,12 +193,19 @@ def bound(name, ins, outs, root=None):
 
 
 # The seven collectives (count = elements of the logical tensor X).
-def all_reduce(ins, outs, stream=None):
-    return collective(PARTIAL, REPLICATED, "reduce", ins, outs, ins[0].numel(), stream)
+def _reduce_op(order):
+    if order not in ("fixed", "tree"):
+        raise ValueError(f"unknown reduce order {order!r}")
+    return "reduce" if order == "fixed" else "reduce_tree"
 
 
-def reduce_scatter(ins, outs, stream=None):
-    return collective(PARTIAL, SHARD, "reduce", ins, outs, ins[0].numel(), stream)
+def all_reduce(ins, outs, stream=None, order="fixed"):
+    """order: 'fixed' (rank order 0..R-1) or 'tree' (pairwise, opt-in)."""
+    return collective(PARTIAL, REPLICATED, _reduce_op(order), ins, outs, ins[0].numel(), stream)
+
+
+def reduce_scatter(ins, outs, stream=None, order="fixed"):
+    return collective(PARTIAL, SHARD, _reduce_op(order), ins, outs, ins[0].numel(), stream)
 
 
 def all_gather(ins, outs, stream=None):
@@ -201,8 +220,8 @@ def broadcast(ins, outs, root, stream=None):
     return collective(ROOT(root), REPLICATED, "copy", ins, outs, ins[root].numel(), stream)
 
 
-def reduce(ins, outs, root, stream=None):
-    return collective(PARTIAL, ROOT(root), "reduce", ins, outs, ins[0].numel(), stream)
+def reduce(ins, outs, root, stream=None, order="fixed"):
+    return collective(PARTIAL, ROOT(root), _reduce_op(order), ins, outs, ins[0].numel(), stream)
 
 
 def gather(ins, outs, root, stream=None):

@@ -80,8 +80,9 @@ __device__ __forceinline__ int xcd_tile(int local, int C) {
 
 // ---- kernels ---------------------------------------------------------------
 
-template <int R, int U, bool BF16, bool NTL, bool NTS>
-__global__ void __launch_bounds__(256) reduce_vec_kernel(UniArgs a) {
+// Body of the vector reduce; TREE selects the tree-order fold.
+template <int R, int U, bool BF16, bool NTL, bool NTS, bool TREE>
+__device__ __forceinline__ void reduce_vec_body(const UniArgs &a) {
   const int bs = blockDim.x;
   const int item = blockIdx.x / a.tiles;
   const int tile = xcd_tile(blockIdx.x - item * a.tiles, a.xcd_chunk);
@@ -102,7 +103,7 @@ __global__ void __launch_bounds__(256) reduce_vec_kernel(UniArgs a) {
   for (int u = 0; u < U; ++u) {
     const int64_t i = base + static_cast<int64_t>(u) * bs;
     if (i < a.nvec) {
-      const uint4 res = BF16 ? fold_bf16x8<R>(v[u]) : fold_f32x4<R>(v[u]);
+      const uint4 res = fold_vec<R, BF16, TREE>(v[u]);
       for (uint32_t m = it.dst_mask; m; m &= m - 1) {
         const int q = __builtin_ctz(m);
         st16<NTS>(a.out[q] + it.dst_off + i * 16, res);
@@ -114,21 +115,26 @@ __global__ void __launch_bounds__(256) reduce_vec_kernel(UniArgs a) {
   if (a.tail && tile == a.tiles - 1 && threadIdx.x < a.tail) {
     const int64_t e = a.nvec * (BF16 ? 8 : 4) + threadIdx.x;
     const int esz = BF16 ? 2 : 4;
-    if (BF16) {
-      float acc = bf16_to_f32(*reinterpret_cast<const uint16_t *>(a.in[0] + it.src_off + e * esz));
+    float t[R];
 #pragma unroll
-      for (int r = 1; r < R; ++r)
-        acc = acc + bf16_to_f32(*reinterpret_cast<const uint16_t *>(a.in[r] + it.src_off + e * esz));
+    for (int r = 0; r < R; ++r)
+      t[r] = BF16 ? bf16_to_f32(*reinterpret_cast<const uint16_t *>(a.in[r] + it.src_off + e * esz))
+                  : *reinterpret_cast<const float *>(a.in[r] + it.src_off + e * esz);
+    float acc;
+    if (TREE) {
+      acc = tree_sum<R>(t);
+    } else {
+      acc = t[0];
+#pragma unroll
+      for (int r = 1; r < R; ++r) acc = acc + t[r];
+    }
+    if (BF16) {
       const uint16_t b = f32_to_bf16_rne(acc);
       for (uint32_t m = it.dst_mask; m; m &= m - 1) {
         const int q = __builtin_ctz(m);
         *reinterpret_cast<uint16_t *>(a.out[q] + it.dst_off + e * esz) = b;
       }
     } else {
-      float acc = *reinterpret_cast<const float *>(a.in[0] + it.src_off + e * esz);
-#pragma unroll
-      for (int r = 1; r < R; ++r)
-        acc = acc + *reinterpret_cast<const float *>(a.in[r] + it.src_off + e * esz);
       for (uint32_t m = it.dst_mask; m; m &= m - 1) {
         const int q = __builtin_ctz(m);
         *reinterpret_cast<float *>(a.out[q] + it.dst_off + e * esz) = acc;
@@ -137,15 +143,44 @@ __global__ void __launch_bounds__(256) reduce_vec_kernel(UniArgs a) {
   }
 }
 
+template <int R, int U, bool BF16, bool NTL, bool NTS>
+__global__ void __launch_bounds__(256) reduce_vec_kernel(UniArgs a) {
+  reduce_vec_body<R, U, BF16, NTL, NTS, false>(a);
+}
+
+// Tree-order reduce (opt-in op RRB_REDUCE_SUM_TREE), one vector per lane.
+template <int R, bool BF16, bool NTL, bool NTS>
+__global__ void __launch_bounds__(256) reduce_tree_vec_kernel(UniArgs a) {
+  reduce_vec_body<R, 1, BF16, NTL, NTS, true>(a);
+}
+
 // Element-at-a-time reduce for buffers or offsets that are not 16-byte
 // aligned: correct for any layout, not tuned.
-template <bool BF16>
-__global__ void __launch_bounds__(256) reduce_elem_kernel(UniArgs a) {
+template <bool BF16, bool TREE>
+__device__ __forceinline__ void reduce_elem_body(const UniArgs &a) {
   const int item = blockIdx.x / a.tiles;
   const int tile = blockIdx.x - item * a.tiles;
   const KItem it = a.items[item];
   const int64_t e = static_cast<int64_t>(tile) * blockDim.x + threadIdx.x;
   if (e >= a.nelem) return;
+  if (TREE) {
+    float t[RRB_MAX_RANKS];
+#pragma unroll
+    for (int r = 0; r < RRB_MAX_RANKS; ++r)
+      t[r] = r >= a.nranks ? 0.f
+             : BF16 ? bf16_to_f32(*reinterpret_cast<const uint16_t *>(a.in[r] + it.src_off + e * 2))
+                    : *reinterpret_cast<const float *>(a.in[r] + it.src_off + e * 4);
+    const float acc = tree_sum_n<RRB_MAX_RANKS>(t, a.nranks);
+    if (BF16) {
+      const uint16_t b = f32_to_bf16_rne(acc);
+      for (uint32_t m = it.dst_mask; m; m &= m - 1)
+        *reinterpret_cast<uint16_t *>(a.out[__builtin_ctz(m)] + it.dst_off + e * 2) = b;
+    } else {
+      for (uint32_t m = it.dst_mask; m; m &= m - 1)
+        *reinterpret_cast<float *>(a.out[__builtin_ctz(m)] + it.dst_off + e * 4) = acc;
+    }
+    return;
+  }
   if (BF16) {
     float acc = bf16_to_f32(*reinterpret_cast<const uint16_t *>(a.in[0] + it.src_off + e * 2));
     for (int r = 1; r < a.nranks; ++r)
@@ -160,6 +195,16 @@ __global__ void __launch_bounds__(256) reduce_elem_kernel(UniArgs a) {
     for (uint32_t m = it.dst_mask; m; m &= m - 1)
       *reinterpret_cast<float *>(a.out[__builtin_ctz(m)] + it.dst_off + e * 4) = acc;
   }
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(256) reduce_elem_kernel(UniArgs a) {
+  reduce_elem_body<BF16, false>(a);
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(256) reduce_tree_elem_kernel(UniArgs a) {
+  reduce_elem_body<BF16, true>(a);
 }
 
 template <int U, bool NTS>
@@ -226,14 +271,14 @@ constexpr int kOneBlock = 64;
 // past the end repeat the last vector's work and store the same bits.
 // ALL: every rank is a destination (ndst == R), so the stores unroll with
 // all destination pointers fetched up front.
-template <int R, bool BF16, bool ALL>
-__global__ void __launch_bounds__(kOneBlock) reduce_one_kernel(OneArgs a) {
+template <int R, bool BF16, bool ALL, bool TREE>
+__device__ __forceinline__ void reduce_one_body(const OneArgs &a) {
   const int i = min(static_cast<int>(blockIdx.x) * kOneBlock + static_cast<int>(threadIdx.x),
                     a.nvec - 1);
   uint4 v[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) v[r] = *reinterpret_cast<const uint4 *>(a.in[r] + static_cast<int64_t>(i) * 16);
-  const uint4 res = BF16 ? fold_bf16x8<R>(v) : fold_f32x4<R>(v);
+  const uint4 res = fold_vec<R, BF16, TREE>(v);
   if (ALL) {
 #pragma unroll
     for (int q = 0; q < R; ++q) *reinterpret_cast<uint4 *>(a.out[q] + static_cast<int64_t>(i) * 16) = res;
@@ -243,19 +288,36 @@ __global__ void __launch_bounds__(kOneBlock) reduce_one_kernel(OneArgs a) {
   }
   if (a.tail && blockIdx.x == gridDim.x - 1 && static_cast<int>(threadIdx.x) < a.tail) {
     const int64_t e = static_cast<int64_t>(a.nvec) * (BF16 ? 8 : 4) + threadIdx.x;
-    if (BF16) {
-      float acc = bf16_to_f32(*reinterpret_cast<const uint16_t *>(a.in[0] + e * 2));
+    float t[R];
 #pragma unroll
-      for (int r = 1; r < R; ++r) acc = acc + bf16_to_f32(*reinterpret_cast<const uint16_t *>(a.in[r] + e * 2));
+    for (int r = 0; r < R; ++r)
+      t[r] = BF16 ? bf16_to_f32(*reinterpret_cast<const uint16_t *>(a.in[r] + e * 2))
+                  : *reinterpret_cast<const float *>(a.in[r] + e * 4);
+    float acc;
+    if (TREE) {
+      acc = tree_sum<R>(t);
+    } else {
+      acc = t[0];
+#pragma unroll
+      for (int r = 1; r < R; ++r) acc = acc + t[r];
+    }
+    if (BF16) {
       const uint16_t b = f32_to_bf16_rne(acc);
       for (int q = 0; q < a.ndst; ++q) *reinterpret_cast<uint16_t *>(a.out[q] + e * 2) = b;
     } else {
-      float acc = *reinterpret_cast<const float *>(a.in[0] + e * 4);
-#pragma unroll
-      for (int r = 1; r < R; ++r) acc = acc + *reinterpret_cast<const float *>(a.in[r] + e * 4);
       for (int q = 0; q < a.ndst; ++q) *reinterpret_cast<float *>(a.out[q] + e * 4) = acc;
     }
   }
+}
+
+template <int R, bool BF16, bool ALL>
+__global__ void __launch_bounds__(kOneBlock) reduce_one_kernel(OneArgs a) {
+  reduce_one_body<R, BF16, ALL, false>(a);
+}
+
+template <int R, bool BF16, bool ALL>
+__global__ void __launch_bounds__(kOneBlock) reduce_tree_one_kernel(OneArgs a) {
+  reduce_one_body<R, BF16, ALL, true>(a);
 }
 
 __global__ void __launch_bounds__(kOneBlock) copy_one_kernel(OneArgs a) {
@@ -278,6 +340,20 @@ __global__ void empty_kernel() {}
 namespace {
 
 using ReduceFn = void (*)(UniArgs);
+
+template <bool BF16, bool NTL, bool NTS>
+ReduceFn reduce_tree_vec_for(int R) {
+  switch (R) {
+#define RRB_CASE(n) \
+  case n:           \
+    return reduce_tree_vec_kernel<n, BF16, NTL, NTS>;
+    RRB_CASE(1) RRB_CASE(2) RRB_CASE(3) RRB_CASE(4) RRB_CASE(5) RRB_CASE(6) RRB_CASE(7)
+    RRB_CASE(8) RRB_CASE(9) RRB_CASE(10) RRB_CASE(11) RRB_CASE(12) RRB_CASE(13)
+    RRB_CASE(14) RRB_CASE(15) RRB_CASE(16)
+#undef RRB_CASE
+  }
+  return nullptr;
+}
 
 template <int U, bool BF16, bool NTL, bool NTS>
 ReduceFn reduce_vec_for(int R) {
@@ -325,12 +401,13 @@ rrb_status check_buffers(const Plan &p, const void *const *in, void *const *out)
 
 using OneFn = void (*)(OneArgs);
 
-template <bool BF16, bool ALL>
+template <bool BF16, bool ALL, bool TREE>
 OneFn reduce_one_for(int R) {
   switch (R) {
 #define RRB_CASE(n) \
   case n:           \
-    return reduce_one_kernel<n, BF16, ALL>;
+    if constexpr (TREE) return reduce_tree_one_kernel<n, BF16, ALL>; \
+    else return reduce_one_kernel<n, BF16, ALL>;
     RRB_CASE(1) RRB_CASE(2) RRB_CASE(3) RRB_CASE(4) RRB_CASE(5) RRB_CASE(6) RRB_CASE(7)
     RRB_CASE(8) RRB_CASE(9) RRB_CASE(10) RRB_CASE(11) RRB_CASE(12) RRB_CASE(13)
     RRB_CASE(14) RRB_CASE(15) RRB_CASE(16)
@@ -366,7 +443,8 @@ constexpr int64_t kOneMaxVectors = 4096;
 rrb_status launch_one(const Plan &p, const void *const *in, void *const *out, Emitter &emit) {
   const int esz = elem_size(p.dtype);
   const Segment &sg = p.segs[0];
-  const bool reduce = p.op == RRB_REDUCE_SUM;
+  const bool reduce = p.op != RRB_COPY;
+  const bool tree = p.op == RRB_REDUCE_SUM_TREE;
   OneArgs a;
   std::memset(&a, 0, sizeof a);
   if (reduce) {
@@ -383,11 +461,17 @@ rrb_status launch_one(const Plan &p, const void *const *in, void *const *out, Em
   const unsigned grid = static_cast<unsigned>((a.nvec + kOneBlock - 1) / kOneBlock);
   const bool all = a.ndst == p.nranks;
   const bool bf16 = p.dtype == RRB_BF16;
-  OneFn kern = reduce ? (all ? (bf16 ? reduce_one_for<true, true>(p.nranks)
-                                     : reduce_one_for<false, true>(p.nranks))
-                             : (bf16 ? reduce_one_for<true, false>(p.nranks)
-                                     : reduce_one_for<false, false>(p.nranks)))
-                      : copy_one_kernel;
+  OneFn kern = copy_one_kernel;
+  if (reduce && !tree)
+    kern = all ? (bf16 ? reduce_one_for<true, true, false>(p.nranks)
+                       : reduce_one_for<false, true, false>(p.nranks))
+               : (bf16 ? reduce_one_for<true, false, false>(p.nranks)
+                       : reduce_one_for<false, false, false>(p.nranks));
+  else if (reduce)
+    kern = all ? (bf16 ? reduce_one_for<true, true, true>(p.nranks)
+                       : reduce_one_for<false, true, true>(p.nranks))
+               : (bf16 ? reduce_one_for<true, false, true>(p.nranks)
+                       : reduce_one_for<false, false, true>(p.nranks));
   return emit(kern, dim3(grid), dim3(kOneBlock), a, reduce ? "reduce" : "copy");
 }
 
@@ -416,7 +500,8 @@ rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out
   }
   a.nranks = p.nranks;
   a.nelem = len;
-  const bool reduce = p.op == RRB_REDUCE_SUM;
+  const bool reduce = p.op != RRB_COPY;
+  const bool tree = p.op == RRB_REDUCE_SUM_TREE;
   const bool bf16 = p.dtype == RRB_BF16;
 
   int bs;
@@ -439,8 +524,15 @@ rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out
     bs = small ? 64 : 256;
     if (reduce) {
       const bool fan = __builtin_popcount(p.segs[0].dst_mask) > 1;
-      U = (small || !big || p.nranks > 8) ? 1 : 2;
-      if (U == 1) {
+      U = (small || !big || p.nranks > 8 || tree) ? 1 : 2;
+      if (tree) {
+        kern = stream ? (fan ? (bf16 ? reduce_tree_vec_for<true, true, true>(p.nranks)
+                                     : reduce_tree_vec_for<false, true, true>(p.nranks))
+                             : (bf16 ? reduce_tree_vec_for<true, true, false>(p.nranks)
+                                     : reduce_tree_vec_for<false, true, false>(p.nranks)))
+                      : (bf16 ? reduce_tree_vec_for<true, false, false>(p.nranks)
+                              : reduce_tree_vec_for<false, false, false>(p.nranks));
+      } else if (U == 1) {
         kern = stream ? (fan ? (bf16 ? reduce_vec_for<1, true, true, true>(p.nranks)
                                      : reduce_vec_for<1, false, true, true>(p.nranks))
                              : (bf16 ? reduce_vec_for<1, true, true, false>(p.nranks)
@@ -469,7 +561,9 @@ rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out
   } else {
     bs = 256;
     U = 1;
-    kern = reduce ? (bf16 ? reduce_elem_kernel<true> : reduce_elem_kernel<false>) : copy_elem_kernel;
+    kern = !reduce ? copy_elem_kernel
+           : tree  ? (bf16 ? reduce_tree_elem_kernel<true> : reduce_tree_elem_kernel<false>)
+                   : (bf16 ? reduce_elem_kernel<true> : reduce_elem_kernel<false>);
     // the element copy moves 2-byte units
     if (!reduce) a.nelem = len * esz / 2;
     a.tiles = static_cast<int32_t>((a.nelem + bs - 1) / bs);
@@ -533,7 +627,8 @@ rrb_status rrb_reduce(rrb_plan_t plan, const void *const *d_in, void *const *d_o
   clear_error();
   if (!plan) return fail(RRB_EINVAL, "NULL plan");
   const Plan &p = plan->p;
-  if (p.op != RRB_REDUCE_SUM) return fail(RRB_EINVAL, "rrb_reduce needs a reduce plan");
+  if (p.op != RRB_REDUCE_SUM && p.op != RRB_REDUCE_SUM_TREE)
+    return fail(RRB_EINVAL, "rrb_reduce needs a reduce plan");
   rrb_status s = check_buffers(p, d_in, d_out);
   if (s != RRB_OK) return s;
   if (p.kind != PlanKind::Uniform) return launch_rows(p, d_in, d_out, stream);

@@ -54,6 +54,75 @@ __device__ __forceinline__ uint4 fold_bf16x8(const uint4 (&v)[R]) {
   return o;
 }
 
+// Tree-order sum of R fp32 terms held in t[] (overwritten): pairwise, level
+// by level -- at stride s the partial sum at index i (a multiple of 2s) takes
+// in the one at i + s when that exists -- so adjacent items pair up and an odd
+// last item passes up unchanged; R = 8 gives ((0+1)+(2+3))+((4+5)+(6+7)).
+// Every index is a compile-time constant after unrolling (registers only).
+template <int R>
+__device__ __forceinline__ float tree_sum(float (&t)[R]) {
+#pragma unroll
+  for (int s = 1; s < R; s *= 2) {
+#pragma unroll
+    for (int i = 0; i + s < R; i += 2 * s) t[i] = t[i] + t[i + s];
+  }
+  return t[0];
+}
+
+// The same tree for a run-time rank count n <= N (predicated, still in
+// registers).
+template <int N>
+__device__ __forceinline__ float tree_sum_n(float (&t)[N], int n) {
+#pragma unroll
+  for (int s = 1; s < N; s *= 2) {
+#pragma unroll
+    for (int i = 0; i + s < N; i += 2 * s)
+      if (i + s < n) t[i] = t[i] + t[i + s];
+  }
+  return t[0];
+}
+
+// Tree-order fold of 8 bf16 lanes from R sources, one rounding at the end.
+template <int R>
+__device__ __forceinline__ uint4 fold_tree_bf16x8(const uint4 (&v)[R]) {
+  float s[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    float t[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t w = k < 2 ? v[r].x : k < 4 ? v[r].y : k < 6 ? v[r].z : v[r].w;
+      t[r] = (k & 1) ? bf16_hi(w) : bf16_lo(w);
+    }
+    s[k] = tree_sum<R>(t);
+  }
+  uint4 o;
+  o.x = pack_bf16x2(s[0], s[1]);
+  o.y = pack_bf16x2(s[2], s[3]);
+  o.z = pack_bf16x2(s[4], s[5]);
+  o.w = pack_bf16x2(s[6], s[7]);
+  return o;
+}
+
+template <int R>
+__device__ __forceinline__ uint4 fold_tree_f32x4(const uint4 (&v)[R]) {
+  float s[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float t[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      t[r] = __uint_as_float(k == 0 ? v[r].x : k == 1 ? v[r].y : k == 2 ? v[r].z : v[r].w);
+    s[k] = tree_sum<R>(t);
+  }
+  uint4 o;
+  o.x = __float_as_uint(s[0]);
+  o.y = __float_as_uint(s[1]);
+  o.z = __float_as_uint(s[2]);
+  o.w = __float_as_uint(s[3]);
+  return o;
+}
+
 template <int R>
 __device__ __forceinline__ uint4 fold_f32x4(const uint4 (&v)[R]) {
   float a0 = __uint_as_float(v[0].x), a1 = __uint_as_float(v[0].y);
@@ -71,6 +140,13 @@ __device__ __forceinline__ uint4 fold_f32x4(const uint4 (&v)[R]) {
   o.z = __float_as_uint(a2);
   o.w = __float_as_uint(a3);
   return o;
+}
+
+// One 16-byte vector of R sources in the fixed rank order or in tree order.
+template <int R, bool BF16, bool TREE>
+__device__ __forceinline__ uint4 fold_vec(const uint4 (&v)[R]) {
+  if (TREE) return BF16 ? fold_tree_bf16x8<R>(v) : fold_tree_f32x4<R>(v);
+  return BF16 ? fold_bf16x8<R>(v) : fold_f32x4<R>(v);
 }
 
 }  // namespace rrb

@@ -89,7 +89,7 @@ rrb_status build_uniform_plan(const rrb_spec &spec, Plan &plan) {
     return fail(RRB_EINVAL, "nranks %d outside 1..%d", R, RRB_MAX_RANKS);
   if (spec.dtype != RRB_BF16 && spec.dtype != RRB_F32)
     return fail(RRB_EINVAL, "unknown dtype %d", spec.dtype);
-  if (spec.op != RRB_COPY && spec.op != RRB_REDUCE_SUM)
+  if (spec.op != RRB_COPY && spec.op != RRB_REDUCE_SUM && spec.op != RRB_REDUCE_SUM_TREE)
     return fail(RRB_EINVAL, "unknown op %d", spec.op);
   if (spec.count < 0) return fail(RRB_EINVAL, "negative count");
   if (spec.reserved != 0) return fail(RRB_EINVAL, "reserved field must be 0");
@@ -103,7 +103,7 @@ rrb_status build_uniform_plan(const rrb_spec &spec, Plan &plan) {
     return fail(RRB_EINVAL, "PARTIAL names contributions and cannot be an output layout");
   if (m_space(in.kind) != m_space(out.kind))
     return fail(RRB_EINVAL, "BLOCK_ROW/BLOCK_COL only pair with each other");
-  const bool reduce = spec.op == RRB_REDUCE_SUM;
+  const bool reduce = spec.op != RRB_COPY;
   if (reduce != (in.kind == RRB_PARTIAL))
     return fail(RRB_EINVAL, reduce ? "reduce needs a PARTIAL input layout"
                                    : "a PARTIAL input needs the reduce op");

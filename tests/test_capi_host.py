@@ -128,6 +128,8 @@ def test_other_namings(librrb):
     ((17, 64, api.PARTIAL, api.REPLICATED, "reduce"), "nranks"),
     ((8, 64, api.REPLICATED, api.PARTIAL, "copy"), "cannot be an output"),
     ((8, 64, api.ROOT(1), api.BLOCK_COL, "copy"), "only pair"),
+    ((8, 64, api.SHARD, api.REPLICATED, "reduce_tree"), "PARTIAL input"),
+    ((8, 64, api.PARTIAL, api.REPLICATED, 3), "unknown op"),
 ])
 def test_invalid_specs(librrb, spec, msg):
     R, n, i, o, op = spec
@@ -135,6 +137,17 @@ def test_invalid_specs(librrb, spec, msg):
         api.Plan(R, n, "bf16", i, o, op)
     assert e.value.status == L.RRB_EINVAL
     assert msg in str(e.value)
+
+
+def test_tree_op_plans_like_reduce(librrb):
+    """The tree order changes only the fold inside the kernel: the index map
+    is the fixed-order reduce's."""
+    for out in (api.REPLICATED, api.SHARD, api.ROOT(2)):
+        a = api.Plan(8, 64, "bf16", api.PARTIAL, out, "reduce")
+        b = api.Plan(8, 64, "bf16", api.PARTIAL, out, "reduce_tree")
+        assert a.segments() == b.segments()
+        assert (a.in_count, a.out_count) == (b.in_count, b.out_count)
+        assert b.op == L.RRB_REDUCE_SUM_TREE
 
 
 def test_zero_count_plan(librrb):
