@@ -12,6 +12,9 @@ Also reported on the same line:
 * ``roofline``: the dominant kernel (the 256 MiB All-Reduce reduce kernel):
   algorithmic bytes per launch / its mean duration from HIP events on the
   launch stream, against the 8 TB/s HBM peak;
+* ``sweep``: per size and collective, the in-step (warm) rate and a cold
+  rate (a 1 GiB scratch read before each call empties the caches; measured
+  after the timed region);
 * ``decode``: the batch-1 decode All-Reduce (8 ranks x 4096 bf16), kernel
   time from events and back-to-back time per call, next to an empty kernel;
 * ``cpu_baseline``: the CPU oracle on a bounded sample of the same workload.
@@ -148,6 +151,30 @@ def main():
     ar_bytes = alg_bytes(big[2])[0]
     ar_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in per_case_events[big[0]]]))
     achieved = ar_bytes / (ar_ms * 1e-3) / 1e9
+
+    # ---- cold-cache timings (outside the timed region) ---------------------
+    # Before each timed call an untimed read of a 1 GiB scratch buffer (written
+    # once) evicts the 256 MB Infinity Cache and the L2s and leaves them
+    # holding clean lines, so inputs come from HBM and no earlier dirty data
+    # is written back during the call; median of 5 per operation.
+    scratch = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    for label, dtype, Sb, *_ in cases:
+        ab = alg_bytes(Sb)
+        cold = {}
+        for k, op, b in zip(("all_reduce", "reduce_scatter", "all_gather"), ops[label], ab):
+            ts = []
+            for _ in range(5):
+                scratch.sum()
+                e0, e1 = ev(), ev()
+                e0.record()
+                op()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            m = float(np.median(ts))
+            cold[k] = {"us": round(m * 1e3, 2), "GBps": round(b / (m * 1e-3) / 1e9, 1)}
+        sweep[label]["cold"] = cold
+    del scratch
 
     # ---- decode All-Reduce latency (8 x 4096 bf16) -------------------------
     dec_host = inputs.decode_allreduce()
@@ -467,8 +494,15 @@ def cpu_baseline(host_inputs):
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": round(total / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
-            "host_cores_visible": cores, "kind": "oracle", "seconds": round(dt, 2),
+            "host_cores_visible": cores, "cpu_model": model, "kind": "oracle",
+            "seconds": round(dt, 2),
             "sample": "one full step: All-Reduce -> Reduce-Scatter -> All-Gather, 8 ranks x "
                       "{1,4,16,64,256} MiB bf16 + 64 MiB fp32 (numpy, single thread)"}
 
