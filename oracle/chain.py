@@ -10,7 +10,7 @@ to match the barrier variant exactly over 100k iterations).  So the oracle of
 the chain is the per-epoch All-Reduce, with no orchestration at all.
 """
 
-from . import fold
+from . import collectives, fold
 
 
 def allreduce_chain(ins_by_epoch, dtype="bf16"):
@@ -19,3 +19,13 @@ def allreduce_chain(ins_by_epoch, dtype="bf16"):
     Every rank's output at epoch e is this same array (bit-identical).
     """
     return [fold.reduce(list(ins), dtype) for ins in ins_by_epoch]
+
+
+def collective_chain(name, ins_by_epoch, dtype="bf16", root=None):
+    """A chain of any of the seven named collectives: epoch e's outputs are the
+    plain collective of that epoch's R inputs (Purlin news page, "The Purlin
+    PDF describes a three-layer design": the orchestration layer is reused
+    unchanged whatever collective the datapath runs).  Returns, per epoch, the
+    list of R outputs (None where the output layout gives a rank nothing).
+    ``root`` defaults to the root the seven-collective workload uses."""
+    return [collectives.named(name, list(ins), dtype, root=root) for ins in ins_by_epoch]

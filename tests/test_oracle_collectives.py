@@ -174,3 +174,25 @@ def test_ragged_all_reduce_any_n():
     ins = _payloads(R, n, 15)
     got = C.collective(C.PARTIAL, C.REPLICATED, "reduce", ins, R, n)
     _same(got, C.all_reduce(ins))
+
+
+def test_collective_chain_is_per_epoch_collective():
+    """The chain oracle adds no orchestration: an All-Reduce chain equals the
+    All-Reduce chain oracle on every rank, and an All-Gather chain's epoch e
+    is the concatenation of that epoch's shards."""
+    from oracle import chain as OC
+    rng = np.random.default_rng(21)
+    E, R, c = 3, 4, 8
+    ins = [[bf16.rne(rng.standard_normal(R * c).astype(np.float32)) for _ in range(R)]
+           for _ in range(E)]
+    ar = OC.collective_chain("all_reduce", ins)
+    for e, want in enumerate(OC.allreduce_chain(ins)):
+        for q in range(R):
+            assert np.array_equal(ar[e][q], want)
+    shards = [[x[:c] for x in ins[e]] for e in range(E)]
+    ag = OC.collective_chain("all_gather", shards)
+    for e in range(E):
+        for q in range(R):
+            assert np.array_equal(ag[e][q], np.concatenate(shards[e]))
+    g = OC.collective_chain("gather", shards, root=2)
+    assert all(g[e][q] is None for e in range(E) for q in range(R) if q != 2)
