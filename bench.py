@@ -357,9 +357,43 @@ def bench_chain(args, dev):
                 "us_per_allreduce": round(graph_us_per_launch(torch, separate, per_graph=1, replays=20) / E, 3)}
             rows.append(res)
             log(json.dumps(res))
+    # Chains of every layout-named collective through the plan-driven SNAC
+    # kernel: 8 ranks, a 16 KiB bf16 tensor per rank (shards of 2 KiB).
+    n = 8192
+    plan_rows = {}
+    for name in ("all_reduce", "reduce_scatter", "all_gather", "all_to_all", "broadcast",
+                 "reduce", "gather"):
+        lin, lout, op = {
+            "all_reduce": (rrb.PARTIAL, rrb.REPLICATED, "reduce"),
+            "reduce_scatter": (rrb.PARTIAL, rrb.SHARD, "reduce"),
+            "all_gather": (rrb.SHARD, rrb.REPLICATED, "copy"),
+            "all_to_all": (rrb.BLOCK_ROW, rrb.BLOCK_COL, "copy"),
+            "broadcast": (rrb.ROOT(3), rrb.REPLICATED, "copy"),
+            "reduce": (rrb.PARTIAL, rrb.ROOT(0), "reduce"),
+            "gather": (rrb.SHARD, rrb.ROOT(5), "copy"),
+        }[name]
+        plan = rrb.Plan(R, n, "bf16", lin, lout, op)
+        res = {}
+        for v in ("barrier", "dual", "speculative", "graph"):
+            ch = rrb.SnacPlanChain(plan, v)
+            si, so = ch.strides
+            pin = torch.from_numpy(inputs.chain(E, R, si, kind=40).view(np.int16)).to(dev)
+            pout = torch.empty((E, R, so), dtype=torch.int16, device=dev)
+            stats = torch.zeros(4, dtype=torch.int64, device=dev)
+            for _ in range(3):
+                ch.run(pin, pout)
+            ms = _events_ms(torch, lambda: ch.run(pin, pout, stats=stats), max(5, args.steps))
+            ch.check()
+            res[v] = {"us_per_collective": round(float(np.median(ms)) * 1e3 / E, 3),
+                      "misspec_per_call": round(stats[0].item() / max(5, args.steps), 2)}
+        plan_rows[name] = res
+        log(json.dumps({name: res}))
     print(json.dumps({"metric": "us per All-Reduce in a 64-deep decode chain", "unit": "us",
                       "higher_is_better": False, "workload": "decode chain, 8 ranks, b x h bf16 N(0,0.02)",
-                      "rows": rows}), flush=True)
+                      "rows": rows,
+                      "plan_chains": {"workload": "64-deep chains of each layout-named collective, "
+                                                  "8 ranks, 16 KiB bf16 tensor per rank",
+                                      "rows": plan_rows}}), flush=True)
 
 
 def bench_moe(args, dev):

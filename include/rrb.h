@@ -340,6 +340,41 @@ rrb_status rrb_snac_allreduce_chain(rrb_snac_t h, int32_t epochs,
                                     rrb_snac_stats *d_stats,
                                     const uint32_t *d_stagger,
                                     uint32_t spin_limit, rrb_stream_t stream);
+/*
+ * Chains of any layout-named collective (Purlin news page, "The Purlin PDF
+ * describes a three-layer design": the orchestration layer is the same
+ * whatever collective the datapath runs).  `plan` is a uniform plan from
+ * rrb_plan_create (copy or fixed-order reduce; the handle keeps its own copy,
+ * so the plan may be destroyed afterwards).  Every map entry must start, end
+ * and sit on 16-byte boundaries, and every rank's input must be a 16-byte
+ * multiple (RRB_EUNSUPPORTED otherwise).  flags: 0 (top and bottom barrier),
+ * RRB_SNAC_DUAL_BUFFER, RRB_SNAC_DUAL_BUFFER | RRB_SNAC_SPECULATIVE (flags
+ * read first, whole consume, then the reduced check of all R x slices
+ * flags), or RRB_SNAC_GRAPH (one Atom launch per epoch in a cached HIP
+ * graph).  Workgroup (r, s) stages slice s of rank r's input and computes
+ * piece s of every map entry whose output is rank r; the top barrier covers
+ * every rank's every slice, since a piece may read any of them.
+ * Workspace, bind, check and destroy as for rrb_snac_create.
+ */
+rrb_status rrb_snac_create_plan(rrb_plan_t plan, uint32_t flags, int32_t slices,
+                                rrb_snac_t *out);
+/* Bytes between consecutive ranks' buffers in d_in / d_out of a chain: the
+ * largest per-rank input (output) of the plan, rounded up to 16 bytes; for an
+ * All-Reduce handle both are count x element size. */
+rrb_status rrb_snac_strides(rrb_snac_t h, int64_t *in_stride, int64_t *out_stride);
+/*
+ * Run `epochs` collectives of the handle's plan (or All-Reduces of an
+ * rrb_snac_create handle).  Rank r's input of epoch e starts at
+ * d_in + (e * R + r) * in_stride bytes and holds in_count[r] elements; its
+ * output at d_out + (e * R + r) * out_stride holds out_count[r] elements
+ * (outputs of ranks the plan does not write are left untouched).  Other
+ * arguments, the epoch counter and ordering rules as for
+ * rrb_snac_allreduce_chain, which is this call restricted to All-Reduce
+ * handles.
+ */
+rrb_status rrb_snac_chain(rrb_snac_t h, int32_t epochs, const void *d_in, void *d_out,
+                          rrb_snac_stats *d_stats, const uint32_t *d_stagger,
+                          uint32_t spin_limit, rrb_stream_t stream);
 /* Synchronise `stream` and report RRB_ETIMEOUT if any chain call on this
  * handle since bind timed out (the handle is unusable until rebound). */
 rrb_status rrb_snac_check(rrb_snac_t h, rrb_stream_t stream);

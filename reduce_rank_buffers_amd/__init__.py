@@ -10,7 +10,7 @@ it has no fallback: without ``librrb.so`` every call raises.
 
 from .api import (  # noqa: F401
     PARTIAL, REPLICATED, SHARD, BLOCK_ROW, BLOCK_COL, ROOT,
-    Plan, MoePlan, MoeDevicePlan, SnacChain, plan, collective,
+    Plan, MoePlan, MoeDevicePlan, SnacChain, SnacPlanChain, plan, collective,
     all_reduce, reduce_scatter, all_gather, all_to_all, broadcast, reduce, gather,
     empty_kernel, bound, Bound,
 )

@@ -45,6 +45,7 @@ EXPORTS = (
     "rrb_plan_segments", "rrb_plan_destroy",
     "rrb_copy", "rrb_reduce", "rrb_empty_kernel",
     "rrb_snac_create", "rrb_snac_workspace", "rrb_snac_bind", "rrb_snac_allreduce_chain",
+    "rrb_snac_create_plan", "rrb_snac_strides", "rrb_snac_chain",
     "rrb_snac_check", "rrb_snac_destroy",
 )
 
@@ -103,6 +104,9 @@ _SIGS = {
     "rrb_snac_workspace": (_I32, [_P, ctypes.POINTER(_SZ)]),
     "rrb_snac_bind": (_I32, [_P, _P, _SZ, _P]),
     "rrb_snac_allreduce_chain": (_I32, [_P, _I32, _P, _P, _P, _P, _U32, _P]),
+    "rrb_snac_create_plan": (_I32, [_P, _U32, _I32, ctypes.POINTER(_P)]),
+    "rrb_snac_strides": (_I32, [_P, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
+    "rrb_snac_chain": (_I32, [_P, _I32, _P, _P, _P, _P, _U32, _P]),
     "rrb_snac_check": (_I32, [_P, _P]),
     "rrb_snac_destroy": (None, [_P]),
 }

@@ -351,3 +351,46 @@ class SnacChain:
         if h is not None and h.value:
             self._lib.rrb_snac_destroy(h)
             self.handle = None
+
+
+PLAN_CHAIN_VARIANTS = {"barrier": 0, "dual": L.RRB_SNAC_DUAL_BUFFER,
+                       "speculative": L.RRB_SNAC_DUAL_BUFFER | L.RRB_SNAC_SPECULATIVE,
+                       "graph": L.RRB_SNAC_GRAPH}
+
+
+class SnacPlanChain(SnacChain):
+    """A bound SNAC handle chaining any layout-named collective (a Plan):
+    back-to-back collectives of that plan in one persistent kernel (or a
+    graph of Atom launches for variant 'graph').  Inputs are
+    [epochs, R, in_stride] and outputs [epochs, R, out_stride] in elements
+    (``strides``)."""
+
+    def __init__(self, plan, variant="dual", slices=0, device=None, stream=None):
+        self._lib = L.lib()
+        h = ctypes.c_void_p()
+        L.check(self._lib.rrb_snac_create_plan(plan.handle, PLAN_CHAIN_VARIANTS[variant], int(slices),
+                                               ctypes.byref(h)), "rrb_snac_create_plan")
+        self.handle = h
+        self.nranks = plan.nranks
+        self.variant = variant
+        self.esize = 4 if plan.dtype == L.RRB_F32 else 2
+        si, so = ctypes.c_int64(), ctypes.c_int64()
+        L.check(self._lib.rrb_snac_strides(h, ctypes.byref(si), ctypes.byref(so)), "rrb_snac_strides")
+        self.strides = (si.value // self.esize, so.value // self.esize)
+        ws = ctypes.c_size_t()
+        L.check(self._lib.rrb_snac_workspace(h, ctypes.byref(ws)), "rrb_snac_workspace")
+        dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self._ws = torch.empty(ws.value + 256, dtype=torch.uint8, device=dev)
+        base = (self._ws.data_ptr() + 255) // 256 * 256
+        L.check(self._lib.rrb_snac_bind(h, ctypes.c_void_p(base), ws.value, _stream(stream)),
+                "rrb_snac_bind")
+
+    def run(self, inp, out, stats=None, stagger=None, spin_limit=0, stream=None):
+        """inp: [epochs, R, in_stride], out: [epochs, R, out_stride] device tensors."""
+        E = inp.shape[0]
+        L.check(self._lib.rrb_snac_chain(
+            self.handle, int(E), ctypes.c_void_p(inp.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+            ctypes.c_void_p(stats.data_ptr() if stats is not None else 0),
+            ctypes.c_void_p(stagger.data_ptr() if stagger is not None else 0),
+            int(spin_limit), _stream(stream)), "rrb_snac_chain")
+        return out

@@ -87,7 +87,8 @@ struct SnacArgs {
 };
 
 struct Layout {
-  int64_t staging_off, reduced_off, flag_off, flag2_off, done_off, tagged_off, status_off, total;
+  int64_t staging_off, entries_off, reduced_off, flag_off, flag2_off, done_off, tagged_off,
+      status_off, total;
 };
 
 // staging [2][R][count] | reduced [2][count] | flags [2][R][S] | flags2 [2][R][S]
@@ -101,6 +102,7 @@ Layout layout_for(int32_t R, int64_t count, int32_t dtype, int32_t S, bool lampo
   Layout l;
   l.staging_off = 0;
   const int64_t staging = lamport ? 0 : up(2LL * R * rank_bytes);
+  l.entries_off = staging;
   l.reduced_off = staging;
   const int64_t reduced = lamport ? 0 : up(2LL * rank_bytes);
   l.flag_off = l.reduced_off + reduced;
@@ -111,6 +113,32 @@ Layout layout_for(int32_t R, int64_t count, int32_t dtype, int32_t S, bool lampo
   l.tagged_off = l.done_off + done;
   const int64_t tagged = lamport ? up(2LL * R * 2 * rank_bytes) : 0;
   l.status_off = l.tagged_off + tagged;
+  l.total = l.status_off + 256;
+  return l;
+}
+
+// Chains of any uniform plan: one consume entry per (output rank, segment),
+// offsets and lengths in 16-byte vectors.  src_rank < 0: reduce over all
+// ranks in rank order.
+struct PlanEntry {
+  int64_t src_off, dst_off, len;
+  int32_t src_rank, pad;
+};
+
+// staging [2][R][in_stride] | entries | flags [2][R][S] | done [R][S] | status;
+// the entries are uploaded at bind, everything from flag_off on is cleared.
+Layout layout_for_plan(int32_t R, int64_t in_stride, int32_t S, int64_t nentries) {
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  Layout l;
+  l.staging_off = 0;
+  l.entries_off = up(2LL * R * in_stride);
+  l.reduced_off = l.entries_off + up(nentries * static_cast<int64_t>(sizeof(PlanEntry)));
+  l.flag_off = l.reduced_off;
+  const int64_t flags = up(2LL * R * S * kFlagStride * 4);
+  l.flag2_off = l.flag_off + flags;
+  l.done_off = l.flag2_off;
+  l.tagged_off = l.done_off + up(1LL * R * S * kFlagStride * 4);
+  l.status_off = l.tagged_off;
   l.total = l.status_off + 256;
   return l;
 }
@@ -609,6 +637,248 @@ __global__ void __launch_bounds__(64) lamport_chain_kernel(SnacArgs a) {
   }
 }
 
+// ---- chains of any uniform plan ---------------------------------------------
+//
+// The same stage / notify / consume orchestration over a plan's index map
+// (Purlin news page, "The Purlin PDF describes a three-layer design": the
+// orchestration layer stays the same while the collective changes).
+// Workgroup (r, s) stages slice s of rank r's input, publishes
+// flag[buf][r][s] = epoch, then computes piece s of every map entry whose
+// output is rank r (a copy from one staged rank, or a rank-order fold over
+// all of them).  A piece can read any staged slice of its sources, so the top
+// barrier waits for every rank's every slice: with two buffers that also
+// proves that every reader of this workgroup's slice finished the previous
+// epoch on this buffer, the write-after-read guard of dual buffering.
+// Speculation reads all flags first, then consumes with device-coherent loads
+// and keeps the result only if the flags summed to (R S) epoch; otherwise it
+// waits and consumes again (outputs are only read after the kernel).
+
+struct PlanChainArgs {
+  const unsigned char *in;   // [E][R][in_stride bytes]
+  unsigned char *out;        // [E][R][out_stride bytes]
+  unsigned char *staging;    // [2][R][in_stride bytes]
+  uint32_t *flag;            // [2][R][S] x kFlagStride
+  uint32_t *done;            // [R][S] x kFlagStride
+  uint32_t *status;
+  rrb_snac_stats *stats;
+  const uint32_t *stagger;
+  const PlanEntry *entries;  // rank r's entries at [first[r], first[r] + cnt[r])
+  int64_t in_stride, out_stride;
+  int64_t slice_vec;         // staging slice length in vectors
+  int64_t in_vec[RRB_MAX_RANKS];
+  int32_t first[RRB_MAX_RANKS], cnt[RRB_MAX_RANKS];
+  uint32_t epoch0;
+  int32_t epochs;
+  int32_t S;
+  uint32_t spin_limit;
+};
+
+// Every lane waits for its share of the n flags at base + i * kFlagStride;
+// then the (single-wave) workgroup takes one agent-scope acquire.  True in
+// every lane if all n waits succeeded.
+__device__ bool wait_all_n(const uint32_t *base, int n, uint32_t want, uint32_t *status,
+                           uint32_t limit) {
+  bool ok = true;
+  for (int i = threadIdx.x; i < n && ok; i += blockDim.x)
+    ok = wait_at_least(base + static_cast<int64_t>(i) * kFlagStride, want, status, limit);
+  const bool all = __all(ok) != 0;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return all;
+}
+
+// Piece s of every entry of rank r: staged data read with device-coherent
+// loads, results stored to rank r's output of this epoch.
+template <int R, bool BF16>
+__device__ void plan_consume(const PlanChainArgs &a, int r, int s,
+                             const unsigned char *stage_base, unsigned char *dst) {
+  const int bs = blockDim.x;
+  constexpr int CU = R <= 8 ? 2 : 1;
+  constexpr int CC = 4;  // copy vectors per lane in flight
+  for (int g = a.first[r]; g < a.first[r] + a.cnt[r]; ++g) {
+    const PlanEntry e = a.entries[g];
+    const int64_t pl = (e.len + a.S - 1) / a.S;
+    const int64_t lo = min(e.len, static_cast<int64_t>(s) * pl);
+    const int64_t hi = min(e.len, lo + pl);
+    if (e.src_rank < 0) {
+      for (int64_t i0 = lo + threadIdx.x; i0 < hi; i0 += static_cast<int64_t>(bs) * CU) {
+        uint4 v[CU][R];
+#pragma unroll
+        for (int u = 0; u < CU; ++u) {
+          const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+          if (i < hi) {
+#pragma unroll
+            for (int q = 0; q < R; ++q)
+              v[u][q] = load_coherent(rsrc(stage_base + static_cast<int64_t>(q) * a.in_stride,
+                                           a.in_stride),
+                                      static_cast<int32_t>((e.src_off + i) * 16));
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < CU; ++u) {
+          const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+          if (i < hi) reduce_pass<R, BF16>(v[u], dst + (e.dst_off + i) * 16);
+        }
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t src =
+          rsrc(stage_base + static_cast<int64_t>(e.src_rank) * a.in_stride, a.in_stride);
+      for (int64_t i0 = lo + threadIdx.x; i0 < hi; i0 += static_cast<int64_t>(bs) * CC) {
+        uint4 x[CC];
+#pragma unroll
+        for (int u = 0; u < CC; ++u) {
+          const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+          if (i < hi) x[u] = load_coherent(src, static_cast<int32_t>((e.src_off + i) * 16));
+        }
+#pragma unroll
+        for (int u = 0; u < CC; ++u) {
+          const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+          if (i < hi) *reinterpret_cast<uint4 *>(dst + (e.dst_off + i) * 16) = x[u];
+        }
+      }
+    }
+  }
+}
+
+template <int R, bool BF16, int VAR>
+__global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
+  const int r = blockIdx.x / a.S;
+  const int s = blockIdx.x - r * a.S;
+  const int bs = blockDim.x;
+  const int nflags = R * a.S;
+  const int64_t v0 = static_cast<int64_t>(s) * a.slice_vec;
+  const int64_t v1 = min(a.in_vec[r], v0 + a.slice_vec);
+  unsigned long long misspec = 0, retries = 0, timeouts = 0, done_epochs = 0;
+
+  for (int k = 0; k < a.epochs; ++k) {
+    const uint32_t ep = a.epoch0 + static_cast<uint32_t>(k);
+    const int b = VAR == kBarrier ? 0 : static_cast<int>(ep & 1u);
+    unsigned char *stage_base = a.staging + static_cast<int64_t>(b) * R * a.in_stride;
+    uint32_t *flags_b = a.flag + static_cast<int64_t>(b) * nflags * kFlagStride;
+
+    // Test hook: a late rank.
+    if (a.stagger) {
+      const uint32_t d = a.stagger[r];
+      for (uint32_t i = 0; i < d; ++i) __builtin_amdgcn_s_sleep(1);
+    }
+
+    // Stage slice s of rank r's input.
+    const unsigned char *src = a.in + (static_cast<int64_t>(k) * R + r) * a.in_stride;
+    unsigned char *mine = stage_base + static_cast<int64_t>(r) * a.in_stride;
+    for (int64_t i0 = v0 + threadIdx.x; i0 < v1; i0 += static_cast<int64_t>(bs) * kStageU) {
+      v4u x[kStageU];
+#pragma unroll
+      for (int u = 0; u < kStageU; ++u) {
+        const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+        if (i < v1) x[u] = *reinterpret_cast<const v4u *>(src + i * 16);
+      }
+#pragma unroll
+      for (int u = 0; u < kStageU; ++u) {
+        const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+        if (i < v1) *reinterpret_cast<v4u *>(mine + i * 16) = x[u];
+      }
+    }
+
+    // Notify.
+    notify(flags_b + (static_cast<int64_t>(r) * a.S + s) * kFlagStride, ep);
+
+    unsigned char *dst = a.out + (static_cast<int64_t>(k) * R + r) * a.out_stride;
+    bool ok = true;
+    if (VAR == kSpeculative) {
+      // Flags first (relaxed, no wait), the whole consume right after.
+      uint32_t sum = 0;
+      for (int i = threadIdx.x; i < nflags; i += bs)
+        sum += load_flag_relaxed(flags_b + static_cast<int64_t>(i) * kFlagStride);
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      plan_consume<R, BF16>(a, r, s, stage_base, dst);
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) sum += __shfl_xor(sum, m);
+      // Each flag is epoch or epoch - 2, so the sum is exact (no wrap-around
+      // false match: 2 x the stale count stays below 2^32).
+      if (sum == static_cast<uint32_t>(nflags) * ep) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      } else {
+        ++misspec;
+        ++retries;
+        ok = wait_all_n(flags_b, nflags, ep, a.status, a.spin_limit);
+        if (ok) plan_consume<R, BF16>(a, r, s, stage_base, dst);
+      }
+    } else {
+      ok = wait_all_n(flags_b, nflags, ep, a.status, a.spin_limit);
+      if (ok) plan_consume<R, BF16>(a, r, s, stage_base, dst);
+    }
+    if (!ok) {
+      ++timeouts;
+      break;
+    }
+    if (VAR == kBarrier) {
+      // Bottom barrier: every reader of every staged slice is done.
+      notify(a.done + (static_cast<int64_t>(r) * a.S + s) * kFlagStride, ep);
+      if (!wait_all_n(a.done, nflags, ep, a.status, a.spin_limit)) {
+        ++timeouts;
+        break;
+      }
+    }
+    ++done_epochs;
+  }
+
+  if (a.stats && threadIdx.x == 0) {
+    if (misspec) atomicAdd(&a.stats->misspec, misspec);
+    if (retries) atomicAdd(&a.stats->retries, retries);
+    if (timeouts) atomicAdd(&a.stats->timeouts, timeouts);
+    atomicAdd(&a.stats->epochs, done_epochs);
+  }
+}
+
+using PlanChainFn = void (*)(PlanChainArgs);
+
+template <bool BF16, int VAR>
+PlanChainFn snac_plan_for(int R) {
+  switch (R) {
+#define RRB_CASE(n) \
+  case n:           \
+    return snac_plan_kernel<n, BF16, VAR>;
+    RRB_CASE(1) RRB_CASE(2) RRB_CASE(3) RRB_CASE(4) RRB_CASE(5) RRB_CASE(6) RRB_CASE(7)
+    RRB_CASE(8) RRB_CASE(9) RRB_CASE(10) RRB_CASE(11) RRB_CASE(12) RRB_CASE(13)
+    RRB_CASE(14) RRB_CASE(15) RRB_CASE(16)
+#undef RRB_CASE
+  }
+  return nullptr;
+}
+
+// Single-wave workgroups per rank: the caller's count, or chosen from the
+// payload's vectors.  Each wave's own release / acquire covers exactly its
+// own accesses.
+int32_t default_slices(int32_t slices, int64_t nvec, int32_t nranks, uint32_t flags) {
+  int32_t S = slices;
+  if (S == 0) {
+    if (flags & RRB_SNAC_LAMPORT) {
+      // Flag-in-data has no fences; its time follows the coherent loads per
+      // lane, so small payloads take one vector per lane (64 per workgroup),
+      // then 32 per workgroup; above 256 KiB, 128 workgroups per rank (more
+      // of them only add poll traffic).  Measured on MI355X, 8 ranks.
+      if (nvec < 4096) {
+        S = static_cast<int32_t>(std::max<int64_t>(1, nvec / 64));
+      } else if (nvec <= 16384) {
+        S = static_cast<int32_t>(std::min<int64_t>(256, nvec / 32));
+      } else {
+        S = 128;
+      }
+    } else if (nvec <= 4096) {
+      // Measured on MI355X (8 ranks): decode payloads up to 64 KiB per rank
+      // are fastest with 8 workgroups per rank (each workgroup's agent-scope
+      // fences serialise, so more of them cost more than they parallelise);
+      // larger payloads with about 1024 vectors per workgroup, up to 32.
+      S = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(8, nvec / 64)));
+    } else {
+      S = static_cast<int32_t>(std::min<int64_t>(32, std::max<int64_t>(8, nvec / 1024)));
+    }
+    S = std::min<int32_t>(S, 2048 / nranks);
+  }
+  if (S > nvec) S = static_cast<int32_t>(nvec);
+  return S;
+}
+
 __global__ void fill_u32_kernel(uint32_t *p, int64_t n, uint32_t v) {
   for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x)
@@ -645,6 +915,14 @@ struct rrb_snac_s {
   rrb::Layout lay{};
   unsigned char *ws = nullptr;
   uint32_t next_epoch = 1;
+  // Bytes per rank per epoch in d_in / d_out (count * elem size for an
+  // All-Reduce handle).
+  int64_t in_stride = 0, out_stride = 0;
+  // Chains of a plan (rrb_snac_create_plan): the consume entries per rank.
+  bool from_plan = false;
+  std::vector<rrb::PlanEntry> entries;
+  int64_t in_vec[RRB_MAX_RANKS] = {};
+  int32_t first[RRB_MAX_RANKS] = {}, cnt[RRB_MAX_RANKS] = {};
   // RRB_SNAC_GRAPH: one Atom All-Reduce kernel node per epoch, chained in a
   // HIP graph that is cached for the last (in, out, epochs).
   rrb::Plan ar_plan;
@@ -676,15 +954,14 @@ namespace {
 // as a decode step's All-Reduces do.
 rrb_status build_chain_graph(rrb_snac_s *h, int32_t epochs, const void *d_in, void *d_out) {
   h->drop_graph();
-  const int64_t rank_bytes = h->count * elem_size(h->dtype);
   hipError_t e = hipGraphCreate(&h->graph, 0);
   if (e != hipSuccess) return fail(RRB_EHIP, "graph create: %s", hipGetErrorString(e));
   std::vector<const void *> in(h->R);
   std::vector<void *> out(h->R);
   for (int32_t k = 0; k < epochs; ++k) {
     for (int32_t r = 0; r < h->R; ++r) {
-      in[r] = static_cast<const unsigned char *>(d_in) + (static_cast<int64_t>(k) * h->R + r) * rank_bytes;
-      out[r] = static_cast<unsigned char *>(d_out) + (static_cast<int64_t>(k) * h->R + r) * rank_bytes;
+      in[r] = static_cast<const unsigned char *>(d_in) + (static_cast<int64_t>(k) * h->R + r) * h->in_stride;
+      out[r] = static_cast<unsigned char *>(d_out) + (static_cast<int64_t>(k) * h->R + r) * h->out_stride;
     }
     const rrb_status st = describe_uniform(h->ar_plan, in.data(), out.data(), h->g_descs);
     if (st != RRB_OK) {
@@ -722,6 +999,56 @@ rrb_status build_chain_graph(rrb_snac_s *h, int32_t epochs, const void *d_in, vo
   return RRB_OK;
 }
 
+// Issues one plan-chain call (the handle is bound and not in graph mode).
+rrb_status launch_plan_chain(rrb_snac_s *h, int32_t epochs, const void *d_in, void *d_out,
+                             rrb_snac_stats *d_stats, const uint32_t *d_stagger,
+                             uint32_t spin_limit, rrb_stream_t stream) {
+  PlanChainArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.in = static_cast<const unsigned char *>(d_in);
+  a.out = static_cast<unsigned char *>(d_out);
+  a.staging = h->ws + h->lay.staging_off;
+  a.flag = reinterpret_cast<uint32_t *>(h->ws + h->lay.flag_off);
+  a.done = reinterpret_cast<uint32_t *>(h->ws + h->lay.done_off);
+  a.status = reinterpret_cast<uint32_t *>(h->ws + h->lay.status_off);
+  a.stats = d_stats;
+  a.stagger = d_stagger;
+  a.entries = reinterpret_cast<const PlanEntry *>(h->ws + h->lay.entries_off);
+  a.in_stride = h->in_stride;
+  a.out_stride = h->out_stride;
+  int64_t in_vec_max = 0;
+  for (int r = 0; r < h->R; ++r) {
+    a.in_vec[r] = h->in_vec[r];
+    a.first[r] = h->first[r];
+    a.cnt[r] = h->cnt[r];
+    in_vec_max = std::max(in_vec_max, h->in_vec[r]);
+  }
+  a.slice_vec = (in_vec_max + h->S - 1) / h->S;
+  a.epoch0 = h->next_epoch;
+  a.epochs = epochs;
+  a.S = h->S;
+  a.spin_limit = spin_limit ? spin_limit : kDefaultSpin;
+  const bool bf16 = h->dtype == RRB_BF16;
+  const int var = (h->flags & RRB_SNAC_SPECULATIVE) ? kSpeculative
+                  : (h->flags & RRB_SNAC_DUAL_BUFFER) ? kDual : kBarrier;
+  PlanChainFn fn = nullptr;
+  if (bf16)
+    fn = var == kBarrier ? snac_plan_for<true, kBarrier>(h->R)
+         : var == kDual  ? snac_plan_for<true, kDual>(h->R)
+                         : snac_plan_for<true, kSpeculative>(h->R);
+  else
+    fn = var == kBarrier ? snac_plan_for<false, kBarrier>(h->R)
+         : var == kDual  ? snac_plan_for<false, kDual>(h->R)
+                         : snac_plan_for<false, kSpeculative>(h->R);
+  void *args[] = {&a};
+  const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(fn),
+                                                  dim3(h->R * h->S), dim3(h->bs), args, 0,
+                                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RRB_EHIP, "plan chain launch: %s", hipGetErrorString(e));
+  h->next_epoch += static_cast<uint32_t>(epochs);
+  return RRB_OK;
+}
+
 }  // namespace
 }  // namespace rrb
 
@@ -756,36 +1083,7 @@ rrb_status rrb_snac_create(int32_t nranks, int64_t count, int32_t dtype, uint32_
   if (slices < 0 || slices > kMaxSlices)
     return fail(RRB_EINVAL, "slices %d outside 0..%d", slices, kMaxSlices);
   const int64_t nvec = count * esz / 16;
-  // Single-wave workgroups: each wave's own release / acquire covers exactly
-  // its own accesses.  One pass (64 vectors) per workgroup where possible,
-  // up to kMaxSlices workgroups per rank.
-  const int bs = 64;
-  int32_t S = slices;
-  if (S == 0) {
-    // Measured on MI355X (8 ranks): decode payloads up to 64 KiB per rank are
-    // fastest with 8 workgroups per rank (each workgroup's agent-scope fences
-    // serialise, so more of them cost more than they parallelise); larger
-    // payloads with about 1024 vectors per workgroup, up to 32 per rank.
-    if (flags & RRB_SNAC_LAMPORT) {
-      // Flag-in-data has no fences; its time follows the coherent loads per
-      // lane, so small payloads take one vector per lane (64 per workgroup),
-      // then 32 per workgroup; above 256 KiB, 128 workgroups per rank (more
-      // of them only add poll traffic).  Measured on MI355X, 8 ranks.
-      if (nvec < 4096) {
-        S = static_cast<int32_t>(std::max<int64_t>(1, nvec / 64));
-      } else if (nvec <= 16384) {
-        S = static_cast<int32_t>(std::min<int64_t>(256, nvec / 32));
-      } else {
-        S = 128;
-      }
-    } else if (nvec <= 4096) {
-      S = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(8, nvec / 64)));
-    } else {
-      S = static_cast<int32_t>(std::min<int64_t>(32, std::max<int64_t>(8, nvec / 1024)));
-    }
-    S = std::min<int32_t>(S, 2048 / nranks);
-  }
-  if (S > nvec) S = static_cast<int32_t>(nvec);
+  const int32_t S = default_slices(slices, nvec, nranks, flags);
   rrb_snac_s *h = new (std::nothrow) rrb_snac_s;
   if (!h) return fail(RRB_ENOMEM, "handle allocation failed");
   h->R = nranks;
@@ -793,7 +1091,8 @@ rrb_status rrb_snac_create(int32_t nranks, int64_t count, int32_t dtype, uint32_
   h->dtype = dtype;
   h->flags = flags;
   h->S = S;
-  h->bs = bs;
+  h->bs = 64;
+  h->in_stride = h->out_stride = count * esz;
   h->lay = layout_for(nranks, count, dtype, S, (flags & RRB_SNAC_LAMPORT) != 0);
   if (flags & RRB_SNAC_GRAPH) {
     rrb_spec sp;
@@ -814,6 +1113,85 @@ rrb_status rrb_snac_create(int32_t nranks, int64_t count, int32_t dtype, uint32_
   return RRB_OK;
 }
 
+rrb_status rrb_snac_create_plan(rrb_plan_t plan, uint32_t flags, int32_t slices, rrb_snac_t *out) {
+  clear_error();
+  if (!out) return fail(RRB_EINVAL, "NULL out");
+  *out = nullptr;
+  if (!plan) return fail(RRB_EINVAL, "NULL plan");
+  const Plan &p = plan->p;
+  if (p.kind != PlanKind::Uniform)
+    return fail(RRB_EUNSUPPORTED, "chains take layout-named (uniform) plans, not MoE row plans");
+  if (p.op == RRB_REDUCE_SUM_TREE)
+    return fail(RRB_EUNSUPPORTED, "chains fold in the fixed rank order only");
+  if (flags != 0 && flags != RRB_SNAC_DUAL_BUFFER &&
+      flags != (RRB_SNAC_DUAL_BUFFER | RRB_SNAC_SPECULATIVE) && flags != RRB_SNAC_GRAPH)
+    return fail(RRB_EUNSUPPORTED,
+                "plan chains take 0, DUAL_BUFFER, DUAL_BUFFER|SPECULATIVE or GRAPH (flags 0x%x)", flags);
+  if (slices < 0 || slices > kMaxSlices)
+    return fail(RRB_EINVAL, "slices %d outside 0..%d", slices, kMaxSlices);
+  const int R = p.nranks;
+  const int esz = elem_size(p.dtype);
+  int64_t in_max = 0, out_max = 0;
+  for (int r = 0; r < R; ++r) {
+    in_max = std::max(in_max, p.in_count[r] * esz);
+    out_max = std::max(out_max, p.out_count[r] * esz);
+  }
+  if (in_max == 0 || out_max == 0) return fail(RRB_EINVAL, "the plan moves no data");
+  for (const Segment &g : p.segs)
+    if ((g.src_off * esz) % 16 || (g.dst_off * esz) % 16 || (g.len * esz) % 16)
+      return fail(RRB_EUNSUPPORTED, "chains need every map entry on 16-byte boundaries");
+  for (int r = 0; r < R; ++r)
+    if ((p.in_count[r] * esz) % 16)
+      return fail(RRB_EUNSUPPORTED, "chains need 16-byte multiples of input per rank");
+  const int64_t in_stride = (in_max + 15) / 16 * 16;
+  const int64_t out_stride = (out_max + 15) / 16 * 16;
+  if (2LL * R * in_stride > 0x7fffffffLL) return fail(RRB_EUNSUPPORTED, "staging above 2 GiB");
+  rrb_snac_s *h = new (std::nothrow) rrb_snac_s;
+  if (!h) return fail(RRB_ENOMEM, "handle allocation failed");
+  try {
+    h->ar_plan = p;
+    for (int r = 0; r < R; ++r) {
+      h->in_vec[r] = p.in_count[r] * esz / 16;
+      h->first[r] = static_cast<int32_t>(h->entries.size());
+      for (const Segment &g : p.segs) {
+        if (!(g.dst_mask >> r & 1u)) continue;
+        PlanEntry e;
+        e.src_off = g.src_off * esz / 16;
+        e.dst_off = g.dst_off * esz / 16;
+        e.len = g.len * esz / 16;
+        e.src_rank = g.src_rank;
+        e.pad = 0;
+        h->entries.push_back(e);
+      }
+      h->cnt[r] = static_cast<int32_t>(h->entries.size()) - h->first[r];
+    }
+  } catch (const std::bad_alloc &) {
+    delete h;
+    return fail(RRB_ENOMEM, "handle allocation failed");
+  }
+  const int64_t nvec = std::max(in_max, out_max) / 16;
+  h->R = R;
+  h->count = p.count;
+  h->dtype = p.dtype;
+  h->flags = flags;
+  h->S = default_slices(slices, nvec, R, flags);
+  h->bs = 64;
+  h->in_stride = in_stride;
+  h->out_stride = out_stride;
+  h->from_plan = true;
+  h->lay = layout_for_plan(R, in_stride, h->S, static_cast<int64_t>(h->entries.size()));
+  *out = h;
+  return RRB_OK;
+}
+
+rrb_status rrb_snac_strides(rrb_snac_t h, int64_t *in_stride, int64_t *out_stride) {
+  clear_error();
+  if (!h) return fail(RRB_EINVAL, "NULL handle");
+  if (in_stride) *in_stride = h->in_stride;
+  if (out_stride) *out_stride = h->out_stride;
+  return RRB_OK;
+}
+
 rrb_status rrb_snac_workspace(rrb_snac_t h, size_t *bytes) {
   clear_error();
   if (!h || !bytes) return fail(RRB_EINVAL, "NULL handle or bytes");
@@ -830,12 +1208,21 @@ rrb_status rrb_snac_bind(rrb_snac_t h, void *d_ws, size_t bytes, rrb_stream_t st
   h->ws = static_cast<unsigned char *>(d_ws);
   h->next_epoch = 1;
   h->drop_graph();
+  hipError_t e = hipSuccess;
+  if (h->from_plan && !(h->flags & RRB_SNAC_GRAPH) && !h->entries.empty()) {
+    // The consume entries; synchronous so the host vector may change later.
+    e = hipMemcpyAsync(h->ws + h->lay.entries_off, h->entries.data(),
+                       h->entries.size() * sizeof(PlanEntry), hipMemcpyHostToDevice,
+                       static_cast<hipStream_t>(stream));
+    if (e == hipSuccess) e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(RRB_EHIP, "entry upload: %s", hipGetErrorString(e));
+  }
   // Clear flags, done words and status with a fill kernel (graph-safe).
   uint32_t *p = reinterpret_cast<uint32_t *>(h->ws + h->lay.flag_off);
   const int64_t n = (h->lay.total - h->lay.flag_off) / 4;
   hipLaunchKernelGGL(fill_u32_kernel, dim3(64), dim3(256), 0, static_cast<hipStream_t>(stream), p, n,
                      0u);
-  const hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return fail(RRB_EHIP, "flag clear: %s", hipGetErrorString(e));
   return RRB_OK;
 }
@@ -843,6 +1230,15 @@ rrb_status rrb_snac_bind(rrb_snac_t h, void *d_ws, size_t bytes, rrb_stream_t st
 rrb_status rrb_snac_allreduce_chain(rrb_snac_t h, int32_t epochs, const void *d_in, void *d_out,
                                     rrb_snac_stats *d_stats, const uint32_t *d_stagger,
                                     uint32_t spin_limit, rrb_stream_t stream) {
+  clear_error();
+  if (!h) return fail(RRB_EINVAL, "NULL handle");
+  if (h->from_plan) return fail(RRB_EINVAL, "a plan chain runs through rrb_snac_chain");
+  return rrb_snac_chain(h, epochs, d_in, d_out, d_stats, d_stagger, spin_limit, stream);
+}
+
+rrb_status rrb_snac_chain(rrb_snac_t h, int32_t epochs, const void *d_in, void *d_out,
+                          rrb_snac_stats *d_stats, const uint32_t *d_stagger,
+                          uint32_t spin_limit, rrb_stream_t stream) {
   clear_error();
   if (!h) return fail(RRB_EINVAL, "NULL handle");
   if (!h->ws) return fail(RRB_EINVAL, "handle is not bound to a workspace");
@@ -863,6 +1259,7 @@ rrb_status rrb_snac_allreduce_chain(rrb_snac_t h, int32_t epochs, const void *d_
   }
   if (h->next_epoch > 0xffffffffu - static_cast<uint32_t>(epochs) - 2)
     return fail(RRB_EUNSUPPORTED, "epoch counter exhausted; rebind the handle");
+  if (h->from_plan) return launch_plan_chain(h, epochs, d_in, d_out, d_stats, d_stagger, spin_limit, stream);
   const int esz = elem_size(h->dtype);
   SnacArgs a;
   std::memset(&a, 0, sizeof a);

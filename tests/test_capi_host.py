@@ -252,3 +252,32 @@ def test_device_row_plan_sizes_and_limits(librrb):
     assert lib.rrb_plan_create_rows_device(R, T, h, 2048, k, 0, ctypes.byref(hdl)) == L.RRB_EUNSUPPORTED
     assert lib.rrb_plan_create_rows_device(R, T, h, E, 17, 0, ctypes.byref(hdl)) == L.RRB_EUNSUPPORTED
     assert lib.rrb_plan_create_rows_device(R, T + 1, h, E, k, 0, ctypes.byref(hdl)) == L.RRB_EINVAL
+
+
+def test_snac_plan_chain_validation(librrb):
+    """rrb_snac_create_plan: plans, flags and alignment it refuses; strides
+    and workspace of one it accepts (host only, no kernel runs)."""
+    import ctypes
+    lib = L.lib()
+    h = ctypes.c_void_p()
+    ag = api.Plan(8, 8 * 64, "bf16", api.SHARD, api.REPLICATED, "copy")
+    assert lib.rrb_snac_create_plan(ag.handle, L.RRB_SNAC_LAMPORT | L.RRB_SNAC_DUAL_BUFFER, 0,
+                                    ctypes.byref(h)) == L.RRB_EUNSUPPORTED
+    assert lib.rrb_snac_create_plan(ag.handle, L.RRB_SNAC_SPECULATIVE, 0,
+                                    ctypes.byref(h)) == L.RRB_EUNSUPPORTED
+    tree = api.Plan(8, 8 * 64, "bf16", api.PARTIAL, api.REPLICATED, "reduce_tree")
+    assert lib.rrb_snac_create_plan(tree.handle, 1, 0, ctypes.byref(h)) == L.RRB_EUNSUPPORTED
+    ragged = api.Plan(8, 8 * 3, "bf16", api.SHARD, api.REPLICATED, "copy")
+    assert lib.rrb_snac_create_plan(ragged.handle, 1, 0, ctypes.byref(h)) == L.RRB_EUNSUPPORTED
+    assert lib.rrb_snac_create_plan(None, 1, 0, ctypes.byref(h)) == L.RRB_EINVAL
+    assert lib.rrb_snac_create_plan(ag.handle, 1, 0, ctypes.byref(h)) == L.RRB_OK
+    si, so = ctypes.c_int64(), ctypes.c_int64()
+    assert lib.rrb_snac_strides(h, ctypes.byref(si), ctypes.byref(so)) == L.RRB_OK
+    assert (si.value, so.value) == (64 * 2, 8 * 64 * 2)
+    ws = ctypes.c_size_t()
+    assert lib.rrb_snac_workspace(h, ctypes.byref(ws)) == L.RRB_OK
+    assert ws.value >= 2 * 8 * 128 + 256
+    # a plan chain does not run through the All-Reduce entry point
+    assert lib.rrb_snac_allreduce_chain(h, 1, None, None, None, None, 0, None) == L.RRB_EINVAL
+    lib.rrb_snac_destroy(h)
+    del ag  # the handle keeps its own copy of the plan
