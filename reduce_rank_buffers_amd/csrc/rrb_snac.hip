@@ -60,7 +60,10 @@ constexpr uint32_t kDefaultSpin = 1u << 21;  // polls (about 1 us each)
 constexpr int kMaxSlices = 256;
 constexpr int kStageU = 8;  // vectors in flight per lane in the stage copy
 
-enum Variant : int32_t { kBarrier = 0, kDual = 1, kSpeculative = 2, kTwoshot = 3, kLamport = 4 };
+// kLamportOne: the flag-in-data kernel shaped for slices of at most one
+// vector per lane.
+enum Variant : int32_t { kBarrier = 0, kDual = 1, kSpeculative = 2, kTwoshot = 3, kLamport = 4,
+                         kLamportOne = 5 };
 
 struct SnacArgs {
   const unsigned char *in;   // [E][R][count]
@@ -521,8 +524,9 @@ __device__ __forceinline__ uint4 untag(v4u lo, v4u hi) {
 // Workgroup (r, s): stage slice s of rank r's payload as tagged words, then
 // poll slice s of all R ranks' tagged payloads and fold it in rank order into
 // rank r's output.  stats.retries counts poll rounds that found a word not yet
-// tagged (lane 0 of each workgroup).
-template <int R, bool BF16>
+// tagged (lane 0 of each workgroup).  CU / kLU: payload vectors per lane per
+// consume / stage pass (one each when a slice is one vector per lane).
+template <int R, bool BF16, int CU, int kLU>
 __global__ void __launch_bounds__(64) lamport_chain_kernel(SnacArgs a) {
   const int r = blockIdx.x / a.S;
   const int s = blockIdx.x - r * a.S;
@@ -530,8 +534,6 @@ __global__ void __launch_bounds__(64) lamport_chain_kernel(SnacArgs a) {
   const int64_t v0 = static_cast<int64_t>(s) * a.slice_vec;
   const int64_t v1 = min(a.nvec, v0 + a.slice_vec);
   const int64_t tbytes = 2 * a.rank_bytes;  // tagged bytes per rank
-  constexpr int CU = R <= 8 ? 2 : 1;        // payload vectors per lane per pass
-  constexpr int kLU = 4;                    // payload vectors per lane per stage pass
   unsigned long long polls = 0, timeouts = 0, done_epochs = 0;
 
   for (int k = 0; k < a.epochs; ++k) {
@@ -892,7 +894,8 @@ SnacFn snac_for(int R) {
   switch (R) {
 #define RRB_CASE(n) \
   case n:           \
-    if constexpr (VAR == kLamport) return lamport_chain_kernel<n, BF16>; \
+    if constexpr (VAR == kLamport) return lamport_chain_kernel<n, BF16, (n <= 8 ? 2 : 1), 4>; \
+    else if constexpr (VAR == kLamportOne) return lamport_chain_kernel<n, BF16, 1, 1>; \
     else return snac_chain_kernel<n, BF16, VAR>;
     RRB_CASE(1) RRB_CASE(2) RRB_CASE(3) RRB_CASE(4) RRB_CASE(5) RRB_CASE(6) RRB_CASE(7)
     RRB_CASE(8) RRB_CASE(9) RRB_CASE(10) RRB_CASE(11) RRB_CASE(12) RRB_CASE(13)
@@ -1286,7 +1289,9 @@ rrb_status rrb_snac_chain(rrb_snac_t h, int32_t epochs, const void *d_in, void *
   a.spin_limit = spin_limit ? spin_limit : kDefaultSpin;
 
   const bool bf16 = h->dtype == RRB_BF16;
-  const int var = (h->flags & RRB_SNAC_LAMPORT) ? kLamport
+  // Measured on MI355X: slices of one vector per lane run 7-8% faster with
+  // one vector per lane in flight (8 and 16 KiB payloads).
+  const int var = (h->flags & RRB_SNAC_LAMPORT) ? (a.slice_vec <= h->bs ? kLamportOne : kLamport)
                   : (h->flags & RRB_SNAC_TWOSHOT) ? kTwoshot
                   : (h->flags & RRB_SNAC_SPECULATIVE) ? kSpeculative
                   : (h->flags & RRB_SNAC_DUAL_BUFFER) ? kDual : kBarrier;
@@ -1296,12 +1301,14 @@ rrb_status rrb_snac_chain(rrb_snac_t h, int32_t epochs, const void *d_in, void *
          : var == kDual  ? snac_for<true, kDual>(h->R)
          : var == kTwoshot ? snac_for<true, kTwoshot>(h->R)
          : var == kLamport ? snac_for<true, kLamport>(h->R)
+         : var == kLamportOne ? snac_for<true, kLamportOne>(h->R)
                            : snac_for<true, kSpeculative>(h->R);
   } else {
     fn = var == kBarrier ? snac_for<false, kBarrier>(h->R)
          : var == kDual  ? snac_for<false, kDual>(h->R)
          : var == kTwoshot ? snac_for<false, kTwoshot>(h->R)
          : var == kLamport ? snac_for<false, kLamport>(h->R)
+         : var == kLamportOne ? snac_for<false, kLamportOne>(h->R)
                            : snac_for<false, kSpeculative>(h->R);
   }
   // Every workgroup waits on others: the grid must be co-resident, which a
