@@ -17,7 +17,10 @@ Workloads (sizes are what they are named for, not tuning knobs):
 * decode chain: payload b x h bf16, b in {1..64}, h in {4096, 8192},
   N(0, 0.02) (sigma 0.02), 64 epochs, fresh data per (epoch, rank);
 * MoE: 4096 tokens x 7168 bf16 N(0, 1), logits N(0, 1) [4096, 256],
-  softmax then top-8 (the gate; not part of the datapath).
+  softmax then top-8 (the gate; not part of the datapath);
+* buffers past 2 GiB (the size-limit tests): drawn on the device by torch's
+  seeded generator (``device_normal_bf16``), since a host draw of that size
+  is slow; the oracle checks sampled elements copied back from these inputs.
 """
 
 import numpy as np
@@ -113,3 +116,15 @@ def moe_expert_outputs(rows_per_rank, h=7168):
     """Independently seeded stand-in expert outputs in the dispatch layout."""
     return [normal_bf16(int(n) * h, 1.0, WL_MOE, 2, 0, r).reshape(int(n), h)
             for r, n in enumerate(rows_per_rank)]
+
+
+WL_LARGE = 6
+
+
+def device_normal_bf16(n, rank, device, kind=0):
+    """n bf16 N(0, 1) values drawn on `device` by torch's generator seeded with
+    (WL_LARGE, kind, rank): an int16 tensor holding the bf16 bit patterns."""
+    g = torch.Generator(device=device)
+    g.manual_seed(WL_LARGE * 1_000_003 + int(kind) * 1009 + int(rank))
+    x = torch.randn(int(n), generator=g, device=device, dtype=torch.float32)
+    return x.to(torch.bfloat16).view(torch.int16)

@@ -258,3 +258,42 @@ def test_bound_ops_match_oracle(name):
         for q, w in enumerate(C.named(name, host, "bf16", root=root)):
             if w is not None:
                 assert_bits_equal(from_dev(outs[q]), w, f"bound {name} call {k} rank {q}")
+
+
+def test_buffers_past_2_gib():
+    """2.5 GiB per rank (byte offsets past 2^31): All-Reduce sampled against
+    the oracle (including elements beyond the 2 GiB mark and the last ones),
+    Reduce-Scatter sampled, and All-Gather of the Reduce-Scatter equal to the
+    All-Reduce on all bytes."""
+    require_gpu()
+    R = 2
+    n = ((5 << 30) // 2) // 2  # 2.5 GiB of bf16 per rank
+    c = n // R
+    _say(f"past 2 GiB: R={R} n={n}")
+    ins = [inputs.device_normal_bf16(n, r, DEV, kind=1) for r in range(R)]
+    ar = [torch.empty(n, dtype=torch.int16, device=DEV) for _ in range(R)]
+    api.all_reduce(ins, ar)
+    rs = [torch.empty(c, dtype=torch.int16, device=DEV) for _ in range(R)]
+    api.reduce_scatter(ins, rs)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(61)
+    edge = (1 << 31) // 2  # element at byte offset 2^31
+    idx = np.unique(np.concatenate([rng.integers(0, n, size=1 << 16), np.arange(64),
+                                    np.arange(n - 64, n), np.arange(edge - 32, edge + 32),
+                                    np.arange(c - 8, c + 8)]))
+    tidx = torch.from_numpy(idx).to(DEV)
+    cols = [from_dev(x[tidx]) for x in ins]
+    want = fold.reduce(cols, "bf16")
+    for q in range(R):
+        assert_bits_equal(from_dev(ar[q][tidx]), want, f"AR past 2 GiB rank {q}")
+    for q in range(R):
+        sel = (idx >= q * c) & (idx < (q + 1) * c)
+        got = from_dev(rs[q][torch.from_numpy(idx[sel] - q * c).to(DEV)])
+        assert_bits_equal(got, want[sel], f"RS past 2 GiB rank {q}")
+    del ins
+    ag = [torch.empty(n, dtype=torch.int16, device=DEV) for _ in range(R)]
+    api.all_gather(rs, ag)
+    torch.cuda.synchronize()
+    for q in range(R):
+        assert torch.equal(ag[q], ar[0]), f"AG(RS) rank {q} differs from AR past 2 GiB"
+        assert torch.equal(ar[q], ar[0])
