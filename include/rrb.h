@@ -40,7 +40,7 @@ extern "C" {
 typedef int32_t rrb_status;
 #define RRB_OK            0
 #define RRB_EINVAL       (-1) /* bad argument or an invalid layout naming          */
-#define RRB_EUNSUPPORTED (-2) /* well formed, but outside what this build runs     */
+#define RRB_EUNSUPPORTED (-2) /* well formed, but outside what the library supports */
 #define RRB_EHIP         (-3) /* a HIP runtime call failed; see rrb_last_error()    */
 #define RRB_ETIMEOUT     (-4) /* a bounded wait in a SNAC kernel expired            */
 #define RRB_ENOMEM       (-5) /* a host allocation failed                           */

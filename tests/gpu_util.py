@@ -7,7 +7,7 @@ DEV = torch.device("cuda", 0)
 
 
 def require_gpu():
-    assert torch.cuda.is_available(), "GPU tests need an MI355X; run them with -m gpu on the GPU box"
+    assert torch.cuda.is_available(), "GPU tests need an MI355X (run them with -m gpu where one is present)"
 
 
 def to_dev(a):
