@@ -117,6 +117,9 @@ def test_tolerance_against_fixed_order_wide_range(R):
     fx, tr, tol = _tree_vs_fixed(ins, R)
     assert np.all(np.abs(tr - fx) <= tol)
     assert np.any(tr != fx)
+    # The plain 1-ulp rule can fail under cancellation (reported, not required).
+    over = int(np.sum(np.abs(tr - fx) > ulp_bf16(fx)))
+    print(f"R={R}: {int(np.sum(tr != fx))} differ, {over} beyond 1 bf16 ulp")
 
 
 @pytest.mark.parametrize("R", [4, 8, 16])
@@ -128,6 +131,7 @@ def test_orders_agree_almost_everywhere_on_unit_normal_data(R):
     ins = [bf16.rne(rng.standard_normal(1 << 16).astype(np.float32)) for _ in range(R)]
     fx, tr, tol = _tree_vs_fixed(ins, R)
     assert np.all(np.abs(tr - fx) <= tol)
+    assert np.all(np.abs(tr - fx) <= ulp_bf16(fx))  # the plain 1-ulp rule holds here
     assert np.mean(tr != fx) <= 1e-3
 
 
