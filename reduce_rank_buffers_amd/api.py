@@ -173,9 +173,9 @@ class Bound:
             L.check(st, self._name)
 
 
-def bound(name, ins, outs, root=None):
-    """Pre-bind one of the seven collectives (or 'collective' via a Plan):
-    bound('all_reduce', ins, outs)() launches it."""
+def bound(name, ins, outs, root=None, order="fixed"):
+    """Pre-bind one of the seven collectives: bound('all_reduce', ins, outs)()
+    launches it.  ``order`` applies to the reducing ones ('fixed' or 'tree')."""
     t = next(x for x in ins if x is not None)
     R = len(ins)
     dt = _dtype_of(t)
@@ -189,6 +189,8 @@ def bound(name, ins, outs, root=None):
         "reduce": (PARTIAL, ROOT(root if root is not None else 0), "reduce"),
         "gather": (SHARD, ROOT(root if root is not None else 0), "copy"),
     }[name]
+    if spec[2] == "reduce":
+        spec = (spec[0], spec[1], _reduce_op(order))
     return Bound(plan(R, n, dt, *spec), ins, outs)
 
 

@@ -125,3 +125,18 @@ def test_tree_all_reduce_256mib_sampled_and_within_tolerance():
          f"{over_ulp} beyond 1 bf16 ulp")
     assert over == 0
     assert over_ulp == 0  # on the workload's N(0, 1) data the plain 1-ulp rule holds
+
+
+def test_tree_bound_op():
+    """A pre-bound tree-order All-Reduce gives the tree oracle's bits."""
+    require_gpu()
+    R, n = 8, 8 * 1000
+    rng = np.random.default_rng(14)
+    ins_np = [_wide(rng, n, "bf16") for _ in range(R)]
+    ins = [to_dev(x) for x in ins_np]
+    outs = [empty_like_np(n, "bf16") for _ in range(R)]
+    api.bound("all_reduce", ins, outs, order="tree")()
+    torch.cuda.synchronize()
+    want = fold.reduce_tree(ins_np, "bf16")
+    for q in range(R):
+        assert_bits_equal(from_dev(outs[q]), want, f"bound tree AR rank {q}")
