@@ -345,6 +345,23 @@ class SnacChain:
             int(spin_limit), _stream(stream)), "rrb_snac_allreduce_chain")
         return out
 
+    def bound(self, inp, out, stats=None):
+        """The chain call with its arguments marshalled once: calling the
+        result runs `inp.shape[0]` epochs on torch's current stream."""
+        fn = self._lib.rrb_snac_chain
+        args = (self.handle, ctypes.c_int32(int(inp.shape[0])), ctypes.c_void_p(inp.data_ptr()),
+                ctypes.c_void_p(out.data_ptr()),
+                ctypes.c_void_p(stats.data_ptr() if stats is not None else 0), ctypes.c_void_p(0),
+                ctypes.c_uint32(0))
+        keep = (inp, out, stats)
+
+        def call():
+            st = fn(*args, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if st:
+                L.check(st, "rrb_snac_chain")
+        call.keep = keep
+        return call
+
     def check(self, stream=None):
         L.check(self._lib.rrb_snac_check(self.handle, _stream(stream)), "rrb_snac_check")
 

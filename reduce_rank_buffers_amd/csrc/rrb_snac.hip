@@ -1289,9 +1289,11 @@ rrb_status rrb_snac_chain(rrb_snac_t h, int32_t epochs, const void *d_in, void *
   a.spin_limit = spin_limit ? spin_limit : kDefaultSpin;
 
   const bool bf16 = h->dtype == RRB_BF16;
-  // Measured on MI355X: slices of one vector per lane run 7-8% faster with
-  // one vector per lane in flight (8 and 16 KiB payloads).
-  const int var = (h->flags & RRB_SNAC_LAMPORT) ? (a.slice_vec <= h->bs ? kLamportOne : kLamport)
+  // Measured on MI355X: payloads up to 16 KiB (slices of one vector per
+  // lane) run 7-8% faster with one vector per lane in flight; from 32 KiB
+  // the two-vector shape is as fast or faster.
+  const bool one = a.nvec <= 1024 && a.slice_vec <= h->bs;
+  const int var = (h->flags & RRB_SNAC_LAMPORT) ? (one ? kLamportOne : kLamport)
                   : (h->flags & RRB_SNAC_TWOSHOT) ? kTwoshot
                   : (h->flags & RRB_SNAC_SPECULATIVE) ? kSpeculative
                   : (h->flags & RRB_SNAC_DUAL_BUFFER) ? kDual : kBarrier;

@@ -225,3 +225,22 @@ def test_graph_chain_replays_and_rebuilds():
     _check_chain(out2, OC.allreduce_chain(inputs.chain(8, R, n, kind=95)), "graph rebuild")
     with pytest.raises(L.RrbError):
         ch.run(inp, out, stagger=torch.zeros(R, dtype=torch.int32, device=DEV))
+
+
+@pytest.mark.parametrize("v", ["dual", "lamport", "graph"])
+def test_bound_chain_call_matches_oracle(v):
+    """A chain call marshalled once and issued twice: both bit-exact, and the
+    epoch counter carries across the calls."""
+    require_gpu()
+    n = 8192
+    ins_np = inputs.chain(EPOCHS, R, n, kind=82)
+    want = OC.allreduce_chain(ins_np)
+    inp = to_dev(ins_np)
+    out = torch.empty_like(inp)
+    ch = api.SnacChain(R, n, "bf16", v)
+    call = ch.bound(inp, out)
+    for k in range(2):
+        out.zero_()
+        call()
+        ch.check()
+        _check_chain(out, want, f"bound {v} call {k}")
