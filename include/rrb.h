@@ -288,18 +288,29 @@ rrb_status rrb_empty_kernel(rrb_stream_t stream);
  *                              graph cached for the last (d_in, d_out,
  *                              epochs); no staging, no flags.  d_stats is not
  *                              written and d_stagger must be NULL.
+ *   | RRB_SNAC_COOPERATIVE     (with any persistent variant) always launch
+ *                              cooperatively: co-residency guaranteed beside
+ *                              other work on the device, about 13 us more per
+ *                              call.  Without it, a grid within half the
+ *                              device's co-resident capacity takes a plain
+ *                              launch (and
+ *                              larger grids a cooperative one); if other work
+ *                              keeps such a grid from becoming co-resident,
+ *                              its bounded waits run out and the call reports
+ *                              RRB_ETIMEOUT rather than hang.
  * slices: single-wave workgroups per rank (1..256; 0 = choose from count:
  *         8 up to 64 KiB payloads, then about 16 KiB per workgroup up to 32;
  *         RRB_SNAC_LAMPORT: 1 KiB per workgroup below 64 KiB, then 512 B per
  *         workgroup up to 256, and 128 above 256 KiB; at most 2048 / nranks).
- *         The grid (nranks x slices) must be co-resident: the launch is
- *         cooperative and fails with RRB_EHIP if it cannot be.
+ *         The grid (nranks x slices) must be co-resident; a cooperative
+ *         launch that cannot be fails with RRB_EHIP.
  */
 #define RRB_SNAC_DUAL_BUFFER 1u
 #define RRB_SNAC_SPECULATIVE 2u
 #define RRB_SNAC_GRAPH 4u
 #define RRB_SNAC_TWOSHOT 8u
 #define RRB_SNAC_LAMPORT 16u
+#define RRB_SNAC_COOPERATIVE 32u
 typedef struct rrb_snac_s *rrb_snac_t;
 
 /* Device-side counters a chain call may accumulate into (zeroed by the

@@ -34,6 +34,7 @@ RRB_SNAC_SPECULATIVE = 2
 RRB_SNAC_GRAPH = 4
 RRB_SNAC_TWOSHOT = 8
 RRB_SNAC_LAMPORT = 16
+RRB_SNAC_COOPERATIVE = 32
 
 RRB_MAX_RANKS = 16
 

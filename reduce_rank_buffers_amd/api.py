@@ -317,11 +317,12 @@ class SnacChain:
     """A bound SNAC handle: back-to-back All-Reduces in one persistent kernel."""
 
     def __init__(self, nranks, count, dtype="bf16", variant="dual", slices=0, device=None,
-                 stream=None):
+                 stream=None, cooperative=False):
         self._lib = L.lib()
         h = ctypes.c_void_p()
+        flags = VARIANTS[variant] | (L.RRB_SNAC_COOPERATIVE if cooperative else 0)
         L.check(self._lib.rrb_snac_create(int(nranks), int(count), _dtype_code(dtype),
-                                          VARIANTS[variant], int(slices), ctypes.byref(h)),
+                                          flags, int(slices), ctypes.byref(h)),
                 "rrb_snac_create")
         self.handle = h
         self.nranks = int(nranks)
@@ -384,11 +385,13 @@ class SnacPlanChain(SnacChain):
     [epochs, R, in_stride] and outputs [epochs, R, out_stride] in elements
     (``strides``)."""
 
-    def __init__(self, plan, variant="dual", slices=0, device=None, stream=None):
+    def __init__(self, plan, variant="dual", slices=0, device=None, stream=None,
+                 cooperative=False):
         self._lib = L.lib()
         h = ctypes.c_void_p()
-        L.check(self._lib.rrb_snac_create_plan(plan.handle, PLAN_CHAIN_VARIANTS[variant], int(slices),
-                                               ctypes.byref(h)), "rrb_snac_create_plan")
+        flags = PLAN_CHAIN_VARIANTS[variant] | (L.RRB_SNAC_COOPERATIVE if cooperative else 0)
+        L.check(self._lib.rrb_snac_create_plan(plan.handle, flags, int(slices), ctypes.byref(h)),
+                "rrb_snac_create_plan")
         self.handle = h
         self.nranks = plan.nranks
         self.variant = variant

@@ -926,6 +926,9 @@ struct rrb_snac_s {
   std::vector<rrb::PlanEntry> entries;
   int64_t in_vec[RRB_MAX_RANKS] = {};
   int32_t first[RRB_MAX_RANKS] = {}, cnt[RRB_MAX_RANKS] = {};
+  // Co-resident capacity (workgroups) of the last persistent kernel launched.
+  const void *cap_fn = nullptr;
+  int64_t cap = 0;
   // RRB_SNAC_GRAPH: one Atom All-Reduce kernel node per epoch, chained in a
   // HIP graph that is cached for the last (in, out, epochs).
   rrb::Plan ar_plan;
@@ -1002,6 +1005,45 @@ rrb_status build_chain_graph(rrb_snac_s *h, int32_t epochs, const void *d_in, vo
   return RRB_OK;
 }
 
+// Launches a chain kernel whose workgroups wait on each other, so the grid
+// must be co-resident.  A grid within half the device's co-resident capacity
+// for the kernel (occupancy limit x compute units, cached per handle) takes a
+// plain launch.  Larger grids, and every launch with RRB_SNAC_COOPERATIVE,
+// take a cooperative launch, which guarantees co-residency beside other work
+// (or refuses) but costs about 13 us more per call on MI355X.  If other work
+// keeps a plain-launched grid from becoming co-resident, its bounded waits
+// run out and the call reports RRB_ETIMEOUT; it does not hang.
+template <class Args>
+rrb_status launch_persistent(rrb_snac_s *h, const void *fn, Args &a, hipStream_t stream,
+                             const char *what) {
+  const unsigned grid = static_cast<unsigned>(h->R * h->S);
+  bool coop = (h->flags & RRB_SNAC_COOPERATIVE) != 0;
+  if (!coop) {
+    if (h->cap_fn != fn) {
+      int dev = 0, cus = 0, per = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, h->bs, 0);
+      if (e != hipSuccess) return fail(RRB_EHIP, "%s occupancy query: %s", what, hipGetErrorString(e));
+      h->cap_fn = fn;
+      h->cap = static_cast<int64_t>(per) * cus;
+    }
+    // Half the capacity, as a margin on the occupancy estimate.
+    coop = 2 * static_cast<int64_t>(grid) > h->cap;
+  }
+  hipError_t e;
+  if (coop) {
+    void *args[] = {&a};
+    e = hipLaunchCooperativeKernel(fn, dim3(grid), dim3(h->bs), args, 0, stream);
+  } else {
+    void *args[] = {&a};
+    e = hipLaunchKernel(fn, dim3(grid), dim3(h->bs), args, 0, stream);
+  }
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return fail(RRB_EHIP, "%s launch: %s", what, hipGetErrorString(e));
+  return RRB_OK;
+}
+
 // Issues one plan-chain call (the handle is bound and not in graph mode).
 rrb_status launch_plan_chain(rrb_snac_s *h, int32_t epochs, const void *d_in, void *d_out,
                              rrb_snac_stats *d_stats, const uint32_t *d_stagger,
@@ -1043,11 +1085,9 @@ rrb_status launch_plan_chain(rrb_snac_s *h, int32_t epochs, const void *d_in, vo
     fn = var == kBarrier ? snac_plan_for<false, kBarrier>(h->R)
          : var == kDual  ? snac_plan_for<false, kDual>(h->R)
                          : snac_plan_for<false, kSpeculative>(h->R);
-  void *args[] = {&a};
-  const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(fn),
-                                                  dim3(h->R * h->S), dim3(h->bs), args, 0,
-                                                  static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(RRB_EHIP, "plan chain launch: %s", hipGetErrorString(e));
+  const rrb_status st = launch_persistent(h, reinterpret_cast<const void *>(fn), a,
+                                          static_cast<hipStream_t>(stream), "plan chain");
+  if (st != RRB_OK) return st;
   h->next_epoch += static_cast<uint32_t>(epochs);
   return RRB_OK;
 }
@@ -1068,8 +1108,12 @@ rrb_status rrb_snac_create(int32_t nranks, int64_t count, int32_t dtype, uint32_
     return fail(RRB_EINVAL, "nranks %d outside 1..%d", nranks, RRB_MAX_RANKS);
   if (dtype != RRB_BF16 && dtype != RRB_F32) return fail(RRB_EINVAL, "unknown dtype %d", dtype);
   if (flags & ~(RRB_SNAC_DUAL_BUFFER | RRB_SNAC_SPECULATIVE | RRB_SNAC_GRAPH | RRB_SNAC_TWOSHOT |
-                RRB_SNAC_LAMPORT))
+                RRB_SNAC_LAMPORT | RRB_SNAC_COOPERATIVE))
     return fail(RRB_EINVAL, "unknown SNAC flags 0x%x", flags);
+  if ((flags & RRB_SNAC_COOPERATIVE) && (flags & RRB_SNAC_GRAPH))
+    return fail(RRB_EINVAL, "RRB_SNAC_GRAPH launches no persistent kernel");
+  const uint32_t coop = flags & RRB_SNAC_COOPERATIVE;
+  flags &= ~RRB_SNAC_COOPERATIVE;
   if ((flags & RRB_SNAC_LAMPORT) && flags != (RRB_SNAC_LAMPORT | RRB_SNAC_DUAL_BUFFER))
     return fail(RRB_EINVAL, "RRB_SNAC_LAMPORT goes with RRB_SNAC_DUAL_BUFFER only");
   if ((flags & RRB_SNAC_TWOSHOT) && flags != (RRB_SNAC_TWOSHOT | RRB_SNAC_DUAL_BUFFER))
@@ -1078,6 +1122,7 @@ rrb_status rrb_snac_create(int32_t nranks, int64_t count, int32_t dtype, uint32_
     return fail(RRB_EINVAL, "RRB_SNAC_GRAPH takes no other flag");
   if ((flags & RRB_SNAC_SPECULATIVE) && !(flags & RRB_SNAC_DUAL_BUFFER))
     return fail(RRB_EINVAL, "speculative reduction needs dual buffering");
+  flags |= coop;
   const int esz = elem_size(dtype);
   if (count <= 0 || (count * esz) % 16)
     return fail(RRB_EUNSUPPORTED, "chain payloads must be a positive multiple of 16 bytes");
@@ -1126,10 +1171,13 @@ rrb_status rrb_snac_create_plan(rrb_plan_t plan, uint32_t flags, int32_t slices,
     return fail(RRB_EUNSUPPORTED, "chains take layout-named (uniform) plans, not MoE row plans");
   if (p.op == RRB_REDUCE_SUM_TREE)
     return fail(RRB_EUNSUPPORTED, "chains fold in the fixed rank order only");
-  if (flags != 0 && flags != RRB_SNAC_DUAL_BUFFER &&
-      flags != (RRB_SNAC_DUAL_BUFFER | RRB_SNAC_SPECULATIVE) && flags != RRB_SNAC_GRAPH)
+  const uint32_t base = flags & ~RRB_SNAC_COOPERATIVE;
+  if ((base != 0 && base != RRB_SNAC_DUAL_BUFFER &&
+       base != (RRB_SNAC_DUAL_BUFFER | RRB_SNAC_SPECULATIVE) && base != RRB_SNAC_GRAPH) ||
+      ((flags & RRB_SNAC_COOPERATIVE) && base == RRB_SNAC_GRAPH))
     return fail(RRB_EUNSUPPORTED,
-                "plan chains take 0, DUAL_BUFFER, DUAL_BUFFER|SPECULATIVE or GRAPH (flags 0x%x)", flags);
+                "plan chains take 0, DUAL_BUFFER, DUAL_BUFFER|SPECULATIVE (each optionally "
+                "|COOPERATIVE) or GRAPH (flags 0x%x)", flags);
   if (slices < 0 || slices > kMaxSlices)
     return fail(RRB_EINVAL, "slices %d outside 0..%d", slices, kMaxSlices);
   const int R = p.nranks;
@@ -1313,13 +1361,10 @@ rrb_status rrb_snac_chain(rrb_snac_t h, int32_t epochs, const void *d_in, void *
          : var == kLamportOne ? snac_for<false, kLamportOne>(h->R)
                            : snac_for<false, kSpeculative>(h->R);
   }
-  // Every workgroup waits on others: the grid must be co-resident, which a
-  // cooperative launch guarantees (or refuses).
-  void *args[] = {&a};
-  const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(fn),
-                                                  dim3(h->R * h->S), dim3(h->bs), args, 0,
-                                                  static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(RRB_EHIP, "chain launch: %s", hipGetErrorString(e));
+  // Every workgroup waits on others: the grid must be co-resident.
+  const rrb_status st = launch_persistent(h, reinterpret_cast<const void *>(fn), a,
+                                          static_cast<hipStream_t>(stream), "chain");
+  if (st != RRB_OK) return st;
   h->next_epoch += static_cast<uint32_t>(epochs);
   return RRB_OK;
 }

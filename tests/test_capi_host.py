@@ -210,6 +210,12 @@ def test_snac_create_validation(librrb):
     assert lib.rrb_snac_create(8, 4096, 0, 16, 0, ctypes.byref(h)) == L.RRB_EINVAL  # lamport alone
     assert lib.rrb_snac_create(8, 4096, 0, 19, 0, ctypes.byref(h)) == L.RRB_EINVAL  # + speculative
     assert lib.rrb_snac_create(8, 4096, 0, 25, 0, ctypes.byref(h)) == L.RRB_EINVAL  # + twoshot
+    assert lib.rrb_snac_create(8, 4096, 0, L.RRB_SNAC_COOPERATIVE | L.RRB_SNAC_GRAPH, 0,
+                               ctypes.byref(h)) == L.RRB_EINVAL
+    assert lib.rrb_snac_create(8, 4096, 0, L.RRB_SNAC_COOPERATIVE | 1, 0, ctypes.byref(h)) == L.RRB_OK
+    lib.rrb_snac_destroy(h)
+    assert lib.rrb_snac_create(8, 4096, 0, L.RRB_SNAC_COOPERATIVE | 17, 0, ctypes.byref(h)) == L.RRB_OK
+    lib.rrb_snac_destroy(h)
     assert lib.rrb_snac_create(8, 4096, 0, 17, 0, ctypes.byref(h)) == L.RRB_OK
     ws = ctypes.c_size_t()
     assert lib.rrb_snac_workspace(h, ctypes.byref(ws)) == L.RRB_OK
@@ -270,6 +276,11 @@ def test_snac_plan_chain_validation(librrb):
     ragged = api.Plan(8, 8 * 3, "bf16", api.SHARD, api.REPLICATED, "copy")
     assert lib.rrb_snac_create_plan(ragged.handle, 1, 0, ctypes.byref(h)) == L.RRB_EUNSUPPORTED
     assert lib.rrb_snac_create_plan(None, 1, 0, ctypes.byref(h)) == L.RRB_EINVAL
+    assert lib.rrb_snac_create_plan(ag.handle, L.RRB_SNAC_COOPERATIVE | L.RRB_SNAC_GRAPH, 0,
+                                    ctypes.byref(h)) == L.RRB_EUNSUPPORTED
+    assert lib.rrb_snac_create_plan(ag.handle, L.RRB_SNAC_COOPERATIVE | 1, 0,
+                                    ctypes.byref(h)) == L.RRB_OK
+    lib.rrb_snac_destroy(h)
     assert lib.rrb_snac_create_plan(ag.handle, 1, 0, ctypes.byref(h)) == L.RRB_OK
     si, so = ctypes.c_int64(), ctypes.c_int64()
     assert lib.rrb_snac_strides(h, ctypes.byref(si), ctypes.byref(so)) == L.RRB_OK

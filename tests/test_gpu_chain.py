@@ -244,3 +244,19 @@ def test_bound_chain_call_matches_oracle(v):
         call()
         ch.check()
         _check_chain(out, want, f"bound {v} call {k}")
+
+
+@pytest.mark.parametrize("v", FLAG_VARIANTS)
+def test_chain_cooperative_launch(v):
+    """RRB_SNAC_COOPERATIVE: the same chain through a cooperative launch (the
+    default takes a plain launch when the grid fits the device)."""
+    require_gpu()
+    n = 4096
+    ins_np = inputs.chain(16, R, n, kind=83)
+    want = OC.allreduce_chain(ins_np)
+    inp = to_dev(ins_np)
+    out = torch.empty_like(inp)
+    ch = api.SnacChain(R, n, "bf16", v, cooperative=True)
+    ch.run(inp, out)
+    ch.check()
+    _check_chain(out, want, f"cooperative {v}")

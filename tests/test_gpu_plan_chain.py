@@ -163,3 +163,22 @@ def test_plan_chain_all_reduce_matches_all_reduce_chain():
     pc.run(inp, b)
     pc.check()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("variant", ["barrier", "dual", "speculative"])
+def test_plan_chain_cooperative_launch(variant):
+    require_gpu()
+    R, n, E = 8, 8 * 1024, 8
+    plan = api.Plan(R, n, "bf16", api.SHARD, api.REPLICATED, "copy")
+    ch = api.SnacPlanChain(plan, variant, cooperative=True)
+    si, so = ch.strides
+    ins = inputs.chain(E, R, si, kind=250)
+    inp = to_dev(ins)
+    out = torch.empty((E, R, so), dtype=torch.int16, device=DEV)
+    ch.run(inp, out)
+    ch.check()
+    want = OC.collective_chain("all_gather", [list(ins[e]) for e in range(E)])
+    got = from_dev(out)
+    for e in range(E):
+        for q in range(R):
+            assert_bits_equal(got[e, q], want[e][q], f"cooperative AG {variant} e={e} q={q}")
