@@ -16,7 +16,9 @@ Also reported on the same line:
   rate (a 1 GiB scratch read before each call empties the caches; measured
   after the timed region);
 * ``decode``: the batch-1 decode All-Reduce (8 ranks x 4096 bf16), kernel
-  time from events and back-to-back time per call, next to an empty kernel;
+  time from events and back-to-back time per call, next to an empty kernel,
+  and per All-Reduce in a 64-deep chain (flag-in-data and dual-buffer SNAC
+  kernels, and a graph of Atom launches);
 * ``cpu_baseline``: the CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -212,6 +214,9 @@ def main():
         "allreduce_graph_us": round(g_ar, 3),
         "empty_kernel_graph_us": round(g_em, 3),
         "graph_note": "64 launches captured in one HIP graph, replayed; us per launch",
+        "event_note": "event_us: events around one isolated host call (host launch latency "
+                      "included); back_to_back_us: host-issued calls in a loop; the kernel "
+                      "durations are in the rocprofv3 kernel trace",
         "workload": "All-Reduce, 8 ranks x 4096 bf16 (TP=8 batch-1 decode, hidden 4096)",
         "allreduce_event_us_p50": round(float(np.median(ar_ev)), 2),
         "allreduce_event_us_p10": round(float(np.percentile(ar_ev, 10)), 2),
@@ -220,6 +225,19 @@ def main():
         "allreduce_back_to_back_us": round(back_to_back_us(dec_op, it), 2),
         "empty_back_to_back_us": round(back_to_back_us(rrb.empty_kernel, it), 2),
     }
+    # the same All-Reduce 64 times back to back (a 32-layer decode step):
+    # one persistent SNAC kernel per call, or a graph of Atom launches
+    ch_in = torch.from_numpy(inputs.chain(64, R, 4096, kind=1).view(np.int16)).to(dev)
+    ch_out = torch.empty_like(ch_in)
+    chain = {}
+    for v, key in (("lamport", "flag_in_data_us"), ("dual", "dual_buffer_us"), ("graph", "graph_us")):
+        ch = rrb.SnacChain(R, 4096, "bf16", v)
+        call = ch.bound(ch_in, ch_out)
+        for _ in range(3):
+            call()
+        chain[key] = round(float(np.median(_events_ms(torch, call, 20))) * 1e3 / 64, 3)
+        ch.check()
+    decode["chain_64_per_allreduce"] = chain
 
     # ---- copy calibration: a plain 192 MiB copy through the library -------
     # (one rank, SHARD -> SHARD): the known-size kernel that scales the HBM
