@@ -292,3 +292,26 @@ def test_snac_plan_chain_validation(librrb):
     assert lib.rrb_snac_allreduce_chain(h, 1, None, None, None, None, 0, None) == L.RRB_EINVAL
     lib.rrb_snac_destroy(h)
     del ag  # the handle keeps its own copy of the plan
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """No fallback: with the shared library absent every entry point raises
+    instead of computing anywhere else (checked in a fresh interpreter so
+    this process's loaded library is untouched)."""
+    import subprocess
+    import sys as _sys
+    code = (
+        "import reduce_rank_buffers_amd._lib as L\n"
+        f"L.LIB_PATH = {str(tmp_path / 'absent.so')!r}\n"
+        "import reduce_rank_buffers_amd.api as api\n"
+        "try:\n"
+        "    api.Plan(8, 64, 'bf16', api.PARTIAL, api.REPLICATED, 'reduce')\n"
+        "except RuntimeError as e:\n"
+        "    print('raised:', e)\n"
+        "else:\n"
+        "    raise SystemExit('no error')\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([_sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                         timeout=120)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "is not built" in res.stdout
