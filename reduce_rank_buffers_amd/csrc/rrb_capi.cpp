@@ -122,11 +122,18 @@ rrb_status rrb_moe_route_check(rrb_plan_t plan, rrb_stream_t stream) {
   if (p.kind != PlanKind::RowsDevice || !p.d_ws) return fail(RRB_EINVAL, "not a bound device row plan");
   hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
   int32_t st = 0;
+  std::vector<int32_t> bst(static_cast<size_t>(p.rows.nblk), 0);
   if (e == hipSuccess)
     e = hipMemcpy(&st, static_cast<const char *>(p.d_ws) + p.rows.off_status, 4, hipMemcpyDeviceToHost);
+  // Per-block words of the fused routing kernel (zero for the three-kernel path).
+  if (e == hipSuccess && !bst.empty())
+    e = hipMemcpy(bst.data(), static_cast<const char *>(p.d_ws) + p.rows.off_bstatus,
+                  bst.size() * 4, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return fail(RRB_EHIP, "route status read: %s", hipGetErrorString(e));
+  for (int32_t b : bst) st |= b;
   if (st & 1) return fail(RRB_EINVAL, "routing names an expert outside 0..experts-1");
   if (st & 2) return fail(RRB_EINVAL, "routing selects an expert twice for one token");
+  if (st & 4) return fail(RRB_ETIMEOUT, "routing grid barrier timed out; rebind the plan");
   return RRB_OK;
 }
 

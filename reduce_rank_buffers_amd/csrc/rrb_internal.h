@@ -44,7 +44,10 @@ struct RowMaps {
   // Device-routed plans: byte offsets of the maps inside the workspace.
   int64_t nblk = 0;             // token blocks of kRouteBlock tokens
   size_t off_slot = 0, off_weight = 0, off_counts = 0, off_expert = 0, off_rank = 0,
-         off_bcounts = 0, off_bbase = 0, off_status = 0;
+         off_bcounts = 0, off_bbase = 0, off_status = 0, off_bstatus = 0;
+  // Co-resident capacity (workgroups) of the fused routing kernel, queried
+  // once; 0 = not yet known.
+  int64_t route_cap = 0;
 };
 
 // Tokens per block of the device-side routing kernels.

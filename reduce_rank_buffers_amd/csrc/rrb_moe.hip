@@ -192,6 +192,9 @@ __global__ void __launch_bounds__(256) moe_combine_elem_kernel(RowArgs a) {
 //   slot:  per block, a kRouteBlock-bit token mask per expert in LDS; a
 //          token's position within its expert is the block base plus the
 //          popcount of the mask bits below it.
+// When the token blocks fit on the device at once, one fused kernel does all
+// three (moe_route_fused_kernel): count, a grid-wide barrier, then every
+// block computes the prefixes it needs itself and assigns its slots.
 
 struct RouteArgs {
   const int32_t *idx;     // [T][k]
@@ -205,8 +208,11 @@ struct RouteArgs {
   int32_t *user_rank_off; // optional copy of rank_off
   int32_t *expert_off;    // [E]
   int32_t *counts;        // [E]
+  int32_t *bstatus;       // [nblk] per-block error bits (fused kernel)
+  unsigned long long *sync;  // grid-barrier arrivals, monotonic (fused kernel)
   int64_t T;
   int32_t E, k, R, per, nblk;
+  uint32_t spin;          // polls before the barrier wait gives up
 };
 
 __global__ void moe_fill_kernel(int32_t *p, int64_t n, int32_t v) {
@@ -326,9 +332,184 @@ __global__ void __launch_bounds__(kRouteBlock) moe_route_slot_kernel(RouteArgs a
   }
 }
 
+// Fused routing: one block of kRouteBlock tokens per workgroup, all blocks
+// co-resident.  Phase 1 validates, counts (LDS histogram) and marks (LDS
+// token masks) this block's tokens and publishes the counts; after a grid
+// barrier, each block sums the counts of earlier blocks and of all blocks per
+// expert itself, scans the totals over experts, and assigns its slots.  Block
+// 0 also writes the expert counts, offsets, rank offsets and the status word.
+// The barrier counter only grows: the blocks of one call take arrival numbers
+// g * nblk .. g * nblk + nblk - 1, so each waits for (g + 1) * nblk.
+template <int K>
+__global__ void __launch_bounds__(kRouteBlock) moe_route_fused_kernel(RouteArgs a) {
+  constexpr int W = kRouteBlock / 32;
+  __shared__ uint32_t mask[kRouteMaxExperts * W];
+  __shared__ int32_t hist[kRouteMaxExperts];   // counts, then earlier-block prefix
+  __shared__ int32_t eoff[kRouteMaxExperts];   // exclusive offsets over experts
+  __shared__ int32_t part[kRouteBlock];
+  __shared__ int32_t bad;
+  __shared__ int ok_all;
+  const int tid = threadIdx.x;
+  const int blk = blockIdx.x;
+  for (int i = tid; i < a.E * W; i += kRouteBlock) mask[i] = 0;
+  for (int e = tid; e < a.E; e += kRouteBlock) hist[e] = 0;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+
+  // Phase 1: this block's tokens.
+  const int64_t t = static_cast<int64_t>(blk) * kRouteBlock + tid;
+  const bool live = t < a.T;
+  int32_t e[K];
+  float w[K];
+  bool ok[K];
+  int32_t mybad = 0;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    e[j] = live ? a.idx[t * K + j] : 0;
+    w[j] = live ? a.w[t * K + j] : 0.f;
+    const bool in_range = e[j] >= 0 && e[j] < a.E;
+    bool dup = false;
+#pragma unroll
+    for (int j2 = 0; j2 < j; ++j2) dup = dup || e[j2] == e[j];
+    if (live && !in_range) mybad |= 1;
+    if (live && in_range && dup) mybad |= 2;
+    ok[j] = live && in_range && !dup;
+    if (ok[j]) {
+      atomicAdd(&hist[e[j]], 1);
+      atomicOr(&mask[e[j] * W + (tid >> 5)], 1u << (tid & 31));
+    }
+  }
+  if (mybad) atomicOr(&bad, mybad);
+  __syncthreads();
+  for (int x = tid; x < a.E; x += kRouteBlock) a.bcounts[static_cast<int64_t>(blk) * a.E + x] = hist[x];
+  if (tid == 0) a.bstatus[blk] = bad;
+
+  // Grid barrier: every wave releases its own stores, thread 0 arrives and
+  // waits, every wave acquires.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned long long g =
+        __hip_atomic_fetch_add(a.sync, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) /
+        static_cast<unsigned long long>(a.nblk);
+    const unsigned long long want = (g + 1) * static_cast<unsigned long long>(a.nblk);
+    uint32_t spins = 0;
+    int fine = 1;
+    while (__hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
+      if (++spins >= a.spin) {
+        // This block writes no slots: say so where no later write can undo
+        // it (its own status word; the check reads them all).
+        a.bstatus[blk] = bad | 4;
+        atomicOr(a.status, 4);
+        fine = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    ok_all = fine;
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (!ok_all) return;
+
+  // Phase 2: per expert, the sum over earlier blocks and the total.
+  for (int x = tid; x < a.E; x += kRouteBlock) {
+    int32_t run = 0, tot = 0;
+    for (int b = 0; b < a.nblk; ++b) {
+      const int32_t c = a.bcounts[static_cast<int64_t>(b) * a.E + x];
+      if (b < blk) run += c;
+      tot += c;
+    }
+    hist[x] = run;
+    eoff[x] = tot;
+  }
+  __syncthreads();
+  // Exclusive scan of the totals over experts: each thread sums a run of
+  // consecutive experts, the run sums are scanned, then spread back.
+  const int per_thread = (a.E + kRouteBlock - 1) / kRouteBlock;
+  const int x0 = tid * per_thread, x1 = min(a.E, x0 + per_thread);
+  int32_t sum = 0;
+  for (int x = x0; x < x1; ++x) sum += eoff[x];
+  part[tid] = sum;
+  __syncthreads();
+  for (int d = 1; d < kRouteBlock; d <<= 1) {
+    const int32_t add = tid >= d ? part[tid - d] : 0;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
+  }
+  int32_t base = part[tid] - sum;  // exclusive prefix of this thread's run
+  for (int x = x0; x < x1; ++x) {
+    const int32_t c = eoff[x];
+    eoff[x] = base;
+    if (blk == 0) {
+      a.counts[x] = c;
+      a.expert_off[x] = base;
+    }
+    base += c;
+  }
+  __syncthreads();
+  for (int x = tid; x < a.E; x += kRouteBlock) a.bbase[static_cast<int64_t>(blk) * a.E + x] = hist[x];
+  if (blk == 0) {
+    const int32_t total = part[kRouteBlock - 1];
+    if (tid <= a.R) {
+      const int32_t v = tid < a.R ? eoff[tid * a.per] : total;
+      a.rank_off[tid] = v;
+      if (a.user_rank_off) a.user_rank_off[tid] = v;
+    }
+    if (tid == 0) {
+      int32_t st = 0;
+      for (int b = 0; b < a.nblk; ++b) st |= a.bstatus[b];
+      *a.status = st;
+    }
+  }
+
+  // Phase 3: this block's slots, experts in ascending id.
+  if (!live) return;
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+#pragma unroll
+    for (int j = 0; j + 1 < K - i; ++j) {
+      if (e[j] > e[j + 1]) {
+        const int32_t te = e[j]; e[j] = e[j + 1]; e[j + 1] = te;
+        const float tw = w[j]; w[j] = w[j + 1]; w[j + 1] = tw;
+        const bool to = ok[j]; ok[j] = ok[j + 1]; ok[j + 1] = to;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    int32_t row = 0;
+    float wt = 0.f;
+    if (ok[j]) {
+      const uint32_t *m = mask + e[j] * W;
+      int pos = 0;
+      for (int q = 0; q < (tid >> 5); ++q) pos += __popc(m[q]);
+      pos += __popc(m[tid >> 5] & ((1u << (tid & 31)) - 1u));
+      row = eoff[e[j]] + hist[e[j]] + pos;
+      wt = w[j];
+    }
+    a.slot[t * K + j] = row;
+    a.weight[t * K + j] = wt;
+  }
+}
+
 namespace {
 
 using RouteFn = void (*)(RouteArgs);
+
+RouteFn route_fused_for(int k) {
+  switch (k) {
+#define RRB_CASE(n) \
+  case n:           \
+    return moe_route_fused_kernel<n>;
+    RRB_CASE(1) RRB_CASE(2) RRB_CASE(3) RRB_CASE(4) RRB_CASE(5) RRB_CASE(6) RRB_CASE(7)
+    RRB_CASE(8) RRB_CASE(9) RRB_CASE(10) RRB_CASE(11) RRB_CASE(12) RRB_CASE(13)
+    RRB_CASE(14) RRB_CASE(15) RRB_CASE(16)
+#undef RRB_CASE
+  }
+  return nullptr;
+}
 
 RouteFn route_slot_for(int k) {
   switch (k) {
@@ -359,8 +540,10 @@ rrb_status clear_route_maps(const Plan &p, void *stream) {
   if (n > 0)
     hipLaunchKernelGGL(moe_fill_kernel, dim3(64), dim3(256), 0, s,
                        reinterpret_cast<int32_t *>(ws + m.off_slot), n, 0);
-  hipLaunchKernelGGL(moe_fill_kernel, dim3(1), dim3(64), 0, s,
-                     reinterpret_cast<int32_t *>(ws + m.off_status), static_cast<int64_t>(1), 0);
+  // status word, barrier counter and per-block status words
+  const int64_t words = (static_cast<int64_t>(m.off_bstatus - m.off_status) + m.nblk * 4) / 4;
+  hipLaunchKernelGGL(moe_fill_kernel, dim3(1), dim3(256), 0, s,
+                     reinterpret_cast<int32_t *>(ws + m.off_status), words, 0);
   return route_launch_check("route clear");
 }
 
@@ -381,6 +564,9 @@ rrb_status launch_route(Plan &p, const int32_t *d_idx, const float *d_w, int32_t
   a.bcounts = reinterpret_cast<int32_t *>(ws + m.off_bcounts);
   a.bbase = reinterpret_cast<int32_t *>(ws + m.off_bbase);
   a.status = reinterpret_cast<int32_t *>(ws + m.off_status);
+  a.bstatus = reinterpret_cast<int32_t *>(ws + m.off_bstatus);
+  a.sync = reinterpret_cast<unsigned long long *>(ws + m.off_status + 128);
+  a.spin = 1u << 22;
   a.user_rank_off = d_rank_offsets;
   a.T = m.tokens;
   a.E = m.experts;
@@ -388,6 +574,27 @@ rrb_status launch_route(Plan &p, const int32_t *d_idx, const float *d_w, int32_t
   a.R = p.nranks;
   a.per = m.experts / p.nranks;
   a.nblk = static_cast<int32_t>(m.nblk);
+  // One fused kernel when every token block can be resident at once (half
+  // the device's co-resident capacity, as a margin); its grid barrier waits
+  // are bounded, so a grid that other work keeps apart times out (status
+  // bit 4) instead of hanging.  Otherwise three kernels.
+  if (m.tokens > 0) {
+    RouteFn fused = route_fused_for(m.topk);
+    if (m.route_cap == 0) {
+      int dev = 0, cus = 0, perb = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&perb, reinterpret_cast<const void *>(fused),
+                                                         kRouteBlock, 0);
+      if (e != hipSuccess) return fail(RRB_EHIP, "route occupancy query: %s", hipGetErrorString(e));
+      p.rows.route_cap = static_cast<int64_t>(perb) * cus;
+    }
+    if (2 * m.nblk <= p.rows.route_cap) {
+      hipLaunchKernelGGL(fused, dim3(static_cast<unsigned>(m.nblk)), dim3(kRouteBlock), 0, s, a);
+      return route_launch_check("route");
+    }
+  }
   hipLaunchKernelGGL(moe_fill_kernel, dim3(1), dim3(64), 0, s, a.status, static_cast<int64_t>(1), 0);
   rrb_status st = route_launch_check("route status clear");
   if (st != RRB_OK) return st;

@@ -295,7 +295,8 @@ rrb_status build_row_plan_device(int32_t R, int64_t T, int64_t h, int32_t E, int
   m.off_rank = off;    off += up(static_cast<size_t>(R + 1) * 4);
   m.off_bcounts = off; off += up(static_cast<size_t>(m.nblk) * E * 4);
   m.off_bbase = off;   off += up(static_cast<size_t>(m.nblk) * E * 4);
-  m.off_status = off;  off += 256;
+  m.off_status = off;  off += 256;  // status word; barrier counter at +128
+  m.off_bstatus = off; off += up(static_cast<size_t>(m.nblk) * 4);
   plan.ws_bytes = off;
   plan.kind = PlanKind::RowsDevice;
   plan.nranks = R;

@@ -135,3 +135,17 @@ def test_device_plan_unrouted_is_in_bounds():
     torch.cuda.synchronize()
     a = from_dev(arena).reshape(T * k, h)
     assert np.all(a[1:] == 0) and np.all(a[0] == 3)
+
+
+def test_device_routing_many_blocks():
+    """262,144 tokens = 1024 routing blocks, more than can be resident at
+    once: the three-kernel routing path (smaller token counts take the fused
+    kernel).  Dispatch arena, rank offsets and combine against the oracle."""
+    require_gpu()
+    T, h, E, k, R = 262144, 8, 64, 2, 8
+    rng = np.random.default_rng(91)
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    xa = bf16.rne(rng.standard_normal((T, h)).astype(np.float32))
+    shards = [xa[r * (T // R):(r + 1) * (T // R)] for r in range(R)]
+    _run(T, h, E, k, R, idx, w, shards)
