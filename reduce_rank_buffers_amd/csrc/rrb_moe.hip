@@ -284,6 +284,7 @@ template <int K>
 __global__ void __launch_bounds__(kRouteBlock) moe_route_slot_kernel(RouteArgs a) {
   constexpr int W = kRouteBlock / 32;
   __shared__ uint32_t mask[kRouteMaxExperts * W];
+  __shared__ uint16_t mpre[kRouteMaxExperts * W];  // tokens in the expert's earlier mask words
   for (int i = threadIdx.x; i < a.E * W; i += blockDim.x) mask[i] = 0;
   __syncthreads();
   const int local = threadIdx.x;
@@ -300,6 +301,15 @@ __global__ void __launch_bounds__(kRouteBlock) moe_route_slot_kernel(RouteArgs a
 #pragma unroll
     for (int j2 = 0; j2 < j; ++j2) ok[j] = ok[j] && e[j2] != e[j];
     if (ok[j]) atomicOr(&mask[e[j] * W + (local >> 5)], 1u << (local & 31));
+  }
+  __syncthreads();
+  for (int x = local; x < a.E; x += blockDim.x) {
+    int pre = 0;
+#pragma unroll
+    for (int q = 0; q < W; ++q) {
+      mpre[x * W + q] = static_cast<uint16_t>(pre);
+      pre += __popc(mask[x * W + q]);
+    }
   }
   __syncthreads();
   if (!live) return;
@@ -320,10 +330,8 @@ __global__ void __launch_bounds__(kRouteBlock) moe_route_slot_kernel(RouteArgs a
     int32_t row = 0;
     float wt = 0.f;
     if (ok[j]) {
-      const uint32_t *m = mask + e[j] * W;
-      int pos = 0;
-      for (int q = 0; q < (local >> 5); ++q) pos += __popc(m[q]);
-      pos += __popc(m[local >> 5] & ((1u << (local & 31)) - 1u));
+      const int q = local >> 5;
+      const int pos = mpre[e[j] * W + q] + __popc(mask[e[j] * W + q] & ((1u << (local & 31)) - 1u));
       row = a.expert_off[e[j]] + a.bbase[static_cast<int64_t>(blockIdx.x) * a.E + e[j]] + pos;
       wt = w[j];
     }
@@ -344,6 +352,7 @@ template <int K>
 __global__ void __launch_bounds__(kRouteBlock) moe_route_fused_kernel(RouteArgs a) {
   constexpr int W = kRouteBlock / 32;
   __shared__ uint32_t mask[kRouteMaxExperts * W];
+  __shared__ uint16_t mpre[kRouteMaxExperts * W];  // tokens in the expert's earlier mask words
   __shared__ int32_t hist[kRouteMaxExperts];   // counts, then earlier-block prefix
   __shared__ int32_t eoff[kRouteMaxExperts];   // exclusive offsets over experts
   __shared__ int32_t part[kRouteBlock];
@@ -412,13 +421,29 @@ __global__ void __launch_bounds__(kRouteBlock) moe_route_fused_kernel(RouteArgs 
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (!ok_all) return;
 
-  // Phase 2: per expert, the sum over earlier blocks and the total.
+  // Phase 2: per expert, the prefix counts of its mask words (so a slot
+  // needs two LDS reads), the sum over earlier blocks and the total; eight
+  // independent loads in flight per step (the acquire left the caches cold).
+  for (int x = tid; x < a.E; x += kRouteBlock) {
+    int pre = 0;
+#pragma unroll
+    for (int q = 0; q < W; ++q) {
+      mpre[x * W + q] = static_cast<uint16_t>(pre);
+      pre += __popc(mask[x * W + q]);
+    }
+  }
   for (int x = tid; x < a.E; x += kRouteBlock) {
     int32_t run = 0, tot = 0;
-    for (int b = 0; b < a.nblk; ++b) {
-      const int32_t c = a.bcounts[static_cast<int64_t>(b) * a.E + x];
-      if (b < blk) run += c;
-      tot += c;
+    for (int b0 = 0; b0 < a.nblk; b0 += 8) {
+      int32_t c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        c[u] = b0 + u < a.nblk ? a.bcounts[static_cast<int64_t>(b0 + u) * a.E + x] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (b0 + u < blk) run += c[u];
+        tot += c[u];
+      }
     }
     hist[x] = run;
     eoff[x] = tot;
@@ -482,10 +507,8 @@ __global__ void __launch_bounds__(kRouteBlock) moe_route_fused_kernel(RouteArgs 
     int32_t row = 0;
     float wt = 0.f;
     if (ok[j]) {
-      const uint32_t *m = mask + e[j] * W;
-      int pos = 0;
-      for (int q = 0; q < (tid >> 5); ++q) pos += __popc(m[q]);
-      pos += __popc(m[tid >> 5] & ((1u << (tid & 31)) - 1u));
+      const int q = tid >> 5;
+      const int pos = mpre[e[j] * W + q] + __popc(mask[e[j] * W + q] & ((1u << (tid & 31)) - 1u));
       row = eoff[e[j]] + hist[e[j]] + pos;
       wt = w[j];
     }
