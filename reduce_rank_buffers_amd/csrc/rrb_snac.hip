@@ -18,11 +18,17 @@
 //                flags == R * epoch, per workgroup slice) decides whether the
 //                result stands; on mismatch the slice waits for the flags and
 //                is read again.
+//   twoshot      dual buffers; reduce-scatter into a reduced buffer, a second
+//                flag round, then all-gather (SiFAR review, Fig. 6).
 //   lamport      flag-in-data, the Lamport-style All-Reduce SiFAR compares
 //                against (review page, Fig. 20): no flags, no fences.  Each
 //                16-bit half of the payload is staged in a 32-bit word under
 //                a 16-bit epoch tag; a reader polls every word it needs until
 //                all carry this epoch's tag (lamport_chain_kernel below).
+//   graph        no persistent kernel: one Atom All-Reduce launch per epoch,
+//                chained in a cached HIP graph.
+// Chains of any layout-named collective run the barrier, dual and
+// speculative protocols over the plan's index map (snac_plan_kernel below).
 //
 // One persistent kernel runs the whole chain.  Rank r is a group of S
 // workgroups; workgroup (r, s) stages slice s of rank r's payload, publishes
@@ -42,7 +48,9 @@
 //
 // Every wait is bounded: a wait that exceeds its poll budget raises a status
 // word that every other wait also watches, so the whole grid drains and the
-// host sees RRB_ETIMEOUT.
+// host sees RRB_ETIMEOUT.  The grid must be co-resident: it takes a plain
+// launch when it fits well within the device (launch_persistent), else a
+// cooperative one.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
