@@ -19,8 +19,9 @@
  *     library never allocates, frees or reallocates device memory; it owns
  *     only the host-side plan / SNAC objects it creates.
  *   - Streams: an rrb_stream_t is a hipStream_t (NULL = the null stream).
- *     Entry points that launch work are asynchronous on that stream and never
- *     synchronise it.
+ *     Entry points that launch work are asynchronous on that stream and do
+ *     not synchronise it, except the *_check calls (which report a kernel's
+ *     status) and binds that upload host data (which wait for the upload).
  *   - Pointers named d_* are device pointers; all others are host pointers.
  *   - Element types: RRB_BF16 (IEEE binary32's upper 16 bits) and RRB_F32.
  */
@@ -190,13 +191,18 @@ rrb_status rrb_plan_create_rows_device(int32_t nranks, int64_t tokens, int64_t h
  * id.  d_rank_offsets (nullable, nranks+1 int32, device) receives the arena
  * row where each rank's region starts, then tokens*topk.  Out-of-range or
  * repeated experts are skipped (their slots point at arena row 0, weight 0)
- * and recorded for rrb_moe_route_check.  Asynchronous; deterministic.
+ * and recorded for rrb_moe_route_check.  Asynchronous; deterministic.  When
+ * every block of 256 tokens fits on the device at once, one kernel with a
+ * bounded grid barrier builds the maps; if other work keeps that grid apart,
+ * the barrier wait runs out and rrb_moe_route_check reports RRB_ETIMEOUT
+ * (rebind the plan then).
  */
 rrb_status rrb_moe_route(rrb_plan_t plan, const int32_t *d_topk_idx, const float *d_topk_w,
                          int32_t *d_rank_offsets, rrb_stream_t stream);
 
 /* Synchronise `stream` and report RRB_EINVAL if the last rrb_moe_route on
- * this plan's workspace saw an out-of-range or repeated expert. */
+ * this plan's workspace saw an out-of-range or repeated expert, RRB_ETIMEOUT
+ * if its grid barrier wait ran out. */
 rrb_status rrb_moe_route_check(rrb_plan_t plan, rrb_stream_t stream);
 
 /*
