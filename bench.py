@@ -558,11 +558,35 @@ def cpu_baseline(host_inputs):
             model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), None)
     except OSError:
         pass
+    # The same oracle functions on contiguous element ranges in a thread pool
+    # (numpy releases the GIL inside its loops).
+    from concurrent.futures import ThreadPoolExecutor
+    workers = max(1, min(16, cores))
+
+    def ranged(args):
+        ins, dtype, a, b = args
+        C.all_reduce([x[a:b] for x in ins], dtype)
+        rs = C.reduce_scatter([x[a:b] for x in ins], dtype)
+        C.all_gather(rs)
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        jobs = []
+        for (smib, dtype), ins in host_inputs.items():
+            n = len(ins[0])
+            step = -(-n // (workers * R)) * R  # ranges of a multiple of R elements
+            jobs += [(ins, dtype, a, min(n, a + step)) for a in range(0, n, step)]
+        list(pool.map(ranged, jobs))
+    dt_threads = time.perf_counter() - t0
     return {"value": round(total / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
             "host_cores_visible": cores, "cpu_model": model, "kind": "oracle",
             "seconds": round(dt, 2),
             "sample": "one full step: All-Reduce -> Reduce-Scatter -> All-Gather, 8 ranks x "
-                      "{1,4,16,64,256} MiB bf16 + 64 MiB fp32 (numpy, single thread)"}
+                      "{1,4,16,64,256} MiB bf16 + 64 MiB fp32 (numpy, single thread)",
+            "threaded": {"value": round(total / dt_threads / 1e9, 3), "unit": "GB/s",
+                         "cores": workers, "seconds": round(dt_threads, 2),
+                         "sample": "the same step, the oracle's functions applied to contiguous "
+                                   "element ranges in a thread pool"}}
 
 
 if __name__ == "__main__":
