@@ -78,6 +78,19 @@ __device__ __forceinline__ int xcd_tile(int local, int C) {
   return (k / C) * (8 * C) + x * C + (k % C);
 }
 
+// Store v at byte offset off of every output whose bit is set in mask.  The
+// loop runs over compile-time rank indices, so the output pointers come from
+// one batch of scalar loads instead of a dependent load per set bit: that
+// lifts the streaming 1->8 copy from 6.2 to 6.8 TB/s on MI355X (together with
+// plain tile order).  The reduce keeps its bit loop, 3% faster there.
+template <bool NTS>
+__device__ __forceinline__ void st16_fan(unsigned char *const *out, uint32_t mask, int64_t off,
+                                         uint4 v) {
+#pragma unroll
+  for (int q = 0; q < RRB_MAX_RANKS; ++q)
+    if (mask >> q & 1u) st16<NTS>(out[q] + off, v);
+}
+
 // ---- kernels ---------------------------------------------------------------
 
 // Body of the vector reduce; TREE selects the tree-order fold.
@@ -99,15 +112,21 @@ __device__ __forceinline__ void reduce_vec_body(const UniArgs &a) {
         v[u][r] = ld16<NTL>(a.in[r] + it.src_off + i * 16);
     }
   }
+  // Fold every vector first, then store output by output, each output's U
+  // vectors back to back (measured on MI355X level with, or up to 1% ahead
+  // of, interleaving the outputs vector by vector).
+  uint4 res[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t i = base + static_cast<int64_t>(u) * bs;
-    if (i < a.nvec) {
-      const uint4 res = fold_vec<R, BF16, TREE>(v[u]);
-      for (uint32_t m = it.dst_mask; m; m &= m - 1) {
-        const int q = __builtin_ctz(m);
-        st16<NTS>(a.out[q] + it.dst_off + i * 16, res);
-      }
+    if (i < a.nvec) res[u] = fold_vec<R, BF16, TREE>(v[u]);
+  }
+  for (uint32_t m = it.dst_mask; m; m &= m - 1) {
+    const int q = __builtin_ctz(m);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + static_cast<int64_t>(u) * bs;
+      if (i < a.nvec) st16<NTS>(a.out[q] + it.dst_off + i * 16, res[u]);
     }
   }
   // Elements after the last whole vector of the item (single-segment plans
@@ -224,9 +243,7 @@ __global__ void __launch_bounds__(256) copy_vec_kernel(UniArgs a) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t i = base + static_cast<int64_t>(u) * bs;
-    if (i < a.nvec)
-      for (uint32_t m = it.dst_mask; m; m &= m - 1)
-        st16<NTS>(a.out[__builtin_ctz(m)] + it.dst_off + i * 16, v[u]);
+    if (i < a.nvec) st16_fan<NTS>(a.out, it.dst_mask, it.dst_off + i * 16, v[u]);
   }
   // Tail in 2-byte units (every element type is a multiple of 2 bytes).
   if (a.tail && tile == a.tiles - 1 && threadIdx.x < a.tail) {
@@ -557,7 +574,9 @@ rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out
     if (tiles == 0) tiles = 1;  // tail-only item
     if (a.tail > bs) return fail(RRB_EUNSUPPORTED, "tail longer than a workgroup");
     a.tiles = static_cast<int32_t>(tiles);
-    a.xcd_chunk = (stream && tiles % (8 * kXcdChunk) == 0) ? kXcdChunk : 0;
+    // XCD tile runs help streaming reduces; streaming copies run 9% faster
+    // in plain order (measured on MI355X, 256 MiB per rank).
+    a.xcd_chunk = (stream && reduce && tiles % (8 * kXcdChunk) == 0) ? kXcdChunk : 0;
   } else {
     bs = 256;
     U = 1;
