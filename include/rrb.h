@@ -217,14 +217,17 @@ rrb_status rrb_plan_query(rrb_plan_t plan, size_t *workspace_bytes,
 
 /*
  * Upload the plan's device-side map (row plans) into d_workspace (caller-owned,
- * >= workspace_bytes, 256-byte aligned) with an async copy on `stream`.  The
- * plan keeps d_workspace; it must stay allocated while the plan is used.
- * Plans with workspace_bytes == 0 accept NULL and do nothing.
+ * >= workspace_bytes, 256-byte aligned) with a copy on `stream`, and wait for
+ * that stream (the host-side map stays owned by the plan).  Device-routed row
+ * plans instead zero their map on `stream` without waiting.  The plan keeps
+ * d_workspace; it must stay allocated while the plan is used.  Plans with
+ * workspace_bytes == 0 accept NULL and do nothing.
  */
 rrb_status rrb_plan_bind(rrb_plan_t plan, void *d_workspace, size_t bytes,
                          rrb_stream_t stream);
 
-/* Copy up to `cap` index-map segments into out[]; *n receives the total. */
+/* Copy up to `cap` index-map segments into out[] (which may be NULL when
+ * cap <= 0); *n receives the total. */
 rrb_status rrb_plan_segments(rrb_plan_t plan, rrb_segment *out, int32_t cap,
                              int32_t *n);
 

@@ -95,7 +95,12 @@ rrb_status rrb_plan_create_rows_device(int32_t nranks, int64_t tokens, int64_t h
   *out = nullptr;
   rrb_plan_s *p = new (std::nothrow) rrb_plan_s;
   if (!p) return fail(RRB_ENOMEM, "plan allocation failed");
-  const rrb_status s = build_row_plan_device(nranks, tokens, hidden, experts, topk, dir, p->p);
+  rrb_status s;
+  try {
+    s = build_row_plan_device(nranks, tokens, hidden, experts, topk, dir, p->p);
+  } catch (const std::bad_alloc &) {
+    s = fail(RRB_ENOMEM, "plan allocation failed");
+  }
   if (s != RRB_OK) {
     delete p;
     return s;
@@ -187,6 +192,7 @@ rrb_status rrb_plan_bind(rrb_plan_t plan, void *d_workspace, size_t bytes, rrb_s
 rrb_status rrb_plan_segments(rrb_plan_t plan, rrb_segment *out, int32_t cap, int32_t *n) {
   clear_error();
   if (!plan || !n) return fail(RRB_EINVAL, "NULL plan or n");
+  if (cap > 0 && !out) return fail(RRB_EINVAL, "NULL out with cap %d", cap);
   const Plan &p = plan->p;
   *n = static_cast<int32_t>(p.segs.size());
   for (int32_t i = 0; i < cap && i < *n; ++i) {

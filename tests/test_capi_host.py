@@ -155,6 +155,17 @@ def test_zero_count_plan(librrb):
     assert p.in_count == [0] * 8 and p.out_count == [0] * 8
 
 
+def test_segments_out_may_be_null_only_without_capacity(librrb):
+    import ctypes
+    lib = librrb
+    p = api.Plan(8, 4096, "bf16", api.SHARD, api.REPLICATED, "copy")
+    n = ctypes.c_int32(-1)
+    L.check(lib.rrb_plan_segments(p.handle, None, 0, ctypes.byref(n)), "count only")
+    assert n.value == len(p.segments()) > 0
+    assert lib.rrb_plan_segments(p.handle, None, 4, ctypes.byref(n)) == L.RRB_EINVAL
+    assert b"NULL out" in lib.rrb_last_error()
+
+
 @pytest.mark.parametrize("T,E,k,R", [(64, 32, 4, 8), (4096, 256, 8, 8), (32, 8, 8, 4)])
 def test_row_plan_sizes_match_oracle(librrb, T, E, k, R):
     rng = np.random.default_rng(T)
