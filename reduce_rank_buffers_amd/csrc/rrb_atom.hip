@@ -372,6 +372,8 @@ ReduceFn reduce_tree_vec_for(int R) {
   return nullptr;
 }
 
+// Several vectors per lane (U > 1) only for R <= 8, where the R x U loads
+// still leave room for occupancy; more ranks keep one vector per lane.
 template <int U, bool BF16, bool NTL, bool NTS>
 ReduceFn reduce_vec_for(int R) {
   switch (R) {
@@ -379,9 +381,18 @@ ReduceFn reduce_vec_for(int R) {
   case n:           \
     return reduce_vec_kernel<n, U, BF16, NTL, NTS>;
     RRB_CASE(1) RRB_CASE(2) RRB_CASE(3) RRB_CASE(4) RRB_CASE(5) RRB_CASE(6) RRB_CASE(7)
-    RRB_CASE(8) RRB_CASE(9) RRB_CASE(10) RRB_CASE(11) RRB_CASE(12) RRB_CASE(13)
-    RRB_CASE(14) RRB_CASE(15) RRB_CASE(16)
+    RRB_CASE(8)
 #undef RRB_CASE
+  }
+  if constexpr (U == 1) {
+    switch (R) {
+#define RRB_CASE(n) \
+  case n:           \
+    return reduce_vec_kernel<n, 1, BF16, NTL, NTS>;
+      RRB_CASE(9) RRB_CASE(10) RRB_CASE(11) RRB_CASE(12) RRB_CASE(13) RRB_CASE(14)
+      RRB_CASE(15) RRB_CASE(16)
+#undef RRB_CASE
+    }
   }
   return nullptr;
 }
@@ -395,8 +406,12 @@ constexpr int64_t kStreamBytesReduce = 64LL << 20;
 constexpr int64_t kStreamBytesCopy = 512LL << 20;
 // Tiles per XCD run in the chunked order of streaming launches.
 constexpr int kXcdChunk = 16;
-// Vectors per launch above which a lane handles more than one vector.
+// Vectors per launch from which a reduce lane handles more than one vector:
+// four up to kHugeVectors, two from there on.  Measured on MI355X with
+// interleaved A/B runs of library builds, 8 ranks: four per lane is 2-4%
+// ahead of two at 32, 64 and 128 MiB per rank, and 1-3% behind at 256 MiB.
 constexpr int64_t kBigVectors = 2LL << 20;
+constexpr int64_t kHugeVectors = 16LL << 20;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
@@ -541,7 +556,8 @@ rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out
     bs = small ? 64 : 256;
     if (reduce) {
       const bool fan = __builtin_popcount(p.segs[0].dst_mask) > 1;
-      U = (small || !big || p.nranks > 8 || tree) ? 1 : 2;
+      const bool huge = static_cast<int64_t>(p.segs.size()) * a.nvec >= kHugeVectors;
+      U = (small || !big || p.nranks > 8 || tree) ? 1 : huge ? 2 : 4;
       if (tree) {
         kern = stream ? (fan ? (bf16 ? reduce_tree_vec_for<true, true, true>(p.nranks)
                                      : reduce_tree_vec_for<false, true, true>(p.nranks))
@@ -556,6 +572,13 @@ rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out
                                      : reduce_vec_for<1, false, true, false>(p.nranks)))
                       : (bf16 ? reduce_vec_for<1, true, false, false>(p.nranks)
                               : reduce_vec_for<1, false, false, false>(p.nranks));
+      } else if (U == 4) {
+        kern = stream ? (fan ? (bf16 ? reduce_vec_for<4, true, true, true>(p.nranks)
+                                     : reduce_vec_for<4, false, true, true>(p.nranks))
+                             : (bf16 ? reduce_vec_for<4, true, true, false>(p.nranks)
+                                     : reduce_vec_for<4, false, true, false>(p.nranks)))
+                      : (bf16 ? reduce_vec_for<4, true, false, false>(p.nranks)
+                              : reduce_vec_for<4, false, false, false>(p.nranks));
       } else {
         kern = stream ? (fan ? (bf16 ? reduce_vec_for<2, true, true, true>(p.nranks)
                                      : reduce_vec_for<2, false, true, true>(p.nranks))

@@ -110,6 +110,20 @@ def test_sweep_fp32_64mib():
 ROOTS = {"broadcast": 3, "reduce": 0, "gather": 5}
 
 
+@pytest.mark.parametrize("dtype,n", [("bf16", (1 << 24) + 5), ("f32", (1 << 23) + 3),
+                                     ("bf16", (1 << 25) + 2)])
+def test_unrolled_reduce_with_ragged_tail(dtype, n):
+    """Single-segment reduces of 2M-4M vectors plus a ragged tail (four vectors
+    per lane, then the element tail): All-Reduce and Reduce(root 2), full
+    compare."""
+    require_gpu()
+    _say(f"unrolled reduce {dtype} n={n}")
+    R = 8
+    ins = inputs.rank_payloads(n, R, dtype, 1.0, inputs.WL_LARGE, 7)
+    _run_and_check("all_reduce", ins, dtype)
+    _run_and_check("reduce", ins, dtype, 2)
+
+
 @pytest.mark.parametrize("name", list(C.SEVEN))
 def test_seven_collectives_16mib(name):
     require_gpu()
