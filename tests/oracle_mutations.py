@@ -1,0 +1,98 @@
+"""Mutation check of the oracle's pins (CPU only; not collected by pytest).
+
+Plants one plausible mistake at a time -- a dropped or reordered term, a wrong
+index, root or chunk, a transposed operand, a changed rounding rule -- in a
+scratch copy of the repository's oracle/, runs the CPU test suite there, and
+lists every mistake no test catches.  Run: python tests/oracle_mutations.py
+[name-substring ...].  The repository itself is never modified.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+SRC = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+DST = "/tmp/rrb_mut"
+
+M = [
+    # bf16
+    ("bf16 ties to odd", "oracle/bf16.py", "((lo & np.uint32(1)) == 1)", "((lo & np.uint32(1)) == 0)"),
+    ("bf16 ties always up", "oracle/bf16.py", "pick_hi = (d_hi < d_lo) |", "pick_hi = (d_hi <= d_lo) |"),
+    ("bf16 truncation", "oracle/bf16.py", "mag = np.where(pick_hi, hi, lo)", "mag = lo"),
+    ("bf16 NaN keeps sign", "oracle/bf16.py", "out = np.where(is_nan, CANONICAL_NAN, out)",
+     "out = np.where(is_nan, (sign | np.uint32(0x7FC0)).astype(np.uint16), out)"),
+    ("bf16 no overflow to inf", "oracle/bf16.py", "np.float64(2.0) ** 128, v)", "np.float64(2.0) ** 200, v)"),
+    ("bf16 subnormal flush", "oracle/bf16.py", "    out = (sign | mag).astype(np.uint16)\n",
+     "    mag = np.where(mag < 0x0080, np.uint32(0), mag)\n    out = (sign | mag).astype(np.uint16)\n"),
+    # fold
+    ("fold from +0", "oracle/fold.py", "    s = xs[0].copy()\n    with np.errstate(over=\"ignore\", invalid=\"ignore\"):  # IEEE inf / NaN results\n        for x in xs[1:]:",
+     "    s = np.zeros_like(xs[0])\n    with np.errstate(over=\"ignore\", invalid=\"ignore\"):  # IEEE inf / NaN results\n        for x in xs:"),
+    ("fold drops last rank", "oracle/fold.py", "        for x in xs[1:]:", "        for x in xs[1:-1]:"),
+    ("fold in float64", "oracle/fold.py", "            s = (s + x).astype(np.float32)\n    return s",
+     "            s = s.astype(np.float64) + x\n    return s.astype(np.float32)"),
+    ("fold reversed order", "oracle/fold.py", "    xs = [np.asarray(x, dtype=np.float32) for x in xs]\n    if not xs:\n        raise ValueError(\"fold needs at least one rank\")\n    s = xs[0]",
+     "    xs = [np.asarray(x, dtype=np.float32) for x in xs][::-1]\n    if not xs:\n        raise ValueError(\"fold needs at least one rank\")\n    s = xs[0]"),
+    ("tree odd item first", "oracle/fold.py", "                nxt.append(items[-1])", "                nxt.insert(0, items[-1])"),
+    ("tree left fold", "oracle/fold.py", "            nxt = [(items[i] + items[i + 1]).astype(np.float32)\n                   for i in range(0, len(items) - 1, 2)]",
+     "            nxt = [(items[0] + items[1]).astype(np.float32)] + items[2:]\n            items = nxt\n            continue\n            nxt = []"),
+    ("f32 reduce rounds to bf16", "oracle/fold.py", "    return fold_f32(ins)\n\n\ndef fold_tree_f32",
+     "    return bf16.widen(bf16.rne(fold_f32(ins)))\n\n\ndef fold_tree_f32"),
+    # collectives
+    ("RS reversed chunk", "oracle/collectives.py", "    return [fold.reduce([x[q * c:(q + 1) * c] for x in ins], dtype) for q in range(R)]",
+     "    return [fold.reduce([x[(R - 1 - q) * c:(R - q) * c] for x in ins], dtype) for q in range(R)]"),
+    ("A2A transposed", "oracle/collectives.py", "    return [np.concatenate([np.asarray(ins[r])[q * c:(q + 1) * c] for r in range(R)])",
+     "    return [np.concatenate([np.asarray(ins[q])[r * c:(r + 1) * c] for r in range(R)])"),
+    ("broadcast from rank 0", "oracle/collectives.py", "    return [np.asarray(ins[root]).copy() for _ in ins]",
+     "    return [np.asarray(ins[0]).copy() for _ in ins]"),
+    ("gather reversed", "oracle/collectives.py", "    out[root] = np.concatenate([np.asarray(x) for x in ins])",
+     "    out[root] = np.concatenate([np.asarray(x) for x in ins[::-1]])"),
+    ("reduce root 0", "oracle/collectives.py", "    out[root] = fold.reduce(ins, dtype)", "    out[0] = fold.reduce(ins, dtype)"),
+    ("BLOCK_COL as row", "oracle/collectives.py", "        return [(\"M\", j // c, q, j % c) for j in range(n)]",
+     "        return [(\"M\", q, j // c, j % c) for j in range(n)]"),
+    ("SHARD off by one block", "oracle/collectives.py", "        return [(\"X\", q * c + j) for j in range(c)]",
+     "        return [(\"X\", ((q + 1) % R) * c + j) for j in range(c)]"),
+    ("AG concat reversed", "oracle/collectives.py", "    y = np.concatenate([np.asarray(x) for x in ins])\n    return [y.copy() for _ in ins]",
+     "    y = np.concatenate([np.asarray(x) for x in ins[::-1]])\n    return [y.copy() for _ in ins]"),
+    # moe
+    ("combine top-k order", "oracle/moe.py", "        order = np.argsort(idx[t], kind=\"stable\")  # ascending expert id",
+     "        order = range(k)"),
+    ("combine fused multiply-add", "oracle/moe.py", "            acc = term if acc is None else (acc + term).astype(np.float32)",
+     "            acc = term if acc is None else (acc.astype(np.float64) + np.float64(w[t, j]) * row.astype(np.float64)).astype(np.float32)"),
+    ("combine weight of wrong slot", "oracle/moe.py", "            term = (np.float32(w[t, j]) * row).astype(np.float32)",
+     "            term = (np.float32(w[t, order[0]]) * row).astype(np.float32)"),
+    ("dispatch tokens descending", "oracle/moe.py", "    return [sorted(l) for l in lists]", "    return [sorted(l, reverse=True) for l in lists]"),
+    ("expert rank modulo", "oracle/moe.py", "        r = e // per\n        offsets[e] = rows[r]", "        r = e % R\n        offsets[e] = rows[r]"),
+    # chain
+    ("chain tree order", "oracle/chain.py", "    return [fold.reduce(list(ins), dtype) for ins in ins_by_epoch]",
+     "    return [fold.reduce_tree(list(ins), dtype) for ins in ins_by_epoch]"),
+    ("chain epoch shift", "oracle/chain.py", "    return [fold.reduce(list(ins), dtype) for ins in ins_by_epoch]",
+     "    return [fold.reduce(list(ins), dtype) for ins in ins_by_epoch[:1]] + [fold.reduce(list(ins), dtype) for ins in ins_by_epoch[:-1]]"),
+]
+
+
+def main():
+    only = sys.argv[1:]
+    if os.path.exists(DST):
+        shutil.rmtree(DST)
+    shutil.copytree(SRC, DST, ignore=shutil.ignore_patterns(".git", "_work", "gpurun_out", "__pycache__", "*.log"))
+    survivors = []
+    for name, f, old, new in M:
+        if only and not any(o in name for o in only):
+            continue
+        path = os.path.join(DST, f)
+        orig = open(path).read()
+        assert orig.count(old) == 1, (name, orig.count(old))
+        open(path, "w").write(orig.replace(old, new))
+        r = subprocess.run([sys.executable, "-m", "pytest", "tests", "-x", "-q", "-m", "not gpu", "-n", "4",
+                            "-p", "no:cacheprovider"], cwd=DST, capture_output=True, text=True)
+        open(path, "w").write(orig)
+        caught = r.returncode != 0
+        failing = [l for l in r.stdout.splitlines() if l.startswith("FAILED") or "Error" in l][:2]
+        print(f"{'caught  ' if caught else 'SURVIVED'} {name:32s} {failing[0][:110] if failing else ''}", flush=True)
+        if not caught:
+            survivors.append(name)
+    print("survivors:", survivors)
+
+
+if __name__ == "__main__":
+    main()

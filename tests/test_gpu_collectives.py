@@ -201,6 +201,28 @@ def test_special_values_and_denormals():
     _run_and_check("reduce_scatter", ins, "bf16")
 
 
+@pytest.mark.parametrize("R", [4, 8])
+@pytest.mark.parametrize("n", [37, 4096, 8 * 8192])
+def test_fixed_rank_order_on_cancellation(R, n):
+    """Elements whose rank-order fold differs from any other association
+    ([2^24, 1, 1, -2^24, 0, ...] folds to 0 in rank order, to 1 pairwise)
+    amid wide-range data: All-Reduce and Reduce-Scatter through the decode,
+    vector and tail paths, against the oracle."""
+    require_gpu()
+    rng = np.random.default_rng(R * 10007 + n)
+    from oracle import bf16
+    ins = [bf16.rne((rng.standard_normal(n) * 2.0 ** rng.integers(-24, 25, n)).astype(np.float32))
+           for _ in range(R)]
+    col = bf16.rne(np.array([2.0 ** 24, 1.0, 1.0, -(2.0 ** 24)] + [0.0] * (R - 4), dtype=np.float32))
+    for j in range(0, n, max(1, n // 64)):
+        for r in range(R):
+            ins[r][j] = col[r]
+    assert C.all_reduce(ins)[0][0] == 0x0000
+    _run_and_check("all_reduce", ins, "bf16")
+    if n % R == 0:
+        _run_and_check("reduce_scatter", ins, "bf16")
+
+
 def test_invalid_call_arguments():
     require_gpu()
     p = api.Plan(8, 64, "bf16", api.PARTIAL, api.REPLICATED, "reduce")

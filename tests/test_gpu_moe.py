@@ -78,3 +78,50 @@ def test_moe_skewed_routing():
     xa = bf16.rne(rng.standard_normal((T, h)).astype(np.float32))
     shards = [xa[r * (T // R):(r + 1) * (T // R)] for r in range(R)]
     _roundtrip(T, h, E, k, R, idx, w, shards, "identity")
+
+
+# The fp32 weight whose exact product with 5.0 is 2^-8 + 2^-24 + 2^-33 (the
+# oracle's MoE pins prove the premises): rounding the product before the add
+# gives 1.0 (0x3F80) after 1.0 + product; a contracted multiply-add gives
+# 0x3F81.
+FMA_W_BITS = 978111898
+
+
+def _combine_one_token(k, h, order, w_row, z_vals):
+    """One token, R = 1, E = k: expert e's row is z_vals[e] in every column;
+    the token's top-k list is `order` with weights `w_row`.  Returns the GPU
+    combine row and the oracle's."""
+    idx = np.array([order], dtype=np.int32)
+    w = np.array([w_row], dtype=np.float32)
+    z_np = [bf16.rne(np.repeat(np.array(z_vals, dtype=np.float32)[:, None], h, axis=1))]
+    comb = api.MoePlan(1, h, k, idx, w, "combine")
+    y = [empty_like_np(h, "bf16", -21555)]
+    comb.run([to_dev(z_np[0].reshape(-1))], y)
+    torch.cuda.synchronize()
+    return from_dev(y[0]), OM.combine(z_np, idx, w, k, 1)[0].reshape(-1)
+
+
+@pytest.mark.parametrize("k", [2, 4, 8])
+@pytest.mark.parametrize("h", [8, 16, 13])
+def test_combine_no_contraction_and_ascending_expert_order(k, h):
+    """Crafted rows where a fused multiply-add, or folding in top-k order
+    instead of ascending expert id, changes the bf16 result: the kernel
+    (vector path for h = 8, 16; element path for h = 13) must match the
+    oracle and the hand-derived bits."""
+    require_gpu()
+    w1 = float(np.array([FMA_W_BITS], dtype=np.uint32).view(np.float32)[0])
+    # product rounding: experts 0 (z 1, w 1) and 1 (z 5, w w1), others 0
+    z = [1.0, 5.0] + [0.0] * (k - 2)
+    order = list(range(k))[::-1]
+    w_row = [1.0 if e != 1 else w1 for e in order]
+    got, want = _combine_one_token(k, h, order, w_row, z)
+    assert np.all(want == 0x3F80)
+    assert_bits_equal(got, want, f"combine rounding k={k} h={h}")
+    if k >= 4:
+        # order: 2^24 + 1 - 2^24 + 0... in ascending id is 0; the listed
+        # top-k order 3, 1, 2, 0, ... would give 1
+        z = [2.0 ** 24, 1.0, -(2.0 ** 24)] + [0.0] * (k - 3)
+        order = [3, 1, 2, 0] + list(range(4, k))
+        got, want = _combine_one_token(k, h, order, [1.0] * k, z)
+        assert np.all(want == 0x0000)
+        assert_bits_equal(got, want, f"combine order k={k} h={h}")

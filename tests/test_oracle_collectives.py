@@ -196,3 +196,51 @@ def test_collective_chain_is_per_epoch_collective():
             assert np.array_equal(ag[e][q], np.concatenate(shards[e]))
     g = OC.collective_chain("gather", shards, root=2)
     assert all(g[e][q] is None for e in range(E) for q in range(R) if q != 2)
+
+
+@pytest.mark.parametrize("R", [3, 8])
+def test_root_collectives_at_every_root(R):
+    """Reduce, Gather and Broadcast at each root: the closed forms equal the
+    element-by-element layout definition, the root gets the All-Reduce /
+    All-Gather / its own buffer, and no other rank is written."""
+    c = 4
+    n = R * c
+    ins = _payloads(R, n, 31 + R)
+    shards = [x[:c] for x in ins]
+    ar = C.all_reduce(ins)[0]
+    ag = C.all_gather(shards)[0]
+    for root in range(R):
+        red = C.reduce_root(ins, root)
+        _same(red, C.collective(C.PARTIAL, C.ROOT(root), "reduce", ins, R, n))
+        assert np.array_equal(red[root], ar)
+        assert all(red[q] is None for q in range(R) if q != root)
+        gat = C.gather(shards, root)
+        _same(gat, C.collective(C.SHARD, C.ROOT(root), "copy", shards, R, n))
+        assert np.array_equal(gat[root], ag)
+        assert all(gat[q] is None for q in range(R) if q != root)
+        bc = C.broadcast(ins, root)
+        _same(bc, C.collective(C.ROOT(root), C.REPLICATED, "copy",
+                               [ins[q] if q == root else None for q in range(R)], R, n))
+        assert all(np.array_equal(b, ins[root]) for b in bc)
+
+
+def test_allreduce_chain_folds_in_fixed_rank_order():
+    """Per epoch, every element of the chain oracle equals the exact rational
+    emulation of the fixed-order fold, on data where the tree order differs:
+    [2^24, 1, 1, -2^24] folds to 0 in rank order and to 1 pairwise."""
+    from oracle import chain as OC
+    from tests import _exact
+    R, n, E = 4, 6, 3
+    rng = np.random.default_rng(41)
+    ins = []
+    for e in range(E):
+        xs = [bf16.rne((rng.standard_normal(n) * 2.0 ** rng.integers(-24, 25, n)).astype(np.float32))
+              for _ in range(R)]
+        for r, v in enumerate([2.0 ** 24, 1.0, 1.0, -(2.0 ** 24)]):
+            xs[r][0] = bf16.rne(np.array([v], dtype=np.float32))[0]
+        ins.append(xs)
+    got = OC.allreduce_chain(ins)
+    for e in range(E):
+        assert int(got[e][0]) == 0x0000
+        for j in range(n):
+            assert int(got[e][j]) == _exact.fold_bf16_exact([int(ins[e][r][j]) for r in range(R)])

@@ -96,17 +96,50 @@ def test_combine_exact_emulation_tiny():
 
 
 def test_combine_uses_ascending_expert_order_not_topk_order():
-    # A token whose top-k order differs from ascending id: cancellation makes
-    # the order visible.
-    h = 1
+    # A token whose top-k order differs from ascending id: the fp32 rounding
+    # of 2^24 + 1 makes the order visible.
     idx = np.array([[3, 1, 2, 0]], dtype=np.int32)
     w = np.ones((1, 4), dtype=np.float32)
-    vals = {0: 2.0 ** 20, 1: 1.0, 2: -(2.0 ** 20), 3: 0.0}
+    vals = {0: 2.0 ** 24, 1: 1.0, 2: -(2.0 ** 24), 3: 0.0}
     # one expert per rank with R = 4, E = 4: rank e holds expert e
     z = [bf16.rne(np.array([[vals[e]]], dtype=np.float32)) for e in range(4)]
-    y = moe.combine(z, idx, w, 4, 1)
-    # ascending: 2^20 + 1 = 2^20+1 (exact in f32), - 2^20 = 1, + 0 = 1
-    assert int(np.concatenate(y)[0, 0]) == 0x3F80
+    # T = 4 tokens (one per rank) all routed the same way
+    idx4 = np.repeat(idx, 4, axis=0)
+    w4 = np.repeat(w, 4, axis=0)
+    z4 = [np.repeat(x, 4, axis=0) for x in z]
+    y = np.concatenate(moe.combine(z4, idx4, w4, 4, 1))
+    # ascending id: 2^24 + 1 rounds to 2^24 (tie, even), - 2^24 = 0, + 0 = 0;
+    # the top-k order 3, 1, 2, 0 would give 0 + 1 - 2^24 + 2^24 = 1 (0x3F80)
+    assert np.all(y[:, 0] == 0x0000)
+
+
+# An fp32 weight whose exact product with 5.0 is 2^-8 + 2^-24 + 2^-33: one
+# binary32 multiply rounds it to 2^-8 + 2^-24, and 1 + that is an fp32 tie
+# that goes to 1 + 2^-8, itself a bf16 tie that goes to 1.0.  A fused
+# multiply-add keeps the 2^-33 and lands on 1 + 2^-7 instead.
+FMA_W_BITS = 978111898
+FMA_Z = 5.0
+
+
+def test_fma_case_premises_hold_exactly():
+    w = float(np.array([FMA_W_BITS], dtype=np.uint32).view(np.float32)[0])
+    prod = Fraction(w) * Fraction(FMA_Z)
+    assert prod == Fraction(1, 2 ** 8) + Fraction(1, 2 ** 24) + Fraction(1, 2 ** 33)
+    assert _exact.f32_mul(w, FMA_Z) == 2.0 ** -8 + 2.0 ** -24
+    sep = _exact.f32_add(1.0, _exact.f32_mul(w, FMA_Z))
+    fused = _exact.round_binary(Fraction(1) + prod, 24)
+    assert _exact.to_bf16_bits(sep) == 0x3F80 and _exact.to_bf16_bits(fused) == 0x3F81
+
+
+def test_combine_rounds_the_product_before_the_add():
+    w1 = np.array([FMA_W_BITS], dtype=np.uint32).view(np.float32)[0]
+    # R = 1, E = 2 (rank 0 holds both experts); one token, experts 1 then 0
+    idx = np.array([[1, 0]], dtype=np.int32)
+    w = np.array([[w1, 1.0]], dtype=np.float32)
+    z = [bf16.rne(np.array([[1.0], [FMA_Z]], dtype=np.float32))]
+    y = moe.combine(z, idx, w, 2, 1)
+    # ascending id: expert 0 (z = 1.0, w = 1) then expert 1 (z = 5, w = w1)
+    assert int(y[0][0, 0]) == 0x3F80
 
 
 def test_gate_routing_is_valid():
