@@ -8,9 +8,10 @@
 //   combine (reduce):  every token gathers its k expert rows, folds
 //                      fl32(w * row) in ascending expert id with one multiply
 //                      then one add per step, and rounds once to bf16.
-// One workgroup owns one token row, so the map entries it needs (k slots and
-// weights) are uniform and come through scalar loads; the row itself moves as
-// coalesced 16-byte vectors.  Both kernels are HBM-bound: dispatch reads T*h
+// A token row is split into equal parts, one workgroup per (token, part), so
+// the map entries a workgroup needs (k slots and weights) are uniform and
+// come through scalar loads; the row itself moves as coalesced 16-byte
+// vectors.  Both kernels are HBM-bound: dispatch reads T*h
 // and writes T*k*h elements, combine the reverse.
 #include <hip/hip_runtime.h>
 
@@ -33,41 +34,34 @@ struct RowArgs {
   int64_t row_bytes;     // hidden * 2
   int64_t nvec;          // whole 16-byte vectors per row
   int64_t hidden;
+  int64_t part_vec;      // vector path: vectors per row part (one workgroup each)
+  int32_t parts;         // vector path: parts per row
   int32_t k;
 };
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
-// One token row per workgroup: DU 16-byte vectors per lane in flight, each
+// One workgroup per part of a token row, one 16-byte vector per lane, each
 // written to the token's k receive slots with non-temporal stores (the 1->k
 // fan-out streams past the caches; measured 6.7 TB/s on MI355X for 1->8 vs
-// 5.2 with plain stores).
-template <int DU>
-__global__ void __launch_bounds__(128) moe_dispatch_kernel(RowArgs a) {
-  const int64_t t = blockIdx.x;
+// 5.2 with plain stores).  Parts of at most 256 vectors: for a 7168-wide row,
+// 4 parts of 224 vectors ran 4-7% ahead of one 128-lane workgroup with 8
+// vectors per lane (interleaved A/B runs, 4096 tokens, top-8).
+__global__ void __launch_bounds__(256) moe_dispatch_kernel(RowArgs a) {
+  const int64_t t = blockIdx.x / a.parts;
+  const int64_t v0 = (static_cast<int64_t>(blockIdx.x) - t * a.parts) * a.part_vec;
+  const int64_t v1 = v0 + a.part_vec < a.nvec ? v0 + a.part_vec : a.nvec;
   const int64_t src_rank = t / a.tokens_per_rank;
   const unsigned char *src =
       a.in[src_rank] + (t - src_rank * a.tokens_per_rank) * a.row_bytes;
   const int32_t *slots = a.slot + t * a.k;
-  const int bs = blockDim.x;
-  // Predicated passes of DU vectors per lane (one pass covers a 7168-wide
-  // bf16 row with 128 lanes), so every load of the row is in flight at once.
-  for (int64_t i0 = threadIdx.x; i0 < a.nvec; i0 += static_cast<int64_t>(bs) * DU) {
-    v4u x[DU];
-#pragma unroll
-    for (int u = 0; u < DU; ++u) {
-      const int64_t i = i0 + static_cast<int64_t>(u) * bs;
-      if (i < a.nvec) x[u] = *reinterpret_cast<const v4u *>(src + i * 16);
-    }
+  for (int64_t i = v0 + threadIdx.x; i < v1; i += blockDim.x) {
+    const v4u x = *reinterpret_cast<const v4u *>(src + i * 16);
     for (int j = 0; j < a.k; ++j) {
       const int32_t s = slots[j];
       unsigned char *dst = a.out[s >> kSlotRankShift] +
                            static_cast<int64_t>(s & kSlotRowMask) * a.row_bytes;
-#pragma unroll
-      for (int u = 0; u < DU; ++u) {
-        const int64_t i = i0 + static_cast<int64_t>(u) * bs;
-        if (i < a.nvec) __builtin_nontemporal_store(x[u], reinterpret_cast<v4u *>(dst + i * 16));
-      }
+      __builtin_nontemporal_store(x, reinterpret_cast<v4u *>(dst + i * 16));
     }
   }
 }
@@ -119,12 +113,16 @@ __device__ __forceinline__ v4u combine_vec(const v4u (&z)[K], const float (&w)[K
   return o;
 }
 
-// One token per workgroup of 256 lanes: CU vectors x K rows in flight per
-// lane, non-temporal loads and stores (every expert row is read once and the
-// combined row is not read again here).
+// One workgroup per part of a token row: CU vectors x K rows in flight per
+// lane (K * CU >= 8), non-temporal loads and stores (every expert row is read
+// once and the combined row is not read again here).  Parts of 128 * CU
+// vectors: for a 7168-wide row and top-8, 7 parts of 128 lanes ran 3-4% ahead
+// of one 256-lane workgroup with 4 vectors per lane (interleaved A/B runs).
 template <int K, int CU>
-__global__ void __launch_bounds__(256) moe_combine_kernel(RowArgs a) {
-  const int64_t t = blockIdx.x;
+__global__ void __launch_bounds__(128) moe_combine_kernel(RowArgs a) {
+  const int64_t t = blockIdx.x / a.parts;
+  const int64_t v0 = (static_cast<int64_t>(blockIdx.x) - t * a.parts) * a.part_vec;
+  const int64_t v1 = v0 + a.part_vec < a.nvec ? v0 + a.part_vec : a.nvec;
   const int64_t dst_rank = t / a.tokens_per_rank;
   unsigned char *dst = a.out[dst_rank] + (t - dst_rank * a.tokens_per_rank) * a.row_bytes;
   const int32_t *slots = a.slot + t * K;
@@ -138,12 +136,12 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(RowArgs a) {
     w[j] = ws[j];
   }
   const int bs = blockDim.x;
-  for (int64_t i0 = threadIdx.x; i0 < a.nvec; i0 += static_cast<int64_t>(bs) * CU) {
+  for (int64_t i0 = v0 + threadIdx.x; i0 < v1; i0 += static_cast<int64_t>(bs) * CU) {
     v4u z[CU][K];
 #pragma unroll
     for (int u = 0; u < CU; ++u) {
       const int64_t i = i0 + static_cast<int64_t>(u) * bs;
-      if (i < a.nvec) {
+      if (i < v1) {
 #pragma unroll
         for (int j = 0; j < K; ++j)
           z[u][j] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(rows[j] + i * 16));
@@ -152,7 +150,7 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(RowArgs a) {
 #pragma unroll
     for (int u = 0; u < CU; ++u) {
       const int64_t i = i0 + static_cast<int64_t>(u) * bs;
-      if (i < a.nvec)
+      if (i < v1)
         __builtin_nontemporal_store(combine_vec<K>(z[u], w), reinterpret_cast<v4u *>(dst + i * 16));
     }
   }
@@ -640,16 +638,26 @@ namespace {
 
 using RowFn = void (*)(RowArgs);
 
-RowFn combine_for(int k) {
+// Combine kernel for top-k and its vectors per lane (k * CU >= 8 loads in
+// flight per lane).
+RowFn combine_for(int k, int *cu) {
   switch (k) {
-    case 1: return moe_combine_kernel<1, 8>;
-    case 2: return moe_combine_kernel<2, 8>;
-    case 4: return moe_combine_kernel<4, 4>;
-    case 6: return moe_combine_kernel<6, 4>;
-    case 8: return moe_combine_kernel<8, 4>;
-    case 16: return moe_combine_kernel<16, 2>;
-    default: return nullptr;
+    case 1: *cu = 8; return moe_combine_kernel<1, 8>;
+    case 2: *cu = 4; return moe_combine_kernel<2, 4>;
+    case 4: *cu = 2; return moe_combine_kernel<4, 2>;
+    case 6: *cu = 2; return moe_combine_kernel<6, 2>;
+    case 8: *cu = 1; return moe_combine_kernel<8, 1>;
+    case 16: *cu = 1; return moe_combine_kernel<16, 1>;
+    default: *cu = 0; return nullptr;
   }
+}
+
+// Row parts: the fewest parts of at most `cap` vectors, all of equal size
+// (the last may be shorter).
+void split_row(RowArgs &a, int64_t cap) {
+  a.parts = static_cast<int32_t>((a.nvec + cap - 1) / cap);
+  if (a.parts < 1) a.parts = 1;
+  a.part_vec = (a.nvec + a.parts - 1) / a.parts;
 }
 
 }  // namespace
@@ -683,17 +691,29 @@ rrb_status launch_rows(const Plan &p, const void *const *in, void *const *out, v
   a.nvec = a.row_bytes / 16;
   a.hidden = m.hidden;
   a.k = m.topk;
-  RowFn kern;
+  RowFn kern = nullptr;
   int bs = 256;
+  a.parts = 1;
+  a.part_vec = a.nvec;
   if (m.dir == RRB_MOE_DISPATCH) {
-    kern = vec ? moe_dispatch_kernel<8> : moe_dispatch_elem_kernel;
+    if (vec) {
+      kern = moe_dispatch_kernel;
+      split_row(a, 256);
+    } else {
+      kern = moe_dispatch_elem_kernel;
+    }
   } else {
-    kern = vec ? combine_for(m.topk) : nullptr;
-    if (!kern) kern = moe_combine_elem_kernel;
+    int cu = 0;
+    if (vec) kern = combine_for(m.topk, &cu);
+    if (kern) {
+      bs = 128;
+      split_row(a, 128LL * cu);
+    } else {
+      kern = moe_combine_elem_kernel;
+    }
   }
-  if (vec && m.dir == RRB_MOE_DISPATCH) bs = 128;
-  if (m.tokens > 0x7fffffffLL) return fail(RRB_EUNSUPPORTED, "too many tokens for one launch");
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(m.tokens)), dim3(bs), 0,
+  if (m.tokens * a.parts > 0x7fffffffLL) return fail(RRB_EUNSUPPORTED, "too many tokens for one launch");
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(m.tokens * a.parts)), dim3(bs), 0,
                      static_cast<hipStream_t>(stream), a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(RRB_EHIP, "moe launch: %s", hipGetErrorString(e));
