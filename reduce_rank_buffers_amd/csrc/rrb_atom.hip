@@ -397,13 +397,17 @@ ReduceFn reduce_vec_for(int R) {
   return nullptr;
 }
 
-// Total bytes a launch moves above which it streams past the caches
-// (non-temporal hints).  Measured on the bandwidth sweep on MI355X: reduces
-// gain from 64 MiB up; copies only from 512 MiB up (below that, plain stores
-// leave the outputs in the Infinity Cache, which the next collective of the
-// sweep reads).
+// When a launch streams past the caches (non-temporal hints).  A reduce
+// streams from 64 MiB of traffic (one read and one write per element per
+// rank), measured on the bandwidth sweep on MI355X.  A copy streams when the
+// bytes it writes reach half the 256 MB Infinity Cache: output that large
+// would only evict other lines.  Measured on the sweep step (All-Reduce ->
+// Reduce-Scatter -> All-Gather at 1..256 MiB per rank), interleaved A/B:
+// 2.577 -> 2.515 ms per step against counting copies at 512 MiB of one
+// read and one write per element (64 MiB All-Gather 112 -> 92 us); a
+// 256 MiB threshold gave 2.553 ms.
 constexpr int64_t kStreamBytesReduce = 64LL << 20;
-constexpr int64_t kStreamBytesCopy = 512LL << 20;
+constexpr int64_t kStreamOutCopy = 128LL << 20;
 // Tiles per XCD run in the chunked order of streaming launches.
 constexpr int kXcdChunk = 16;
 // Vectors per launch from which a reduce lane handles more than one vector:
@@ -549,7 +553,9 @@ rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out
     const bool small = a.nvec <= 4096;
     const int64_t traffic = static_cast<int64_t>(p.segs.size()) * len * esz *
                             (reduce ? p.nranks : 1) * 2;
-    const bool stream = traffic >= (reduce ? kStreamBytesReduce : kStreamBytesCopy);
+    int64_t out_bytes = 0;
+    for (const Segment &sg : p.segs) out_bytes += sg.len * esz * __builtin_popcount(sg.dst_mask);
+    const bool stream = reduce ? traffic >= kStreamBytesReduce : out_bytes >= kStreamOutCopy;
     // Mid-size launches keep one vector per lane so the grid still covers
     // every CU several times over; only very large ones unroll.
     const bool big = static_cast<int64_t>(p.segs.size()) * a.nvec >= kBigVectors;
@@ -588,9 +594,12 @@ rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out
                               : reduce_vec_for<2, false, false, false>(p.nranks));
       }
     } else {
+      // Streaming copies: one vector per lane on 128-lane workgroups (the
+      // 64 MiB All-Gather 103 -> 92 us against 256 lanes, 8 ranks).
       U = (small || stream || !big) ? 1 : 4;
       kern = stream ? copy_vec_kernel<1, true> : (U == 1 ? copy_vec_kernel<1, false>
                                                           : copy_vec_kernel<4, false>);
+      if (stream) bs = 128;
     }
     const int64_t per_tile = static_cast<int64_t>(bs) * U;
     int64_t tiles = (a.nvec + per_tile - 1) / per_tile;
