@@ -161,6 +161,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
+// 16-byte store at byte offset `off` of a `bytes`-long buffer with the cache
+// policy of agent-scope atomic stores (sc1): the line is written through
+// rather than left dirty in this XCD's L2, so the next release fence (an L2
+// write-back) has less to do.  The barrier, dual and speculative All-Reduce
+// chains stage and store outputs through here; the fences stay as they are.
+// Measured on MI355X, 8 ranks, 64-epoch chains: 4-13% less time per
+// All-Reduce from 8 KiB to 2 MiB.
+__device__ __forceinline__ void store_wt(unsigned char *base, int64_t bytes, int64_t off, v4u x) {
+  __builtin_amdgcn_raw_buffer_store_b128(x, rsrc(base, bytes), static_cast<int32_t>(off), 0, 16);
+}
+__device__ __forceinline__ void store_wt(unsigned char *base, int64_t bytes, int64_t off, uint4 x) {
+  store_wt(base, bytes, off, v4u{x.x, x.y, x.z, x.w});
+}
+// Write-through (WT) or plain 16-byte store.
+template <bool WT>
+__device__ __forceinline__ void store16(unsigned char *base, int64_t bytes, int64_t off, v4u x) {
+  if (WT) store_wt(base, bytes, off, x);
+  else *reinterpret_cast<v4u *>(base + off) = x;
+}
+
 // Device-coherent 16-byte load (cache policy sc1, as for agent-scope atomic
 // loads): never served from a line another epoch left in this CU's caches.
 __device__ __forceinline__ uint4 load_coherent(__amdgpu_buffer_rsrc_t r, int32_t off) {
@@ -224,11 +244,12 @@ __device__ __forceinline__ void notify(uint32_t *flag, uint32_t ep) {
 }
 
 // Reduce one pass of this workgroup's slice: R loads in flight per lane, fold
-// in rank order, store to this rank's output.
-template <int R, bool BF16>
-__device__ __forceinline__ void reduce_pass(const uint4 (&v)[R], unsigned char *dst) {
-  const uint4 res = BF16 ? fold_bf16x8<R>(v) : fold_f32x4<R>(v);
-  *reinterpret_cast<uint4 *>(dst) = res;
+// in rank order, store the result at byte `off` of the `bytes`-long `dst`.
+template <int R, bool BF16, bool WT = true>
+__device__ __forceinline__ void reduce_pass(const uint4 (&v)[R], unsigned char *dst, int64_t bytes,
+                                            int64_t off) {
+  const uint4 o = BF16 ? fold_bf16x8<R>(v) : fold_f32x4<R>(v);
+  store16<WT>(dst, bytes, off, v4u{o.x, o.y, o.z, o.w});
 }
 
 // Twoshot piece (q, s): slice s of chunk q, as a vector range [lo, hi).
@@ -243,8 +264,8 @@ __device__ __forceinline__ void piece_range(const SnacArgs &a, int q, int s, int
 // Copies pieces (q, s), q = 0..R-1, from `from` to `to` (both payload-shaped):
 // per pass, 2 vectors of every piece per lane in flight (2 R loads, no index
 // division).  COHERENT reads with the device-coherent policy (data another
-// workgroup wrote this epoch).
-template <int R, bool COHERENT>
+// workgroup wrote this epoch); WT stores write through.
+template <int R, bool COHERENT, bool WT>
 __device__ __forceinline__ void copy_pieces(const SnacArgs &a, int s, const unsigned char *from,
                                             unsigned char *to, int64_t bytes) {
   const int bs = blockDim.x;
@@ -274,7 +295,7 @@ __device__ __forceinline__ void copy_pieces(const SnacArgs &a, int s, const unsi
     for (int q = 0; q < R; ++q)
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        if (at[q][u] >= 0) *reinterpret_cast<v4u *>(to + at[q][u]) = x[q][u];
+        if (at[q][u] >= 0) store16<WT>(to, bytes, at[q][u], x[q][u]);
   }
 }
 
@@ -297,8 +318,9 @@ __device__ bool twoshot_epoch(const SnacArgs &a, int r, int s, int k, uint32_t e
   unsigned char *mine = stage_base + static_cast<int64_t>(r) * a.rank_bytes;
   unsigned char *dst = a.out + (static_cast<int64_t>(k) * R + r) * a.rank_bytes;
 
-  // Stage pieces (q, s) of this rank's payload.
-  copy_pieces<R, false>(a, s, src, mine, a.rank_bytes);
+  // Stage pieces (q, s) of this rank's payload.  Twoshot keeps plain stores:
+  // write-through stores made it 10-25% slower per All-Reduce (MI355X).
+  copy_pieces<R, false, false>(a, s, src, mine, a.rank_bytes);
   notify(flags_b + r * stride_rs + s * kFlagStride, ep);
   if (!wait_all<R>(flags_b + s * kFlagStride, stride_rs, ep, a.status, a.spin_limit, lds_ok))
     return false;
@@ -324,7 +346,7 @@ __device__ bool twoshot_epoch(const SnacArgs &a, int r, int s, int k, uint32_t e
 #pragma unroll
       for (int u = 0; u < CU; ++u) {
         const int64_t i = i0 + static_cast<int64_t>(u) * bs;
-        if (i < hi) reduce_pass<R, BF16>(v[u], red + i * 16);
+        if (i < hi) reduce_pass<R, BF16, false>(v[u], red, a.rank_bytes, i * 16);
       }
     }
   }
@@ -333,7 +355,7 @@ __device__ bool twoshot_epoch(const SnacArgs &a, int r, int s, int k, uint32_t e
     return false;
 
   // All-gather: pieces (q, s) of the reduced payload into this rank's output.
-  copy_pieces<R, true>(a, s, red, dst, a.rank_bytes);
+  copy_pieces<R, true, false>(a, s, red, dst, a.rank_bytes);
   return true;
 }
 
@@ -385,10 +407,10 @@ __global__ void __launch_bounds__(64) snac_chain_kernel(SnacArgs a) {
           x[u] = *reinterpret_cast<const v4u *>(src + (i + static_cast<int64_t>(u) * bs) * 16);
 #pragma unroll
         for (int u = 0; u < kStageU; ++u)
-          *reinterpret_cast<v4u *>(mine + (i + static_cast<int64_t>(u) * bs) * 16) = x[u];
+          store_wt(mine, a.rank_bytes, (i + static_cast<int64_t>(u) * bs) * 16, x[u]);
       }
       for (; i < v1; i += bs)
-        *reinterpret_cast<uint4 *>(mine + i * 16) = *reinterpret_cast<const uint4 *>(src + i * 16);
+        store_wt(mine, a.rank_bytes, i * 16, *reinterpret_cast<const v4u *>(src + i * 16));
     }
 
     // Notify.
@@ -426,7 +448,7 @@ __global__ void __launch_bounds__(64) snac_chain_kernel(SnacArgs a) {
       // Orders this rank's next stage after every source's earlier reads.
       if (valid) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       if (valid) {
-        if (i < v1) reduce_pass<R, BF16>(v, dst_base + i * 16);
+        if (i < v1) reduce_pass<R, BF16>(v, dst_base, a.rank_bytes, i * 16);
         first_pass_end = min(v1, v0 + bs);
       } else {
         ++misspec;
@@ -460,7 +482,7 @@ __global__ void __launch_bounds__(64) snac_chain_kernel(SnacArgs a) {
 #pragma unroll
       for (int u = 0; u < CU; ++u) {
         const int64_t i = i0 + static_cast<int64_t>(u) * bs;
-        if (i < v1) reduce_pass<R, BF16>(v[u], dst_base + i * 16);
+        if (i < v1) reduce_pass<R, BF16>(v[u], dst_base, a.rank_bytes, i * 16);
       }
     }
 
@@ -628,7 +650,8 @@ __global__ void __launch_bounds__(64) lamport_chain_kernel(SnacArgs a) {
           uint4 v[R];
 #pragma unroll
           for (int q = 0; q < R; ++q) v[q] = untag(lo[u][q], hi[u][q]);
-          reduce_pass<R, BF16>(v, dst + i * 16);
+          // No fences here, so the output keeps plain stores.
+          *reinterpret_cast<uint4 *>(dst + i * 16) = BF16 ? fold_bf16x8<R>(v) : fold_f32x4<R>(v);
         }
       }
     }
@@ -697,7 +720,9 @@ __device__ bool wait_all_n(const uint32_t *base, int n, uint32_t want, uint32_t 
 }
 
 // Piece s of every entry of rank r: staged data read with device-coherent
-// loads, results stored to rank r's output of this epoch.
+// loads, results stored to rank r's output of this epoch.  Plan chains keep
+// plain stores: write-through stores, in any mix of stage and consume, sped
+// some collectives up and slowed others (All-Gather and Gather by 13-16%).
 template <int R, bool BF16>
 __device__ void plan_consume(const PlanChainArgs &a, int r, int s,
                              const unsigned char *stage_base, unsigned char *dst) {
@@ -726,7 +751,7 @@ __device__ void plan_consume(const PlanChainArgs &a, int r, int s,
 #pragma unroll
         for (int u = 0; u < CU; ++u) {
           const int64_t i = i0 + static_cast<int64_t>(u) * bs;
-          if (i < hi) reduce_pass<R, BF16>(v[u], dst + (e.dst_off + i) * 16);
+          if (i < hi) reduce_pass<R, BF16, false>(v[u], dst, a.out_stride, (e.dst_off + i) * 16);
         }
       }
     } else {
@@ -859,7 +884,7 @@ PlanChainFn snac_plan_for(int R) {
 // Single-wave workgroups per rank: the caller's count, or chosen from the
 // payload's vectors.  Each wave's own release / acquire covers exactly its
 // own accesses.
-int32_t default_slices(int32_t slices, int64_t nvec, int32_t nranks, uint32_t flags) {
+int32_t default_slices(int32_t slices, int64_t nvec, int32_t nranks, uint32_t flags, bool plan) {
   int32_t S = slices;
   if (S == 0) {
     if (flags & RRB_SNAC_LAMPORT) {
@@ -874,14 +899,26 @@ int32_t default_slices(int32_t slices, int64_t nvec, int32_t nranks, uint32_t fl
       } else {
         S = 128;
       }
-    } else if (nvec <= 4096) {
-      // Measured on MI355X (8 ranks): decode payloads up to 64 KiB per rank
-      // are fastest with 8 workgroups per rank (each workgroup's agent-scope
-      // fences serialise, so more of them cost more than they parallelise);
-      // larger payloads with about 1024 vectors per workgroup, up to 32.
-      S = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(8, nvec / 64)));
     } else {
-      S = static_cast<int32_t>(std::min<int64_t>(32, std::max<int64_t>(8, nvec / 1024)));
+      // Each workgroup's agent-scope fences serialise, so more workgroups cost
+      // more than they parallelise.  Measured on MI355X, 8 ranks:
+      // - below 32 KiB, at least 64 vectors per workgroup, up to 8;
+      // - barrier, dual and speculative All-Reduce chains (write-through
+      //   stores): 16 per rank from 32 KiB, 32 from 256 KiB.  Dual buffer, us
+      //   per All-Reduce by slices per rank (8 / 16 / 32): 32 KiB 4.69 /
+      //   3.49 / 4.72, 64 KiB 5.68 / 5.39 / 5.77, 128 KiB 9.70 / 6.51 /
+      //   7.86, 256 KiB - / 10.76 / 8.84, 512 KiB 36.0 / 20.5 / 16.2,
+      //   1 MiB - / 38.2 / 24.6; 64 per rank cost more at every size;
+      // - twoshot and plan chains (every plan-chain workgroup waits for all
+      //   R x S flags): up to 8 to 64 KiB, then about 1024 vectors per
+      //   workgroup, up to 32.
+      const bool ar_flags = !plan && !(flags & RRB_SNAC_TWOSHOT);
+      if (ar_flags ? nvec < 2048 : nvec <= 4096)
+        S = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(8, nvec / 64)));
+      else if (ar_flags)
+        S = nvec < 16384 ? 16 : 32;
+      else
+        S = static_cast<int32_t>(std::min<int64_t>(32, std::max<int64_t>(8, nvec / 1024)));
     }
     S = std::min<int32_t>(S, 2048 / nranks);
   }
@@ -1139,7 +1176,7 @@ rrb_status rrb_snac_create(int32_t nranks, int64_t count, int32_t dtype, uint32_
   if (slices < 0 || slices > kMaxSlices)
     return fail(RRB_EINVAL, "slices %d outside 0..%d", slices, kMaxSlices);
   const int64_t nvec = count * esz / 16;
-  const int32_t S = default_slices(slices, nvec, nranks, flags);
+  const int32_t S = default_slices(slices, nvec, nranks, flags, false);
   rrb_snac_s *h = new (std::nothrow) rrb_snac_s;
   if (!h) return fail(RRB_ENOMEM, "handle allocation failed");
   h->R = nranks;
@@ -1233,7 +1270,7 @@ rrb_status rrb_snac_create_plan(rrb_plan_t plan, uint32_t flags, int32_t slices,
   h->count = p.count;
   h->dtype = p.dtype;
   h->flags = flags;
-  h->S = default_slices(slices, nvec, R, flags);
+  h->S = default_slices(slices, nvec, R, flags, true);
   h->bs = 64;
   h->in_stride = in_stride;
   h->out_stride = out_stride;

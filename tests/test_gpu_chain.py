@@ -73,7 +73,10 @@ def _slices_of(ch):
     if ch.variant == "lamport":
         S = max(1, nvec // 64) if nvec < 4096 else min(256, nvec // 32) if nvec <= 16384 else 128
     else:
-        S = max(1, min(8, nvec // 64)) if nvec <= 4096 else min(32, max(8, nvec // 1024))
+        if ch.variant == "twoshot":
+            S = max(1, min(8, nvec // 64)) if nvec <= 4096 else min(32, max(8, nvec // 1024))
+        else:
+            S = max(1, min(8, nvec // 64)) if nvec < 2048 else 16 if nvec < 16384 else 32
     return min(S, 2048 // R, nvec)
 
 
