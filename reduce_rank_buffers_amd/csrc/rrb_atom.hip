@@ -282,6 +282,18 @@ struct OneArgs {
 
 constexpr int kOneBlock = 64;
 
+// 16-byte store at byte `off` of a `bytes`-long buffer with the cache policy
+// of agent-scope atomic stores (sc1, through a buffer store): written through
+// rather than left dirty in this XCD's L2, so less is left to write back when
+// the kernel completes.  Measured on MI355X: the 8 x 8 KiB All-Reduce
+// replayed from a HIP graph, 1.858 -> 1.793 us per launch (plain and
+// non-temporal stores were level), against 1.65 us for an empty kernel.
+__device__ __forceinline__ void st16_wt(unsigned char *base, int32_t bytes, int32_t off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(
+      v4u{v.x, v.y, v.z, v.w},
+      __builtin_amdgcn_make_buffer_rsrc(base, static_cast<short>(0), bytes, 0x00020000), off, 0, 16);
+}
+
 // The lane index is clamped instead of branched on, and the first store is
 // unconditional, so the compiler issues every source load as soon as the
 // kernel arguments arrive (one scalar round trip instead of three).  Lanes
@@ -296,12 +308,13 @@ __device__ __forceinline__ void reduce_one_body(const OneArgs &a) {
 #pragma unroll
   for (int r = 0; r < R; ++r) v[r] = *reinterpret_cast<const uint4 *>(a.in[r] + static_cast<int64_t>(i) * 16);
   const uint4 res = fold_vec<R, BF16, TREE>(v);
+  const int32_t vb = a.nvec * 16;  // at most kOneMaxVectors vectors
   if (ALL) {
 #pragma unroll
-    for (int q = 0; q < R; ++q) *reinterpret_cast<uint4 *>(a.out[q] + static_cast<int64_t>(i) * 16) = res;
+    for (int q = 0; q < R; ++q) st16_wt(a.out[q], vb, i * 16, res);
   } else {
-    *reinterpret_cast<uint4 *>(a.out[0] + static_cast<int64_t>(i) * 16) = res;
-    for (int q = 1; q < a.ndst; ++q) *reinterpret_cast<uint4 *>(a.out[q] + static_cast<int64_t>(i) * 16) = res;
+    st16_wt(a.out[0], vb, i * 16, res);
+    for (int q = 1; q < a.ndst; ++q) st16_wt(a.out[q], vb, i * 16, res);
   }
   if (a.tail && blockIdx.x == gridDim.x - 1 && static_cast<int>(threadIdx.x) < a.tail) {
     const int64_t e = static_cast<int64_t>(a.nvec) * (BF16 ? 8 : 4) + threadIdx.x;
@@ -341,8 +354,9 @@ __global__ void __launch_bounds__(kOneBlock) copy_one_kernel(OneArgs a) {
   const int i = min(static_cast<int>(blockIdx.x) * kOneBlock + static_cast<int>(threadIdx.x),
                     a.nvec - 1);
   const uint4 x = *reinterpret_cast<const uint4 *>(a.in[0] + static_cast<int64_t>(i) * 16);
-  *reinterpret_cast<uint4 *>(a.out[0] + static_cast<int64_t>(i) * 16) = x;
-  for (int q = 1; q < a.ndst; ++q) *reinterpret_cast<uint4 *>(a.out[q] + static_cast<int64_t>(i) * 16) = x;
+  const int32_t vb = a.nvec * 16;
+  st16_wt(a.out[0], vb, i * 16, x);
+  for (int q = 1; q < a.ndst; ++q) st16_wt(a.out[q], vb, i * 16, x);
   if (a.tail && blockIdx.x == gridDim.x - 1 && static_cast<int>(threadIdx.x) < a.tail) {
     const int64_t off = static_cast<int64_t>(a.nvec) * 16 + threadIdx.x * 2;
     const uint16_t y = *reinterpret_cast<const uint16_t *>(a.in[0] + off);
