@@ -159,7 +159,9 @@ rrb_status rrb_plan_create(const rrb_spec *spec, rrb_plan_t *out);
  *     step (no fused multiply-add) (in = expert outputs in the dispatch
  *     layout, out = token shards).
  * The maps are uploaded by rrb_plan_bind into caller-owned workspace.
- * Errors: RRB_EINVAL (shapes, indices out of range, repeated expert in a row).
+ * Errors: RRB_EINVAL (shapes, indices out of range, repeated expert in a row);
+ * RRB_EUNSUPPORTED for rows of 2 GiB or more (hidden >= 2^30) or
+ * tokens*topk >= 2^26.
  */
 #define RRB_MOE_DISPATCH 0
 #define RRB_MOE_COMBINE 1
@@ -176,7 +178,7 @@ rrb_status rrb_plan_create_rows(int32_t nranks, int64_t tokens, int64_t hidden,
  * ascending within an expert) start at arena row rank_offsets[r] -- passed as
  * pointer 0 of the receive-side array (dispatch: d_out[0]; combine: d_in[0];
  * other ranks' entries are unused).  Limits: experts <= 1024, topk <= 16,
- * tokens*topk < 2^26 (RRB_EUNSUPPORTED otherwise).  Bind a workspace with
+ * tokens*topk < 2^26, hidden < 2^30 (RRB_EUNSUPPORTED otherwise).  Bind a workspace with
  * rrb_plan_bind (it clears the maps: every slot is arena row 0 until routed);
  * a dispatch and a combine plan of the same shape may share one workspace.
  */

@@ -114,8 +114,10 @@ __device__ __forceinline__ v4u combine_vec(const v4u (&z)[K], const float (&w)[K
 }
 
 // One workgroup per part of a token row: CU vectors x K rows in flight per
-// lane (K * CU >= 8), non-temporal loads and stores (every expert row is read
-// once and the combined row is not read again here).  Parts of 128 * CU
+// lane (K * CU >= 8), non-temporal loads (every expert row is read once) and
+// write-through stores (the cache policy of agent-scope atomic stores, sc1):
+// 88.2 us against 90.6 non-temporal and 94.2 plain, 4096 x 7168, top-8,
+// interleaved A/B on MI355X.  Parts of 128 * CU
 // vectors: for a 7168-wide row and top-8, 7 parts of 128 lanes ran 3-4% ahead
 // of one 256-lane workgroup with 4 vectors per lane (interleaved A/B runs).
 template <int K, int CU>
@@ -151,7 +153,11 @@ __global__ void __launch_bounds__(128) moe_combine_kernel(RowArgs a) {
     for (int u = 0; u < CU; ++u) {
       const int64_t i = i0 + static_cast<int64_t>(u) * bs;
       if (i < v1)
-        __builtin_nontemporal_store(combine_vec<K>(z[u], w), reinterpret_cast<v4u *>(dst + i * 16));
+        __builtin_amdgcn_raw_buffer_store_b128(
+            combine_vec<K>(z[u], w),
+            __builtin_amdgcn_make_buffer_rsrc(dst, static_cast<short>(0), static_cast<int>(a.row_bytes),
+                                              0x00020000),
+            static_cast<int32_t>(i * 16), 0, 16);
     }
   }
 }

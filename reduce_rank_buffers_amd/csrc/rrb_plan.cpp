@@ -182,6 +182,7 @@ rrb_status build_row_plan(int32_t R, int64_t T, int64_t h, int32_t E, int32_t k,
   if (T < 0 || h <= 0 || E < 1 || k < 1 || k > E)
     return fail(RRB_EINVAL, "bad MoE shape: tokens %lld hidden %lld experts %d topk %d",
                 (long long)T, (long long)h, E, k);
+  if (h >= (int64_t(1) << 30)) return fail(RRB_EUNSUPPORTED, "token rows of 2 GiB or more");
   if (T % R != 0) return fail(RRB_EINVAL, "tokens must divide evenly over the ranks");
   if (E % R != 0) return fail(RRB_EINVAL, "experts must divide evenly over the ranks");
   if (dir != RRB_MOE_DISPATCH && dir != RRB_MOE_COMBINE)
@@ -267,6 +268,7 @@ rrb_status build_row_plan_device(int32_t R, int64_t T, int64_t h, int32_t E, int
   if (T < 0 || h <= 0 || E < 1 || k < 1 || k > E)
     return fail(RRB_EINVAL, "bad MoE shape: tokens %lld hidden %lld experts %d topk %d",
                 (long long)T, (long long)h, E, k);
+  if (h >= (int64_t(1) << 30)) return fail(RRB_EUNSUPPORTED, "token rows of 2 GiB or more");
   if (T % R != 0) return fail(RRB_EINVAL, "tokens must divide evenly over the ranks");
   if (E % R != 0) return fail(RRB_EINVAL, "experts must divide evenly over the ranks");
   if (dir != RRB_MOE_DISPATCH && dir != RRB_MOE_COMBINE)

@@ -193,6 +193,18 @@ def test_row_plan_sizes_match_oracle(librrb, T, E, k, R):
         lib.rrb_plan_destroy(hdl)
 
 
+def test_row_plans_reject_rows_of_2_gib(librrb):
+    import ctypes
+    lib = librrb
+    h = 1 << 30  # 2 GiB of bf16 per row
+    idx = np.zeros((8, 1), dtype=np.int32)
+    hdl = ctypes.c_void_p()
+    assert lib.rrb_plan_create_rows(8, 8, h, 8, 1, idx.ctypes.data, None, 0,
+                                    ctypes.byref(hdl)) == L.RRB_EUNSUPPORTED
+    assert b"2 GiB" in lib.rrb_last_error()
+    assert lib.rrb_plan_create_rows_device(8, 8, h, 8, 1, 1, ctypes.byref(hdl)) == L.RRB_EUNSUPPORTED
+
+
 def test_row_plan_rejects_bad_routing(librrb):
     import ctypes
     lib = L.lib()
