@@ -499,6 +499,20 @@ ReduceFn reduce_vec_for(int R) {
   return nullptr;
 }
 
+// The vector reduce for U vectors per lane and the element type.
+template <bool NTL, bool NTS>
+ReduceFn reduce_vec_pick(int U, bool bf16, int R) {
+  if (U == 4) return bf16 ? reduce_vec_for<4, true, NTL, NTS>(R) : reduce_vec_for<4, false, NTL, NTS>(R);
+  if (U == 2) return bf16 ? reduce_vec_for<2, true, NTL, NTS>(R) : reduce_vec_for<2, false, NTL, NTS>(R);
+  return bf16 ? reduce_vec_for<1, true, NTL, NTS>(R) : reduce_vec_for<1, false, NTL, NTS>(R);
+}
+
+ReduceFn reduce_wt_pick(int U, bool bf16, int R) {
+  if (U == 4) return bf16 ? reduce_wt_for<4, true>(R) : reduce_wt_for<4, false>(R);
+  if (U == 2) return bf16 ? reduce_wt_for<2, true>(R) : reduce_wt_for<2, false>(R);
+  return bf16 ? reduce_wt_for<1, true>(R) : reduce_wt_for<1, false>(R);
+}
+
 // When a launch streams past the caches (non-temporal hints).  A reduce
 // streams from 64 MiB of traffic (one read and one write per element per
 // rank), measured on the bandwidth sweep on MI355X.  A copy streams when the
@@ -648,10 +662,11 @@ rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out
   if (vec) {
     a.nvec = (len * esz) / 16;
     a.tail = reduce ? (len - a.nvec * (16 / esz)) : ((len * esz - a.nvec * 16) / 2);
-    // Decode-size items spread over more, smaller workgroups.  Streams too
-    // large to live in the Infinity Cache take non-temporal hints: loads and
-    // stores for a fan-out reduce, loads only for a single-destination reduce,
-    // stores for a copy (measured best on MI355X for each shape).
+    // Decode-size items spread over more, smaller workgroups.  Streaming
+    // launches (kStreamBytesReduce, kStreamOutCopy) take non-temporal hints:
+    // loads and stores for a fan-out reduce, loads with write-through stores
+    // for a single-destination reduce, stores for a copy; copies that do not
+    // stream store write-through (measured best on MI355X for each shape).
     const bool small = a.nvec <= 4096;
     const int64_t traffic = static_cast<int64_t>(p.segs.size()) * len * esz *
                             (reduce ? p.nranks : 1) * 2;
@@ -674,30 +689,14 @@ rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out
                       : (bf16 ? reduce_tree_vec_for<true, false, false>(p.nranks)
                               : reduce_tree_vec_for<false, false, false>(p.nranks));
       } else if (stream && !fan) {
-        kern = U == 1 ? (bf16 ? reduce_wt_for<1, true>(p.nranks) : reduce_wt_for<1, false>(p.nranks))
-             : U == 2 ? (bf16 ? reduce_wt_for<2, true>(p.nranks) : reduce_wt_for<2, false>(p.nranks))
-                      : (bf16 ? reduce_wt_for<4, true>(p.nranks) : reduce_wt_for<4, false>(p.nranks));
-      } else if (U == 1) {
-        kern = stream ? (fan ? (bf16 ? reduce_vec_for<1, true, true, true>(p.nranks)
-                                     : reduce_vec_for<1, false, true, true>(p.nranks))
-                             : (bf16 ? reduce_vec_for<1, true, true, false>(p.nranks)
-                                     : reduce_vec_for<1, false, true, false>(p.nranks)))
-                      : (bf16 ? reduce_vec_for<1, true, false, false>(p.nranks)
-                              : reduce_vec_for<1, false, false, false>(p.nranks));
-      } else if (U == 4) {
-        kern = stream ? (fan ? (bf16 ? reduce_vec_for<4, true, true, true>(p.nranks)
-                                     : reduce_vec_for<4, false, true, true>(p.nranks))
-                             : (bf16 ? reduce_vec_for<4, true, true, false>(p.nranks)
-                                     : reduce_vec_for<4, false, true, false>(p.nranks)))
-                      : (bf16 ? reduce_vec_for<4, true, false, false>(p.nranks)
-                              : reduce_vec_for<4, false, false, false>(p.nranks));
+        kern = reduce_wt_pick(U, bf16, p.nranks);
+      } else if (stream) {
+        kern = reduce_vec_pick<true, true>(U, bf16, p.nranks);
       } else {
-        kern = stream ? (fan ? (bf16 ? reduce_vec_for<2, true, true, true>(p.nranks)
-                                     : reduce_vec_for<2, false, true, true>(p.nranks))
-                             : (bf16 ? reduce_vec_for<2, true, true, false>(p.nranks)
-                                     : reduce_vec_for<2, false, true, false>(p.nranks)))
-                      : (bf16 ? reduce_vec_for<2, true, false, false>(p.nranks)
-                              : reduce_vec_for<2, false, false, false>(p.nranks));
+        // Below the streaming threshold a launch has under 2 M vectors, so
+        // one vector per lane.
+        kern = bf16 ? reduce_vec_for<1, true, false, false>(p.nranks)
+                    : reduce_vec_for<1, false, false, false>(p.nranks);
       }
     } else {
       // Streaming copies: one vector per lane on 128-lane workgroups (the
