@@ -201,6 +201,23 @@ def test_special_values_and_denormals():
     _run_and_check("reduce_scatter", ins, "bf16")
 
 
+@pytest.mark.parametrize("R,n,dtype", [(3, (1 << 24) + 7, "bf16"), (5, (1 << 24) + 1, "bf16"),
+                                       (5, (1 << 23) + 2, "f32"), (16, 1 << 20, "bf16"),
+                                       (16, (1 << 20) + 5, "f32")])
+def test_streaming_reduces_other_rank_counts(R, n, dtype):
+    """Streaming launches at rank counts other than 8, full compare: the
+    unrolled All-Reduce (non-temporal stores) and Reduce to a root
+    (write-through stores) at 2M+ vectors with ragged tails, and at 16 ranks
+    (one vector per lane) also the Reduce-Scatter."""
+    require_gpu()
+    _say(f"streaming reduces R={R} n={n} {dtype}")
+    ins = inputs.rank_payloads(n, R, dtype, 1.0, inputs.WL_LARGE, 20 + R)
+    _run_and_check("all_reduce", ins, dtype)
+    _run_and_check("reduce", ins, dtype, R - 1)
+    if n % R == 0:
+        _run_and_check("reduce_scatter", ins, dtype)
+
+
 @pytest.mark.parametrize("R", [4, 8])
 @pytest.mark.parametrize("n", [37, 4096, 8 * 8192])
 def test_fixed_rank_order_on_cancellation(R, n):
