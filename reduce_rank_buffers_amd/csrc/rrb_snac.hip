@@ -98,7 +98,7 @@ struct SnacArgs {
 };
 
 struct Layout {
-  int64_t staging_off, entries_off, reduced_off, flag_off, flag2_off, done_off, tagged_off,
+  int64_t staging_off, entries_off, waits_off = 0, reduced_off, flag_off, flag2_off, done_off, tagged_off,
       status_off, total;
 };
 
@@ -136,14 +136,17 @@ struct PlanEntry {
   int32_t src_rank, pad;
 };
 
-// staging [2][R][in_stride] | entries | flags [2][R][S] | done [R][S] | status;
-// the entries are uploaded at bind, everything from flag_off on is cleared.
-Layout layout_for_plan(int32_t R, int64_t in_stride, int32_t S, int64_t nentries) {
+// staging [2][R][in_stride] | entries | wait lists | flags [2][R][S] |
+// done [R][S] | status; the entries and wait lists are uploaded at bind,
+// everything from flag_off on is cleared.
+Layout layout_for_plan(int32_t R, int64_t in_stride, int32_t S, int64_t nentries,
+                       int64_t nwait_words) {
   auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
   Layout l;
   l.staging_off = 0;
   l.entries_off = up(2LL * R * in_stride);
-  l.reduced_off = l.entries_off + up(nentries * static_cast<int64_t>(sizeof(PlanEntry)));
+  l.waits_off = l.entries_off + up(nentries * static_cast<int64_t>(sizeof(PlanEntry)));
+  l.reduced_off = l.waits_off + up(nwait_words * 4);
   l.flag_off = l.reduced_off;
   const int64_t flags = up(2LL * R * S * kFlagStride * 4);
   l.flag2_off = l.flag_off + flags;
@@ -678,13 +681,15 @@ __global__ void __launch_bounds__(64) lamport_chain_kernel(SnacArgs a) {
 // Workgroup (r, s) stages slice s of rank r's input, publishes
 // flag[buf][r][s] = epoch, then computes piece s of every map entry whose
 // output is rank r (a copy from one staged rank, or a rank-order fold over
-// all of them).  A piece can read any staged slice of its sources, so the top
-// barrier waits for every rank's every slice: with two buffers that also
+// all of them).  Its top barrier waits for the flags on its wait list (built
+// at plan time, build_wait_lists): the slices its pieces read, and the
+// workgroups whose pieces read its own slice -- with two buffers the latter
 // proves that every reader of this workgroup's slice finished the previous
 // epoch on this buffer, the write-after-read guard of dual buffering.
-// Speculation reads all flags first, then consumes with device-coherent loads
-// and keeps the result only if the flags summed to (R S) epoch; otherwise it
-// waits and consumes again (outputs are only read after the kernel).
+// Speculation reads the listed flags first, then consumes with
+// device-coherent loads and keeps the result only if they summed to
+// (list length) x epoch; otherwise it waits and consumes again (outputs are
+// only read after the kernel).
 
 struct PlanChainArgs {
   const unsigned char *in;   // [E][R][in_stride bytes]
@@ -696,6 +701,11 @@ struct PlanChainArgs {
   rrb_snac_stats *stats;
   const uint32_t *stagger;
   const PlanEntry *entries;  // rank r's entries at [first[r], first[r] + cnt[r])
+  // Workgroup w waits on the flags wait_idx[wait_off[w] .. wait_off[w + 1]),
+  // each a flag index r * S + s: the slices its consume reads and the
+  // workgroups that read its own slice.
+  const int32_t *wait_off;
+  const int32_t *wait_idx;
   int64_t in_stride, out_stride;
   int64_t slice_vec;         // staging slice length in vectors
   int64_t in_vec[RRB_MAX_RANKS];
@@ -706,14 +716,14 @@ struct PlanChainArgs {
   uint32_t spin_limit;
 };
 
-// Every lane waits for its share of the n flags at base + i * kFlagStride;
+// Every lane waits for its share of the n flags base + idx[i] * kFlagStride;
 // then the (single-wave) workgroup takes one agent-scope acquire.  True in
 // every lane if all n waits succeeded.
-__device__ bool wait_all_n(const uint32_t *base, int n, uint32_t want, uint32_t *status,
-                           uint32_t limit) {
+__device__ bool wait_list(const uint32_t *base, const int32_t *idx, int n, uint32_t want,
+                          uint32_t *status, uint32_t limit) {
   bool ok = true;
   for (int i = threadIdx.x; i < n && ok; i += blockDim.x)
-    ok = wait_at_least(base + static_cast<int64_t>(i) * kFlagStride, want, status, limit);
+    ok = wait_at_least(base + static_cast<int64_t>(idx[i]) * kFlagStride, want, status, limit);
   const bool all = __all(ok) != 0;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   return all;
@@ -779,16 +789,18 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
   const int r = blockIdx.x / a.S;
   const int s = blockIdx.x - r * a.S;
   const int bs = blockDim.x;
-  const int nflags = R * a.S;
   const int64_t v0 = static_cast<int64_t>(s) * a.slice_vec;
   const int64_t v1 = min(a.in_vec[r], v0 + a.slice_vec);
+  const int32_t w0 = a.wait_off[blockIdx.x];
+  const int nw = a.wait_off[blockIdx.x + 1] - w0;
+  const int32_t *wl = a.wait_idx + w0;
   unsigned long long misspec = 0, retries = 0, timeouts = 0, done_epochs = 0;
 
   for (int k = 0; k < a.epochs; ++k) {
     const uint32_t ep = a.epoch0 + static_cast<uint32_t>(k);
     const int b = VAR == kBarrier ? 0 : static_cast<int>(ep & 1u);
     unsigned char *stage_base = a.staging + static_cast<int64_t>(b) * R * a.in_stride;
-    uint32_t *flags_b = a.flag + static_cast<int64_t>(b) * nflags * kFlagStride;
+    uint32_t *flags_b = a.flag + static_cast<int64_t>(b) * R * a.S * kFlagStride;
 
     // Test hook: a late rank.
     if (a.stagger) {
@@ -821,8 +833,8 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
     if (VAR == kSpeculative) {
       // Flags first (relaxed, no wait), the whole consume right after.
       uint32_t sum = 0;
-      for (int i = threadIdx.x; i < nflags; i += bs)
-        sum += load_flag_relaxed(flags_b + static_cast<int64_t>(i) * kFlagStride);
+      for (int i = threadIdx.x; i < nw; i += bs)
+        sum += load_flag_relaxed(flags_b + static_cast<int64_t>(wl[i]) * kFlagStride);
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("" ::: "memory");
       plan_consume<R, BF16>(a, r, s, stage_base, dst);
@@ -830,16 +842,16 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
       for (int m = 1; m < 64; m <<= 1) sum += __shfl_xor(sum, m);
       // Each flag is epoch or epoch - 2, so the sum is exact (no wrap-around
       // false match: 2 x the stale count stays below 2^32).
-      if (sum == static_cast<uint32_t>(nflags) * ep) {
+      if (sum == static_cast<uint32_t>(nw) * ep) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       } else {
         ++misspec;
         ++retries;
-        ok = wait_all_n(flags_b, nflags, ep, a.status, a.spin_limit);
+        ok = wait_list(flags_b, wl, nw, ep, a.status, a.spin_limit);
         if (ok) plan_consume<R, BF16>(a, r, s, stage_base, dst);
       }
     } else {
-      ok = wait_all_n(flags_b, nflags, ep, a.status, a.spin_limit);
+      ok = wait_list(flags_b, wl, nw, ep, a.status, a.spin_limit);
       if (ok) plan_consume<R, BF16>(a, r, s, stage_base, dst);
     }
     if (!ok) {
@@ -847,9 +859,9 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
       break;
     }
     if (VAR == kBarrier) {
-      // Bottom barrier: every reader of every staged slice is done.
+      // Bottom barrier: every reader of this workgroup's slice is done.
       notify(a.done + (static_cast<int64_t>(r) * a.S + s) * kFlagStride, ep);
-      if (!wait_all_n(a.done, nflags, ep, a.status, a.spin_limit)) {
+      if (!wait_list(a.done, wl, nw, ep, a.status, a.spin_limit)) {
         ++timeouts;
         break;
       }
@@ -969,6 +981,9 @@ struct rrb_snac_s {
   // Chains of a plan (rrb_snac_create_plan): the consume entries per rank.
   bool from_plan = false;
   std::vector<rrb::PlanEntry> entries;
+  // Per workgroup wait lists: R*S + 1 offsets, then the flag indices.
+  std::vector<int32_t> wait_tab;
+  int64_t slice_vec = 0;  // staging slice length in vectors
   int64_t in_vec[RRB_MAX_RANKS] = {};
   int32_t first[RRB_MAX_RANKS] = {}, cnt[RRB_MAX_RANKS] = {};
   // Co-resident capacity (workgroups) of the last persistent kernel launched.
@@ -999,6 +1014,55 @@ struct rrb_snac_s {
 
 namespace rrb {
 namespace {
+
+// Wait lists of a plan chain.  Workgroup w = r * S + s consumes piece s of
+// each of rank r's entries (the same piece bounds as plan_consume); reads(w)
+// is the set of staging slices (q, s') those pieces touch.  w waits for
+// reads(w) (its data is staged) and for every workgroup whose reads include
+// w's own slice (they finished the previous epoch on this buffer before w
+// stages over it).  The relation is symmetric, so no workgroup on w's list
+// gets two epochs ahead of w, and with two buffers every flag w reads holds
+// epoch or epoch - 2: the speculative sum check stays exact.
+void build_wait_lists(rrb_snac_s &h) {
+  const int R = h.R, S = h.S;
+  const int W = R * S;
+  std::vector<std::vector<int32_t>> lists(W);
+  for (int r = 0; r < R; ++r) {
+    for (int s = 0; s < S; ++s) {
+      std::vector<int32_t> &l = lists[r * S + s];
+      for (int g = h.first[r]; g < h.first[r] + h.cnt[r]; ++g) {
+        const PlanEntry &e = h.entries[g];
+        const int64_t pl = (e.len + S - 1) / S;
+        const int64_t lo = std::min(e.len, static_cast<int64_t>(s) * pl);
+        const int64_t hi = std::min(e.len, lo + pl);
+        if (lo >= hi) continue;
+        const int64_t s0 = (e.src_off + lo) / h.slice_vec;
+        const int64_t s1 = (e.src_off + hi - 1) / h.slice_vec;
+        for (int q = 0; q < R; ++q) {
+          if (e.src_rank >= 0 && q != e.src_rank) continue;
+          for (int64_t sp = s0; sp <= s1 && sp < S; ++sp) l.push_back(q * S + static_cast<int32_t>(sp));
+        }
+      }
+      std::sort(l.begin(), l.end());
+      l.erase(std::unique(l.begin(), l.end()), l.end());
+    }
+  }
+  // Add the readers of each slice to that slice's own list.
+  std::vector<std::vector<int32_t>> readers(W);
+  for (int w = 0; w < W; ++w)
+    for (int32_t f : lists[w]) readers[f].push_back(w);
+  h.wait_tab.assign(1, 0);
+  std::vector<int32_t> all;
+  for (int w = 0; w < W; ++w) {
+    std::vector<int32_t> m = lists[w];
+    m.insert(m.end(), readers[w].begin(), readers[w].end());
+    std::sort(m.begin(), m.end());
+    m.erase(std::unique(m.begin(), m.end()), m.end());
+    all.insert(all.end(), m.begin(), m.end());
+    h.wait_tab.push_back(static_cast<int32_t>(all.size()));
+  }
+  h.wait_tab.insert(h.wait_tab.end(), all.begin(), all.end());
+}
 
 // Builds the chain's graph: epoch e's All-Reduce reads in[e][0..R-1] and
 // writes out[e][0..R-1]; each epoch's kernels depend on the previous ones,
@@ -1104,16 +1168,16 @@ rrb_status launch_plan_chain(rrb_snac_s *h, int32_t epochs, const void *d_in, vo
   a.stats = d_stats;
   a.stagger = d_stagger;
   a.entries = reinterpret_cast<const PlanEntry *>(h->ws + h->lay.entries_off);
+  a.wait_off = reinterpret_cast<const int32_t *>(h->ws + h->lay.waits_off);
+  a.wait_idx = a.wait_off + (static_cast<int64_t>(h->R) * h->S + 1);
   a.in_stride = h->in_stride;
   a.out_stride = h->out_stride;
-  int64_t in_vec_max = 0;
   for (int r = 0; r < h->R; ++r) {
     a.in_vec[r] = h->in_vec[r];
     a.first[r] = h->first[r];
     a.cnt[r] = h->cnt[r];
-    in_vec_max = std::max(in_vec_max, h->in_vec[r]);
   }
-  a.slice_vec = (in_vec_max + h->S - 1) / h->S;
+  a.slice_vec = h->slice_vec;
   a.epoch0 = h->next_epoch;
   a.epochs = epochs;
   a.S = h->S;
@@ -1275,7 +1339,17 @@ rrb_status rrb_snac_create_plan(rrb_plan_t plan, uint32_t flags, int32_t slices,
   h->in_stride = in_stride;
   h->out_stride = out_stride;
   h->from_plan = true;
-  h->lay = layout_for_plan(R, in_stride, h->S, static_cast<int64_t>(h->entries.size()));
+  int64_t in_vec_max = 0;
+  for (int r = 0; r < R; ++r) in_vec_max = std::max(in_vec_max, h->in_vec[r]);
+  h->slice_vec = (in_vec_max + h->S - 1) / h->S;
+  try {
+    build_wait_lists(*h);
+  } catch (const std::bad_alloc &) {
+    delete h;
+    return fail(RRB_ENOMEM, "handle allocation failed");
+  }
+  h->lay = layout_for_plan(R, in_stride, h->S, static_cast<int64_t>(h->entries.size()),
+                           static_cast<int64_t>(h->wait_tab.size()));
   *out = h;
   return RRB_OK;
 }
@@ -1310,6 +1384,9 @@ rrb_status rrb_snac_bind(rrb_snac_t h, void *d_ws, size_t bytes, rrb_stream_t st
     e = hipMemcpyAsync(h->ws + h->lay.entries_off, h->entries.data(),
                        h->entries.size() * sizeof(PlanEntry), hipMemcpyHostToDevice,
                        static_cast<hipStream_t>(stream));
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(h->ws + h->lay.waits_off, h->wait_tab.data(), h->wait_tab.size() * 4,
+                         hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
     if (e == hipSuccess) e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(RRB_EHIP, "entry upload: %s", hipGetErrorString(e));
   }
