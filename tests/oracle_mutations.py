@@ -67,6 +67,28 @@ M = [
      "    return [fold.reduce_tree(list(ins), dtype) for ins in ins_by_epoch]"),
     ("chain epoch shift", "oracle/chain.py", "    return [fold.reduce(list(ins), dtype) for ins in ins_by_epoch]",
      "    return [fold.reduce(list(ins), dtype) for ins in ins_by_epoch[:1]] + [fold.reduce(list(ins), dtype) for ins in ins_by_epoch[:-1]]"),
+    # protocol model
+    ("dual on one buffer", "oracle/protocol.py", "    return 1 if variant in (\"barrier\", \"nobottom\", \"lamport_single\") else 2",
+     "    return 1 if variant in (\"barrier\", \"nobottom\", \"lamport_single\", \"dual\") else 2"),
+    ("barrier without bottom wait", "oracle/protocol.py", "            yield lambda: all(mem.done[s] >= e for s in range(R))",
+     "            pass"),
+    ("top barrier waits on one rank", "oracle/protocol.py",
+     "            yield lambda: all(mem.flag[b][s] >= e for s in range(R))\n            acc = [0] * L\n            for s in range(R):\n                for i in range(L):\n                    acc[i] += mem.staging[b][s][i]\n                    yield None\n        else:",
+     "            yield lambda: mem.flag[b][r] >= e\n            acc = [0] * L\n            for s in range(R):\n                for i in range(L):\n                    acc[i] += mem.staging[b][s][i]\n                    yield None\n        else:"),
+    ("speculation accepts a short sum", "oracle/protocol.py", "            if total != R * e:", "            if total < R * (e - 1):"),
+    ("retry keeps the stale sum", "oracle/protocol.py",
+     "                yield lambda: all(mem.flag[b][s] >= e for s in range(R))\n                acc = [0] * L\n",
+     "                yield lambda: all(mem.flag[b][s] >= e for s in range(R))\n"),
+    ("notify before stage", "oracle/protocol.py",
+     "        for i in range(L):\n            mem.staging[b][r][i] = inputs[e - 1][r][i]\n            yield None\n        # Notify.\n        mem.flag[b][r] = e\n",
+     "        mem.flag[b][r] = e\n        for i in range(L):\n            mem.staging[b][r][i] = inputs[e - 1][r][i]\n            yield None\n        # Notify.\n"),
+    ("lamport tag ignores epoch", "oracle/protocol.py", "        tag = e % tag_mod\n", "        tag = 1\n"),
+    ("lamport on one buffer", "oracle/protocol.py", "    return 1 if variant in (\"barrier\", \"nobottom\", \"lamport_single\") else 2",
+     "    return 1 if variant in (\"barrier\", \"nobottom\", \"lamport_single\", \"lamport\") else 2"),
+    ("expected drops a rank", "oracle/protocol.py", "    return [[sum(col) for col in zip(*ins)] for ins in inputs]",
+     "    return [[sum(col[1:]) for col in zip(*ins)] for ins in inputs]"),
+    ("overtaking not recorded", "oracle/protocol.py", "                    if t is not None and first_read[s] <= t < flag_read[s]:",
+     "                    if t is not None and first_read[s] < t < flag_read[s] - 1:"),
 ]
 
 
