@@ -704,14 +704,21 @@ rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out
       // 64 MiB All-Gather 103 -> 92 us against 256 lanes, 8 ranks).
       // Small fan-out copies keep plain stores: write-through made the
       // 8 x 2 KiB All-Gather of a graph chain 2.5 -> 3.8 us per launch.
-      U = (small || stream || !big) ? 1 : 4;
+      // Single-destination copies below the streaming size (Gather,
+      // All-to-All) take two vectors per lane on 128-lane workgroups:
+      // Gather 8 x 2 MiB 5.61 -> 4.31 us, All-to-All 8 x 4 MiB 9.99 -> 7.72
+      // us per launch (graph replays on MI355X; 8 x 128 KiB Gather 2.15 ->
+      // 2.34, the one loss measured).
       bool fan_any = false;
       for (const Segment &sg : p.segs) fan_any = fan_any || __builtin_popcount(sg.dst_mask) > 1;
+      const bool single = !stream && !small && !fan_any;
+      U = single ? 2 : (small || stream || !big) ? 1 : 4;
       kern = stream             ? copy_vec_kernel<1, true>
              : (small && fan_any) ? copy_vec_kernel<1, false>
              : U == 1             ? copy_wt_kernel<1>
+             : U == 2             ? copy_wt_kernel<2>
                                   : copy_wt_kernel<4>;
-      if (stream) bs = 128;
+      if (stream || single) bs = 128;
     }
     const int64_t per_tile = static_cast<int64_t>(bs) * U;
     int64_t tiles = (a.nvec + per_tile - 1) / per_tile;

@@ -138,6 +138,20 @@ def test_seven_collectives_16mib(name):
     _run_and_check(name, ins, "bf16", ROOTS.get(name))
 
 
+@pytest.mark.parametrize("name,R,c", [("gather", 8, 8 * 5001), ("all_to_all", 8, 8 * 5001),
+                                      ("gather", 3, 8 * 9549), ("all_to_all", 5, 8 * 4097),
+                                      ("gather", 1, 8 * 5001 + 3)])
+def test_single_destination_copies_ragged(name, R, c):
+    """Gather and All-to-All below the streaming size (two vectors per lane on
+    128-lane workgroups) with blocks that are not a whole number of tiles, and
+    one block with an element tail: full compare, sentinels outside the root."""
+    require_gpu()
+    _say(f"single-destination copy {name} R={R} c={c}")
+    m = c if name == "gather" else R * c
+    ins = inputs.rank_payloads(m, R, "bf16", 1.0, inputs.WL_SEVEN, 60 + R)
+    _run_and_check(name, ins, "bf16", 5 % R if name == "gather" else None)
+
+
 @pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 16])
 @pytest.mark.parametrize("n", [0, 1, 7, 8, 37, 8 * 513 + 3, 4096])
 def test_edge_all_reduce(R, n):
