@@ -46,6 +46,23 @@
 // (the same cache policy as agent-scope atomic loads), so a line cached from
 // an earlier epoch is never returned.
 //
+// Memory ordering without fences.  Every byte one workgroup writes for
+// another (staged payloads, the twoshot reduced payload) is stored with the
+// cache policy of agent-scope atomic stores (sc1): written through this XCD's
+// L2 to the device's point of coherence.  notify() waits until all of the
+// wave's memory operations have completed (s_waitcnt 0: the write-through
+// stores acknowledged, the loads returned) before the flag store, and
+// readers load that data, after the flag, with the policy of agent-scope
+// atomic loads (sc1), which never returns a line cached from an earlier
+// epoch.  The agent-scope release and acquire fences that would otherwise
+// bracket each flag write back or invalidate the whole L2 of the XCD; with
+// 8-64 workgroups per XCD taking them every epoch they dominated small
+// payloads.  Measured on MI355X, 8 ranks, 64-epoch chains, per All-Reduce:
+// dual 8 KiB 2.52 -> 2.09 us, barrier 256 KiB 13.7 -> 6.6 us, twoshot 512 KiB
+// 21.0 -> 13.3 us, every result bit-exact (including 100k-epoch stress).  The
+// same completion wait covers the write-after-read guards: a rank's flag of
+// epoch e + 1 is stored only after its epoch-e loads have returned.
+//
 // Every wait is bounded: a wait that exceeds its poll budget raises a status
 // word that every other wait also watches, so the whole grid drains and the
 // host sees RRB_ETIMEOUT.  The grid must be co-resident: it takes a plain
@@ -166,11 +183,11 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 // 16-byte store at byte offset `off` of a `bytes`-long buffer with the cache
 // policy of agent-scope atomic stores (sc1): the line is written through
-// rather than left dirty in this XCD's L2, so the next release fence (an L2
-// write-back) has less to do.  The barrier, dual and speculative All-Reduce
-// chains stage and store outputs through here; the fences stay as they are.
-// Measured on MI355X, 8 ranks, 64-epoch chains: 4-13% less time per
-// All-Reduce from 8 KiB to 2 MiB.
+// rather than left dirty in this XCD's L2.  Every staged payload goes through
+// here, since notify() takes no L2 write-back; the barrier, dual and
+// speculative All-Reduce chains also store their outputs this way (4-13%
+// less time per All-Reduce from 8 KiB to 2 MiB than plain output stores,
+// measured on MI355X when the chains still took fences).
 __device__ __forceinline__ void store_wt(unsigned char *base, int64_t bytes, int64_t off, v4u x) {
   __builtin_amdgcn_raw_buffer_store_b128(x, rsrc(base, bytes), static_cast<int32_t>(off), 0, 16);
 }
@@ -229,19 +246,23 @@ __device__ bool wait_all(const uint32_t *base, int64_t stride_words, uint32_t wa
   if (threadIdx.x < R)
     ok[threadIdx.x] = wait_at_least(base + threadIdx.x * stride_words, want, status, limit) ? 1 : 0;
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // No acquire fence: the data that follows is read with device-coherent
+  // loads, issued after the flags were seen.
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   bool all = true;
 #pragma unroll
   for (int t = 0; t < R; ++t) all = all && ok[t] != 0;
   return all;
 }
 
-// Publishes `ep` in *flag after every wave's earlier stores: each wave
-// releases its own stores at agent scope (write-back of L2 plus a wait for
-// its stores), then thread 0 stores the flag after the workgroup barrier.
-// Chain workgroups are a single wave, so this is one release per workgroup.
+// Publishes `ep` in *flag once every wave's earlier memory operations have
+// completed: each wave waits for its own write-through stores to be
+// acknowledged and its loads to return (s_waitcnt 0; no L2 write-back is
+// needed, nothing the readers need sits dirty in L2), then thread 0 stores
+// the flag after the workgroup barrier.
 __device__ __forceinline__ void notify(uint32_t *flag, uint32_t ep) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __syncthreads();
   if (threadIdx.x == 0) __hip_atomic_store(flag, ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -321,9 +342,9 @@ __device__ bool twoshot_epoch(const SnacArgs &a, int r, int s, int k, uint32_t e
   unsigned char *mine = stage_base + static_cast<int64_t>(r) * a.rank_bytes;
   unsigned char *dst = a.out + (static_cast<int64_t>(k) * R + r) * a.rank_bytes;
 
-  // Stage pieces (q, s) of this rank's payload.  Twoshot keeps plain stores:
-  // write-through stores made it 10-25% slower per All-Reduce (MI355X).
-  copy_pieces<R, false, false>(a, s, src, mine, a.rank_bytes);
+  // Stage pieces (q, s) of this rank's payload, written through for the
+  // readers of other XCDs.
+  copy_pieces<R, false, true>(a, s, src, mine, a.rank_bytes);
   notify(flags_b + r * stride_rs + s * kFlagStride, ep);
   if (!wait_all<R>(flags_b + s * kFlagStride, stride_rs, ep, a.status, a.spin_limit, lds_ok))
     return false;
@@ -349,7 +370,7 @@ __device__ bool twoshot_epoch(const SnacArgs &a, int r, int s, int k, uint32_t e
 #pragma unroll
       for (int u = 0; u < CU; ++u) {
         const int64_t i = i0 + static_cast<int64_t>(u) * bs;
-        if (i < hi) reduce_pass<R, BF16, false>(v[u], red, a.rank_bytes, i * 16);
+        if (i < hi) reduce_pass<R, BF16, true>(v[u], red, a.rank_bytes, i * 16);
       }
     }
   }
@@ -438,8 +459,8 @@ __global__ void __launch_bounds__(64) snac_chain_kernel(SnacArgs a) {
                                static_cast<int32_t>(i * 16));
       }
       // Reduced validation flag: the sum over the R sources must be R * epoch.
-      // Wave 0 holds the flags; a valid result takes the acquire there (it
-      // orders this rank's next stage after every source's earlier reads).
+      // Wave 0 holds the flags.  A valid sum also proves every source's reads
+      // of this buffer two epochs ago had returned before its flag.
       if (threadIdx.x < 64) {
         uint32_t sum = threadIdx.x < R ? f : 0u;
 #pragma unroll
@@ -448,8 +469,6 @@ __global__ void __launch_bounds__(64) snac_chain_kernel(SnacArgs a) {
       }
       __syncthreads();
       const bool valid = lds_valid != 0;
-      // Orders this rank's next stage after every source's earlier reads.
-      if (valid) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       if (valid) {
         if (i < v1) reduce_pass<R, BF16>(v, dst_base, a.rank_bytes, i * 16);
         first_pass_end = min(v1, v0 + bs);
@@ -716,23 +735,22 @@ struct PlanChainArgs {
   uint32_t spin_limit;
 };
 
-// Every lane waits for its share of the n flags base + idx[i] * kFlagStride;
-// then the (single-wave) workgroup takes one agent-scope acquire.  True in
-// every lane if all n waits succeeded.
+// Every lane waits for its share of the n flags base + idx[i] * kFlagStride
+// (no acquire fence: the staged data is read with device-coherent loads after
+// the flags were seen).  True in every lane if all n waits succeeded.
 __device__ bool wait_list(const uint32_t *base, const int32_t *idx, int n, uint32_t want,
                           uint32_t *status, uint32_t limit) {
   bool ok = true;
   for (int i = threadIdx.x; i < n && ok; i += blockDim.x)
     ok = wait_at_least(base + static_cast<int64_t>(idx[i]) * kFlagStride, want, status, limit);
   const bool all = __all(ok) != 0;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   return all;
 }
 
 // Piece s of every entry of rank r: staged data read with device-coherent
-// loads, results stored to rank r's output of this epoch.  Plan chains keep
-// plain stores: write-through stores, in any mix of stage and consume, sped
-// some collectives up and slowed others (All-Gather and Gather by 13-16%).
+// loads, results stored to rank r's output of this epoch with plain stores
+// (only the host reads outputs).
 template <int R, bool BF16>
 __device__ void plan_consume(const PlanChainArgs &a, int r, int s,
                              const unsigned char *stage_base, unsigned char *dst) {
@@ -821,7 +839,7 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
 #pragma unroll
       for (int u = 0; u < kStageU; ++u) {
         const int64_t i = i0 + static_cast<int64_t>(u) * bs;
-        if (i < v1) *reinterpret_cast<v4u *>(mine + i * 16) = x[u];
+        if (i < v1) store_wt(mine, a.in_stride, i * 16, x[u]);
       }
     }
 
@@ -842,9 +860,7 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
       for (int m = 1; m < 64; m <<= 1) sum += __shfl_xor(sum, m);
       // Each flag is epoch or epoch - 2, so the sum is exact (no wrap-around
       // false match: 2 x the stale count stays below 2^32).
-      if (sum == static_cast<uint32_t>(nw) * ep) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      } else {
+      if (sum != static_cast<uint32_t>(nw) * ep) {
         ++misspec;
         ++retries;
         ok = wait_list(flags_b, wl, nw, ep, a.status, a.spin_limit);
@@ -894,8 +910,7 @@ PlanChainFn snac_plan_for(int R) {
 }
 
 // Single-wave workgroups per rank: the caller's count, or chosen from the
-// payload's vectors.  Each wave's own release / acquire covers exactly its
-// own accesses.
+// payload's vectors.
 int32_t default_slices(int32_t slices, int64_t nvec, int32_t nranks, uint32_t flags, bool plan) {
   int32_t S = slices;
   if (S == 0) {
@@ -911,26 +926,33 @@ int32_t default_slices(int32_t slices, int64_t nvec, int32_t nranks, uint32_t fl
       } else {
         S = 128;
       }
+    } else if (!plan && !(flags & RRB_SNAC_TWOSHOT)) {
+      // Barrier, dual and speculative All-Reduce chains: 64 vectors per
+      // workgroup, up to 128 workgroups per rank.  Measured on MI355X, 8
+      // ranks, dual buffer, us per All-Reduce by slices per rank:
+      //   32 KiB   16: 2.71  32: 2.29  64: 2.39
+      //   128 KiB  32: 4.40  64: 3.29  128: 2.84  256: 3.59
+      //   256 KiB  64: 4.99  128: 3.83  256: 3.81
+      //   1 MiB    64: 11.36  128: 8.34  256: 9.86
+      // (barrier and speculative alike; 512 KiB 6.50 / 6.77 / 5.79 at 64 /
+      // 128 / 256).  Before the chains dropped their fences, every extra
+      // workgroup added fence time and 16-32 per rank were best.
+      S = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(128, nvec / 64)));
+    } else if (!plan) {
+      // Twoshot: up to 8 workgroups per rank to 64 KiB, then 512 vectors per
+      // workgroup, up to 128 (us per All-Reduce, 8 ranks: 128 KiB 8.75 at 16,
+      // 256 KiB 8.52 at 32, 512 KiB 9.59 at 64, 1 MiB 10.93 at 128).
+      S = nvec <= 4096
+              ? static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(8, nvec / 64)))
+              : static_cast<int32_t>(std::max<int64_t>(8, std::min<int64_t>(128, nvec / 512)));
     } else {
-      // Each workgroup's agent-scope fences serialise, so more workgroups cost
-      // more than they parallelise.  Measured on MI355X, 8 ranks:
-      // - below 32 KiB, at least 64 vectors per workgroup, up to 8;
-      // - barrier, dual and speculative All-Reduce chains (write-through
-      //   stores): 16 per rank from 32 KiB, 32 from 256 KiB.  Dual buffer, us
-      //   per All-Reduce by slices per rank (8 / 16 / 32): 32 KiB 4.69 /
-      //   3.49 / 4.72, 64 KiB 5.68 / 5.39 / 5.77, 128 KiB 9.70 / 6.51 /
-      //   7.86, 256 KiB - / 10.76 / 8.84, 512 KiB 36.0 / 20.5 / 16.2,
-      //   1 MiB - / 38.2 / 24.6; 64 per rank cost more at every size;
-      // - twoshot and plan chains (every plan-chain workgroup waits for all
-      //   R x S flags): up to 8 to 64 KiB, then about 1024 vectors per
-      //   workgroup, up to 32.
-      const bool ar_flags = !plan && !(flags & RRB_SNAC_TWOSHOT);
-      if (ar_flags ? nvec < 2048 : nvec <= 4096)
-        S = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(8, nvec / 64)));
-      else if (ar_flags)
-        S = nvec < 16384 ? 16 : 32;
-      else
-        S = static_cast<int32_t>(std::min<int64_t>(32, std::max<int64_t>(8, nvec / 1024)));
+      // Plan chains: 64 vectors (of the larger of a rank's input and output)
+      // per workgroup, up to 64 per rank.  Dual buffer, 8 ranks, 128 KiB
+      // tensor per rank, us per collective at the old default of 8 per rank
+      // against 64: All-Reduce 10.45 -> 3.14, Reduce 10.80 -> 3.26,
+      // Broadcast 4.32 -> 2.45, Reduce-Scatter 4.35 -> 3.35, All-to-All 8.36
+      // -> 7.90, All-Gather 7.14 -> 7.22, Gather 7.13 -> 7.36.
+      S = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(64, nvec / 64)));
     }
     S = std::min<int32_t>(S, 2048 / nranks);
   }

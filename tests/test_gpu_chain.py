@@ -72,11 +72,10 @@ def _slices_of(ch):
     nvec = ch.count * 2 // 16
     if ch.variant == "lamport":
         S = max(1, nvec // 64) if nvec < 4096 else min(256, nvec // 32) if nvec <= 16384 else 128
+    elif ch.variant == "twoshot":
+        S = max(1, min(8, nvec // 64)) if nvec <= 4096 else max(8, min(128, nvec // 512))
     else:
-        if ch.variant == "twoshot":
-            S = max(1, min(8, nvec // 64)) if nvec <= 4096 else min(32, max(8, nvec // 1024))
-        else:
-            S = max(1, min(8, nvec // 64)) if nvec < 2048 else 16 if nvec < 16384 else 32
+        S = max(1, min(128, nvec // 64))
     return min(S, 2048 // R, nvec)
 
 
@@ -152,12 +151,12 @@ def test_chain_other_rank_counts_and_fp32():
                     assert_bits_equal(got[e, r], want[e], f"R={Rx} {dt} {v} e={e} r={r}")
 
 
-@pytest.mark.parametrize("v", ["speculative", "lamport"])
+@pytest.mark.parametrize("v", FLAG_VARIANTS)
 def test_100k_iterations_exact(v):
     """The pages' correctness check for speculative reduction: 100k chained
     All-Reduces, every result bit-exact (here against precomputed oracle
-    results; payloads cycle through 256 seeded input sets).  Run for the
-    flag-in-data variant as well."""
+    results; payloads cycle through 256 seeded input sets, so a value left
+    from an earlier epoch shows as a mismatch).  Run for every variant."""
     require_gpu()
     n, pool, per_call, total = 4096, 256, 256, 100_000
     ins_np = inputs.chain(pool, R, n, kind=80)
@@ -182,6 +181,31 @@ def test_100k_iterations_exact(v):
     ch.check()
     s = stats.cpu().tolist()
     _say(f"100k {v}: misspec {s[0]} retries {s[1]} epochs {done}")
+
+
+@pytest.mark.parametrize("v", ["barrier", "dual", "speculative", "twoshot"])
+def test_many_slices_stress_exact(v):
+    """128 KiB payloads take 128 workgroups per rank (1024 in all) for the
+    flag variants: 8192 chained All-Reduces over 32 seeded input sets, every
+    result bit-exact."""
+    require_gpu()
+    n, pool, total = 65536, 32, 8192
+    ins_np = inputs.chain(pool, R, n, kind=82)
+    want = np.stack(OC.allreduce_chain(ins_np))
+    inp = to_dev(ins_np)
+    want_dev = to_dev(np.repeat(want[:, None, :], R, axis=1))
+    ch = api.SnacChain(R, n, "bf16", v)
+    out = torch.empty_like(inp)
+    done = 0
+    while done < total:
+        ch.run(inp, out)
+        if not torch.equal(out, want_dev):
+            ch.check()
+            bad = (out != want_dev).nonzero()
+            raise AssertionError(f"{v} mismatch after {done} epochs at {bad[:5].tolist()}")
+        done += pool
+    ch.check()
+    _say(f"many-slices {v}: {done} epochs exact")
 
 
 def test_bounded_wait_times_out_cleanly():
