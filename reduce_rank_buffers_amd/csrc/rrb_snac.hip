@@ -968,25 +968,21 @@ int32_t default_slices(int32_t slices, int64_t nvec, int32_t nranks, uint32_t fl
       } else {
         S = 128;
       }
-    } else if (!plan && !(flags & RRB_SNAC_TWOSHOT)) {
-      // Barrier, dual and speculative All-Reduce chains: 64 vectors per
-      // workgroup, up to 128 workgroups per rank.  Measured on MI355X, 8
-      // ranks, dual buffer, us per All-Reduce by slices per rank:
-      //   32 KiB   16: 2.71  32: 2.29  64: 2.39
-      //   128 KiB  32: 4.40  64: 3.29  128: 2.84  256: 3.59
-      //   256 KiB  64: 4.99  128: 3.83  256: 3.81
-      //   1 MiB    64: 11.36  128: 8.34  256: 9.86
-      // (barrier and speculative alike; 512 KiB 6.50 / 6.77 / 5.79 at 64 /
-      // 128 / 256).  Before the chains dropped their fences, every extra
-      // workgroup added fence time and 16-32 per rank were best.
-      S = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(128, nvec / 64)));
     } else if (!plan) {
-      // Twoshot: up to 8 workgroups per rank to 64 KiB, then 512 vectors per
-      // workgroup, up to 128 (us per All-Reduce, 8 ranks: 128 KiB 8.75 at 16,
-      // 256 KiB 8.52 at 32, 512 KiB 9.59 at 64, 1 MiB 10.93 at 128).
-      S = nvec <= 4096
-              ? static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(8, nvec / 64)))
-              : static_cast<int32_t>(std::max<int64_t>(8, std::min<int64_t>(128, nvec / 512)));
+      // Barrier, dual, speculative and twoshot All-Reduce chains: 64 vectors
+      // per workgroup, up to 128 workgroups per rank.  Measured on MI355X, 8
+      // ranks, us per All-Reduce by slices per rank:
+      //   dual     32 KiB   16: 2.71  32: 2.29  64: 2.39
+      //            128 KiB  32: 4.40  64: 3.29  128: 2.84  256: 3.59
+      //            256 KiB  64: 4.99  128: 3.83  256: 3.81
+      //            1 MiB    64: 11.36  128: 8.34  256: 9.86
+      //   twoshot  32 KiB   16: 4.96  32: 4.51  64: 5.01
+      //            128 KiB  64: 5.39  128: 5.14  256: 6.60
+      //            1 MiB    128: 11.16  256: 10.26
+      // (barrier and speculative as dual; dual 512 KiB 6.50 / 6.77 / 5.79 at
+      // 64 / 128 / 256).  Before the chains dropped their fences, every extra
+      // workgroup added fence time and 8-32 per rank were best.
+      S = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(128, nvec / 64)));
     } else {
       // Plan chains: 64 vectors (of the larger of a rank's input and output)
       // per workgroup, up to 64 per rank.  Dual buffer, 8 ranks, 128 KiB

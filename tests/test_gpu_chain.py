@@ -72,8 +72,6 @@ def _slices_of(ch):
     nvec = ch.count * 2 // 16
     if ch.variant == "lamport":
         S = max(1, nvec // 64) if nvec < 4096 else min(256, nvec // 32) if nvec <= 16384 else 128
-    elif ch.variant == "twoshot":
-        S = max(1, min(8, nvec // 64)) if nvec <= 4096 else max(8, min(128, nvec // 512))
     else:
         S = max(1, min(128, nvec // 64))
     return min(S, 2048 // R, nvec)
