@@ -771,6 +771,9 @@ struct PlanChainArgs {
   int64_t slice_vec;         // staging slice length in vectors
   int64_t in_vec[RRB_MAX_RANKS];
   int32_t first[RRB_MAX_RANKS], cnt[RRB_MAX_RANKS];
+  // Vectors per entry when all of a rank's entries are copies of one length
+  // (and there are at most kFlatEntries of them), else 0.
+  int64_t copy_len[RRB_MAX_RANKS];
   uint32_t epoch0;
   int32_t epochs;
   int32_t S;
@@ -793,12 +796,50 @@ __device__ bool wait_list(const uint32_t *base, const int32_t *idx, int n, uint3
 // Piece s of every entry of rank r: staged data read with device-coherent
 // loads, results stored to rank r's output of this epoch with plain stores
 // (only the host reads outputs).
+//
+// A rank whose entries are all copies of one length (All-Gather, All-to-All,
+// Gather) takes its pieces as one flat index range over all lanes, kCopyU
+// vectors per lane in flight, with the entries held in LDS (`ents`): a pass
+// per entry put the entries' round trips one after another, with most lanes
+// idle when a piece is narrower than the workgroup.
+constexpr int kFlatEntries = 64;
+
 template <int R, bool BF16>
 __device__ void plan_consume(const PlanChainArgs &a, int r, int s,
-                             const unsigned char *stage_base, unsigned char *dst) {
+                             const unsigned char *stage_base, unsigned char *dst,
+                             const PlanEntry *ents) {
   const int bs = blockDim.x;
   constexpr int CU = R <= 8 ? 2 : 1;
   constexpr int CC = 4;  // copy vectors per lane in flight
+  if (a.copy_len[r] > 0) {
+    const int64_t len = a.copy_len[r];
+    const int64_t pl = (len + a.S - 1) / a.S;
+    const int64_t lo = min(len, static_cast<int64_t>(s) * pl);
+    const uint32_t w = static_cast<uint32_t>(min(len, lo + pl) - lo);
+    const uint32_t total = static_cast<uint32_t>(a.cnt[r]) * w;
+    // One descriptor over every rank's staged payload of this buffer.
+    const __amdgpu_buffer_rsrc_t src = rsrc(stage_base, static_cast<int64_t>(R) * a.in_stride);
+    for (uint32_t f0 = threadIdx.x; f0 < total; f0 += static_cast<uint32_t>(bs) * kCopyU) {
+      uint4 x[kCopyU];
+      int64_t at[kCopyU];
+#pragma unroll
+      for (int u = 0; u < kCopyU; ++u) {
+        const uint32_t f = f0 + static_cast<uint32_t>(u * bs);
+        at[u] = -1;
+        if (f < total) {
+          const uint32_t g = f / w;
+          const PlanEntry e = ents[g];
+          const int64_t i = lo + (f - g * w);
+          x[u] = load_coherent(src, static_cast<int32_t>(e.src_rank * a.in_stride + (e.src_off + i) * 16));
+          at[u] = (e.dst_off + i) * 16;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kCopyU; ++u)
+        if (at[u] >= 0) *reinterpret_cast<uint4 *>(dst + at[u]) = x[u];
+    }
+    return;
+  }
   for (int g = a.first[r]; g < a.first[r] + a.cnt[r]; ++g) {
     const PlanEntry e = a.entries[g];
     const int64_t pl = (e.len + a.S - 1) / a.S;
@@ -855,6 +896,11 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
   const int nw = a.wait_off[blockIdx.x + 1] - w0;
   const int32_t *wl = a.wait_idx + w0;
   unsigned long long misspec = 0, retries = 0, timeouts = 0, done_epochs = 0;
+  __shared__ PlanEntry ents[kFlatEntries];
+  if (a.copy_len[r] > 0) {
+    for (int g = threadIdx.x; g < a.cnt[r]; g += bs) ents[g] = a.entries[a.first[r] + g];
+    __syncthreads();
+  }
 
   for (int k = 0; k < a.epochs; ++k) {
     const uint32_t ep = a.epoch0 + static_cast<uint32_t>(k);
@@ -897,7 +943,7 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
         sum += load_flag_relaxed(flags_b + static_cast<int64_t>(wl[i]) * kFlagStride);
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("" ::: "memory");
-      plan_consume<R, BF16>(a, r, s, stage_base, dst);
+      plan_consume<R, BF16>(a, r, s, stage_base, dst, ents);
 #pragma unroll
       for (int m = 1; m < 64; m <<= 1) sum += __shfl_xor(sum, m);
       // Each flag is epoch or epoch - 2, so the sum is exact (no wrap-around
@@ -906,11 +952,11 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
         ++misspec;
         ++retries;
         ok = wait_list(flags_b, wl, nw, ep, a.status, a.spin_limit);
-        if (ok) plan_consume<R, BF16>(a, r, s, stage_base, dst);
+        if (ok) plan_consume<R, BF16>(a, r, s, stage_base, dst, ents);
       }
     } else {
       ok = wait_list(flags_b, wl, nw, ep, a.status, a.spin_limit);
-      if (ok) plan_consume<R, BF16>(a, r, s, stage_base, dst);
+      if (ok) plan_consume<R, BF16>(a, r, s, stage_base, dst, ents);
     }
     if (!ok) {
       ++timeouts;
@@ -1046,6 +1092,7 @@ struct rrb_snac_s {
   int64_t slice_vec = 0;  // staging slice length in vectors
   int64_t in_vec[RRB_MAX_RANKS] = {};
   int32_t first[RRB_MAX_RANKS] = {}, cnt[RRB_MAX_RANKS] = {};
+  int64_t copy_len[RRB_MAX_RANKS] = {};
   // Co-resident capacity (workgroups) of the last persistent kernel launched.
   const void *cap_fn = nullptr;
   int64_t cap = 0;
@@ -1236,6 +1283,7 @@ rrb_status launch_plan_chain(rrb_snac_s *h, int32_t epochs, const void *d_in, vo
     a.in_vec[r] = h->in_vec[r];
     a.first[r] = h->first[r];
     a.cnt[r] = h->cnt[r];
+    a.copy_len[r] = h->copy_len[r];
   }
   a.slice_vec = h->slice_vec;
   a.epoch0 = h->next_epoch;
@@ -1384,6 +1432,11 @@ rrb_status rrb_snac_create_plan(rrb_plan_t plan, uint32_t flags, int32_t slices,
         h->entries.push_back(e);
       }
       h->cnt[r] = static_cast<int32_t>(h->entries.size()) - h->first[r];
+      // Flat consume: copies of one length only, few enough for LDS.
+      bool flat = h->cnt[r] >= 1 && h->cnt[r] <= kFlatEntries;
+      for (int g = h->first[r]; flat && g < h->first[r] + h->cnt[r]; ++g)
+        flat = h->entries[g].src_rank >= 0 && h->entries[g].len == h->entries[h->first[r]].len;
+      h->copy_len[r] = flat ? h->entries[h->first[r]].len : 0;
     }
   } catch (const std::bad_alloc &) {
     delete h;
