@@ -310,7 +310,7 @@ rrb_status rrb_empty_kernel(rrb_stream_t stream);
  *                              its bounded waits run out and the call reports
  *                              RRB_ETIMEOUT rather than hang.
  * slices: single-wave workgroups per rank (1..256; 0 = choose from count:
- *         8 up to 64 KiB payloads, then about 16 KiB per workgroup up to 32;
+ *         1 KiB of payload per workgroup, up to 128;
  *         RRB_SNAC_LAMPORT: 1 KiB per workgroup below 64 KiB, then 512 B per
  *         workgroup up to 256, and 128 above 256 KiB; at most 2048 / nranks).
  *         The grid (nranks x slices) must be co-resident; a cooperative
@@ -371,11 +371,13 @@ rrb_status rrb_snac_allreduce_chain(rrb_snac_t h, int32_t epochs,
  * and sit on 16-byte boundaries, and every rank's input must be a 16-byte
  * multiple (RRB_EUNSUPPORTED otherwise).  flags: 0 (top and bottom barrier),
  * RRB_SNAC_DUAL_BUFFER, RRB_SNAC_DUAL_BUFFER | RRB_SNAC_SPECULATIVE (flags
- * read first, whole consume, then the reduced check of all R x slices
- * flags), or RRB_SNAC_GRAPH (one Atom launch per epoch in a cached HIP
- * graph).  Workgroup (r, s) stages slice s of rank r's input and computes
- * piece s of every map entry whose output is rank r; the top barrier covers
- * every rank's every slice, since a piece may read any of them.
+ * read first, whole consume, then the reduced check of the workgroup's
+ * listed flags), or RRB_SNAC_GRAPH (one Atom launch per epoch in a cached
+ * HIP graph).  Workgroup (r, s) stages slice s of rank r's input and
+ * computes piece s of every map entry whose output is rank r; it waits on a
+ * list of flags built at create time: the staged slices its pieces read and
+ * the workgroups that read its own slice.  slices = 0 gives each workgroup
+ * 1 KiB of the larger of a rank's input and output, up to 64 per rank.
  * Workspace, bind, check and destroy as for rrb_snac_create.
  */
 rrb_status rrb_snac_create_plan(rrb_plan_t plan, uint32_t flags, int32_t slices,
