@@ -15,6 +15,7 @@
 // fetching a table from memory.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstring>
 
 #include "rrb_internal.h"
@@ -66,6 +67,7 @@ struct UniArgs {
   int32_t tiles;  // workgroups per item
   int32_t nranks;
   int32_t xcd_chunk;  // 0, or C: XCD-chunked tile order (tiles % (8 * C) == 0)
+  int32_t fan;        // copy_split_kernel: workgroups per tile (largest fan-out)
 };
 
 // Workgroups are dealt to the 8 XCDs round-robin in blockIdx order.  With a
@@ -317,6 +319,33 @@ __global__ void __launch_bounds__(256) copy_wt_kernel(UniArgs a) {
     const uint16_t x = *reinterpret_cast<const uint16_t *>(src + off);
     for (uint32_t m = it.dst_mask; m; m &= m - 1)
       *reinterpret_cast<uint16_t *>(a.out[__builtin_ctz(m)] + it.dst_off + off) = x;
+  }
+}
+
+// Small fan-out copies: one workgroup per (item, destination, tile), each
+// reading its tile and writing it to one destination, so a fan-out's stores
+// spread over `fan` times more workgroups.  Graph-replayed All-Gather, 8
+// ranks, MI355X: 8 x 256 B 2.69 -> 2.21 us per launch, 8 x 2 KiB 2.81 ->
+// 2.31, 8 x 16 KiB 2.87 -> 2.41; at 8 x 64 KiB it lost (3.30 -> 3.50), so
+// blocks above 1024 vectors keep one workgroup per tile.
+__global__ void __launch_bounds__(256) copy_split_kernel(UniArgs a) {
+  const int bs = blockDim.x;
+  const int per_item = a.tiles * a.fan;
+  const int item = blockIdx.x / per_item;
+  const int rem = blockIdx.x - item * per_item;
+  const int d = rem / a.tiles;
+  const int tile = rem - d * a.tiles;
+  const KItem it = a.items[item];
+  uint32_t m = it.dst_mask;
+  for (int j = 0; j < d && m; ++j) m &= m - 1;
+  if (!m) return;  // this item fans out to fewer destinations
+  unsigned char *dst = a.out[__builtin_ctz(m)] + it.dst_off;
+  const unsigned char *src = a.in[it.src_rank] + it.src_off;
+  const int64_t i = static_cast<int64_t>(tile) * bs + threadIdx.x;
+  if (i < a.nvec) *reinterpret_cast<uint4 *>(dst + i * 16) = *reinterpret_cast<const uint4 *>(src + i * 16);
+  if (a.tail && tile == a.tiles - 1 && threadIdx.x < a.tail) {
+    const int64_t off = a.nvec * 16 + static_cast<int64_t>(threadIdx.x) * 2;
+    *reinterpret_cast<uint16_t *>(dst + off) = *reinterpret_cast<const uint16_t *>(src + off);
   }
 }
 
@@ -709,11 +738,15 @@ rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out
       // Gather 8 x 2 MiB 5.61 -> 4.31 us, All-to-All 8 x 4 MiB 9.99 -> 7.72
       // us per launch (graph replays on MI355X; 8 x 128 KiB Gather 2.15 ->
       // 2.34, the one loss measured).
-      bool fan_any = false;
-      for (const Segment &sg : p.segs) fan_any = fan_any || __builtin_popcount(sg.dst_mask) > 1;
+      int fan = 1;
+      for (const Segment &sg : p.segs) fan = std::max(fan, __builtin_popcount(sg.dst_mask));
+      const bool fan_any = fan > 1;
       const bool single = !stream && !small && !fan_any;
+      const bool split = small && fan_any && a.nvec <= 1024;
+      a.fan = fan;
       U = single ? 2 : (small || stream || !big) ? 1 : 4;
       kern = stream             ? copy_vec_kernel<1, true>
+             : split            ? copy_split_kernel
              : (small && fan_any) ? copy_vec_kernel<1, false>
              : U == 1             ? copy_wt_kernel<1>
              : U == 2             ? copy_wt_kernel<2>
@@ -751,7 +784,8 @@ rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out
       a.items[i].src_rank = s.src_rank < 0 ? 0 : s.src_rank;
       a.items[i].dst_mask = s.dst_mask;
     }
-    const unsigned grid = static_cast<unsigned>(cnt) * static_cast<unsigned>(a.tiles);
+    const unsigned grid = static_cast<unsigned>(cnt) * static_cast<unsigned>(a.tiles) *
+                          static_cast<unsigned>(kern == copy_split_kernel ? a.fan : 1);
     const rrb_status st = emit(kern, dim3(grid), dim3(bs), a, reduce ? "reduce" : "copy");
     if (st != RRB_OK) return st;
   }

@@ -152,6 +152,17 @@ def test_single_destination_copies_ragged(name, R, c):
     _run_and_check(name, ins, "bf16", 5 % R if name == "gather" else None)
 
 
+@pytest.mark.parametrize("R", [2, 3, 8, 16])
+@pytest.mark.parametrize("c", [8, 8 * 64 + 8, 8 * 1024, 8 * 2048])
+def test_small_fanout_all_gather(R, c):
+    """All-Gathers of small shards (one workgroup per destination and tile up
+    to 1024 vectors per shard, one per tile above): full compare."""
+    require_gpu()
+    _say(f"small fan-out all-gather R={R} c={c}")
+    ins = inputs.rank_payloads(c, R, "bf16", 1.0, inputs.WL_SEVEN, 70 + R)
+    _run_and_check("all_gather", ins, "bf16")
+
+
 @pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 16])
 @pytest.mark.parametrize("n", [0, 1, 7, 8, 37, 8 * 513 + 3, 4096])
 def test_edge_all_reduce(R, n):
