@@ -325,6 +325,23 @@ def graph_us_per_launch(torch, fn, per_graph=64, replays=50):
     return a.elapsed_time(b) * 1e3 / (replays * per_graph)
 
 
+def _cold_ms(torch, fn, scratch, reps=5):
+    """Median of `reps` calls, each after an untimed read of a 1 GiB scratch
+    buffer that evicts the 256 MB Infinity Cache and the L2s (the inputs then
+    come from HBM and no earlier dirty data is written back during the call)."""
+    ts = []
+    for _ in range(reps):
+        scratch.sum()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    return float(np.median(ts))
+
+
 def _events_ms(torch, fn, iters):
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
     for a, b in ev:
@@ -453,6 +470,10 @@ def bench_moe(args, dev):
     r_ms = float(np.median(_events_ms(torch, lambda: ddisp.route(d_idx, d_w), max(10, args.steps))))
     dd_ms = float(np.median(_events_ms(torch, lambda: ddisp.run(xs, [arena] + none), max(10, args.steps))))
     dc_ms = float(np.median(_events_ms(torch, lambda: dcomb.run([arena] + none, y), max(10, args.steps))))
+    scratch = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    cd_ms = _cold_ms(torch, lambda: ddisp.run(xs, [arena] + none), scratch)
+    cc_ms = _cold_ms(torch, lambda: dcomb.run([arena] + none, y), scratch)
+    del scratch
     t0 = time.perf_counter()
     for _ in range(10):
         rrb.MoePlan(R, h, E, idx, w, "dispatch")
@@ -470,7 +491,12 @@ def bench_moe(args, dev):
                           "dispatch_arena": {"us": round(dd_ms * 1e3, 2),
                                              "GBps": round(d_bytes / (dd_ms * 1e-3) / 1e9, 1)},
                           "combine_arena": {"us": round(dc_ms * 1e3, 2),
-                                            "GBps": round(c_bytes / (dc_ms * 1e-3) / 1e9, 1)}}}),
+                                            "GBps": round(c_bytes / (dc_ms * 1e-3) / 1e9, 1)},
+                          "cold": {"note": "one call after a 1 GiB cache-evicting read, median of 5",
+                                   "dispatch_arena_us": round(cd_ms * 1e3, 2),
+                                   "dispatch_arena_GBps": round(d_bytes / (cd_ms * 1e-3) / 1e9, 1),
+                                   "combine_arena_us": round(cc_ms * 1e3, 2),
+                                   "combine_arena_GBps": round(c_bytes / (cc_ms * 1e-3) / 1e9, 1)}}}),
           flush=True)
 
 
@@ -521,8 +547,16 @@ def bench_seven(args, dev):
         res[name] = {"us": round(ms * 1e3, 2), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
                      "frac": round(b / (ms * 1e-3) / 1e9 / PEAK_GBS, 4), "bytes": b,
                      "event_us": round(ev_ms * 1e3, 2)}
+    scratch = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    for name, (fn, b) in cases.items():
+        cm = _cold_ms(torch, fn, scratch)
+        res[name]["cold_event_us"] = round(cm * 1e3, 2)
+        res[name]["cold_GBps"] = round(b / (cm * 1e-3) / 1e9, 1)
+    del scratch
     print(json.dumps({"metric": "achieved GB/s, seven collectives, 8 ranks x 16 MiB bf16 (cache-resident sizes)",
-                      "unit": "GB/s", "timing": f"{G} launches in one HIP graph, replayed; us per launch",
+                      "unit": "GB/s", "timing": f"{G} launches in one HIP graph, replayed; us per launch; "
+                                                "cold_event_us: one host-issued launch after a 1 GiB "
+                                                "cache-evicting read, median of 5",
                       "results": res}), flush=True)
 
 
