@@ -222,8 +222,8 @@ __device__ __forceinline__ uint32_t load_flag_relaxed(const uint32_t *p) {
 __device__ bool wait_at_least(const uint32_t *p, uint32_t want, uint32_t *status,
                               uint32_t limit) {
   uint32_t spins = 0;
-  // Relaxed (device-coherent) polls; the caller's acquire fence orders what
-  // follows a successful wait.
+  // Relaxed (device-coherent) polls; what follows a successful wait reads
+  // with device-coherent loads, issued after the flag value has returned.
   while (load_flag_relaxed(p) < want) {
     if ((spins & 63) == 0 && load_flag_relaxed(status) != 0) return false;
     if (++spins >= limit) {
@@ -235,11 +235,9 @@ __device__ bool wait_at_least(const uint32_t *p, uint32_t want, uint32_t *status
   return true;
 }
 
-// Threads 0..R-1 each wait for one rank's word at `base + t * stride_words`;
-// then every wave takes its own agent-scope acquire (a fence in one wave does
-// not order another wave's loads: measured, sharing one fence per workgroup
-// returned stale staging data).  Returns, in every thread, whether all R
-// waits succeeded.  `ok` is an LDS array of R flags.
+// Threads 0..R-1 each wait for one rank's word at `base + t * stride_words`.
+// Returns, in every thread, whether all R waits succeeded.  `ok` is an LDS
+// array of R flags.
 template <int R>
 __device__ bool wait_all(const uint32_t *base, int64_t stride_words, uint32_t want,
                          uint32_t *status, uint32_t limit, int *ok) {
