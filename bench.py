@@ -289,6 +289,7 @@ def main():
             "traffic": traffic_bytes(),
             "alg_bytes_per_launch": ar_bytes,
             "mean_launch_us": round(ar_ms * 1e3, 2),
+            "serial_bound": serial_bound(sweep),
         },
         "decode": decode,
         "copy_calibration": copy_cal,
@@ -296,6 +297,24 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def serial_bound(sweep):
+    """The 256 MiB All-Reduce against this run's own serial read + write
+    bound.  An HBM channel's read and write time add up, so with t = bytes
+    read / read rate + bytes written / write rate, the cold Reduce-Scatter
+    (reads R*S, writes S) and the cold All-Gather (reads S, writes R*S)
+    together read and write (R+1)*S each, and the All-Reduce (2*R*S: R*S
+    each way) is bounded below by (t_RS + t_AG) * R / (R + 1)."""
+    cold = sweep.get("256MiB-bf16", {}).get("cold")
+    if not cold:
+        return None
+    t_rs, t_ag, t_ar = (cold[k]["us"] for k in ("reduce_scatter", "all_gather", "all_reduce"))
+    bound = (t_rs + t_ag) * R / (R + 1)
+    return {"model": "cold Reduce-Scatter + cold All-Gather of the same run, times R/(R+1)",
+            "bound_us": round(bound, 2), "all_reduce_cold_us": t_ar,
+            "frac_of_bound": round(bound / t_ar, 4),
+            "bound_frac_of_peak": round(2 * R * (256 << 20) / (bound * 1e-6) / 1e9 / PEAK_GBS, 4)}
 
 
 def graph_us_per_launch(torch, fn, per_graph=64, replays=50):
