@@ -125,3 +125,28 @@ def test_combine_no_contraction_and_ascending_expert_order(k, h):
         got, want = _combine_one_token(k, h, order, [1.0] * k, z)
         assert np.all(want == 0x0000)
         assert_bits_equal(got, want, f"combine order k={k} h={h}")
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_moe_random_shapes(seed):
+    """Seeded random token counts, hidden sizes (vector and element paths, row
+    parts with a short last part), expert counts, top-k (the vector kernels'
+    k and others) and rank counts; expert choice uniform or skewed."""
+    require_gpu()
+    rng = np.random.default_rng([9003, seed])
+    R = int(rng.choice([1, 2, 4, 8]))
+    T = R * int(rng.integers(1, 65))
+    E = R * int(rng.choice([1, 2, 4, 8, 32]))
+    k = int(rng.choice([k for k in (1, 2, 3, 4, 6, 8, 16) if k <= E]))
+    h = int(rng.choice([1, 7, 8, 24, 40, 8 * int(rng.integers(1, 300)), 7168]))
+    skew = bool(rng.integers(0, 2))
+    _say(f"moe random {seed}: T={T} h={h} E={E} k={k} R={R} skew={skew}")
+    p = None
+    if skew:
+        p = 1.0 / (np.arange(E) + 1.0) ** 1.5
+        p = p / p.sum()
+    idx = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    xa = bf16.rne(rng.standard_normal((T, h)).astype(np.float32))
+    shards = [xa[r * (T // R):(r + 1) * (T // R)] for r in range(R)]
+    _roundtrip(T, h, E, k, R, idx, w, shards, str(rng.choice(["identity", "seeded"])))
