@@ -149,3 +149,28 @@ def test_device_routing_many_blocks():
     xa = bf16.rne(rng.standard_normal((T, h)).astype(np.float32))
     shards = [xa[r * (T // R):(r + 1) * (T // R)] for r in range(R)]
     _run(T, h, E, k, R, idx, w, shards)
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_device_routing_random_shapes(seed):
+    """Seeded random token counts (one to many blocks of 256, so the fused
+    kernel and the three-kernel path both run), expert counts, top-k, rank
+    counts and hidden sizes; expert choice uniform or skewed."""
+    require_gpu()
+    rng = np.random.default_rng([9004, seed])
+    R = int(rng.choice([1, 2, 4, 8]))
+    T = R * int(rng.choice([1, 3, 32, 100, 600, 4096]))
+    E = R * int(rng.choice([1, 2, 8, 32]))
+    k = int(rng.choice([k for k in (1, 2, 3, 4, 8, 16) if k <= E]))
+    h = int(rng.choice([1, 8, 24, 64]))
+    skew = bool(rng.integers(0, 2))
+    _say(f"device routing random {seed}: T={T} h={h} E={E} k={k} R={R} skew={skew}")
+    p = None
+    if skew:
+        p = 1.0 / (np.arange(E) + 1.0) ** 1.5
+        p = p / p.sum()
+    idx = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    xa = bf16.rne(rng.standard_normal((T, h)).astype(np.float32))
+    shards = [xa[r * (T // R):(r + 1) * (T // R)] for r in range(R)]
+    _run(T, h, E, k, R, idx, w, shards)
