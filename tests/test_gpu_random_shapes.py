@@ -147,3 +147,29 @@ def test_random_plan_chain(seed):
                 assert np.all(got[e, q] == sent), f"{name} {variant} seed {seed}: rank {q} written"
             else:
                 assert_bits_equal(got[e, q, :len(w)], w, f"{name} {variant} seed {seed} e={e} q={q}")
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_allreduce_chain(seed):
+    """All-Reduce chains of a random variant, rank count, payload and slice
+    count, every epoch of every rank bit-exact."""
+    require_gpu()
+    rng = np.random.default_rng([9005, seed])
+    variant = str(rng.choice(["barrier", "dual", "speculative", "twoshot", "lamport", "graph"]))
+    R = int(rng.choice([2, 3, 5, 8, 16]))
+    dtype = "bf16" if variant == "lamport" else str(rng.choice(["bf16", "f32"]))
+    per16 = 8 if dtype == "bf16" else 4
+    n = per16 * int(rng.choice([1, 7, 64, 512, 1000, 8192]))
+    slices = 0 if variant == "graph" else int(rng.choice([0, 0, 1, 5, 32]))
+    E = 8
+    _say(f"random all-reduce chain {seed}: {variant} R={R} n={n} {dtype} slices={slices}")
+    ins = np.stack([np.stack([_payload(rng, n, dtype) for _ in range(R)]) for _ in range(E)])
+    want = OC.allreduce_chain(ins, dtype)
+    ch = api.SnacChain(R, n, dtype, variant, slices=slices)
+    out = to_dev(np.zeros_like(ins))
+    ch.run(to_dev(ins), out)
+    ch.check()
+    got = from_dev(out)
+    for e in range(E):
+        for r in range(R):
+            assert_bits_equal(got[e, r], want[e], f"{variant} seed {seed} e={e} r={r}")
