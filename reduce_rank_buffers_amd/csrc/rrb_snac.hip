@@ -462,19 +462,29 @@ __global__ void __launch_bounds__(64) snac_chain_kernel(SnacArgs a) {
     // Stage: this rank's slice lands in its staged buffer.
     const unsigned char *src = a.in + (static_cast<int64_t>(k) * R + r) * a.rank_bytes;
     unsigned char *mine = stage_base + static_cast<int64_t>(r) * a.rank_bytes;
-    {
-      int64_t i = v0 + threadIdx.x;
-      for (; i + static_cast<int64_t>(kStageU - 1) * bs < v1; i += static_cast<int64_t>(bs) * kStageU) {
-        v4u x[kStageU];  // (HIP's uint4 struct here would be placed in scratch)
+    // Every pass issues all of its loads before its stores, a partial last
+    // pass included: a remainder loop of one load and one store per step
+    // put a slice of 2-7 vectors per lane through as many round trips (8
+    // ranks, 512 KiB payload, 256 vectors per workgroup: 6.9 -> 5.4 us per
+    // All-Reduce, dual buffer).  A slice of at most one vector per lane
+    // takes a single load and store (2-6% less time per All-Reduce at 8-32
+    // KiB than the masked pass).
+    if (v1 - v0 <= bs) {
+      const int64_t i = v0 + threadIdx.x;
+      if (i < v1) store_wt(mine, a.rank_bytes, i * 16, *reinterpret_cast<const v4u *>(src + i * 16));
+    } else
+    for (int64_t i0 = v0 + threadIdx.x; i0 < v1; i0 += static_cast<int64_t>(bs) * kStageU) {
+      v4u x[kStageU];  // (HIP's uint4 struct here would be placed in scratch)
 #pragma unroll
-        for (int u = 0; u < kStageU; ++u)
-          x[u] = *reinterpret_cast<const v4u *>(src + (i + static_cast<int64_t>(u) * bs) * 16);
-#pragma unroll
-        for (int u = 0; u < kStageU; ++u)
-          store_wt(mine, a.rank_bytes, (i + static_cast<int64_t>(u) * bs) * 16, x[u]);
+      for (int u = 0; u < kStageU; ++u) {
+        const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+        if (i < v1) x[u] = *reinterpret_cast<const v4u *>(src + i * 16);
       }
-      for (; i < v1; i += bs)
-        store_wt(mine, a.rank_bytes, i * 16, *reinterpret_cast<const v4u *>(src + i * 16));
+#pragma unroll
+      for (int u = 0; u < kStageU; ++u) {
+        const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+        if (i < v1) store_wt(mine, a.rank_bytes, i * 16, x[u]);
+      }
     }
 
     // Notify.
@@ -1022,10 +1032,12 @@ int32_t default_slices(int32_t slices, int64_t nvec, int32_t nranks, uint32_t fl
       //            1 MiB    64: 11.36  128: 8.34  256: 9.86
       //   twoshot  32 KiB   16: 4.96  32: 4.51  64: 5.01
       //            128 KiB  64: 5.39  128: 5.14  256: 6.60
-      //            1 MiB    128: 11.16  256: 10.26
-      // (barrier and speculative as dual; dual 512 KiB 6.50 / 6.77 / 5.79 at
-      // 64 / 128 / 256).  Before the chains dropped their fences, every extra
-      // workgroup added fence time and 8-32 per rank were best.
+      //            256 KiB  128: 5.81  256: 6.19
+      //            1 MiB    128: 11.13  256: 10.24
+      // (barrier and speculative as dual; 256 per rank for twoshot from 512
+      // KiB won in one sweep and lost in the bench, so it keeps 128).
+      // Before the chains dropped their fences, every extra workgroup added
+      // fence time and 8-32 per rank were best.
       S = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(128, nvec / 64)));
     } else {
       // Plan chains: 64 vectors (of the larger of a rank's input and output)
