@@ -206,6 +206,24 @@ def test_many_slices_stress_exact(v):
     _say(f"many-slices {v}: {done} epochs exact")
 
 
+@pytest.mark.parametrize("v", ["barrier", "dual", "speculative", "twoshot", "lamport"])
+def test_many_slices_staggered_exact(v):
+    """128 KiB payloads (128 workgroups per rank) with late ranks: rank r
+    sleeps about r x 4k cycles, or rank 3 about 40k, before every stage, so
+    the write-after-read guards are crossed at skew; every epoch bit-exact."""
+    require_gpu()
+    n, E = 65536, 32
+    ins_np = inputs.chain(E, R, n, kind=83)
+    want = OC.allreduce_chain(ins_np)
+    inp = to_dev(ins_np)
+    for st in ([r * 64 for r in range(R)], [0, 0, 0, 640, 0, 0, 0, 0]):
+        ch = api.SnacChain(R, n, "bf16", v)
+        out = torch.empty_like(inp)
+        ch.run(inp, out, stagger=torch.tensor(st, dtype=torch.int32, device=DEV))
+        ch.check()
+        _check_chain(out, want, f"many slices staggered {v} {st}")
+
+
 def test_bounded_wait_times_out_cleanly():
     """A poll budget of 1 with one rank delayed: waits expire, every
     workgroup leaves, and the host gets RRB_ETIMEOUT (no hang)."""
