@@ -162,6 +162,17 @@ def test_plan_chain_stress_exact(name, variant):
     ch.check()
 
 
+@pytest.mark.parametrize("name", ["all_gather", "all_to_all", "gather", "reduce_scatter"])
+def test_plan_chain_large_staggered(name):
+    """128 KiB tensors per rank (64 workgroups per rank, flat copy consume
+    for the copies) with late ranks, every variant, every epoch bit-exact."""
+    require_gpu()
+    R = 8
+    stagger = torch.tensor([r * 64 for r in range(R)], dtype=torch.int32, device=DEV)
+    for variant in ("barrier", "dual", "speculative"):
+        _run_chain(name, R, 8 * 8192, "bf16", variant, E=16, stagger=stagger, kind=11)
+
+
 def test_plan_chain_times_out_cleanly():
     require_gpu()
     R, n = 8, 8 * 1024
