@@ -127,7 +127,12 @@ rrb_status rrb_moe_route_check(rrb_plan_t plan, rrb_stream_t stream) {
   if (p.kind != PlanKind::RowsDevice || !p.d_ws) return fail(RRB_EINVAL, "not a bound device row plan");
   hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
   int32_t st = 0;
-  std::vector<int32_t> bst(static_cast<size_t>(p.rows.nblk), 0);
+  std::vector<int32_t> bst;
+  try {
+    bst.assign(static_cast<size_t>(p.rows.nblk), 0);
+  } catch (const std::bad_alloc &) {
+    return fail(RRB_ENOMEM, "route status buffer allocation failed");
+  }
   if (e == hipSuccess)
     e = hipMemcpy(&st, static_cast<const char *>(p.d_ws) + p.rows.off_status, 4, hipMemcpyDeviceToHost);
   // Per-block words of the fused routing kernel (zero for the three-kernel path).

@@ -1546,7 +1546,13 @@ rrb_status rrb_snac_chain(rrb_snac_t h, int32_t epochs, const void *d_in, void *
   if (h->flags & RRB_SNAC_GRAPH) {
     if (d_stagger) return fail(RRB_EINVAL, "the stagger hook applies to the flag protocol only");
     if (!(h->exec && h->g_in == d_in && h->g_out == d_out && h->g_epochs == epochs)) {
-      const rrb_status st = build_chain_graph(h, epochs, d_in, d_out);
+      rrb_status st;
+      try {
+        st = build_chain_graph(h, epochs, d_in, d_out);
+      } catch (const std::bad_alloc &) {
+        h->drop_graph();
+        st = fail(RRB_ENOMEM, "graph description allocation failed");
+      }
       if (st != RRB_OK) return st;
     }
     const hipError_t e = hipGraphLaunch(h->exec, static_cast<hipStream_t>(stream));
