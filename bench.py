@@ -8,20 +8,27 @@ plus the same three at fp32, 64 MiB.  Inputs are resident in HBM before the
 timed region.  ``value`` = algorithmic bytes of the whole step (every input
 byte read once, every output byte written once) / step time.
 
-Also reported on the same line:
-* ``roofline``: the dominant kernel (the 256 MiB All-Reduce reduce kernel):
-  algorithmic bytes per launch / its mean duration from HIP events on the
-  launch stream, against the 8 TB/s HBM peak;
+Also reported on the same line (all measured after the timed region):
+* ``roofline``: the dominant kernel (the 256 MiB All-Reduce, named as the
+  library reports its launch): algorithmic bytes per launch / its mean
+  duration from HIP events on the launch stream, against the 8 TB/s HBM
+  peak; ``serial_bound`` sets it against the fastest Reduce-Scatter and
+  All-Gather of the same run;
 * ``sweep``: per size and collective, the in-step (warm) rate and a cold
-  rate (a 1 GiB scratch read before each call empties the caches; measured
-  after the timed region);
+  rate (a 1 GiB scratch read before each call empties the caches);
 * ``decode``: the batch-1 decode All-Reduce (8 ranks x 4096 bf16), kernel
-  time from events and back-to-back time per call, next to an empty kernel,
-  and per All-Reduce in a 64-deep chain (flag-in-data and dual-buffer SNAC
-  kernels, and a graph of Atom launches);
-* ``cpu_baseline``: the CPU oracle on a bounded sample of the same workload.
+  time from events and back-to-back time per call, next to an empty kernel;
+* ``seven``: the seven layout-named collectives at 8 x 16 MiB bf16 (us per
+  launch replayed from a HIP graph, GB/s, fraction of peak);
+* ``chain``: the decode chain, 64 back-to-back All-Reduces per call for every
+  b x h payload (b = 1..64, h = 4096, 8192) and every orchestration variant,
+  us per All-Reduce, and the speculative variant's mis-speculation rate;
+* ``moe``: MoE dispatch and combine, 4096 x 7168 bf16, 256 experts over 8
+  ranks, top-8 (host-built and device-routed maps);
+* ``cpu_baseline``: the CPU oracle on a bounded sample of the sweep workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs LIST]
+       python bench.py --workload chain|moe|seven   (detailed single workloads)
 """
 
 import argparse
@@ -52,7 +59,11 @@ def parse():
     ap.add_argument("--decode-iters", type=int, default=2000)
     ap.add_argument("--workload", default="sweep", choices=["sweep", "chain", "moe", "seven"],
                     help="sweep (default) is the headline line; the others print "
-                         "their own line for the decode chain, MoE and the seven collectives")
+                         "their own detailed line for the decode chain, MoE and the seven "
+                         "collectives")
+    ap.add_argument("--legs", default="decode,seven,chain,moe",
+                    help="legs measured after the sweep's timed region and added to its line "
+                         "(comma list of decode, seven, chain, moe; 'none' for the sweep alone)")
     return ap.parse_args()
 
 
@@ -178,66 +189,14 @@ def main():
         sweep[label]["cold"] = cold
     del scratch
 
-    # ---- decode All-Reduce latency (8 x 4096 bf16) -------------------------
-    dec_host = inputs.decode_allreduce()
-    dins = [torch.from_numpy(h.view(np.int16)).to(dev) for h in dec_host]
-    douts = [torch.empty(4096, dtype=torch.int16, device=dev) for _ in range(R)]
-    for _ in range(50):
-        rrb.all_reduce(dins, douts)
-        rrb.empty_kernel()
+    roof_kernel = ops[big[0]][0].kernels()
+    # the sweep's buffers are not needed by the legs that follow
+    del ops, cases, big
     torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
-    def per_launch_us(fn, iters):
-        es = [(ev(), ev()) for _ in range(iters)]
-        for a, b in es:
-            a.record()
-            fn()
-            b.record()
-        torch.cuda.synchronize()
-        return np.array([a.elapsed_time(b) * 1e3 for a, b in es])
-
-    def back_to_back_us(fn, iters):
-        torch.cuda.synchronize()
-        t = time.perf_counter()
-        for _ in range(iters):
-            fn()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t) * 1e6 / iters
-
-    it = args.decode_iters
-    dec_op = rrb.bound("all_reduce", dins, douts)
-    ar_ev = per_launch_us(dec_op, it)
-    em_ev = per_launch_us(rrb.empty_kernel, it)
-    g_ar = graph_us_per_launch(torch, dec_op)
-    g_em = graph_us_per_launch(torch, rrb.empty_kernel)
-    decode = {
-        "allreduce_graph_us": round(g_ar, 3),
-        "empty_kernel_graph_us": round(g_em, 3),
-        "graph_note": "64 launches captured in one HIP graph, replayed; us per launch",
-        "event_note": "event_us: events around one isolated host call (host launch latency "
-                      "included); back_to_back_us: host-issued calls in a loop; the kernel "
-                      "durations are in the rocprofv3 kernel trace",
-        "workload": "All-Reduce, 8 ranks x 4096 bf16 (TP=8 batch-1 decode, hidden 4096)",
-        "allreduce_event_us_p50": round(float(np.median(ar_ev)), 2),
-        "allreduce_event_us_p10": round(float(np.percentile(ar_ev, 10)), 2),
-        "allreduce_event_us_p90": round(float(np.percentile(ar_ev, 90)), 2),
-        "empty_kernel_event_us_p50": round(float(np.median(em_ev)), 2),
-        "allreduce_back_to_back_us": round(back_to_back_us(dec_op, it), 2),
-        "empty_back_to_back_us": round(back_to_back_us(rrb.empty_kernel, it), 2),
-    }
-    # the same All-Reduce 64 times back to back (a 32-layer decode step):
-    # one persistent SNAC kernel per call, or a graph of Atom launches
-    ch_in = torch.from_numpy(inputs.chain(64, R, 4096, kind=1).view(np.int16)).to(dev)
-    ch_out = torch.empty_like(ch_in)
-    chain = {}
-    for v, key in (("lamport", "flag_in_data_us"), ("dual", "dual_buffer_us"), ("graph", "graph_us")):
-        ch = rrb.SnacChain(R, 4096, "bf16", v)
-        call = ch.bound(ch_in, ch_out)
-        for _ in range(3):
-            call()
-        chain[key] = round(float(np.median(_events_ms(torch, call, 20))) * 1e3 / 64, 3)
-        ch.check()
-    decode["chain_64_per_allreduce"] = chain
+    legs = [x for x in args.legs.split(",") if x and x != "none"]
+    decode = decode_leg(args, torch, rrb, inputs, dev) if "decode" in legs else None
 
     # ---- copy calibration: a plain 192 MiB copy through the library -------
     # (one rank, SHARD -> SHARD): the known-size kernel that scales the HBM
@@ -248,9 +207,15 @@ def main():
     cal_plan = rrb.Plan(1, cal_bytes // 2, "bf16", rrb.SHARD, rrb.SHARD, "copy")
     for _ in range(3):
         cal_plan.run([cal_in], [cal_out])
-    cal_ev = per_launch_us(lambda: cal_plan.run([cal_in], [cal_out]), 10)
+    cal_ev = _per_launch_us(torch, lambda: cal_plan.run([cal_in], [cal_out]), 10)
     copy_cal = {"bytes": 2 * cal_bytes, "us": round(float(np.median(cal_ev)), 2),
                 "GBps": round(2 * cal_bytes / (float(np.median(cal_ev)) * 1e-6) / 1e9, 1)}
+    del cal_in, cal_out
+
+    seven = seven_leg(args, torch, rrb, inputs, dev) if "seven" in legs else None
+    moe = moe_leg(args, torch, rrb, inputs, dev) if "moe" in legs else None
+    chain = chain_leg(args, torch, rrb, inputs, dev) if "chain" in legs else None
+    log(f"legs done: {','.join(legs) or 'none'}")
 
     # ---- CPU oracle on a bounded sample ------------------------------------
     cpu = None
@@ -281,7 +246,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "reduce_vec_kernel<8,2,bf16> (All-Reduce, 256 MiB per rank)",
+            "kernel": roof_kernel,
             "achieved": round(achieved, 1),
             "peak": PEAK_GBS,
             "unit": "GB/s",
@@ -289,32 +254,241 @@ def main():
             "traffic": traffic_bytes(),
             "alg_bytes_per_launch": ar_bytes,
             "mean_launch_us": round(ar_ms * 1e3, 2),
-            "serial_bound": serial_bound(sweep),
+            "serial_bound": serial_bound(sweep, ar_ms * 1e3),
         },
+        "sweep": sweep,
         "decode": decode,
         "copy_calibration": copy_cal,
-        "sweep": sweep,
         "cpu_baseline": cpu,
+        # compact summaries last, so the end of the line carries them
+        "seven": seven,
+        "moe": moe,
+        "chain": chain,
     }
     print(json.dumps(out), flush=True)
 
 
-def serial_bound(sweep):
+def serial_bound(sweep, ar_us):
     """The 256 MiB All-Reduce against this run's own serial read + write
     bound.  An HBM channel's read and write time add up, so with t = bytes
-    read / read rate + bytes written / write rate, the cold Reduce-Scatter
-    (reads R*S, writes S) and the cold All-Gather (reads S, writes R*S)
-    together read and write (R+1)*S each, and the All-Reduce (2*R*S: R*S
-    each way) is bounded below by (t_RS + t_AG) * R / (R + 1)."""
-    cold = sweep.get("256MiB-bf16", {}).get("cold")
-    if not cold:
+    read / read rate + bytes written / write rate, a Reduce-Scatter (reads
+    R*S, writes S) and an All-Gather (reads S, writes R*S) together read and
+    write (R+1)*S each, and the All-Reduce (2*R*S: R*S each way) is bounded
+    below by (t_RS + t_AG) * R / (R + 1).  t_RS and t_AG are the fastest times
+    the run measured for them (in the step or cold), so the bound is the
+    tightest this run supports."""
+    c = sweep.get("256MiB-bf16")
+    if not c or "cold" not in c:
         return None
-    t_rs, t_ag, t_ar = (cold[k]["us"] for k in ("reduce_scatter", "all_gather", "all_reduce"))
+    t_rs = min(c["reduce_scatter"]["us"], c["cold"]["reduce_scatter"]["us"])
+    t_ag = min(c["all_gather"]["us"], c["cold"]["all_gather"]["us"])
     bound = (t_rs + t_ag) * R / (R + 1)
-    return {"model": "cold Reduce-Scatter + cold All-Gather of the same run, times R/(R+1)",
-            "bound_us": round(bound, 2), "all_reduce_cold_us": t_ar,
-            "frac_of_bound": round(bound / t_ar, 4),
+    t_ar = min(ar_us, c["cold"]["all_reduce"]["us"])
+    return {"model": "fastest Reduce-Scatter + fastest All-Gather of the same run (in-step or "
+                     "cold), times R/(R+1)",
+            "rs_us": t_rs, "ag_us": t_ag, "bound_us": round(bound, 2),
+            "all_reduce_us": round(t_ar, 2), "frac_of_bound": round(bound / t_ar, 4),
             "bound_frac_of_peak": round(2 * R * (256 << 20) / (bound * 1e-6) / 1e9 / PEAK_GBS, 4)}
+
+
+def _per_launch_us(torch, fn, iters):
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+
+
+def _back_to_back_us(torch, fn, iters):
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(iters):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t) * 1e6 / iters
+
+
+def decode_leg(args, torch, rrb, inputs, dev):
+    """The batch-1 decode All-Reduce (8 ranks x 4096 bf16) next to an empty
+    kernel: events around single host calls, host-issued back to back, and
+    replayed from a HIP graph."""
+    dec_host = inputs.decode_allreduce()
+    dins = [torch.from_numpy(h.view(np.int16)).to(dev) for h in dec_host]
+    douts = [torch.empty(4096, dtype=torch.int16, device=dev) for _ in range(R)]
+    dec_op = rrb.bound("all_reduce", dins, douts)
+    for _ in range(50):
+        dec_op()
+        rrb.empty_kernel()
+    torch.cuda.synchronize()
+    it = args.decode_iters
+    ar_ev = _per_launch_us(torch, dec_op, it)
+    em_ev = _per_launch_us(torch, rrb.empty_kernel, it)
+    g_ar = graph_us_per_launch(torch, dec_op)
+    g_em = graph_us_per_launch(torch, rrb.empty_kernel)
+    return {
+        "workload": "All-Reduce, 8 ranks x 4096 bf16 (TP=8 batch-1 decode, hidden 4096)",
+        "kernel": dec_op.kernels(),
+        "allreduce_graph_us": round(g_ar, 3),
+        "empty_kernel_graph_us": round(g_em, 3),
+        "graph_note": "64 launches captured in one HIP graph, replayed; us per launch",
+        "event_note": "event_us: events around one isolated host call (host launch latency "
+                      "included); back_to_back_us: host-issued calls in a loop; the kernel "
+                      "durations are in the rocprofv3 kernel trace",
+        "allreduce_event_us_p50": round(float(np.median(ar_ev)), 2),
+        "allreduce_event_us_p10": round(float(np.percentile(ar_ev, 10)), 2),
+        "allreduce_event_us_p90": round(float(np.percentile(ar_ev, 90)), 2),
+        "empty_kernel_event_us_p50": round(float(np.median(em_ev)), 2),
+        "allreduce_back_to_back_us": round(_back_to_back_us(torch, dec_op, it), 2),
+        "empty_back_to_back_us": round(_back_to_back_us(torch, rrb.empty_kernel, it), 2),
+    }
+
+
+SEVEN = ("all_reduce", "reduce_scatter", "all_gather", "all_to_all", "broadcast", "reduce", "gather")
+
+
+def seven_cases(torch, rrb, inputs, dev):
+    """The seven collectives at 8 x 16 MiB bf16, pre-bound: name -> (launch,
+    algorithmic bytes).  Roots: Broadcast 3, Reduce 0, Gather 5."""
+    S = 16 << 20
+    n = S // 2
+    c = n // R
+    full = [torch.from_numpy(x.view(np.int16)).to(dev) for x in inputs.sweep(16)]
+    shards = [x[:c].clone() for x in full]
+    outs = [torch.empty(n, dtype=torch.int16, device=dev) for _ in range(R)]
+    souts = [torch.empty(c, dtype=torch.int16, device=dev) for _ in range(R)]
+    return {
+        "all_reduce": (rrb.bound("all_reduce", full, outs), 2 * R * S),
+        "all_reduce_tree_order": (rrb.bound("all_reduce", full, outs, order="tree"), 2 * R * S),
+        "reduce_scatter": (rrb.bound("reduce_scatter", full, souts), (R + 1) * S),
+        "all_gather": (rrb.bound("all_gather", shards, outs), (R + 1) * S),
+        "all_to_all": (rrb.bound("all_to_all", full, outs), 2 * R * S),
+        "broadcast": (rrb.bound("broadcast", full, outs, 3), (R + 1) * S),
+        "reduce": (rrb.bound("reduce", full, outs, 0), (R + 1) * S),
+        "gather": (rrb.bound("gather", shards, outs, 5), 2 * S),
+    }
+
+
+def _graph_replay_ms(torch, fn, G, reps):
+    """fn captured G times in one HIP graph, replayed `reps` times; median ms
+    per launch (the graph is released before returning)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(G):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    ms = float(np.median(_events_ms(torch, g.replay, reps))) / G
+    torch.cuda.synchronize()
+    del g
+    return ms
+
+
+def seven_leg(args, torch, rrb, inputs, dev):
+    """Compact seven-collective figures: [us per launch replayed from a HIP
+    graph, GB/s, fraction of 8 TB/s]."""
+    cases = seven_cases(torch, rrb, inputs, dev)
+    res = {"workload": "8 ranks x 16 MiB bf16 N(0,1); Broadcast root 3, Reduce root 0, Gather root 5; "
+                       "[us per launch (20 launches per HIP graph, replayed), GB/s, frac of 8 TB/s]; "
+                       "cache-resident sizes"}
+    for name, (fn, b) in cases.items():
+        for _ in range(3):
+            fn()
+        ms = _graph_replay_ms(torch, fn, 20, 10)
+        res[name] = [round(ms * 1e3, 2), round(b / (ms * 1e-3) / 1e9, 1),
+                     round(b / (ms * 1e-3) / 1e9 / PEAK_GBS, 3)]
+    return res
+
+
+CHAIN_VARIANTS = ("barrier", "dual", "speculative", "twoshot", "lamport", "graph")
+
+
+def chain_leg(args, torch, rrb, inputs, dev, reps=10):
+    """The decode chain: for every b x h payload, us per All-Reduce of a
+    64-deep chain (median call time / 64) for every variant, and the
+    speculative variant's mis-speculation rate (failed validations per
+    validation: epochs x ranks x slices)."""
+    E = 64
+    res = {"workload": "64 back-to-back All-Reduces per call, 8 ranks, b x h bf16 N(0,0.02); "
+                       "us per All-Reduce", "cols": list(CHAIN_VARIANTS) + ["spec_misspec_rate"]}
+    for h in (4096, 8192):
+        for b in (1, 2, 4, 8, 16, 32, 64):
+            n = b * h
+            inp = torch.from_numpy(inputs.chain(E, R, n).view(np.int16)).to(dev)
+            out = torch.empty_like(inp)
+            row = []
+            rate = None
+            for v in CHAIN_VARIANTS:
+                ch = rrb.SnacChain(R, n, "bf16", v)
+                stats = torch.zeros(4, dtype=torch.int64, device=dev)
+                call = ch.bound(inp, out, stats)
+                for _ in range(3):
+                    call()
+                torch.cuda.synchronize()
+                stats.zero_()
+                ms = float(np.median(_events_ms(torch, call, reps)))
+                ch.check()
+                row.append(round(ms * 1e3 / E, 3))
+                if v == "speculative":
+                    st = stats.cpu().tolist()
+                    rate = round(st[0] / max(1, st[3]), 3)  # st[3]: epochs x ranks x slices
+                del call
+                ch.close()
+            res[f"b{b}h{h}"] = row + [rate]
+            del inp, out
+    return res
+
+
+def moe_leg(args, torch, rrb, inputs, dev, reps=20):
+    """MoE dispatch / combine at 4096 x 7168 bf16, 256 experts over 8 ranks,
+    top-8: [us (median of events around each call), GB/s, frac of 8 TB/s] for
+    host-built maps and for device-routed maps into one arena, and the
+    device routing time."""
+    T, h, E, k = 4096, 7168, 256, 8
+    idx, w = inputs.moe_routing(T, E, k)
+    shards = inputs.moe_tokens(T, h, R)
+    xs = [torch.from_numpy(x.reshape(-1).view(np.int16)).to(dev) for x in shards]
+    disp = rrb.MoePlan(R, h, E, idx, w, "dispatch")
+    comb = rrb.MoePlan(R, h, E, idx, w, "combine")
+    recv = [torch.empty(r * h, dtype=torch.int16, device=dev) for r in disp.rows_per_rank]
+    y = [torch.empty(T // R * h, dtype=torch.int16, device=dev) for _ in range(R)]
+    d_bytes = T * h * 2 * (1 + k)
+    c_bytes = T * h * 2 * (k + 1) + T * k * 8
+
+    def rate(ms, b):
+        return [round(ms * 1e3, 2), round(b / (ms * 1e-3) / 1e9, 1), round(b / (ms * 1e-3) / 1e9 / PEAK_GBS, 3)]
+
+    for _ in range(3):
+        disp.run(xs, recv)
+        comb.run(recv, y)
+    d_ms = float(np.median(_events_ms(torch, lambda: disp.run(xs, recv), reps)))
+    c_ms = float(np.median(_events_ms(torch, lambda: comb.run(recv, y), reps)))
+    ddisp = rrb.MoeDevicePlan(R, T, h, E, k, "dispatch")
+    dcomb = rrb.MoeDevicePlan(R, T, h, E, k, "combine", share=ddisp)
+    d_idx = torch.from_numpy(idx).to(dev)
+    d_w = torch.from_numpy(w).to(dev)
+    arena = torch.empty(T * k * h, dtype=torch.int16, device=dev)
+    none = [None] * (R - 1)
+    for _ in range(3):
+        ddisp.route(d_idx, d_w)
+        ddisp.run(xs, [arena] + none)
+        dcomb.run([arena] + none, y)
+    ddisp.check()
+    r_ms = float(np.median(_events_ms(torch, lambda: ddisp.route(d_idx, d_w), reps)))
+    dd_ms = float(np.median(_events_ms(torch, lambda: ddisp.run(xs, [arena] + none), reps)))
+    dc_ms = float(np.median(_events_ms(torch, lambda: dcomb.run([arena] + none, y), reps)))
+    return {"workload": "4096 tokens x 7168 bf16, 256 experts over 8 ranks, top-8; [us, GB/s, frac]",
+            "dispatch": rate(d_ms, d_bytes), "combine": rate(c_ms, c_bytes),
+            "dispatch_arena": rate(dd_ms, d_bytes), "combine_arena": rate(dc_ms, c_bytes),
+            "route_us": round(r_ms * 1e3, 2)}
 
 
 def graph_us_per_launch(torch, fn, per_graph=64, replays=50):
@@ -398,7 +572,10 @@ def bench_chain(args, dev):
                 st = stats.cpu().tolist()
                 res[v] = {"us_per_allreduce": round(float(np.median(ms)) * 1e3 / E, 3),
                           "misspec_per_call": round(st[0] / max(5, args.steps), 2),
-                          "retries_per_call": round(st[1] / max(5, args.steps), 2)}
+                          "retries_per_call": round(st[1] / max(5, args.steps), 2),
+                          "misspec_rate": round(st[0] / max(1, st[3]), 3)}
+                del call
+                ch.close()  # HIP objects released here, not at interpreter exit
             ops = [rrb.bound("all_reduce", [inp[e, r] for r in range(R)],
                              [out[e, r] for r in range(R)]) for e in range(E)]
 
@@ -444,6 +621,8 @@ def bench_chain(args, dev):
             ch.check()
             res[v] = {"us_per_collective": round(float(np.median(ms)) * 1e3 / E, 3),
                       "misspec_per_call": round(stats[0].item() / max(5, args.steps), 2)}
+            del call
+            ch.close()
         plan_rows[name] = res
         log(json.dumps({name: res}))
     print(json.dumps({"metric": "us per All-Reduce in a 64-deep decode chain", "unit": "us",
@@ -524,25 +703,7 @@ def bench_seven(args, dev):
     import torch
     import reduce_rank_buffers_amd as rrb
     from reduce_rank_buffers_amd import inputs
-    S = 16 << 20
-    n = S // 2
-    c = n // R
-    full = [torch.from_numpy(x.view(np.int16)).to(dev) for x in inputs.sweep(16)]
-    shards = [x[:c].clone() for x in full]
-    outs = [torch.empty(n, dtype=torch.int16, device=dev) for _ in range(R)]
-    souts = [torch.empty(c, dtype=torch.int16, device=dev) for _ in range(R)]
-    # pre-bound launches (plan, pointers and entry point resolved once), so
-    # the timed region holds the kernels, not Python argument marshalling
-    cases = {
-        "all_reduce": (rrb.bound("all_reduce", full, outs), 2 * R * S),
-        "all_reduce_tree_order": (rrb.bound("all_reduce", full, outs, order="tree"), 2 * R * S),
-        "reduce_scatter": (rrb.bound("reduce_scatter", full, souts), (R + 1) * S),
-        "all_gather": (rrb.bound("all_gather", shards, outs), (R + 1) * S),
-        "all_to_all": (rrb.bound("all_to_all", full, outs), 2 * R * S),
-        "broadcast": (rrb.bound("broadcast", full, outs, 3), (R + 1) * S),
-        "reduce": (rrb.bound("reduce", full, outs, 0), (R + 1) * S),
-        "gather": (rrb.bound("gather", shards, outs, 5), 2 * S),
-    }
+    cases = seven_cases(torch, rrb, inputs, dev)
     # Two timings per collective: G launches captured in one HIP graph and
     # replayed (us per launch, no host gaps: the GB/s figure), and events
     # around one host-issued launch (event_us, host launch gaps included).
@@ -552,17 +713,7 @@ def bench_seven(args, dev):
         for _ in range(3):
             fn()
         ev_ms = float(np.median(_events_ms(torch, fn, max(10, args.steps))))
-        side = torch.cuda.Stream()
-        with torch.cuda.stream(side):
-            fn()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(G):
-                fn()
-        g.replay()
-        torch.cuda.synchronize()
-        ms = float(np.median(_events_ms(torch, g.replay, max(10, args.steps)))) / G
+        ms = _graph_replay_ms(torch, fn, G, max(10, args.steps))
         res[name] = {"us": round(ms * 1e3, 2), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
                      "frac": round(b / (ms * 1e-3) / 1e9 / PEAK_GBS, 4), "bytes": b,
                      "event_us": round(ev_ms * 1e3, 2)}

@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define RRB_ABI_VERSION 1
+#define RRB_ABI_VERSION 2
 #define RRB_MAX_RANKS 16
 
 typedef int32_t rrb_status;
@@ -191,9 +191,12 @@ rrb_status rrb_plan_create_rows_device(int32_t nranks, int64_t tokens, int64_t h
  * (int32) and d_topk_w[tokens][topk] (float32), device arrays: expert
  * histogram, prefix offsets and the per-token slot list in ascending expert
  * id.  d_rank_offsets (nullable, nranks+1 int32, device) receives the arena
- * row where each rank's region starts, then tokens*topk.  Out-of-range or
- * repeated experts are skipped (their slots point at arena row 0, weight 0)
- * and recorded for rrb_moe_route_check.  Asynchronous; deterministic.  When
+ * row where each rank's region starts, then tokens*topk.  An out-of-range or
+ * repeated expert is recorded in the workspace's routing status, which
+ * rrb_moe_route_check reports; while it is set, rrb_copy and rrb_reduce on
+ * every device plan bound to that workspace write nothing (no valid row is
+ * overwritten), until an rrb_moe_route without errors (or a rebind) clears
+ * it.  Asynchronous; deterministic.  When
  * every block of 256 tokens fits on the device at once, one kernel with a
  * bounded grid barrier builds the maps; if other work keeps that grid apart,
  * the barrier wait runs out and rrb_moe_route_check reports RRB_ETIMEOUT
@@ -255,9 +258,28 @@ rrb_status rrb_copy(rrb_plan_t plan, const void *const *d_in,
  * RRB_REDUCE_SUM_TREE).  Elementwise fold in the plan's order with fp32
  * accumulation and one round-to-nearest-even to bf16 (the result is
  * bit-identical in every output that receives it).
+ * d_weights (nullable, device, float32, 4-byte aligned): per-call combine
+ * weights for an MoE combine plan, [tokens][topk] in the column order of the
+ * routing arrays the plan was built from (topk_idx of rrb_plan_create_rows,
+ * or d_topk_idx of the last rrb_moe_route for a device plan): the weight of
+ * token t's expert topk_idx[t][j] is d_weights[t * topk + j].  They replace
+ * the weights bound to the plan for this call only; NULL uses the plan's
+ * (topk_w at creation, or d_topk_w at the last route).  The fold order stays
+ * ascending expert id.  A layout-named reduce is an unweighted sum:
+ * d_weights must be NULL for uniform plans (RRB_EINVAL otherwise).  The
+ * buffer must stay valid until the launch completes.
  */
 rrb_status rrb_reduce(rrb_plan_t plan, const void *const *d_in,
-                      void *const *d_out, rrb_stream_t stream);
+                      void *const *d_out, const float *d_weights,
+                      rrb_stream_t stream);
+
+/* Introspection: the kernel launches rrb_copy / rrb_reduce would issue for a
+ * layout-named plan with these buffers (nothing is launched), as text --
+ * "kernel<template arguments> grid=G block=B", several separated by "; " --
+ * written NUL-terminated into buf (host, cap bytes, truncated to fit).
+ * Errors: RRB_EINVAL, RRB_EUNSUPPORTED for MoE row plans, RRB_ENOMEM. */
+rrb_status rrb_plan_launch_info(rrb_plan_t plan, const void *const *d_in,
+                                void *const *d_out, char *buf, int32_t cap);
 
 /* Launch an empty kernel (one workgroup) on `stream`: the launch floor that
  * decode-size collectives are measured against. */
@@ -276,10 +298,16 @@ rrb_status rrb_empty_kernel(rrb_stream_t stream);
  *   0                          top barrier + bottom barrier, one buffer
  *   RRB_SNAC_DUAL_BUFFER       two staging buffers by epoch parity; the
  *                              bottom barrier is dropped
- *   | RRB_SNAC_SPECULATIVE     (with DUAL_BUFFER) no top barrier: read first,
- *                              then check the reduced validation flag
- *                              (sum of the R flags == R * epoch) and retry on
- *                              mismatch (SiFAR review, Fig. 14)
+ *   | RRB_SNAC_SPECULATIVE     (with DUAL_BUFFER) no top barrier: one read of
+ *                              the R sources' flags, then the payload is read
+ *                              whatever they said, and the reduced validation
+ *                              flag (sum of the R flags == R * epoch) decides
+ *                              (SiFAR review, Fig. 14); on a mismatch only the
+ *                              stale sources are waited for and read again.
+ *                              The payload loads are issued after the flag
+ *                              values have returned, so the check holds under
+ *                              any order in which the memory system serves
+ *                              the loads.
  *   RRB_SNAC_TWOSHOT | DUAL    twoshot (SiFAR review, Fig. 6): stage, then each
  *                              rank reduces chunk r of the payload over all
  *                              ranks, then every rank gathers the R reduced
@@ -325,9 +353,12 @@ rrb_status rrb_empty_kernel(rrb_stream_t stream);
 typedef struct rrb_snac_s *rrb_snac_t;
 
 /* Device-side counters a chain call may accumulate into (zeroed by the
- * caller).  misspec: validations that failed; retries: slice re-reads;
- * timeouts: bounded waits that expired; epochs: epochs completed (per rank
- * and slice, summed). */
+ * caller).  misspec: speculative validations that failed; retries: stale
+ * sources re-read after a failed validation (All-Reduce chains: source
+ * slices; plan chains: source ranks whose entries were redone), or for
+ * RRB_SNAC_LAMPORT poll rounds that found an untagged word; timeouts:
+ * bounded waits that expired; epochs: epochs completed (per rank and slice,
+ * summed). */
 typedef struct {
   unsigned long long misspec;
   unsigned long long retries;
@@ -370,10 +401,11 @@ rrb_status rrb_snac_allreduce_chain(rrb_snac_t h, int32_t epochs,
  * so the plan may be destroyed afterwards).  Every map entry must start, end
  * and sit on 16-byte boundaries, and every rank's input must be a 16-byte
  * multiple (RRB_EUNSUPPORTED otherwise).  flags: 0 (top and bottom barrier),
- * RRB_SNAC_DUAL_BUFFER, RRB_SNAC_DUAL_BUFFER | RRB_SNAC_SPECULATIVE (flags
- * read first, whole consume, then the reduced check of the workgroup's
- * listed flags), or RRB_SNAC_GRAPH (one Atom launch per epoch in a cached
- * HIP graph).  Workgroup (r, s) stages slice s of rank r's input and
+ * RRB_SNAC_DUAL_BUFFER, RRB_SNAC_DUAL_BUFFER | RRB_SNAC_SPECULATIVE (one
+ * read of the workgroup's listed flags, the whole consume once their values
+ * have returned, then the reduced check; on a mismatch it waits for the list
+ * and redoes only the map entries that read a rank whose flag was stale), or
+ * RRB_SNAC_GRAPH (one Atom launch per epoch in a cached HIP graph).  Workgroup (r, s) stages slice s of rank r's input and
  * computes piece s of every map entry whose output is rank r; it waits on a
  * list of flags built at create time: the staged slices its pieces read and
  * the workgroups that read its own slice.  slices = 0 gives each workgroup

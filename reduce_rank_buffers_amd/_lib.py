@@ -44,7 +44,7 @@ EXPORTS = (
     "rrb_plan_create", "rrb_plan_create_rows", "rrb_plan_create_rows_device", "rrb_moe_route",
     "rrb_moe_route_check", "rrb_plan_query", "rrb_plan_bind",
     "rrb_plan_segments", "rrb_plan_destroy",
-    "rrb_copy", "rrb_reduce", "rrb_empty_kernel",
+    "rrb_copy", "rrb_reduce", "rrb_plan_launch_info", "rrb_empty_kernel",
     "rrb_snac_create", "rrb_snac_workspace", "rrb_snac_bind", "rrb_snac_allreduce_chain",
     "rrb_snac_create_plan", "rrb_snac_strides", "rrb_snac_chain",
     "rrb_snac_check", "rrb_snac_destroy",
@@ -99,7 +99,8 @@ _SIGS = {
     "rrb_plan_segments": (_I32, [_P, ctypes.POINTER(Segment), _I32, ctypes.POINTER(_I32)]),
     "rrb_plan_destroy": (None, [_P]),
     "rrb_copy": (_I32, [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), _P]),
-    "rrb_reduce": (_I32, [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), _P]),
+    "rrb_reduce": (_I32, [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), _P, _P]),
+    "rrb_plan_launch_info": (_I32, [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.c_char_p, _I32]),
     "rrb_empty_kernel": (_I32, [_P]),
     "rrb_snac_create": (_I32, [_I32, _I64, _I32, _U32, _I32, ctypes.POINTER(_P)]),
     "rrb_snac_workspace": (_I32, [_P, ctypes.POINTER(_SZ)]),

@@ -1,16 +1,83 @@
 """Torch-facing binding of librrb: plans, Atom copy / reduce, MoE, SNAC chain.
 
 PyTorch supplies device memory and the current stream; every step of the
-datapath runs in librrb's HIP kernels.  Tensors are passed by pointer; bf16
-data may be any 2-byte tensor (torch.bfloat16, int16, uint16 views), fp32 data
-any 4-byte tensor.
+datapath runs in librrb's HIP kernels.  Tensors are passed by pointer after
+the checks below; bf16 data is a torch.bfloat16 tensor or an int16 / uint16
+view of bf16 bit patterns, fp32 data a torch.float32 tensor.  Every tensor
+must be contiguous, on the current GPU, and hold at least the elements the
+plan or chain reads or writes there; anything else raises ValueError before
+the library is called (an undersized or strided buffer would otherwise become
+an out-of-bounds device access).
 """
 
 import ctypes
+import sys
 
 import torch
 
 from . import _lib as L
+
+# Element types each library dtype accepts.
+_BF16_TYPES = tuple(t for t in (torch.bfloat16, torch.int16, getattr(torch, "uint16", None))
+                    if t is not None)
+_F32_TYPES = (torch.float32,)
+
+
+def _accepts(dtype_code):
+    return _BF16_TYPES if dtype_code == L.RRB_BF16 else _F32_TYPES
+
+
+def _on_gpu(t, what):
+    if t.device.type != "cuda" or t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{what}: tensor on {t.device}, not on the current GPU")
+
+
+def _check_tensor(t, what, dtype_code, min_elems):
+    """Raise ValueError unless `t` is a contiguous tensor of the library dtype
+    with at least `min_elems` elements (the device is checked separately)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{what}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.dtype not in _accepts(dtype_code):
+        names = "bfloat16, int16 or uint16" if dtype_code == L.RRB_BF16 else "float32"
+        raise ValueError(f"{what}: dtype {t.dtype} is not {names}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: tensor is not contiguous")
+    if t.numel() < min_elems:
+        raise ValueError(f"{what}: {t.numel()} elements, at least {min_elems} needed")
+
+
+def _check_rank_list(tensors, R, counts, dtype_code, what):
+    """Per-rank buffers: at most R entries; entry r is required (and sized)
+    when counts[r] > 0 and may be None otherwise.  Returns the tensors given."""
+    if tensors is None or len(tensors) > R:
+        raise ValueError(f"{what}: expected a list of at most {R} tensors")
+    given = []
+    for r in range(R):
+        t = tensors[r] if r < len(tensors) else None
+        if counts[r] > 0 and t is None:
+            raise ValueError(f"{what}[{r}]: rank {r} needs a buffer of {counts[r]} elements")
+        if t is not None:
+            _check_tensor(t, f"{what}[{r}]", dtype_code, counts[r])
+            given.append((t, f"{what}[{r}]"))
+    return given
+
+
+def _check_aux(t, what, dtypes, min_elems):
+    """An optional auxiliary array (stats, stagger, routing); returns it with
+    its name for the device check, or nothing when absent."""
+    if t is None:
+        return []
+    if not isinstance(t, torch.Tensor) or t.dtype not in dtypes:
+        raise ValueError(f"{what}: expected a tensor of {' or '.join(map(str, dtypes))}")
+    if not t.is_contiguous() or t.numel() < min_elems:
+        raise ValueError(f"{what}: expected a contiguous tensor of at least {min_elems} elements")
+    return [(t, what)]
+
+
+def _all_on_gpu(checked):
+    for t, what in checked:
+        _on_gpu(t, what)
+
 
 # layout kinds, for collective()
 PARTIAL = L.RRB_PARTIAL
@@ -114,17 +181,41 @@ class Plan:
                                             self.workspace_bytes, _stream(stream)), "rrb_plan_bind")
         return self
 
-    def run(self, ins, outs, stream=None):
-        """Atom copy or reduce, whichever the plan names, on torch's stream."""
-        fn = self._lib.rrb_copy if self.op == L.RRB_COPY else self._lib.rrb_reduce
-        L.check(fn(self.handle, _ptrs(ins, self.nranks), _ptrs(outs, self.nranks), _stream(stream)),
-                "rrb_copy" if self.op == L.RRB_COPY else "rrb_reduce")
+    def check_buffers(self, ins, outs):
+        """ValueError unless ins / outs fit the plan (see the module doc)."""
+        _all_on_gpu(_check_rank_list(ins, self.nranks, self.in_count, self.dtype, "ins") +
+                    _check_rank_list(outs, self.nranks, self.out_count, self.dtype, "outs"))
 
-    def __del__(self):
+    def run(self, ins, outs, stream=None, weights=None):
+        """Atom copy or reduce, whichever the plan names, on torch's stream.
+        weights: MoE combine plans only, float32 [tokens, topk] in the
+        routing order (replaces the plan's weights for this call)."""
+        if weights is not None and getattr(self, "tk", None) is None:
+            raise ValueError("weights apply to MoE combine plans only")
+        self.check_buffers(ins, outs)
+        if self.op == L.RRB_COPY:
+            L.check(self._lib.rrb_copy(self.handle, _ptrs(ins, self.nranks), _ptrs(outs, self.nranks),
+                                       _stream(stream)), "rrb_copy")
+            return
+        wp = None
+        if weights is not None:
+            rows = getattr(self, "tk", None)
+            if rows is None:
+                raise ValueError("weights apply to MoE combine plans only")
+            _all_on_gpu(_check_aux(weights, "weights", _F32_TYPES, rows))
+            wp = weights.data_ptr()
+        L.check(self._lib.rrb_reduce(self.handle, _ptrs(ins, self.nranks), _ptrs(outs, self.nranks),
+                                     wp, _stream(stream)), "rrb_reduce")
+
+    def close(self):
+        """Release the library handle now (also done when the object is collected)."""
         h = getattr(self, "handle", None)
         if h is not None and h.value:
             self._lib.rrb_plan_destroy(h)
-            self.handle = None
+        self.handle = None
+
+    def __del__(self):
+        self.close()  # host memory only: safe at interpreter exit
 
 
 _PLANS = {}
@@ -140,7 +231,14 @@ def plan(nranks, count, dtype, in_layout, out_layout, op):
 
 
 def _dtype_of(t):
-    return L.RRB_F32 if t.element_size() == 4 else L.RRB_BF16
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"expected a torch.Tensor, got {type(t).__name__}")
+    if t.dtype in _BF16_TYPES:
+        return L.RRB_BF16
+    if t.dtype in _F32_TYPES:
+        return L.RRB_F32
+    raise ValueError(f"dtype {t.dtype} is neither bf16 (bfloat16 / int16 / uint16 bit patterns) "
+                     "nor float32")
 
 
 def collective(in_layout, out_layout, op, ins, outs, count, stream=None):
@@ -159,8 +257,15 @@ class Bound:
     __slots__ = ("_fn", "_h", "_in", "_out", "_keep", "_name")
 
     def __init__(self, p, ins, outs):
-        self._fn = p._lib.rrb_copy if p.op == L.RRB_COPY else p._lib.rrb_reduce
-        self._name = "rrb_copy" if p.op == L.RRB_COPY else "rrb_reduce"
+        p.check_buffers(ins, outs)
+        if p.op == L.RRB_COPY:
+            fn = p._lib.rrb_copy
+            self._fn = lambda h, i, o, s: fn(h, i, o, s)
+            self._name = "rrb_copy"
+        else:
+            fn = p._lib.rrb_reduce
+            self._fn = lambda h, i, o, s: fn(h, i, o, None, s)
+            self._name = "rrb_reduce"
         self._h = p.handle
         self._in = _ptrs(ins, p.nranks)
         self._out = _ptrs(outs, p.nranks)
@@ -171,6 +276,10 @@ class Bound:
                       torch.cuda.current_stream().cuda_stream if stream is None else stream.cuda_stream)
         if st:
             L.check(st, self._name)
+
+    def kernels(self):
+        """The kernel launches this call issues, as the library names them."""
+        return launch_info(self._keep[0], self._keep[1], self._keep[2])
 
 
 def bound(name, ins, outs, root=None, order="fixed"):
@@ -230,6 +339,15 @@ def gather(ins, outs, root, stream=None):
     return collective(SHARD, ROOT(root), "copy", ins, outs, ins[0].numel() * len(ins), stream)
 
 
+def launch_info(p, ins, outs):
+    """The launches rrb_copy / rrb_reduce would issue for plan `p` on these
+    buffers, as the library names them (nothing is launched)."""
+    buf = ctypes.create_string_buffer(1024)
+    L.check(p._lib.rrb_plan_launch_info(p.handle, _ptrs(ins, p.nranks), _ptrs(outs, p.nranks), buf,
+                                        len(buf)), "rrb_plan_launch_info")
+    return buf.value.decode()
+
+
 def empty_kernel(stream=None):
     L.check(L.lib().rrb_empty_kernel(_stream(stream)), "rrb_empty_kernel")
 
@@ -259,6 +377,7 @@ class MoePlan(Plan):
         self._query()
         self.rows_per_rank = [(c if d == L.RRB_MOE_DISPATCH else i) // self.hidden
                               for i, c in zip(self.in_count, self.out_count)]
+        self.tk = int(T) * int(k) if d == L.RRB_MOE_COMBINE else None
         self.bind(device)
 
 
@@ -283,6 +402,7 @@ class MoeDevicePlan(Plan):
         self.op = L.RRB_COPY if d == L.RRB_MOE_DISPATCH else L.RRB_REDUCE_SUM
         self.dtype = L.RRB_BF16
         self.tokens, self.hidden, self.experts, self.topk = int(tokens), int(hidden), int(experts), int(topk)
+        self.tk = self.tokens * self.topk if d == L.RRB_MOE_COMBINE else None
         self._ws = None
         self._query()
         if share is not None:
@@ -295,6 +415,12 @@ class MoeDevicePlan(Plan):
 
     def route(self, topk_idx, topk_w, rank_offsets=None, stream=None):
         """topk_idx int32 [T, k], topk_w float32 [T, k]: device tensors."""
+        n = self.tokens * self.topk
+        if topk_idx is None or topk_w is None:
+            raise ValueError("topk_idx and topk_w are required")
+        _all_on_gpu(_check_aux(topk_idx, "topk_idx", (torch.int32,), n) +
+                    _check_aux(topk_w, "topk_w", _F32_TYPES, n) +
+                    _check_aux(rank_offsets, "rank_offsets", (torch.int32,), self.nranks + 1))
         L.check(self._lib.rrb_moe_route(
             self.handle, ctypes.c_void_p(topk_idx.data_ptr()), ctypes.c_void_p(topk_w.data_ptr()),
             ctypes.c_void_p(rank_offsets.data_ptr() if rank_offsets is not None else 0),
@@ -328,6 +454,8 @@ class SnacChain:
         self.nranks = int(nranks)
         self.count = int(count)
         self.variant = variant
+        self.dtype = _dtype_code(dtype)
+        self.strides = (self.count, self.count)  # elements per rank in d_in / d_out
         ws = ctypes.c_size_t()
         L.check(self._lib.rrb_snac_workspace(h, ctypes.byref(ws)), "rrb_snac_workspace")
         dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
@@ -336,8 +464,25 @@ class SnacChain:
         L.check(self._lib.rrb_snac_bind(h, ctypes.c_void_p(base), ws.value, _stream(stream)),
                 "rrb_snac_bind")
 
+    def check_buffers(self, inp, out, stats=None, stagger=None):
+        """ValueError unless inp is [epochs, R, in_stride], out is [epochs, R,
+        out_stride] (elements), stats an int64[4] and stagger an int32[R]."""
+        R = self.nranks
+        checked = []
+        for t, what, n in ((inp, "inp", self.strides[0]), (out, "out", self.strides[1])):
+            if not isinstance(t, torch.Tensor) or t.dim() != 3 or t.shape[1] != R or t.shape[2] != n:
+                raise ValueError(f"{what}: expected a tensor of shape [epochs, {R}, {n}]")
+            _check_tensor(t, what, self.dtype, 0)
+            checked.append((t, what))
+        if inp.shape[0] != out.shape[0]:
+            raise ValueError("inp and out hold different numbers of epochs")
+        checked += _check_aux(stats, "stats", (torch.int64,), 4)
+        checked += _check_aux(stagger, "stagger", (torch.int32,), R)
+        _all_on_gpu(checked)
+
     def run(self, inp, out, stats=None, stagger=None, spin_limit=0, stream=None):
         """inp, out: [epochs, R, count] device tensors; stats: int64[4] device tensor."""
+        self.check_buffers(inp, out, stats, stagger)
         E = inp.shape[0]
         L.check(self._lib.rrb_snac_allreduce_chain(
             self.handle, int(E), ctypes.c_void_p(inp.data_ptr()), ctypes.c_void_p(out.data_ptr()),
@@ -349,6 +494,7 @@ class SnacChain:
     def bound(self, inp, out, stats=None):
         """The chain call with its arguments marshalled once: calling the
         result runs `inp.shape[0]` epochs on torch's current stream."""
+        self.check_buffers(inp, out, stats)
         fn = self._lib.rrb_snac_chain
         args = (self.handle, ctypes.c_int32(int(inp.shape[0])), ctypes.c_void_p(inp.data_ptr()),
                 ctypes.c_void_p(out.data_ptr()),
@@ -366,11 +512,19 @@ class SnacChain:
     def check(self, stream=None):
         L.check(self._lib.rrb_snac_check(self.handle, _stream(stream)), "rrb_snac_check")
 
-    def __del__(self):
+    def close(self):
+        """Destroy the library handle now (a graph-mode handle releases its
+        HIP graph here).  Call it before the interpreter exits: collection
+        at exit skips the destroy, since the HIP runtime may already be gone."""
         h = getattr(self, "handle", None)
         if h is not None and h.value:
             self._lib.rrb_snac_destroy(h)
-            self.handle = None
+        self.handle = None
+
+    def __del__(self):
+        if sys.is_finalizing():
+            return
+        self.close()
 
 
 PLAN_CHAIN_VARIANTS = {"barrier": 0, "dual": L.RRB_SNAC_DUAL_BUFFER,
@@ -395,6 +549,7 @@ class SnacPlanChain(SnacChain):
         self.handle = h
         self.nranks = plan.nranks
         self.variant = variant
+        self.dtype = plan.dtype
         self.esize = 4 if plan.dtype == L.RRB_F32 else 2
         si, so = ctypes.c_int64(), ctypes.c_int64()
         L.check(self._lib.rrb_snac_strides(h, ctypes.byref(si), ctypes.byref(so)), "rrb_snac_strides")
@@ -409,6 +564,7 @@ class SnacPlanChain(SnacChain):
 
     def run(self, inp, out, stats=None, stagger=None, spin_limit=0, stream=None):
         """inp: [epochs, R, in_stride], out: [epochs, R, out_stride] device tensors."""
+        self.check_buffers(inp, out, stats, stagger)
         E = inp.shape[0]
         L.check(self._lib.rrb_snac_chain(
             self.handle, int(E), ctypes.c_void_p(inp.data_ptr()), ctypes.c_void_p(out.data_ptr()),

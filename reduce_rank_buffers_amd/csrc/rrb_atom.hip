@@ -16,7 +16,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdio>
 #include <cstring>
+#include <string>
 
 #include "rrb_internal.h"
 #include "rrb_kernels.h"
@@ -603,7 +605,8 @@ struct Emitter {
   hipStream_t stream = nullptr;
   std::vector<LaunchDesc> *descs = nullptr;
   template <class Args>
-  rrb_status operator()(void (*kern)(Args), dim3 grid, dim3 block, const Args &a, const char *what) {
+  rrb_status operator()(void (*kern)(Args), dim3 grid, dim3 block, const Args &a, const char *what,
+                        const std::string &name) {
     if (descs) {
       LaunchDesc d;
       d.func = reinterpret_cast<const void *>(kern);
@@ -611,6 +614,7 @@ struct Emitter {
       d.block = block;
       d.args.assign(reinterpret_cast<const unsigned char *>(&a),
                     reinterpret_cast<const unsigned char *>(&a) + sizeof a);
+      d.name = name;
       descs->push_back(std::move(d));
       return RRB_OK;
     }
@@ -654,7 +658,12 @@ rrb_status launch_one(const Plan &p, const void *const *in, void *const *out, Em
                        : reduce_one_for<false, true, true>(p.nranks))
                : (bf16 ? reduce_one_for<true, false, true>(p.nranks)
                        : reduce_one_for<false, false, true>(p.nranks));
-  return emit(kern, dim3(grid), dim3(kOneBlock), a, reduce ? "reduce" : "copy");
+  std::string name;  // built only when describing, not on the launch path
+  if (emit.descs)
+    name = !reduce ? std::string("copy_one_kernel")
+                   : std::string(tree ? "reduce_tree_one_kernel<" : "reduce_one_kernel<") +
+                         std::to_string(p.nranks) + (bf16 ? ",bf16" : ",f32") + (all ? ",all>" : ",list>");
+  return emit(kern, dim3(grid), dim3(kOneBlock), a, reduce ? "reduce" : "copy", name);
 }
 
 rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out,
@@ -689,6 +698,11 @@ rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out
   int bs;
   int U;
   void (*kern)(UniArgs) = nullptr;
+  // Kernel name for introspection, built only when describing.
+  std::string name;
+  const bool named = emit.descs != nullptr;
+  const std::string R_ = named ? std::to_string(p.nranks) : std::string(),
+                    dt = named ? (bf16 ? "bf16" : "f32") : "";
   if (vec) {
     a.nvec = (len * esz) / 16;
     a.tail = reduce ? (len - a.nvec * (16 / esz)) : ((len * esz - a.nvec * 16) / 2);
@@ -718,15 +732,20 @@ rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out
                                      : reduce_tree_vec_for<false, true, false>(p.nranks)))
                       : (bf16 ? reduce_tree_vec_for<true, false, false>(p.nranks)
                               : reduce_tree_vec_for<false, false, false>(p.nranks));
+        if (named) name = "reduce_tree_vec_kernel<" + R_ + "," + dt + (stream ? ",nt-load" : "") +
+               (stream && fan ? ",nt-store>" : ">");
       } else if (stream && !fan) {
         kern = reduce_wt_pick(U, bf16, p.nranks);
+        if (named) name = "reduce_wt_kernel<" + R_ + "," + std::to_string(U) + "," + dt + ">";
       } else if (stream) {
         kern = reduce_vec_pick<true, true>(U, bf16, p.nranks);
+        if (named) name = "reduce_vec_kernel<" + R_ + "," + std::to_string(U) + "," + dt + ",nt-load,nt-store>";
       } else {
         // Below the streaming threshold a launch has under 2 M vectors, so
         // one vector per lane.
         kern = bf16 ? reduce_vec_for<1, true, false, false>(p.nranks)
                     : reduce_vec_for<1, false, false, false>(p.nranks);
+        if (named) name = "reduce_vec_kernel<" + R_ + ",1," + dt + ">";
       }
     } else {
       // Streaming copies: one vector per lane on 128-lane workgroups (the
@@ -751,6 +770,10 @@ rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out
              : U == 1             ? copy_wt_kernel<1>
              : U == 2             ? copy_wt_kernel<2>
                                   : copy_wt_kernel<4>;
+      if (named) name = stream ? "copy_vec_kernel<1,nt-store>"
+             : split ? "copy_split_kernel"
+             : (small && fan_any) ? "copy_vec_kernel<1>"
+                                  : "copy_wt_kernel<" + std::to_string(U) + ">";
       if (stream || single) bs = 128;
     }
     const int64_t per_tile = static_cast<int64_t>(bs) * U;
@@ -767,6 +790,7 @@ rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out
     kern = !reduce ? copy_elem_kernel
            : tree  ? (bf16 ? reduce_tree_elem_kernel<true> : reduce_tree_elem_kernel<false>)
                    : (bf16 ? reduce_elem_kernel<true> : reduce_elem_kernel<false>);
+    if (named) name = !reduce ? "copy_elem_kernel" : (tree ? "reduce_tree_elem_kernel<" : "reduce_elem_kernel<") + dt + ">";
     // the element copy moves 2-byte units
     if (!reduce) a.nelem = len * esz / 2;
     a.tiles = static_cast<int32_t>((a.nelem + bs - 1) / bs);
@@ -786,7 +810,7 @@ rrb_status launch_uniform(const Plan &p, const void *const *in, void *const *out
     }
     const unsigned grid = static_cast<unsigned>(cnt) * static_cast<unsigned>(a.tiles) *
                           static_cast<unsigned>(kern == copy_split_kernel ? a.fan : 1);
-    const rrb_status st = emit(kern, dim3(grid), dim3(bs), a, reduce ? "reduce" : "copy");
+    const rrb_status st = emit(kern, dim3(grid), dim3(bs), a, reduce ? "reduce" : "copy", name);
     if (st != RRB_OK) return st;
   }
   return RRB_OK;
@@ -822,21 +846,51 @@ rrb_status rrb_copy(rrb_plan_t plan, const void *const *d_in, void *const *d_out
   if (p.op != RRB_COPY) return fail(RRB_EINVAL, "rrb_copy needs a copy plan");
   rrb_status s = check_buffers(p, d_in, d_out);
   if (s != RRB_OK) return s;
-  if (p.kind != PlanKind::Uniform) return launch_rows(p, d_in, d_out, stream);
+  if (p.kind != PlanKind::Uniform) return launch_rows(p, d_in, d_out, nullptr, stream);
   return launch_uniform_on(p, d_in, d_out, static_cast<hipStream_t>(stream));
 }
 
 rrb_status rrb_reduce(rrb_plan_t plan, const void *const *d_in, void *const *d_out,
-                      rrb_stream_t stream) {
+                      const float *d_weights, rrb_stream_t stream) {
   clear_error();
   if (!plan) return fail(RRB_EINVAL, "NULL plan");
   const Plan &p = plan->p;
   if (p.op != RRB_REDUCE_SUM && p.op != RRB_REDUCE_SUM_TREE)
     return fail(RRB_EINVAL, "rrb_reduce needs a reduce plan");
+  if (d_weights && p.kind == PlanKind::Uniform)
+    return fail(RRB_EINVAL, "weights apply to MoE combine plans only (a layout-named reduce is an "
+                            "unweighted sum)");
+  if (d_weights && (reinterpret_cast<uintptr_t>(d_weights) & 3))
+    return fail(RRB_EINVAL, "weights must be 4-byte aligned");
   rrb_status s = check_buffers(p, d_in, d_out);
   if (s != RRB_OK) return s;
-  if (p.kind != PlanKind::Uniform) return launch_rows(p, d_in, d_out, stream);
+  if (p.kind != PlanKind::Uniform) return launch_rows(p, d_in, d_out, d_weights, stream);
   return launch_uniform_on(p, d_in, d_out, static_cast<hipStream_t>(stream));
+}
+
+rrb_status rrb_plan_launch_info(rrb_plan_t plan, const void *const *d_in, void *const *d_out,
+                                char *buf, int32_t cap) {
+  clear_error();
+  if (!plan || !buf || cap < 1) return fail(RRB_EINVAL, "NULL plan or buffer");
+  buf[0] = 0;
+  const Plan &p = plan->p;
+  if (p.kind != PlanKind::Uniform) return fail(RRB_EUNSUPPORTED, "launch info covers layout-named plans");
+  rrb_status s = check_buffers(p, d_in, d_out);
+  if (s != RRB_OK) return s;
+  std::string text;
+  try {
+    std::vector<LaunchDesc> descs;
+    s = describe_uniform(p, d_in, d_out, descs);
+    if (s != RRB_OK) return s;
+    for (const LaunchDesc &d : descs) {
+      if (!text.empty()) text += "; ";
+      text += d.name + " grid=" + std::to_string(d.grid.x) + " block=" + std::to_string(d.block.x);
+    }
+  } catch (const std::bad_alloc &) {
+    return fail(RRB_ENOMEM, "launch description allocation failed");
+  }
+  std::snprintf(buf, static_cast<size_t>(cap), "%s", text.c_str());
+  return RRB_OK;
 }
 
 rrb_status rrb_empty_kernel(rrb_stream_t stream) {

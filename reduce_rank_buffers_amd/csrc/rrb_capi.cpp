@@ -177,14 +177,15 @@ rrb_status rrb_plan_bind(rrb_plan_t plan, void *d_workspace, size_t bytes, rrb_s
   }
   const RowMaps &m = p.rows;
   const size_t n = m.slot.size();
-  const size_t slot_bytes = ((n * 4 + 255) / 256) * 256;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (n) {
-    e = hipMemcpyAsync(d_workspace, m.slot.data(), n * 4, hipMemcpyHostToDevice, s);
+    char *ws = static_cast<char *>(d_workspace);
+    e = hipMemcpyAsync(ws + m.off_slot, m.slot.data(), n * 4, hipMemcpyHostToDevice, s);
     if (e == hipSuccess)
-      e = hipMemcpyAsync(static_cast<char *>(d_workspace) + slot_bytes, m.weight.data(), n * 4,
-                         hipMemcpyHostToDevice, s);
+      e = hipMemcpyAsync(ws + m.off_weight, m.weight.data(), n * 4, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(ws + m.off_col, m.col.data(), n * 4, hipMemcpyHostToDevice, s);
     // The host maps belong to the plan; wait so a later destroy cannot free
     // them under an in-flight copy.
     if (e == hipSuccess) e = hipStreamSynchronize(s);

@@ -34,16 +34,20 @@ enum class PlanKind { Uniform, Rows, RowsDevice };
 // Row maps of an expert-parallel plan, as uploaded to the device.
 // Entry (t, i), i < topk, is token t's i-th expert in ascending expert id:
 //   slot_rank[t*k+i], slot_row[t*k+i]  where the row sits in the dispatch
-//   layout; weight[t*k+i] its combine weight.
+//   layout; weight[t*k+i] its combine weight; col[t*k+i] the column j of the
+//   routing arrays (topk_idx[t][j]) it came from, so per-call weights given in
+//   the routing order can be applied.
 struct RowMaps {
   int64_t tokens = 0, hidden = 0;
   int32_t experts = 0, topk = 0, dir = 0;
   std::vector<int32_t> slot;    // [T*k] packed (rank << 26) | row
   std::vector<float> weight;    // [T*k]
+  std::vector<int32_t> col;     // [T*k]
   std::vector<int64_t> rows_per_rank;
-  // Device-routed plans: byte offsets of the maps inside the workspace.
+  // Byte offsets of the maps inside the workspace (host-built plans: slot,
+  // weight and col; device-routed plans: all of them).
   int64_t nblk = 0;             // token blocks of kRouteBlock tokens
-  size_t off_slot = 0, off_weight = 0, off_counts = 0, off_expert = 0, off_rank = 0,
+  size_t off_slot = 0, off_weight = 0, off_col = 0, off_counts = 0, off_expert = 0, off_rank = 0,
          off_bcounts = 0, off_bbase = 0, off_status = 0, off_bstatus = 0;
   // Co-resident capacity (workgroups) of the fused routing kernel, queried
   // once; 0 = not yet known.
@@ -77,6 +81,7 @@ struct LaunchDesc {
   const void *func = nullptr;
   dim3 grid, block;
   std::vector<unsigned char> args;
+  std::string name;  // the kernel and its template arguments, for introspection
 };
 
 // The launches rrb_copy / rrb_reduce would issue for a uniform plan with
@@ -103,8 +108,10 @@ rrb_status launch_route(Plan &plan, const int32_t *d_idx, const float *d_w,
 rrb_status clear_route_maps(const Plan &plan, void *stream);
 
 // Launches a MoE row plan (rrb_moe.hip).  `stream` is a hipStream_t.
+// d_weights (combine only, nullable): per-call weights [T][k] in the order of
+// the routing arrays, in place of the plan's own.
 rrb_status launch_rows(const Plan &plan, const void *const *in, void *const *out,
-                       void *stream);
+                       const float *d_weights, void *stream);
 
 constexpr int kSlotRankShift = 26;
 constexpr int32_t kSlotRowMask = (1 << kSlotRankShift) - 1;

@@ -30,6 +30,8 @@ struct RowArgs {
   unsigned char *out[RRB_MAX_RANKS];
   const int32_t *slot;   // [T*k] (rank << kSlotRankShift) | row, ascending expert
   const float *weight;   // [T*k]
+  const int32_t *col;    // [T*k] routing-array column of each slot
+  const float *wover;    // combine: per-call weights [T][k] in routing order, or NULL
   int64_t tokens_per_rank;
   int64_t row_bytes;     // hidden * 2
   int64_t nvec;          // whole 16-byte vectors per row
@@ -37,7 +39,17 @@ struct RowArgs {
   int64_t part_vec;      // vector path: vectors per row part (one workgroup each)
   int32_t parts;         // vector path: parts per row
   int32_t k;
+  // Device-routed plans: the routing status word; nonzero (a routing with an
+  // invalid entry, or a barrier wait that ran out) stops the launch before
+  // it writes anything.  NULL for host-built plans.
+  const int32_t *route_status;
 };
+
+// True when the plan's last device-side routing failed: the kernel then
+// leaves every output untouched (rrb_moe_route_check reports why).
+__device__ __forceinline__ bool route_failed(const RowArgs &a) {
+  return a.route_status && *a.route_status != 0;
+}
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
@@ -48,6 +60,7 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 // 4 parts of 224 vectors ran 4-7% ahead of one 128-lane workgroup with 8
 // vectors per lane (interleaved A/B runs, 4096 tokens, top-8).
 __global__ void __launch_bounds__(256) moe_dispatch_kernel(RowArgs a) {
+  if (route_failed(a)) return;
   const int64_t t = blockIdx.x / a.parts;
   const int64_t v0 = (static_cast<int64_t>(blockIdx.x) - t * a.parts) * a.part_vec;
   const int64_t v1 = v0 + a.part_vec < a.nvec ? v0 + a.part_vec : a.nvec;
@@ -68,6 +81,7 @@ __global__ void __launch_bounds__(256) moe_dispatch_kernel(RowArgs a) {
 
 // Any hidden size: 2-byte units.
 __global__ void __launch_bounds__(256) moe_dispatch_elem_kernel(RowArgs a) {
+  if (route_failed(a)) return;
   const int64_t t = blockIdx.x;
   const int64_t src_rank = t / a.tokens_per_rank;
   const unsigned char *src =
@@ -122,6 +136,7 @@ __device__ __forceinline__ v4u combine_vec(const v4u (&z)[K], const float (&w)[K
 // of one 256-lane workgroup with 4 vectors per lane (interleaved A/B runs).
 template <int K, int CU>
 __global__ void __launch_bounds__(128) moe_combine_kernel(RowArgs a) {
+  if (route_failed(a)) return;
   const int64_t t = blockIdx.x / a.parts;
   const int64_t v0 = (static_cast<int64_t>(blockIdx.x) - t * a.parts) * a.part_vec;
   const int64_t v1 = v0 + a.part_vec < a.nvec ? v0 + a.part_vec : a.nvec;
@@ -135,7 +150,7 @@ __global__ void __launch_bounds__(128) moe_combine_kernel(RowArgs a) {
   for (int j = 0; j < K; ++j) {
     const int32_t s = slots[j];
     rows[j] = a.in[s >> kSlotRankShift] + static_cast<int64_t>(s & kSlotRowMask) * a.row_bytes;
-    w[j] = ws[j];
+    w[j] = a.wover ? a.wover[t * K + a.col[t * K + j]] : ws[j];
   }
   const int bs = blockDim.x;
   for (int64_t i0 = v0 + threadIdx.x; i0 < v1; i0 += static_cast<int64_t>(bs) * CU) {
@@ -164,18 +179,21 @@ __global__ void __launch_bounds__(128) moe_combine_kernel(RowArgs a) {
 
 // Any k and any hidden size: one element per lane, k rows folded in order.
 __global__ void __launch_bounds__(256) moe_combine_elem_kernel(RowArgs a) {
+  if (route_failed(a)) return;
   const int64_t t = blockIdx.x;
   const int64_t dst_rank = t / a.tokens_per_rank;
   unsigned char *dst = a.out[dst_rank] + (t - dst_rank * a.tokens_per_rank) * a.row_bytes;
   const int32_t *slots = a.slot + t * a.k;
   const float *ws = a.weight + t * a.k;
+  const int32_t *cols = a.col + t * a.k;
   for (int64_t i = threadIdx.x; i < a.hidden; i += blockDim.x) {
     float acc = 0.f;
     for (int j = 0; j < a.k; ++j) {
       const int32_t s = slots[j];
       const unsigned char *row =
           a.in[s >> kSlotRankShift] + static_cast<int64_t>(s & kSlotRowMask) * a.row_bytes;
-      const float term = ws[j] * bf16_to_f32(*reinterpret_cast<const uint16_t *>(row + i * 2));
+      const float wj = a.wover ? a.wover[t * a.k + cols[j]] : ws[j];
+      const float term = wj * bf16_to_f32(*reinterpret_cast<const uint16_t *>(row + i * 2));
       acc = j == 0 ? term : acc + term;
     }
     *reinterpret_cast<uint16_t *>(dst + i * 2) = f32_to_bf16_rne(acc);
@@ -205,6 +223,7 @@ struct RouteArgs {
   const float *w;         // [T][k]
   int32_t *slot;          // [T][k] arena row, ascending expert per token
   float *weight;          // [T][k]
+  int32_t *col;           // [T][k] routing-array column of each slot
   int32_t *rank_off;      // [R + 1]
   int32_t *bcounts;       // [nblk][E]
   int32_t *bbase;         // [nblk][E]
@@ -318,6 +337,9 @@ __global__ void __launch_bounds__(kRouteBlock) moe_route_slot_kernel(RouteArgs a
   __syncthreads();
   if (!live) return;
   // Ascending expert id (bubble sort over registers; K is small and static).
+  int32_t c[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) c[j] = j;
 #pragma unroll
   for (int i = 0; i < K; ++i) {
 #pragma unroll
@@ -326,6 +348,7 @@ __global__ void __launch_bounds__(kRouteBlock) moe_route_slot_kernel(RouteArgs a
         const int32_t te = e[j]; e[j] = e[j + 1]; e[j + 1] = te;
         const float tw = w[j]; w[j] = w[j + 1]; w[j + 1] = tw;
         const bool to = ok[j]; ok[j] = ok[j + 1]; ok[j + 1] = to;
+        const int32_t tc = c[j]; c[j] = c[j + 1]; c[j + 1] = tc;
       }
     }
   }
@@ -341,6 +364,7 @@ __global__ void __launch_bounds__(kRouteBlock) moe_route_slot_kernel(RouteArgs a
     }
     a.slot[t * K + j] = row;
     a.weight[t * K + j] = wt;
+    a.col[t * K + j] = c[j];
   }
 }
 
@@ -399,7 +423,10 @@ __global__ void __launch_bounds__(kRouteBlock) moe_route_fused_kernel(RouteArgs 
   for (int x = tid; x < a.E; x += kRouteBlock)
     __hip_atomic_store(a.bcounts + static_cast<int64_t>(blk) * a.E + x, hist[x], __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-  if (tid == 0) a.bstatus[blk] = bad;
+  // This block's error bits, read by block 0 after the barrier: written
+  // through like the counts.
+  if (tid == 0)
+    __hip_atomic_store(a.bstatus + blk, bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // Grid barrier without fences: every wave waits until its stores have
   // completed, thread 0 arrives and waits, and the counts are then read with
@@ -421,7 +448,7 @@ __global__ void __launch_bounds__(kRouteBlock) moe_route_fused_kernel(RouteArgs 
       if (++spins >= a.spin) {
         // This block writes no slots: say so where no later write can undo
         // it (its own status word; the check reads them all).
-        a.bstatus[blk] = bad | 4;
+        __hip_atomic_store(a.bstatus + blk, bad | 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         atomicOr(a.status, 4);
         fine = 0;
         break;
@@ -499,13 +526,17 @@ __global__ void __launch_bounds__(kRouteBlock) moe_route_fused_kernel(RouteArgs 
     }
     if (tid == 0) {
       int32_t st = 0;
-      for (int b = 0; b < a.nblk; ++b) st |= a.bstatus[b];
+      for (int b = 0; b < a.nblk; ++b)
+        st |= __hip_atomic_load(a.bstatus + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       *a.status = st;
     }
   }
 
   // Phase 3: this block's slots, experts in ascending id.
   if (!live) return;
+  int32_t c[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) c[j] = j;
 #pragma unroll
   for (int i = 0; i < K; ++i) {
 #pragma unroll
@@ -514,6 +545,7 @@ __global__ void __launch_bounds__(kRouteBlock) moe_route_fused_kernel(RouteArgs 
         const int32_t te = e[j]; e[j] = e[j + 1]; e[j + 1] = te;
         const float tw = w[j]; w[j] = w[j + 1]; w[j + 1] = tw;
         const bool to = ok[j]; ok[j] = ok[j + 1]; ok[j + 1] = to;
+        const int32_t tc = c[j]; c[j] = c[j + 1]; c[j + 1] = tc;
       }
     }
   }
@@ -529,6 +561,7 @@ __global__ void __launch_bounds__(kRouteBlock) moe_route_fused_kernel(RouteArgs 
     }
     a.slot[t * K + j] = row;
     a.weight[t * K + j] = wt;
+    a.col[t * K + j] = c[j];
   }
 }
 
@@ -575,9 +608,13 @@ rrb_status clear_route_maps(const Plan &p, void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   char *ws = static_cast<char *>(p.d_ws);
   const int64_t n = m.tokens * m.topk;
-  if (n > 0)
+  if (n > 0) {
+    // Slots and columns: row 0 of the arena and column 0, both in bounds.
     hipLaunchKernelGGL(moe_fill_kernel, dim3(64), dim3(256), 0, s,
                        reinterpret_cast<int32_t *>(ws + m.off_slot), n, 0);
+    hipLaunchKernelGGL(moe_fill_kernel, dim3(64), dim3(256), 0, s,
+                       reinterpret_cast<int32_t *>(ws + m.off_col), n, 0);
+  }
   // status word, barrier counter and per-block status words
   const int64_t words = (static_cast<int64_t>(m.off_bstatus - m.off_status) + m.nblk * 4) / 4;
   hipLaunchKernelGGL(moe_fill_kernel, dim3(1), dim3(256), 0, s,
@@ -596,6 +633,7 @@ rrb_status launch_route(Plan &p, const int32_t *d_idx, const float *d_w, int32_t
   a.w = d_w;
   a.slot = reinterpret_cast<int32_t *>(ws + m.off_slot);
   a.weight = reinterpret_cast<float *>(ws + m.off_weight);
+  a.col = reinterpret_cast<int32_t *>(ws + m.off_col);
   a.counts = reinterpret_cast<int32_t *>(ws + m.off_counts);
   a.expert_off = reinterpret_cast<int32_t *>(ws + m.off_expert);
   a.rank_off = reinterpret_cast<int32_t *>(ws + m.off_rank);
@@ -679,7 +717,8 @@ void split_row(RowArgs &a, int64_t cap) {
 
 }  // namespace
 
-rrb_status launch_rows(const Plan &p, const void *const *in, void *const *out, void *stream) {
+rrb_status launch_rows(const Plan &p, const void *const *in, void *const *out, const float *d_weights,
+                       void *stream) {
   const RowMaps &m = p.rows;
   if (m.tokens == 0) return RRB_OK;
   if (!p.d_ws) return fail(RRB_EINVAL, "row plan is not bound to a workspace");
@@ -693,16 +732,14 @@ rrb_status launch_rows(const Plan &p, const void *const *in, void *const *out, v
         (p.out_count[r] && (reinterpret_cast<uintptr_t>(out[r]) & 15)))
       vec = false;
   }
-  if (p.kind == PlanKind::RowsDevice) {
-    // Slots are arena rows (rank bits 0): the arena is pointer 0.
-    a.slot = reinterpret_cast<const int32_t *>(static_cast<const char *>(p.d_ws) + m.off_slot);
-    a.weight = reinterpret_cast<const float *>(static_cast<const char *>(p.d_ws) + m.off_weight);
-  } else {
-    const size_t n = m.slot.size();
-    const size_t slot_bytes = ((n * 4 + 255) / 256) * 256;
-    a.slot = static_cast<const int32_t *>(p.d_ws);
-    a.weight = reinterpret_cast<const float *>(static_cast<const char *>(p.d_ws) + slot_bytes);
-  }
+  // Device-routed plans: slots are arena rows (rank bits 0), the arena is
+  // pointer 0.
+  const char *ws = static_cast<const char *>(p.d_ws);
+  a.slot = reinterpret_cast<const int32_t *>(ws + m.off_slot);
+  a.weight = reinterpret_cast<const float *>(ws + m.off_weight);
+  a.col = reinterpret_cast<const int32_t *>(ws + m.off_col);
+  a.wover = m.dir == RRB_MOE_COMBINE ? d_weights : nullptr;
+  if (p.kind == PlanKind::RowsDevice) a.route_status = reinterpret_cast<const int32_t *>(ws + m.off_status);
   a.tokens_per_rank = m.tokens / p.nranks;
   a.row_bytes = m.hidden * 2;
   a.nvec = a.row_bytes / 16;

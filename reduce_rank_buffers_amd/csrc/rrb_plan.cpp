@@ -219,6 +219,7 @@ rrb_status build_row_plan(int32_t R, int64_t T, int64_t h, int32_t E, int32_t k,
   std::vector<int64_t> fill(E, 0);
   m.slot.assign(static_cast<size_t>(T * k), 0);
   m.weight.assign(static_cast<size_t>(T * k), 0.f);
+  m.col.assign(static_cast<size_t>(T * k), 0);
   std::vector<std::pair<int32_t, int32_t>> order(k);
   for (int64_t t = 0; t < T; ++t) {
     for (int32_t j = 0; j < k; ++j) order[j] = {idx[t * k + j], j};
@@ -228,6 +229,7 @@ rrb_status build_row_plan(int32_t R, int64_t T, int64_t h, int32_t E, int32_t k,
       const int64_t row = off[e] + fill[e]++;
       m.slot[t * k + i] = ((e / per) << kSlotRankShift) | static_cast<int32_t>(row);
       m.weight[t * k + i] = w ? w[t * k + order[i].second] : 0.f;
+      m.col[t * k + i] = order[i].second;
     }
   }
   m.tokens = T;
@@ -255,9 +257,13 @@ rrb_status build_row_plan(int32_t R, int64_t T, int64_t h, int32_t E, int32_t k,
       plan.out_count[r] = Tr * h;
     }
   }
-  // Device map: slot[T*k] int32, then weight[T*k] float, 256-byte aligned.
-  const size_t slot_bytes = ((static_cast<size_t>(T * k) * 4 + 255) / 256) * 256;
-  plan.ws_bytes = slot_bytes + ((static_cast<size_t>(T * k) * 4 + 255) / 256) * 256;
+  // Device map: slot[T*k] int32, weight[T*k] float, col[T*k] int32, each
+  // 256-byte aligned.
+  const size_t map_bytes = ((static_cast<size_t>(T * k) * 4 + 255) / 256) * 256;
+  m.off_slot = 0;
+  m.off_weight = map_bytes;
+  m.off_col = 2 * map_bytes;
+  plan.ws_bytes = 3 * map_bytes;
   return RRB_OK;
 }
 
@@ -292,6 +298,7 @@ rrb_status build_row_plan_device(int32_t R, int64_t T, int64_t h, int32_t E, int
   const size_t tk = static_cast<size_t>(T * k);
   m.off_slot = off;    off += up(tk * 4);
   m.off_weight = off;  off += up(tk * 4);
+  m.off_col = off;     off += up(tk * 4);
   m.off_counts = off;  off += up(static_cast<size_t>(E) * 4);
   m.off_expert = off;  off += up(static_cast<size_t>(E) * 4);
   m.off_rank = off;    off += up(static_cast<size_t>(R + 1) * 4);

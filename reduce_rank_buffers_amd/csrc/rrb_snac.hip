@@ -13,11 +13,12 @@
 //   dual         two staging buffers by epoch parity; the next epoch's top
 //                barrier already proves the readers of this buffer finished,
 //                so the bottom barrier goes.
-//   speculative  dual buffers and no top barrier: the consume loads start at
-//                once and a reduced validation flag (sum of the R sources'
-//                flags == R * epoch, per workgroup slice) decides whether the
-//                result stands; on mismatch the slice waits for the flags and
-//                is read again.
+//   speculative  dual buffers and no top barrier: one read of the sources'
+//                flags, then the consume loads start at once and a reduced
+//                validation flag (sum of the R sources' flags == R * epoch,
+//                per workgroup slice) decides whether the result stands; on
+//                mismatch only the stale sources are waited for and read
+//                again.
 //   twoshot      dual buffers; reduce-scatter into a reduced buffer, a second
 //                flag round, then all-gather (SiFAR review, Fig. 6).
 //   lamport      flag-in-data, the Lamport-style All-Reduce SiFAR compares
@@ -38,14 +39,16 @@
 //
 // Speculation order.  The pages read the payload first and the flags after,
 // and rely on no rank overtaking the reader between those two loads.  Here
-// the flag loads are issued first and the payload loads right after them,
-// with no wait in between: a flag equal to the epoch then means the source
-// finished staging before the payload loads were issued, and a stale read
-// needs a later-issued load to be served before an earlier one by more than
-// the writer's stage-to-flag gap.  The speculative loads are device-coherent
-// (the same cache policy as agent-scope atomic loads), so a line cached from
-// an earlier epoch is never returned.
-//
+// the flags are read first, and the payload loads are issued once the flag
+// values have returned (loads from one wave may be served in any order, so
+// issuing them together would rest on the memory system serving the flag
+// first).  A flag equal to the epoch then proves the source finished staging
+// before its payload loads were issued; the speculation is that the payload
+// is loaded whatever the flags said, and the reduced flag decides afterwards.
+// The speculative loads are device-coherent (the same cache policy as
+// agent-scope atomic loads), so a line cached from an earlier epoch is never
+// returned.
+
 // Memory ordering without fences.  Every byte one workgroup writes for
 // another (staged payloads, the twoshot reduced payload) is stored with the
 // cache policy of agent-scope atomic stores (sc1): written through this XCD's
@@ -191,9 +194,6 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void store_wt(unsigned char *base, int64_t bytes, int64_t off, v4u x) {
   __builtin_amdgcn_raw_buffer_store_b128(x, rsrc(base, bytes), static_cast<int32_t>(off), 0, 16);
 }
-__device__ __forceinline__ void store_wt(unsigned char *base, int64_t bytes, int64_t off, uint4 x) {
-  store_wt(base, bytes, off, v4u{x.x, x.y, x.z, x.w});
-}
 // Write-through (WT) or plain 16-byte store.
 template <bool WT>
 __device__ __forceinline__ void store16(unsigned char *base, int64_t bytes, int64_t off, v4u x) {
@@ -215,6 +215,30 @@ __device__ __forceinline__ uint4 load_coherent(__amdgpu_buffer_rsrc_t r, int32_t
 
 __device__ __forceinline__ uint32_t load_flag_relaxed(const uint32_t *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Orders every later memory access of the wave after the values it has
+// loaded so far: waits until all of its outstanding memory operations have
+// completed (s_waitcnt 0) and keeps the compiler from moving later accesses
+// above this point.  Loads from one wave to different addresses may be served
+// in any order, so a payload load that must not see data older than a flag
+// is issued only after the flag's value has returned.
+__device__ __forceinline__ void wait_returned() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Sum and bitwise or over the 64 lanes of the wave (every lane gets the result).
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_or(uint32_t x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x |= __shfl_xor(x, m);
+  return x;
 }
 
 // Polls *p until it reaches `want`; false if the budget ran out or another
@@ -426,7 +450,6 @@ __device__ bool twoshot_epoch(const SnacArgs &a, int r, int s, int k, uint32_t e
 template <int R, bool BF16, int VAR>
 __global__ void __launch_bounds__(64) snac_chain_kernel(SnacArgs a) {
   __shared__ int lds_ok[R];
-  __shared__ int lds_valid;
   const int r = blockIdx.x / a.S;
   const int s = blockIdx.x - r * a.S;
   const int bs = blockDim.x;
@@ -492,41 +515,75 @@ __global__ void __launch_bounds__(64) snac_chain_kernel(SnacArgs a) {
 
     unsigned char *dst_base = a.out + (static_cast<int64_t>(k) * R + r) * a.rank_bytes;
     bool ok = true;
-    int64_t first_pass_end = v0;  // vectors already reduced speculatively
+    // Consume: fold the R staged slices in rank order, CU vectors x R
+    // sources in flight per lane.
+    constexpr int CU = R <= 8 ? 4 : 2;
+    int64_t first = v0 + threadIdx.x;  // first vector of the ordinary passes
 
     if (VAR == kSpeculative) {
-      // Consume without a top barrier: flag loads first, payload right after.
+      // No top barrier.  One read of the R sources' flags (lanes 0..R-1);
+      // once those values have returned, the first pass loads every source
+      // at once, whatever its flag said.  The reduced validation flag (SiFAR
+      // review, Fig. 14) then decides: the flags must sum to R * epoch.
+      // Every flag holds epoch or epoch - 2 (dual buffering keeps each rank
+      // within one epoch of its readers), so the sum is exact, and a valid
+      // sum also proves every source's reads of this buffer two epochs ago
+      // returned before its flag.  A source whose flag read as the epoch was
+      // complete before its loads were issued, so on a mismatch only the
+      // stale sources are waited for and read again; the fresh ones' data is
+      // kept in registers.
       uint32_t f = 0;
       if (threadIdx.x < R) f = load_flag_relaxed(flags_b + threadIdx.x * stride_rs + s * kFlagStride);
-      __builtin_amdgcn_sched_barrier(0);
-      asm volatile("" ::: "memory");
-      const int64_t i = v0 + threadIdx.x;
-      uint4 v[R];
-      if (i < v1) {
+      const uint32_t sum = wave_sum(threadIdx.x < R ? f : 0u);
+      const uint32_t stale = wave_or(threadIdx.x < R && f != ep ? 1u << threadIdx.x : 0u);
+      wait_returned();
+      constexpr uint32_t kAll = R >= 32 ? ~0u : (1u << R) - 1u;
+      const bool valid = sum == static_cast<uint32_t>(R) * ep;
+      const uint32_t redo = valid ? 0u : (stale ? stale : kAll);
+      uint4 v[CU][R];
 #pragma unroll
-        for (int q = 0; q < R; ++q)
-          v[q] = load_coherent(rsrc(stage_base + static_cast<int64_t>(q) * a.rank_bytes, a.rank_bytes),
-                               static_cast<int32_t>(i * 16));
-      }
-      // Reduced validation flag: the sum over the R sources must be R * epoch.
-      // Wave 0 holds the flags.  A valid sum also proves every source's reads
-      // of this buffer two epochs ago had returned before its flag.
-      if (threadIdx.x < 64) {
-        uint32_t sum = threadIdx.x < R ? f : 0u;
+      for (int u = 0; u < CU; ++u) {
+        const int64_t i = first + static_cast<int64_t>(u) * bs;
+        if (i < v1) {
 #pragma unroll
-        for (int m = 1; m < 64; m <<= 1) sum += __shfl_xor(sum, m);
-        if (threadIdx.x == 0) lds_valid = sum == static_cast<uint32_t>(R) * ep ? 1 : 0;
+          for (int q = 0; q < R; ++q)
+            v[u][q] = load_coherent(rsrc(stage_base + static_cast<int64_t>(q) * a.rank_bytes, a.rank_bytes),
+                                    static_cast<int32_t>(i * 16));
+        }
       }
-      __syncthreads();
-      const bool valid = lds_valid != 0;
-      if (valid) {
-        if (i < v1) reduce_pass<R, BF16>(v, dst_base, a.rank_bytes, i * 16);
-        first_pass_end = min(v1, v0 + bs);
-      } else {
+      if (redo) {
         ++misspec;
-        ++retries;
-        ok = wait_all<R>(flags_b + s * kFlagStride, stride_rs, ep, a.status, a.spin_limit, lds_ok);
+        retries += static_cast<unsigned long long>(__builtin_popcount(redo));
+        bool mine = true;
+        if (threadIdx.x < R && (redo >> threadIdx.x & 1u))
+          mine = wait_at_least(flags_b + threadIdx.x * stride_rs + s * kFlagStride, ep, a.status,
+                               a.spin_limit);
+        ok = __all(mine) != 0;
+        if (ok) {
+          wait_returned();
+#pragma unroll
+          for (int q = 0; q < R; ++q) {
+            if (redo >> q & 1u) {
+#pragma unroll
+              for (int u = 0; u < CU; ++u) {
+                const int64_t i = first + static_cast<int64_t>(u) * bs;
+                if (i < v1)
+                  v[u][q] = load_coherent(rsrc(stage_base + static_cast<int64_t>(q) * a.rank_bytes,
+                                               a.rank_bytes),
+                                          static_cast<int32_t>(i * 16));
+              }
+            }
+          }
+        }
       }
+      if (ok) {
+#pragma unroll
+        for (int u = 0; u < CU; ++u) {
+          const int64_t i = first + static_cast<int64_t>(u) * bs;
+          if (i < v1) reduce_pass<R, BF16>(v[u], dst_base, a.rank_bytes, i * 16);
+        }
+      }
+      first += static_cast<int64_t>(bs) * CU;
     } else {
       ok = wait_all<R>(flags_b + s * kFlagStride, stride_rs, ep, a.status, a.spin_limit, lds_ok);
     }
@@ -535,10 +592,7 @@ __global__ void __launch_bounds__(64) snac_chain_kernel(SnacArgs a) {
       break;
     }
 
-    // Consume: fold the R staged slices in rank order, CU vectors x R
-    // sources in flight per lane.
-    constexpr int CU = R <= 8 ? 4 : 2;
-    for (int64_t i0 = first_pass_end + threadIdx.x; i0 < v1; i0 += static_cast<int64_t>(bs) * CU) {
+    for (int64_t i0 = first; i0 < v1; i0 += static_cast<int64_t>(bs) * CU) {
       uint4 v[CU][R];
 #pragma unroll
       for (int u = 0; u < CU; ++u) {
@@ -788,6 +842,12 @@ struct PlanChainArgs {
   uint32_t spin_limit;
 };
 
+// A wait-list entry is a flag index r * S + s; entries that only guard the
+// write-after-read order (a workgroup that reads this workgroup's slice, but
+// whose own slice this workgroup does not read) also carry kGuardOnly.
+constexpr int32_t kGuardOnly = 1 << 30;
+constexpr int32_t kFlagIndexMask = kGuardOnly - 1;
+
 // Every lane waits for its share of the n flags base + idx[i] * kFlagStride
 // (no acquire fence: the staged data is read with device-coherent loads after
 // the flags were seen).  True in every lane if all n waits succeeded.
@@ -795,7 +855,8 @@ __device__ bool wait_list(const uint32_t *base, const int32_t *idx, int n, uint3
                           uint32_t *status, uint32_t limit) {
   bool ok = true;
   for (int i = threadIdx.x; i < n && ok; i += blockDim.x)
-    ok = wait_at_least(base + static_cast<int64_t>(idx[i]) * kFlagStride, want, status, limit);
+    ok = wait_at_least(base + static_cast<int64_t>(idx[i] & kFlagIndexMask) * kFlagStride, want, status,
+                       limit);
   const bool all = __all(ok) != 0;
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   return all;
@@ -803,7 +864,9 @@ __device__ bool wait_list(const uint32_t *base, const int32_t *idx, int n, uint3
 
 // Piece s of every entry of rank r: staged data read with device-coherent
 // loads, results stored to rank r's output of this epoch with plain stores
-// (only the host reads outputs).
+// (only the host reads outputs).  `only` (bit q: source rank q) restricts the
+// pass to the entries that read a rank in the mask -- a copy from such a rank,
+// or any fold -- so a failed speculative check redoes just those.
 //
 // A rank whose entries are all copies of one length (All-Gather, All-to-All,
 // Gather) takes its pieces as one flat index range over all lanes, kCopyU
@@ -815,7 +878,7 @@ constexpr int kFlatEntries = 64;
 template <int R, bool BF16>
 __device__ void plan_consume(const PlanChainArgs &a, int r, int s,
                              const unsigned char *stage_base, unsigned char *dst,
-                             const PlanEntry *ents) {
+                             const PlanEntry *ents, uint32_t only) {
   const int bs = blockDim.x;
   constexpr int CU = R <= 8 ? 2 : 1;
   constexpr int CC = 4;  // copy vectors per lane in flight
@@ -837,9 +900,11 @@ __device__ void plan_consume(const PlanChainArgs &a, int r, int s,
         if (f < total) {
           const uint32_t g = f / w;
           const PlanEntry e = ents[g];
-          const int64_t i = lo + (f - g * w);
-          x[u] = load_coherent(src, static_cast<int32_t>(e.src_rank * a.in_stride + (e.src_off + i) * 16));
-          at[u] = (e.dst_off + i) * 16;
+          if (only >> e.src_rank & 1u) {
+            const int64_t i = lo + (f - g * w);
+            x[u] = load_coherent(src, static_cast<int32_t>(e.src_rank * a.in_stride + (e.src_off + i) * 16));
+            at[u] = (e.dst_off + i) * 16;
+          }
         }
       }
 #pragma unroll
@@ -850,6 +915,7 @@ __device__ void plan_consume(const PlanChainArgs &a, int r, int s,
   }
   for (int g = a.first[r]; g < a.first[r] + a.cnt[r]; ++g) {
     const PlanEntry e = a.entries[g];
+    if (e.src_rank < 0 ? only == 0 : !(only >> e.src_rank & 1u)) continue;
     const int64_t pl = (e.len + a.S - 1) / a.S;
     const int64_t lo = min(e.len, static_cast<int64_t>(s) * pl);
     const int64_t hi = min(e.len, lo + pl);
@@ -945,26 +1011,36 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
     unsigned char *dst = a.out + (static_cast<int64_t>(k) * R + r) * a.out_stride;
     bool ok = true;
     if (VAR == kSpeculative) {
-      // Flags first (relaxed, no wait), the whole consume right after.
-      uint32_t sum = 0;
-      for (int i = threadIdx.x; i < nw; i += bs)
-        sum += load_flag_relaxed(flags_b + static_cast<int64_t>(wl[i]) * kFlagStride);
-      __builtin_amdgcn_sched_barrier(0);
-      asm volatile("" ::: "memory");
-      plan_consume<R, BF16>(a, r, s, stage_base, dst, ents);
-#pragma unroll
-      for (int m = 1; m < 64; m <<= 1) sum += __shfl_xor(sum, m);
-      // Each flag is epoch or epoch - 2, so the sum is exact (no wrap-around
-      // false match: 2 x the stale count stays below 2^32).
+      // One read of the listed flags; once their values have returned, the
+      // whole consume runs, whatever they said.  The reduced check: they must
+      // sum to (list length) x epoch (each is epoch or epoch - 2, so the sum
+      // is exact).  On a mismatch the workgroup waits for every listed flag
+      // (the write-after-read guards included) and redoes only the entries
+      // that read a rank whose data flag was stale; entries whose sources
+      // were all fresh stand, their loads having been issued after the flags.
+      uint32_t sum = 0, stale = 0;
+      for (int i = threadIdx.x; i < nw; i += bs) {
+        const int32_t w = wl[i];
+        const uint32_t f = load_flag_relaxed(flags_b + static_cast<int64_t>(w & kFlagIndexMask) * kFlagStride);
+        sum += f;
+        if (f != ep && !(w & kGuardOnly)) stale |= 1u << ((w & kFlagIndexMask) / a.S);
+      }
+      sum = wave_sum(sum);
+      stale = wave_or(stale);
+      wait_returned();
+      plan_consume<R, BF16>(a, r, s, stage_base, dst, ents, ~0u);
       if (sum != static_cast<uint32_t>(nw) * ep) {
         ++misspec;
-        ++retries;
+        retries += static_cast<unsigned long long>(__builtin_popcount(stale));
         ok = wait_list(flags_b, wl, nw, ep, a.status, a.spin_limit);
-        if (ok) plan_consume<R, BF16>(a, r, s, stage_base, dst, ents);
+        if (ok) {
+          wait_returned();
+          if (stale) plan_consume<R, BF16>(a, r, s, stage_base, dst, ents, stale);
+        }
       }
     } else {
       ok = wait_list(flags_b, wl, nw, ep, a.status, a.spin_limit);
-      if (ok) plan_consume<R, BF16>(a, r, s, stage_base, dst, ents);
+      if (ok) plan_consume<R, BF16>(a, r, s, stage_base, dst, ents, ~0u);
     }
     if (!ok) {
       ++timeouts;
@@ -1172,8 +1248,11 @@ void build_wait_lists(rrb_snac_s &h) {
   std::vector<int32_t> all;
   for (int w = 0; w < W; ++w) {
     std::vector<int32_t> m = lists[w];
-    m.insert(m.end(), readers[w].begin(), readers[w].end());
-    std::sort(m.begin(), m.end());
+    for (int32_t f : readers[w])
+      if (!std::binary_search(lists[w].begin(), lists[w].end(), f)) m.push_back(f | kGuardOnly);
+    std::sort(m.begin(), m.end(), [](int32_t x, int32_t y) {
+      return (x & kFlagIndexMask) < (y & kFlagIndexMask);
+    });
     m.erase(std::unique(m.begin(), m.end()), m.end());
     all.insert(all.end(), m.begin(), m.end());
     h.wait_tab.push_back(static_cast<int32_t>(all.size()));
@@ -1319,6 +1398,99 @@ rrb_status launch_plan_chain(rrb_snac_s *h, int32_t epochs, const void *d_in, vo
   return RRB_OK;
 }
 
+// Argument rules of an All-Reduce chain handle (rrb_snac_create).
+rrb_status check_ar_chain_args(int32_t nranks, int64_t count, int32_t dtype, uint32_t flags,
+                               int32_t slices) {
+  if (nranks < 1 || nranks > RRB_MAX_RANKS)
+    return fail(RRB_EINVAL, "nranks %d outside 1..%d", nranks, RRB_MAX_RANKS);
+  if (dtype != RRB_BF16 && dtype != RRB_F32) return fail(RRB_EINVAL, "unknown dtype %d", dtype);
+  if (flags & ~(RRB_SNAC_DUAL_BUFFER | RRB_SNAC_SPECULATIVE | RRB_SNAC_GRAPH | RRB_SNAC_TWOSHOT |
+                RRB_SNAC_LAMPORT | RRB_SNAC_COOPERATIVE))
+    return fail(RRB_EINVAL, "unknown SNAC flags 0x%x", flags);
+  if ((flags & RRB_SNAC_COOPERATIVE) && (flags & RRB_SNAC_GRAPH))
+    return fail(RRB_EINVAL, "RRB_SNAC_GRAPH launches no persistent kernel");
+  flags &= ~RRB_SNAC_COOPERATIVE;
+  if ((flags & RRB_SNAC_LAMPORT) && flags != (RRB_SNAC_LAMPORT | RRB_SNAC_DUAL_BUFFER))
+    return fail(RRB_EINVAL, "RRB_SNAC_LAMPORT goes with RRB_SNAC_DUAL_BUFFER only");
+  if ((flags & RRB_SNAC_TWOSHOT) && flags != (RRB_SNAC_TWOSHOT | RRB_SNAC_DUAL_BUFFER))
+    return fail(RRB_EINVAL, "RRB_SNAC_TWOSHOT goes with RRB_SNAC_DUAL_BUFFER only");
+  if ((flags & RRB_SNAC_GRAPH) && flags != RRB_SNAC_GRAPH)
+    return fail(RRB_EINVAL, "RRB_SNAC_GRAPH takes no other flag");
+  if ((flags & RRB_SNAC_SPECULATIVE) && !(flags & RRB_SNAC_DUAL_BUFFER))
+    return fail(RRB_EINVAL, "speculative reduction needs dual buffering");
+  const int esz = elem_size(dtype);
+  if (count <= 0 || (count * esz) % 16)
+    return fail(RRB_EUNSUPPORTED, "chain payloads must be a positive multiple of 16 bytes");
+  if (2LL * nranks * count * esz * ((flags & RRB_SNAC_LAMPORT) ? 2 : 1) > 0x7fffffffLL)
+    return fail(RRB_EUNSUPPORTED, "staging above 2 GiB");
+  if (slices < 0 || slices > kMaxSlices)
+    return fail(RRB_EINVAL, "slices %d outside 0..%d", slices, kMaxSlices);
+  return RRB_OK;
+}
+
+// Issues one All-Reduce chain call of a persistent variant on the handle's
+// workspace h->ws (bound, not graph mode, not a plan chain).
+rrb_status launch_ar_chain(rrb_snac_s *h, int32_t epochs, const void *d_in, void *d_out,
+                           rrb_snac_stats *d_stats, const uint32_t *d_stagger, uint32_t spin_limit,
+                           rrb_stream_t stream) {
+  const int esz = elem_size(h->dtype);
+  SnacArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.in = static_cast<const unsigned char *>(d_in);
+  a.out = static_cast<unsigned char *>(d_out);
+  a.staging = h->ws + h->lay.staging_off;
+  a.flag = reinterpret_cast<uint32_t *>(h->ws + h->lay.flag_off);
+  a.done = reinterpret_cast<uint32_t *>(h->ws + h->lay.done_off);
+  a.status = reinterpret_cast<uint32_t *>(h->ws + h->lay.status_off);
+  a.stats = d_stats;
+  a.stagger = d_stagger;
+  a.count = h->count;
+  a.rank_bytes = h->count * esz;
+  a.nvec = a.rank_bytes / 16;
+  a.slice_vec = (a.nvec + h->S - 1) / h->S;
+  a.reduced = h->ws + h->lay.reduced_off;
+  a.flag2 = reinterpret_cast<uint32_t *>(h->ws + h->lay.flag2_off);
+  a.chunk_vec = (a.nvec + h->R - 1) / h->R;
+  a.piece_vec = (a.chunk_vec + h->S - 1) / h->S;
+  a.tagged = h->ws + h->lay.tagged_off;
+  a.epoch0 = h->next_epoch;
+  a.epochs = epochs;
+  a.S = h->S;
+  a.spin_limit = spin_limit ? spin_limit : kDefaultSpin;
+
+  const bool bf16 = h->dtype == RRB_BF16;
+  // Measured on MI355X: payloads up to 16 KiB (slices of one vector per
+  // lane) run 7-8% faster with one vector per lane in flight; from 32 KiB
+  // the two-vector shape is as fast or faster.
+  const bool one = a.nvec <= 1024 && a.slice_vec <= h->bs;
+  const int var = (h->flags & RRB_SNAC_LAMPORT) ? (one ? kLamportOne : kLamport)
+                  : (h->flags & RRB_SNAC_TWOSHOT) ? kTwoshot
+                  : (h->flags & RRB_SNAC_SPECULATIVE) ? kSpeculative
+                  : (h->flags & RRB_SNAC_DUAL_BUFFER) ? kDual : kBarrier;
+  SnacFn fn = nullptr;
+  if (bf16) {
+    fn = var == kBarrier ? snac_for<true, kBarrier>(h->R)
+         : var == kDual  ? snac_for<true, kDual>(h->R)
+         : var == kTwoshot ? snac_for<true, kTwoshot>(h->R)
+         : var == kLamport ? snac_for<true, kLamport>(h->R)
+         : var == kLamportOne ? snac_for<true, kLamportOne>(h->R)
+                           : snac_for<true, kSpeculative>(h->R);
+  } else {
+    fn = var == kBarrier ? snac_for<false, kBarrier>(h->R)
+         : var == kDual  ? snac_for<false, kDual>(h->R)
+         : var == kTwoshot ? snac_for<false, kTwoshot>(h->R)
+         : var == kLamport ? snac_for<false, kLamport>(h->R)
+         : var == kLamportOne ? snac_for<false, kLamportOne>(h->R)
+                           : snac_for<false, kSpeculative>(h->R);
+  }
+  // Every workgroup waits on others: the grid must be co-resident.
+  const rrb_status st = launch_persistent(h, reinterpret_cast<const void *>(fn), a,
+                                          static_cast<hipStream_t>(stream), "chain");
+  if (st != RRB_OK) return st;
+  h->next_epoch += static_cast<uint32_t>(epochs);
+  return RRB_OK;
+}
+
 }  // namespace
 }  // namespace rrb
 
@@ -1331,32 +1503,9 @@ rrb_status rrb_snac_create(int32_t nranks, int64_t count, int32_t dtype, uint32_
   clear_error();
   if (!out) return fail(RRB_EINVAL, "NULL out");
   *out = nullptr;
-  if (nranks < 1 || nranks > RRB_MAX_RANKS)
-    return fail(RRB_EINVAL, "nranks %d outside 1..%d", nranks, RRB_MAX_RANKS);
-  if (dtype != RRB_BF16 && dtype != RRB_F32) return fail(RRB_EINVAL, "unknown dtype %d", dtype);
-  if (flags & ~(RRB_SNAC_DUAL_BUFFER | RRB_SNAC_SPECULATIVE | RRB_SNAC_GRAPH | RRB_SNAC_TWOSHOT |
-                RRB_SNAC_LAMPORT | RRB_SNAC_COOPERATIVE))
-    return fail(RRB_EINVAL, "unknown SNAC flags 0x%x", flags);
-  if ((flags & RRB_SNAC_COOPERATIVE) && (flags & RRB_SNAC_GRAPH))
-    return fail(RRB_EINVAL, "RRB_SNAC_GRAPH launches no persistent kernel");
-  const uint32_t coop = flags & RRB_SNAC_COOPERATIVE;
-  flags &= ~RRB_SNAC_COOPERATIVE;
-  if ((flags & RRB_SNAC_LAMPORT) && flags != (RRB_SNAC_LAMPORT | RRB_SNAC_DUAL_BUFFER))
-    return fail(RRB_EINVAL, "RRB_SNAC_LAMPORT goes with RRB_SNAC_DUAL_BUFFER only");
-  if ((flags & RRB_SNAC_TWOSHOT) && flags != (RRB_SNAC_TWOSHOT | RRB_SNAC_DUAL_BUFFER))
-    return fail(RRB_EINVAL, "RRB_SNAC_TWOSHOT goes with RRB_SNAC_DUAL_BUFFER only");
-  if ((flags & RRB_SNAC_GRAPH) && flags != RRB_SNAC_GRAPH)
-    return fail(RRB_EINVAL, "RRB_SNAC_GRAPH takes no other flag");
-  if ((flags & RRB_SNAC_SPECULATIVE) && !(flags & RRB_SNAC_DUAL_BUFFER))
-    return fail(RRB_EINVAL, "speculative reduction needs dual buffering");
-  flags |= coop;
+  const rrb_status cs = check_ar_chain_args(nranks, count, dtype, flags, slices);
+  if (cs != RRB_OK) return cs;
   const int esz = elem_size(dtype);
-  if (count <= 0 || (count * esz) % 16)
-    return fail(RRB_EUNSUPPORTED, "chain payloads must be a positive multiple of 16 bytes");
-  if (2LL * nranks * count * esz * ((flags & RRB_SNAC_LAMPORT) ? 2 : 1) > 0x7fffffffLL)
-    return fail(RRB_EUNSUPPORTED, "staging above 2 GiB");
-  if (slices < 0 || slices > kMaxSlices)
-    return fail(RRB_EINVAL, "slices %d outside 0..%d", slices, kMaxSlices);
   const int64_t nvec = count * esz / 16;
   const int32_t S = default_slices(slices, nvec, nranks, flags, false);
   rrb_snac_s *h = new (std::nothrow) rrb_snac_s;
@@ -1562,62 +1711,7 @@ rrb_status rrb_snac_chain(rrb_snac_t h, int32_t epochs, const void *d_in, void *
   if (h->next_epoch > 0xffffffffu - static_cast<uint32_t>(epochs) - 2)
     return fail(RRB_EUNSUPPORTED, "epoch counter exhausted; rebind the handle");
   if (h->from_plan) return launch_plan_chain(h, epochs, d_in, d_out, d_stats, d_stagger, spin_limit, stream);
-  const int esz = elem_size(h->dtype);
-  SnacArgs a;
-  std::memset(&a, 0, sizeof a);
-  a.in = static_cast<const unsigned char *>(d_in);
-  a.out = static_cast<unsigned char *>(d_out);
-  a.staging = h->ws + h->lay.staging_off;
-  a.flag = reinterpret_cast<uint32_t *>(h->ws + h->lay.flag_off);
-  a.done = reinterpret_cast<uint32_t *>(h->ws + h->lay.done_off);
-  a.status = reinterpret_cast<uint32_t *>(h->ws + h->lay.status_off);
-  a.stats = d_stats;
-  a.stagger = d_stagger;
-  a.count = h->count;
-  a.rank_bytes = h->count * esz;
-  a.nvec = a.rank_bytes / 16;
-  a.slice_vec = (a.nvec + h->S - 1) / h->S;
-  a.reduced = h->ws + h->lay.reduced_off;
-  a.flag2 = reinterpret_cast<uint32_t *>(h->ws + h->lay.flag2_off);
-  a.chunk_vec = (a.nvec + h->R - 1) / h->R;
-  a.piece_vec = (a.chunk_vec + h->S - 1) / h->S;
-  a.tagged = h->ws + h->lay.tagged_off;
-  a.epoch0 = h->next_epoch;
-  a.epochs = epochs;
-  a.S = h->S;
-  a.spin_limit = spin_limit ? spin_limit : kDefaultSpin;
-
-  const bool bf16 = h->dtype == RRB_BF16;
-  // Measured on MI355X: payloads up to 16 KiB (slices of one vector per
-  // lane) run 7-8% faster with one vector per lane in flight; from 32 KiB
-  // the two-vector shape is as fast or faster.
-  const bool one = a.nvec <= 1024 && a.slice_vec <= h->bs;
-  const int var = (h->flags & RRB_SNAC_LAMPORT) ? (one ? kLamportOne : kLamport)
-                  : (h->flags & RRB_SNAC_TWOSHOT) ? kTwoshot
-                  : (h->flags & RRB_SNAC_SPECULATIVE) ? kSpeculative
-                  : (h->flags & RRB_SNAC_DUAL_BUFFER) ? kDual : kBarrier;
-  SnacFn fn = nullptr;
-  if (bf16) {
-    fn = var == kBarrier ? snac_for<true, kBarrier>(h->R)
-         : var == kDual  ? snac_for<true, kDual>(h->R)
-         : var == kTwoshot ? snac_for<true, kTwoshot>(h->R)
-         : var == kLamport ? snac_for<true, kLamport>(h->R)
-         : var == kLamportOne ? snac_for<true, kLamportOne>(h->R)
-                           : snac_for<true, kSpeculative>(h->R);
-  } else {
-    fn = var == kBarrier ? snac_for<false, kBarrier>(h->R)
-         : var == kDual  ? snac_for<false, kDual>(h->R)
-         : var == kTwoshot ? snac_for<false, kTwoshot>(h->R)
-         : var == kLamport ? snac_for<false, kLamport>(h->R)
-         : var == kLamportOne ? snac_for<false, kLamportOne>(h->R)
-                           : snac_for<false, kSpeculative>(h->R);
-  }
-  // Every workgroup waits on others: the grid must be co-resident.
-  const rrb_status st = launch_persistent(h, reinterpret_cast<const void *>(fn), a,
-                                          static_cast<hipStream_t>(stream), "chain");
-  if (st != RRB_OK) return st;
-  h->next_epoch += static_cast<uint32_t>(epochs);
-  return RRB_OK;
+  return launch_ar_chain(h, epochs, d_in, d_out, d_stats, d_stagger, spin_limit, stream);
 }
 
 rrb_status rrb_snac_check(rrb_snac_t h, rrb_stream_t stream) {

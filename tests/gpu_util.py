@@ -1,4 +1,8 @@
-"""Helpers for the GPU parity tests: numpy <-> device, sampling, sentinels."""
+"""Helpers for the GPU parity tests: numpy <-> device, sentinels, and the
+oracle applied in contiguous ranges for full-size compares."""
+
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -48,3 +52,28 @@ def assert_bits_equal(got, want, what=""):
         bad = np.nonzero(gi != wi)[0]
         raise AssertionError(f"{what}: {len(bad)} mismatches, first at {bad[:5]}: "
                              f"got {gi[bad[:5]]} want {wi[bad[:5]]}")
+
+
+def oracle_elementwise(fn, ins, chunk=1 << 22):
+    """fn (an elementwise oracle function of R equal-length arrays, such as
+    oracle.fold.reduce) applied to contiguous element ranges in a thread pool,
+    the results joined.  The oracle itself is unchanged: an elementwise
+    definition gives the same bits on any split of the range.  Threads: the
+    host's CPU share, at most 16."""
+    n = len(ins[0])
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    out = None
+
+    def part(a):
+        b = min(n, a + chunk)
+        return a, fn([x[a:b] for x in ins])
+
+    with ThreadPoolExecutor(max_workers=max(1, min(16, cores))) as pool:
+        for a, r in pool.map(part, range(0, n, chunk)):
+            if out is None:
+                out = np.empty(n, dtype=r.dtype)
+            out[a:a + len(r)] = r
+    return out

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(librrb):
     for n in names:
         assert hasattr(librrb, n), n
     assert set(names) == set(L.EXPORTS)
-    assert librrb.rrb_abi_version() == 1
+    assert librrb.rrb_abi_version() == 2
 
 
 def _apply(segments, ins, in_count, out_count, R, dtype):

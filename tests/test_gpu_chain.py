@@ -105,6 +105,9 @@ def test_chain_staggered_ranks(v):
         if v == "speculative":
             _say(f"  misspec {s[0]} retries {s[1]}")
             assert s[0] > 0  # late ranks force the retry path
+            # a failed check re-reads only the stale sources: at least one,
+            # and never the workgroup's own rank
+            assert s[0] <= s[1] <= s[0] * (R - 1)
         if v == "lamport":
             _say(f"  poll rounds {s[1]}")
             assert s[1] > 0  # late ranks leave untagged words to poll again

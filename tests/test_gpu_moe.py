@@ -150,3 +150,34 @@ def test_moe_random_shapes(seed):
     xa = bf16.rne(rng.standard_normal((T, h)).astype(np.float32))
     shards = [xa[r * (T // R):(r + 1) * (T // R)] for r in range(R)]
     _roundtrip(T, h, E, k, R, idx, w, shards, str(rng.choice(["identity", "seeded"])))
+
+
+@pytest.mark.parametrize("T,h,E,k,R", [(4096, 7168, 256, 8, 8), (64, 24, 16, 4, 8), (32, 13, 8, 3, 4),
+                                       (16, 8, 16, 16, 2)])
+def test_combine_per_call_weights(T, h, E, k, R):
+    """rrb_reduce's d_weights on a host-built combine plan: weights given in
+    the routing arrays' column order replace the plan's for one call (vector
+    and element kernels); the next call without them uses the plan's again."""
+    require_gpu()
+    rng = np.random.default_rng(T * 31 + k)
+    if T == 4096:
+        idx, w = inputs.moe_routing(T, E, k)
+    else:
+        idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+        w = rng.random((T, k)).astype(np.float32)
+    w2 = (rng.standard_normal((T, k)) * 2).astype(np.float32)
+    comb = api.MoePlan(R, h, E, idx, w, "combine")
+    rows = [c // h for c in comb.in_count]
+    z_np = [bf16.rne(rng.standard_normal((n, h)).astype(np.float32)) for n in rows]
+    z = [to_dev(a.reshape(-1)) for a in z_np]
+    y = [empty_like_np(T // R * h, "bf16", -21555) for _ in range(R)]
+    comb.run(z, y, weights=torch.from_numpy(w2).to(z[0].device))
+    torch.cuda.synchronize()
+    want2 = OM.combine(z_np, idx, w2, E, T // R)
+    for r in range(R):
+        assert_bits_equal(from_dev(y[r]).reshape(-1, h), want2[r], f"per-call weights rank {r}")
+    comb.run(z, y)
+    torch.cuda.synchronize()
+    want = OM.combine(z_np, idx, w, E, T // R)
+    for r in range(R):
+        assert_bits_equal(from_dev(y[r]).reshape(-1, h), want[r], f"plan weights rank {r}")

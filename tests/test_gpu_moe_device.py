@@ -107,21 +107,73 @@ def test_device_rerouting_and_host_plan_agree():
         assert_bits_equal(from_dev(arena), cat, f"step {step}: device vs host row plan")
 
 
-def test_device_routing_rejects_bad_routing_in_bounds():
+@pytest.mark.parametrize("T", [64, 4096, 262144])
+def test_device_routing_bad_rows_write_nothing(T):
+    """A routing with a repeated or out-of-range expert is reported by the
+    check, and the dispatch and combine that follow write nothing: every
+    receive row and every token output keeps its earlier contents (no valid
+    row is overwritten).  A later valid routing works again.  T = 64 and 4096
+    take the fused routing kernel, 262,144 tokens the three-kernel path."""
     require_gpu()
-    T, h, E, k, R = 64, 16, 16, 2, 4
-    idx = np.tile(np.array([[1, 2]], dtype=np.int32), (T, 1))
-    idx[3] = [5, 5]    # repeated expert
-    idx[9] = [1, 99]   # out of range
-    w = np.ones((T, k), dtype=np.float32)
-    disp = api.MoeDevicePlan(R, T, h, E, k, "dispatch")
-    disp.route(torch.from_numpy(idx).to(DEV), torch.from_numpy(w).to(DEV))
-    arena = empty_like_np(T * k * h, "bf16")
-    xs = [empty_like_np(T // R * h, "bf16", 1) for _ in range(R)]
-    disp.run(xs, [arena] + [None] * (R - 1))
-    with pytest.raises(L.RrbError) as e:
+    h, E, k, R = 16, 16, 2, 4
+    rng = np.random.default_rng(T)
+    good = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    for bad_kind in ("repeat", "range"):
+        idx = good.copy()
+        if bad_kind == "repeat":
+            idx[T // 3] = [5, 5]
+        else:
+            idx[T - 1] = [1, 99]
+        w = rng.random((T, k)).astype(np.float32)
+        disp = api.MoeDevicePlan(R, T, h, E, k, "dispatch")
+        comb = api.MoeDevicePlan(R, T, h, E, k, "combine", share=disp)
+        disp.route(torch.from_numpy(idx).to(DEV), torch.from_numpy(w).to(DEV))
+        arena = empty_like_np(T * k * h, "bf16", -21555)
+        y = [empty_like_np(T // R * h, "bf16", -21555) for _ in range(R)]
+        xs = [empty_like_np(T // R * h, "bf16", 1) for _ in range(R)]
+        disp.run(xs, [arena] + [None] * (R - 1))
+        comb.run([arena] + [None] * (R - 1), y)
+        with pytest.raises(L.RrbError) as e:
+            disp.check()
+        assert e.value.status == L.RRB_EINVAL, bad_kind
+        assert np.all(from_dev(arena) == np.uint16(0xABCD)), f"{bad_kind}: dispatch wrote rows"
+        for r in range(R):
+            assert np.all(from_dev(y[r]) == np.uint16(0xABCD)), f"{bad_kind}: combine wrote rank {r}"
+        # a valid routing on the same workspace clears the failure
+        disp.route(torch.from_numpy(good).to(DEV), torch.from_numpy(w).to(DEV))
+        disp.run(xs, [arena] + [None] * (R - 1))
         disp.check()
-    assert e.value.status == L.RRB_EINVAL
+        shards = [np.ones((T // R, h), np.uint16) for _ in range(R)]
+        want = np.concatenate(OM.dispatch(shards, good, E), axis=0)
+        assert_bits_equal(from_dev(arena).reshape(T * k, h), want, f"{bad_kind}: re-routed dispatch")
+
+
+def test_device_combine_per_call_weights():
+    """rrb_reduce's per-call weights on a device-routed combine plan: weights
+    given in the routing order replace the routed ones for that call only."""
+    require_gpu()
+    T, h, E, k, R = 512, 136, 32, 4, 8
+    rng = np.random.default_rng(77)
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    w2 = (rng.standard_normal((T, k)) * 3).astype(np.float32)
+    xa = bf16.rne(rng.standard_normal((T, h)).astype(np.float32))
+    shards = [xa[r * (T // R):(r + 1) * (T // R)] for r in range(R)]
+    _, _, _, rows = OM.layout(idx, E, R)
+    z = [bf16.rne(rng.standard_normal((int(n), h)).astype(np.float32)) for n in rows]
+    disp, comb = _run(T, h, E, k, R, idx, w, shards, z)
+    z_arena = to_dev(np.concatenate(z, axis=0).reshape(-1))
+    y = [empty_like_np(T // R * h, "bf16", -21555) for _ in range(R)]
+    comb.run([z_arena] + [None] * (R - 1), y, weights=torch.from_numpy(w2).to(DEV))
+    torch.cuda.synchronize()
+    want2 = OM.combine(z, idx, w2, E, T // R)
+    for r in range(R):
+        assert_bits_equal(from_dev(y[r]).reshape(-1, h), want2[r], f"per-call weights rank {r}")
+    comb.run([z_arena] + [None] * (R - 1), y)
+    torch.cuda.synchronize()
+    want = OM.combine(z, idx, w, E, T // R)
+    for r in range(R):
+        assert_bits_equal(from_dev(y[r]).reshape(-1, h), want[r], f"routed weights again rank {r}")
 
 
 def test_device_plan_unrouted_is_in_bounds():

@@ -122,8 +122,11 @@ def test_plan_chain_staggered_speculation(name):
     st = [r * 64 for r in range(R)]
     stagger = torch.tensor(st, dtype=torch.int32, device=DEV)
     stats, _ = _run_chain(name, R, 8 * 1024, "bf16", "speculative", E=24, stagger=stagger, kind=9)
-    _say(f"  {name}: misspec {stats[0]}")
+    _say(f"  {name}: misspec {stats[0]} retries {stats[1]}")
     assert stats[0] > 0
+    # retries count the source ranks whose entries were redone after a failed
+    # check (none when only write-after-read guards were stale)
+    assert 0 <= stats[1] <= stats[0] * R
     for variant in ("barrier", "dual"):
         _run_chain(name, R, 8 * 1024, "bf16", variant, E=12, stagger=stagger, kind=9)
 
