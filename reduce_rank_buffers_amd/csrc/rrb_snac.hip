@@ -217,28 +217,38 @@ __device__ __forceinline__ uint32_t load_flag_relaxed(const uint32_t *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Orders every later memory access of the wave after the values it has
-// loaded so far: waits until all of its outstanding memory operations have
-// completed (s_waitcnt 0) and keeps the compiler from moving later accesses
-// above this point.  Loads from one wave to different addresses may be served
-// in any order, so a payload load that must not see data older than a flag
-// is issued only after the flag's value has returned.
-__device__ __forceinline__ void wait_returned() {
-  __builtin_amdgcn_s_waitcnt(0);
+// Keeps the compiler from moving later memory accesses above this point,
+// without waiting for anything: for payload loads that must follow flag
+// values the wave has already consumed (in a branch or a reduction), which
+// the hardware only issues after those values have returned.  Loads from one
+// wave to different addresses may be served in any order, so a payload load
+// that must not see data older than a flag is issued only after the flag's
+// value is back; issuing the two together would rest on service order.
+__device__ __forceinline__ void order_after_values() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Sum and bitwise or over the 64 lanes of the wave (every lane gets the result).
-__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
-  return x;
+// Reduced validation flag of the first n lanes' flag values f (n <= 64,
+// uniform): their sum, and the set of lanes whose flag is not `ep`, both
+// wave-uniform.  Each value is read into a scalar register (v_readlane), so
+// the reduction stays in registers and the results steer scalar branches;
+// cross-lane shuffles through LDS cost about 0.5 us per epoch here.
+__device__ __forceinline__ uint32_t lanes_sum(uint32_t f, int n) {
+  uint32_t sum = 0;
+  for (int l = 0; l < n; ++l) sum += __builtin_amdgcn_readlane(f, l);
+  return sum;
 }
-__device__ __forceinline__ uint32_t wave_or(uint32_t x) {
+template <int N>
+__device__ __forceinline__ void flags_reduce(uint32_t f, uint32_t ep, uint32_t &sum, uint32_t &stale) {
+  sum = 0;
+  stale = 0;
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x |= __shfl_xor(x, m);
-  return x;
+  for (int l = 0; l < N; ++l) {
+    const uint32_t fl = __builtin_amdgcn_readlane(f, l);
+    sum += fl;
+    if (fl != ep) stale |= 1u << l;
+  }
 }
 
 // Polls *p until it reaches `want`; false if the budget ran out or another
@@ -296,6 +306,37 @@ __device__ __forceinline__ void reduce_pass(const uint4 (&v)[R], unsigned char *
                                             int64_t off) {
   const uint4 o = BF16 ? fold_bf16x8<R>(v) : fold_f32x4<R>(v);
   store16<WT>(dst, bytes, off, v4u{o.x, o.y, o.z, o.w});
+}
+
+// Stage: vectors [v0, v1) of a rank's payload `src` into its staged buffer
+// `mine` (rank_bytes long), written through, by all the workgroup's lanes.
+// Every pass issues all of its loads before its stores, a partial last pass
+// included: a remainder loop of one load and one store per step put a slice
+// of 2-7 vectors per lane through as many round trips (8 ranks, 512 KiB
+// payload, 256 vectors per workgroup: 6.9 -> 5.4 us per All-Reduce, dual
+// buffer).  A slice of at most one vector per lane takes a single load and
+// store (2-6% less time per All-Reduce at 8-32 KiB than the masked pass).
+__device__ __forceinline__ void stage_slice(const unsigned char *src, unsigned char *mine,
+                                            int64_t rank_bytes, int64_t v0, int64_t v1) {
+  const int bs = blockDim.x;
+  if (v1 - v0 <= bs) {
+    const int64_t i = v0 + threadIdx.x;
+    if (i < v1) store_wt(mine, rank_bytes, i * 16, *reinterpret_cast<const v4u *>(src + i * 16));
+    return;
+  }
+  for (int64_t i0 = v0 + threadIdx.x; i0 < v1; i0 += static_cast<int64_t>(bs) * kStageU) {
+    v4u x[kStageU];  // (HIP's uint4 struct here would be placed in scratch)
+#pragma unroll
+    for (int u = 0; u < kStageU; ++u) {
+      const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+      if (i < v1) x[u] = *reinterpret_cast<const v4u *>(src + i * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < kStageU; ++u) {
+      const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+      if (i < v1) store_wt(mine, rank_bytes, i * 16, x[u]);
+    }
+  }
 }
 
 // Twoshot piece (q, s): slice s of chunk q, as a vector range [lo, hi).
@@ -483,63 +524,38 @@ __global__ void __launch_bounds__(64) snac_chain_kernel(SnacArgs a) {
     }
 
     // Stage: this rank's slice lands in its staged buffer.
-    const unsigned char *src = a.in + (static_cast<int64_t>(k) * R + r) * a.rank_bytes;
-    unsigned char *mine = stage_base + static_cast<int64_t>(r) * a.rank_bytes;
-    // Every pass issues all of its loads before its stores, a partial last
-    // pass included: a remainder loop of one load and one store per step
-    // put a slice of 2-7 vectors per lane through as many round trips (8
-    // ranks, 512 KiB payload, 256 vectors per workgroup: 6.9 -> 5.4 us per
-    // All-Reduce, dual buffer).  A slice of at most one vector per lane
-    // takes a single load and store (2-6% less time per All-Reduce at 8-32
-    // KiB than the masked pass).
-    if (v1 - v0 <= bs) {
-      const int64_t i = v0 + threadIdx.x;
-      if (i < v1) store_wt(mine, a.rank_bytes, i * 16, *reinterpret_cast<const v4u *>(src + i * 16));
-    } else
-    for (int64_t i0 = v0 + threadIdx.x; i0 < v1; i0 += static_cast<int64_t>(bs) * kStageU) {
-      v4u x[kStageU];  // (HIP's uint4 struct here would be placed in scratch)
-#pragma unroll
-      for (int u = 0; u < kStageU; ++u) {
-        const int64_t i = i0 + static_cast<int64_t>(u) * bs;
-        if (i < v1) x[u] = *reinterpret_cast<const v4u *>(src + i * 16);
-      }
-#pragma unroll
-      for (int u = 0; u < kStageU; ++u) {
-        const int64_t i = i0 + static_cast<int64_t>(u) * bs;
-        if (i < v1) store_wt(mine, a.rank_bytes, i * 16, x[u]);
-      }
-    }
+    stage_slice(a.in + (static_cast<int64_t>(k) * R + r) * a.rank_bytes,
+                stage_base + static_cast<int64_t>(r) * a.rank_bytes, a.rank_bytes, v0, v1);
 
     // Notify.
     notify(flags_b + r * stride_rs + s * kFlagStride, ep);
 
-    unsigned char *dst_base = a.out + (static_cast<int64_t>(k) * R + r) * a.rank_bytes;
-    bool ok = true;
     // Consume: fold the R staged slices in rank order, CU vectors x R
     // sources in flight per lane.
+    unsigned char *dst_base = a.out + (static_cast<int64_t>(k) * R + r) * a.rank_bytes;
     constexpr int CU = R <= 8 ? 4 : 2;
     int64_t first = v0 + threadIdx.x;  // first vector of the ordinary passes
-
     if (VAR == kSpeculative) {
       // No top barrier.  One read of the R sources' flags (lanes 0..R-1);
       // once those values have returned, the first pass loads every source
-      // at once, whatever its flag said.  The reduced validation flag (SiFAR
-      // review, Fig. 14) then decides: the flags must sum to R * epoch.
-      // Every flag holds epoch or epoch - 2 (dual buffering keeps each rank
-      // within one epoch of its readers), so the sum is exact, and a valid
-      // sum also proves every source's reads of this buffer two epochs ago
-      // returned before its flag.  A source whose flag read as the epoch was
-      // complete before its loads were issued, so on a mismatch only the
-      // stale sources are waited for and read again; the fresh ones' data is
-      // kept in registers.
+      // whatever its flag said.  The reduced validation flag (SiFAR review,
+      // Fig. 14) decides: the flags must sum to R * epoch.  Every flag holds
+      // epoch or epoch - 2 (dual buffering keeps each rank within one epoch
+      // of its readers), so the sum is exact, and a valid sum also proves
+      // every source's reads of this buffer two epochs ago returned before
+      // its flag.  A source whose flag read as the epoch had finished staging
+      // before its loads were issued, so on a mismatch only the stale sources
+      // are waited for and read again; the others' data stays in registers.
       uint32_t f = 0;
       if (threadIdx.x < R) f = load_flag_relaxed(flags_b + threadIdx.x * stride_rs + s * kFlagStride);
-      const uint32_t sum = wave_sum(threadIdx.x < R ? f : 0u);
-      const uint32_t stale = wave_or(threadIdx.x < R && f != ep ? 1u << threadIdx.x : 0u);
-      wait_returned();
+      uint32_t sum, stale;
+      flags_reduce<R>(f, ep, sum, stale);
+      order_after_values();
       constexpr uint32_t kAll = R >= 32 ? ~0u : (1u << R) - 1u;
       const bool valid = sum == static_cast<uint32_t>(R) * ep;
-      const uint32_t redo = valid ? 0u : (stale ? stale : kAll);
+      // re-read after the wait (a failed sum always has a stale flag; all,
+      // should it not)
+      const uint32_t late = valid ? 0u : (stale ? stale : kAll);
       uint4 v[CU][R];
 #pragma unroll
       for (int u = 0; u < CU; ++u) {
@@ -551,19 +567,20 @@ __global__ void __launch_bounds__(64) snac_chain_kernel(SnacArgs a) {
                                     static_cast<int32_t>(i * 16));
         }
       }
-      if (redo) {
+      bool ok = true;
+      if (late) {
         ++misspec;
-        retries += static_cast<unsigned long long>(__builtin_popcount(redo));
+        retries += static_cast<unsigned long long>(__builtin_popcount(late));
         bool mine = true;
-        if (threadIdx.x < R && (redo >> threadIdx.x & 1u))
+        if (threadIdx.x < R && (late >> threadIdx.x & 1u))
           mine = wait_at_least(flags_b + threadIdx.x * stride_rs + s * kFlagStride, ep, a.status,
                                a.spin_limit);
         ok = __all(mine) != 0;
         if (ok) {
-          wait_returned();
+          order_after_values();
 #pragma unroll
           for (int q = 0; q < R; ++q) {
-            if (redo >> q & 1u) {
+            if (late >> q & 1u) {
 #pragma unroll
               for (int u = 0; u < CU; ++u) {
                 const int64_t i = first + static_cast<int64_t>(u) * bs;
@@ -576,18 +593,18 @@ __global__ void __launch_bounds__(64) snac_chain_kernel(SnacArgs a) {
           }
         }
       }
-      if (ok) {
+      if (!ok) {
+        ++timeouts;
+        break;
+      }
 #pragma unroll
-        for (int u = 0; u < CU; ++u) {
-          const int64_t i = first + static_cast<int64_t>(u) * bs;
-          if (i < v1) reduce_pass<R, BF16>(v[u], dst_base, a.rank_bytes, i * 16);
-        }
+      for (int u = 0; u < CU; ++u) {
+        const int64_t i = first + static_cast<int64_t>(u) * bs;
+        if (i < v1) reduce_pass<R, BF16>(v[u], dst_base, a.rank_bytes, i * 16);
       }
       first += static_cast<int64_t>(bs) * CU;
-    } else {
-      ok = wait_all<R>(flags_b + s * kFlagStride, stride_rs, ep, a.status, a.spin_limit, lds_ok);
-    }
-    if (!ok) {
+    } else if (!wait_all<R>(flags_b + s * kFlagStride, stride_rs, ep, a.status, a.spin_limit, lds_ok)) {
+      // the top barrier over the R sources' flags of this slice
       ++timeouts;
       break;
     }
@@ -862,11 +879,12 @@ __device__ bool wait_list(const uint32_t *base, const int32_t *idx, int n, uint3
   return all;
 }
 
-// Piece s of every entry of rank r: staged data read with device-coherent
-// loads, results stored to rank r's output of this epoch with plain stores
-// (only the host reads outputs).  `only` (bit q: source rank q) restricts the
-// pass to the entries that read a rank in the mask -- a copy from such a rank,
-// or any fold -- so a failed speculative check redoes just those.
+// Piece s of the entries of rank r that read a rank in `stale` (a copy from
+// such a rank, or any fold when `stale` is not empty) if `touching`, else of
+// the others: staged data read with device-coherent loads, results stored to
+// rank r's output of this epoch with plain stores (only the host reads
+// outputs).  stale = 0 with touching = false selects every entry; the
+// speculative consume runs the two halves on either side of its wait.
 //
 // A rank whose entries are all copies of one length (All-Gather, All-to-All,
 // Gather) takes its pieces as one flat index range over all lanes, kCopyU
@@ -878,7 +896,7 @@ constexpr int kFlatEntries = 64;
 template <int R, bool BF16>
 __device__ void plan_consume(const PlanChainArgs &a, int r, int s,
                              const unsigned char *stage_base, unsigned char *dst,
-                             const PlanEntry *ents, uint32_t only) {
+                             const PlanEntry *ents, uint32_t stale, bool touching) {
   const int bs = blockDim.x;
   constexpr int CU = R <= 8 ? 2 : 1;
   constexpr int CC = 4;  // copy vectors per lane in flight
@@ -900,7 +918,7 @@ __device__ void plan_consume(const PlanChainArgs &a, int r, int s,
         if (f < total) {
           const uint32_t g = f / w;
           const PlanEntry e = ents[g];
-          if (only >> e.src_rank & 1u) {
+          if ((stale >> e.src_rank & 1u) == static_cast<uint32_t>(touching)) {
             const int64_t i = lo + (f - g * w);
             x[u] = load_coherent(src, static_cast<int32_t>(e.src_rank * a.in_stride + (e.src_off + i) * 16));
             at[u] = (e.dst_off + i) * 16;
@@ -915,7 +933,7 @@ __device__ void plan_consume(const PlanChainArgs &a, int r, int s,
   }
   for (int g = a.first[r]; g < a.first[r] + a.cnt[r]; ++g) {
     const PlanEntry e = a.entries[g];
-    if (e.src_rank < 0 ? only == 0 : !(only >> e.src_rank & 1u)) continue;
+    if ((e.src_rank < 0 ? stale != 0 : (stale >> e.src_rank & 1u) != 0) != touching) continue;
     const int64_t pl = (e.len + a.S - 1) / a.S;
     const int64_t lo = min(e.len, static_cast<int64_t>(s) * pl);
     const int64_t hi = min(e.len, lo + pl);
@@ -1012,35 +1030,45 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
     bool ok = true;
     if (VAR == kSpeculative) {
       // One read of the listed flags; once their values have returned, the
-      // whole consume runs, whatever they said.  The reduced check: they must
-      // sum to (list length) x epoch (each is epoch or epoch - 2, so the sum
-      // is exact).  On a mismatch the workgroup waits for every listed flag
-      // (the write-after-read guards included) and redoes only the entries
-      // that read a rank whose data flag was stale; entries whose sources
-      // were all fresh stand, their loads having been issued after the flags.
+      // whole consume runs, whatever they said.  The reduced check: the flags
+      // must sum to (list length) x epoch (each is epoch or epoch - 2, so the
+      // sum is exact).  On a mismatch the workgroup waits for every listed
+      // flag (the write-after-read guards included) and redoes only the
+      // entries that read a rank whose data flag was stale; the others stand,
+      // their loads having been issued after their sources' flags showed the
+      // epoch.
       uint32_t sum = 0, stale = 0;
-      for (int i = threadIdx.x; i < nw; i += bs) {
-        const int32_t w = wl[i];
-        const uint32_t f = load_flag_relaxed(flags_b + static_cast<int64_t>(w & kFlagIndexMask) * kFlagStride);
-        sum += f;
-        if (f != ep && !(w & kGuardOnly)) stale |= 1u << ((w & kFlagIndexMask) / a.S);
+      for (int i0 = 0; i0 < nw; i0 += bs) {
+        const int i = i0 + static_cast<int>(threadIdx.x);
+        int32_t w = 0;
+        uint32_t f = ep;
+        if (i < nw) {
+          w = wl[i];
+          f = load_flag_relaxed(flags_b + static_cast<int64_t>(w & kFlagIndexMask) * kFlagStride);
+        }
+        sum += lanes_sum(f, min(bs, nw - i0));
+        // Lanes holding a stale data flag: their ranks' entries wait.
+        for (uint64_t bad = __ballot(i < nw && f != ep && !(w & kGuardOnly)); bad; bad &= bad - 1) {
+          const int l = __builtin_ctzll(bad);
+          stale |= 1u << ((__builtin_amdgcn_readlane(w, l) & kFlagIndexMask) / a.S);
+        }
       }
-      sum = wave_sum(sum);
-      stale = wave_or(stale);
-      wait_returned();
-      plan_consume<R, BF16>(a, r, s, stage_base, dst, ents, ~0u);
-      if (sum != static_cast<uint32_t>(nw) * ep) {
+      order_after_values();
+      const bool valid = sum == static_cast<uint32_t>(nw) * ep;
+      if (valid) stale = 0;  // (a valid sum has no stale flag)
+      plan_consume<R, BF16>(a, r, s, stage_base, dst, ents, 0u, false);
+      if (!valid) {
         ++misspec;
         retries += static_cast<unsigned long long>(__builtin_popcount(stale));
         ok = wait_list(flags_b, wl, nw, ep, a.status, a.spin_limit);
         if (ok) {
-          wait_returned();
-          if (stale) plan_consume<R, BF16>(a, r, s, stage_base, dst, ents, stale);
+          order_after_values();
+          if (stale) plan_consume<R, BF16>(a, r, s, stage_base, dst, ents, stale, true);
         }
       }
     } else {
       ok = wait_list(flags_b, wl, nw, ep, a.status, a.spin_limit);
-      if (ok) plan_consume<R, BF16>(a, r, s, stage_base, dst, ents, ~0u);
+      if (ok) plan_consume<R, BF16>(a, r, s, stage_base, dst, ents, 0u, false);
     }
     if (!ok) {
       ++timeouts;
