@@ -431,6 +431,32 @@ rrb_status rrb_snac_strides(rrb_snac_t h, int64_t *in_stride, int64_t *out_strid
 rrb_status rrb_snac_chain(rrb_snac_t h, int32_t epochs, const void *d_in, void *d_out,
                           rrb_snac_stats *d_stats, const uint32_t *d_stagger,
                           uint32_t spin_limit, rrb_stream_t stream);
+/*
+ * rrb_snac_allreduce_chain without allocation, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Creates, binds and runs an All-Reduce
+ * chain handle of (nranks, count, dtype, flags, slices) in one call, with the
+ * staging buffers, flags and status word in a static device array of 20 MiB
+ * per GPU (held until the process ends) instead of caller workspace; no
+ * handle, no hipMalloc.  flags: 0, RRB_SNAC_DUAL_BUFFER,
+ * RRB_SNAC_DUAL_BUFFER | RRB_SNAC_SPECULATIVE or RRB_SNAC_TWOSHOT |
+ * RRB_SNAC_DUAL_BUFFER (each optionally | RRB_SNAC_COOPERATIVE);
+ * RRB_SNAC_GRAPH and RRB_SNAC_LAMPORT return RRB_EUNSUPPORTED.  A chain whose
+ * staging and flags exceed the array (8 ranks of up to 1 MiB each fit)
+ * returns RRB_EUNSUPPORTED with the bytes it needs.  d_in, d_out, d_stats,
+ * spin_limit and the results as for rrb_snac_allreduce_chain; a wait that
+ * ran out is reported in d_stats->timeouts (pass d_stats to see it).  Every
+ * call on a GPU shares that GPU's array: each call clears the flags with a
+ * fill kernel on `stream` and restarts at epoch 1, so calls that overlap on
+ * one GPU (other streams, other host threads) race and must be serialised
+ * by the caller.
+ */
+rrb_status rrb_snac_allreduce_chain_noalloc(int32_t nranks, int64_t count, int32_t dtype,
+                                            uint32_t flags, int32_t slices, int32_t epochs,
+                                            const void *d_in, void *d_out,
+                                            rrb_snac_stats *d_stats, uint32_t spin_limit,
+                                            rrb_stream_t stream);
+
 /* Synchronise `stream` and report RRB_ETIMEOUT if any chain call on this
  * handle since bind timed out (the handle is unusable until rebound). */
 rrb_status rrb_snac_check(rrb_snac_t h, rrb_stream_t stream);

@@ -47,7 +47,7 @@ EXPORTS = (
     "rrb_copy", "rrb_reduce", "rrb_plan_launch_info", "rrb_empty_kernel",
     "rrb_snac_create", "rrb_snac_workspace", "rrb_snac_bind", "rrb_snac_allreduce_chain",
     "rrb_snac_create_plan", "rrb_snac_strides", "rrb_snac_chain",
-    "rrb_snac_check", "rrb_snac_destroy",
+    "rrb_snac_allreduce_chain_noalloc", "rrb_snac_check", "rrb_snac_destroy",
 )
 
 
@@ -109,6 +109,7 @@ _SIGS = {
     "rrb_snac_create_plan": (_I32, [_P, _U32, _I32, ctypes.POINTER(_P)]),
     "rrb_snac_strides": (_I32, [_P, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
     "rrb_snac_chain": (_I32, [_P, _I32, _P, _P, _P, _P, _U32, _P]),
+    "rrb_snac_allreduce_chain_noalloc": (_I32, [_I32, _I64, _I32, _U32, _I32, _I32, _P, _P, _P, _U32, _P]),
     "rrb_snac_check": (_I32, [_P, _P]),
     "rrb_snac_destroy": (None, [_P]),
 }

@@ -527,6 +527,35 @@ class SnacChain:
         self.close()
 
 
+def allreduce_chain_noalloc(inp, out, variant="dual", stats=None, spin_limit=0, stream=None,
+                            cooperative=False):
+    """`inp.shape[0]` chained All-Reduces of inp [epochs, R, count] into out,
+    with the library's static per-GPU scratch instead of a workspace
+    (rrb_snac_allreduce_chain_noalloc: no device allocation).  variant:
+    barrier, dual, speculative or twoshot.  Calls that overlap on one GPU
+    race; a wait that ran out shows in stats[2]."""
+    if variant not in ("barrier", "dual", "speculative", "twoshot"):
+        raise ValueError(f"variant {variant!r} has no allocation-free form")
+    if not isinstance(inp, torch.Tensor) or inp.dim() != 3:
+        raise ValueError("inp: expected a tensor of shape [epochs, R, count]")
+    E, R, n = inp.shape
+    dt = _dtype_of(inp)
+    checked = []
+    for t, what in ((inp, "inp"), (out, "out")):
+        if not isinstance(t, torch.Tensor) or tuple(t.shape) != (E, R, n):
+            raise ValueError(f"{what}: expected a tensor of shape [{E}, {R}, {n}]")
+        _check_tensor(t, what, dt, 0)
+        checked.append((t, what))
+    checked += _check_aux(stats, "stats", (torch.int64,), 4)
+    _all_on_gpu(checked)
+    flags = VARIANTS[variant] | (L.RRB_SNAC_COOPERATIVE if cooperative else 0)
+    L.check(L.lib().rrb_snac_allreduce_chain_noalloc(
+        int(R), int(n), dt, flags, 0, int(E), ctypes.c_void_p(inp.data_ptr()),
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stats.data_ptr() if stats is not None else 0),
+        int(spin_limit), _stream(stream)), "rrb_snac_allreduce_chain_noalloc")
+    return out
+
+
 PLAN_CHAIN_VARIANTS = {"barrier": 0, "dual": L.RRB_SNAC_DUAL_BUFFER,
                        "speculative": L.RRB_SNAC_DUAL_BUFFER | L.RRB_SNAC_SPECULATIVE,
                        "graph": L.RRB_SNAC_GRAPH}

@@ -1757,3 +1757,98 @@ rrb_status rrb_snac_check(rrb_snac_t h, rrb_stream_t stream) {
 void rrb_snac_destroy(rrb_snac_t h) { delete h; }
 
 }  // extern "C"
+
+// ---- the All-Reduce chain without allocation ---------------------------------
+//
+// For callers that cannot allocate device memory (code under HIP graph
+// capture, tight serving loops, harnesses that forbid allocation): the
+// staging buffers, flags and status word of a chain call live in `scratch`, a
+// file-scope device array of fixed size.  Each GPU the library runs on holds
+// its own copy until the process ends; every call on a GPU shares it.
+
+#include <mutex>
+
+namespace {
+// 8 ranks of up to 1 MiB each, twoshot included, fit (about 18.7 MiB).
+constexpr int64_t kNoAllocScratchBytes = 20LL << 20;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+unsigned char *g_scratch[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, by its device address, looked up
+// once per device with that device current.  In host code the array's name
+// is only a stand-in: it is never passed to a kernel or a copy.
+rrb_status device_scratch(unsigned char **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(RRB_EHIP, "current device: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(RRB_EUNSUPPORTED, "device %d: the static scratch covers devices 0..%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(RRB_EHIP, "static scratch address on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch[dev] = static_cast<unsigned char *>(p);
+  }
+  *out = g_scratch[dev];
+  return RRB_OK;
+}
+
+}  // namespace
+
+extern "C" rrb_status rrb_snac_allreduce_chain_noalloc(int32_t nranks, int64_t count, int32_t dtype,
+                                                       uint32_t flags, int32_t slices, int32_t epochs,
+                                                       const void *d_in, void *d_out,
+                                                       rrb_snac_stats *d_stats, uint32_t spin_limit,
+                                                       rrb_stream_t stream) {
+  clear_error();
+  rrb_status st = check_ar_chain_args(nranks, count, dtype, flags, slices);
+  if (st != RRB_OK) return st;
+  if (flags & (RRB_SNAC_GRAPH | RRB_SNAC_LAMPORT))
+    return fail(RRB_EUNSUPPORTED,
+                "the allocation-free chain runs the flag protocols (barrier, dual, speculative, twoshot)");
+  if (epochs < 0) return fail(RRB_EINVAL, "negative epoch count");
+  const int esz = elem_size(dtype);
+  // The handle's fields on the stack; its containers stay empty, so nothing
+  // is allocated.
+  rrb_snac_s h;
+  h.R = nranks;
+  h.count = count;
+  h.dtype = dtype;
+  h.flags = flags;
+  h.S = default_slices(slices, count * esz / 16, nranks, flags, false);
+  h.bs = 64;
+  h.in_stride = h.out_stride = count * esz;
+  h.lay = layout_for(nranks, count, dtype, h.S, false);
+  if (h.lay.total > kNoAllocScratchBytes)
+    return fail(RRB_EUNSUPPORTED,
+                "this chain needs %lld bytes of scratch; the static scratch holds %lld (8 ranks of up "
+                "to 1 MiB each)",
+                (long long)h.lay.total, (long long)kNoAllocScratchBytes);
+  if (epochs == 0) return RRB_OK;
+  if (!d_in || !d_out) return fail(RRB_EINVAL, "NULL payload pointer");
+  if ((reinterpret_cast<uintptr_t>(d_in) | reinterpret_cast<uintptr_t>(d_out)) & 15)
+    return fail(RRB_EINVAL, "payloads must be 16-byte aligned");
+  unsigned char *ws = nullptr;
+  st = device_scratch(&ws);
+  if (st != RRB_OK) return st;
+  h.ws = ws;
+  h.next_epoch = 1;
+  // The array keeps the last call's contents: every call clears its flags,
+  // done words and status word and starts again at epoch 1.  A fill kernel on
+  // the stream, not a memset, so a captured graph replays it correctly.
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(64), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     reinterpret_cast<uint32_t *>(ws + h.lay.flag_off),
+                     static_cast<int64_t>((h.lay.total - h.lay.flag_off) / 4), 0u);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(RRB_EHIP, "scratch flag clear: %s", hipGetErrorString(e));
+  return launch_ar_chain(&h, epochs, d_in, d_out, d_stats, nullptr, spin_limit, stream);
+}
