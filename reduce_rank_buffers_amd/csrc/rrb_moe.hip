@@ -51,6 +51,14 @@ __device__ __forceinline__ bool route_failed(const RowArgs &a) {
   return a.route_status && *a.route_status != 0;
 }
 
+// The routing status word, 0 for host-built plans.  The branch is on a
+// kernel argument, so the load is a scalar load issued without a wait.
+__device__ __forceinline__ int32_t route_status_word(const RowArgs &a) {
+  int32_t st = 0;
+  if (a.route_status) st = *a.route_status;
+  return st;
+}
+
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 // One workgroup per part of a token row, one 16-byte vector per lane, each
@@ -59,7 +67,48 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 // 5.2 with plain stores).  Parts of at most 256 vectors: for a 7168-wide row,
 // 4 parts of 224 vectors ran 4-7% ahead of one 128-lane workgroup with 8
 // vectors per lane (interleaved A/B runs, 4096 tokens, top-8).
+//
+// The token's K slots are read before the first store.  Reads that no store
+// precedes are scalar loads issued in one batch; a slot read between stores
+// becomes a vector load, and the wait for it (vmcnt counts stores too) makes
+// each of the K stores finish before the next one is issued.  Token and
+// vector indices fit 32 bits (tokens * k < 2^26, rows < 2^31 bytes).
+//
+// The routing status is read in the same batch and decides without a branch:
+// after a failed routing every slot reads as 0 (a failed routing may leave
+// them unset) and the row loop is empty, so nothing is written.
+template <int K>
 __global__ void __launch_bounds__(256) moe_dispatch_kernel(RowArgs a) {
+  const uint32_t parts = static_cast<uint32_t>(a.parts);
+  const uint32_t t = blockIdx.x / parts;
+  const int32_t status = route_status_word(a);
+  const int32_t *slots = a.slot + static_cast<int64_t>(t) * K;
+  int32_t s[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) s[j] = slots[j];
+  const bool ok = status == 0;
+#pragma unroll
+  for (int j = 0; j < K; ++j) s[j] = ok ? s[j] : 0;
+  const uint32_t tpr = static_cast<uint32_t>(a.tokens_per_rank);
+  const uint32_t src_rank = t / tpr;
+  const unsigned char *src = a.in[src_rank] + static_cast<int64_t>(t - src_rank * tpr) * a.row_bytes;
+  unsigned char *dst[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j)
+    dst[j] = a.out[s[j] >> kSlotRankShift] + static_cast<int64_t>(s[j] & kSlotRowMask) * a.row_bytes;
+  const uint32_t pv = static_cast<uint32_t>(a.part_vec), nv = static_cast<uint32_t>(a.nvec);
+  const uint32_t v0 = (blockIdx.x - t * parts) * pv;
+  const uint32_t v1 = !ok ? v0 : v0 + pv < nv ? v0 + pv : nv;
+  for (uint32_t i = v0 + threadIdx.x; i < v1; i += blockDim.x) {
+    const v4u x = *reinterpret_cast<const v4u *>(src + i * 16);
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      __builtin_nontemporal_store(x, reinterpret_cast<v4u *>(dst[j] + i * 16));
+  }
+}
+
+// Any other k: the same copy with the slots read per store.
+__global__ void __launch_bounds__(256) moe_dispatch_any_kernel(RowArgs a) {
   if (route_failed(a)) return;
   const int64_t t = blockIdx.x / a.parts;
   const int64_t v0 = (static_cast<int64_t>(blockIdx.x) - t * a.parts) * a.part_vec;
@@ -136,28 +185,47 @@ __device__ __forceinline__ v4u combine_vec(const v4u (&z)[K], const float (&w)[K
 // of one 256-lane workgroup with 4 vectors per lane (interleaved A/B runs).
 template <int K, int CU>
 __global__ void __launch_bounds__(128) moe_combine_kernel(RowArgs a) {
-  if (route_failed(a)) return;
-  const int64_t t = blockIdx.x / a.parts;
-  const int64_t v0 = (static_cast<int64_t>(blockIdx.x) - t * a.parts) * a.part_vec;
-  const int64_t v1 = v0 + a.part_vec < a.nvec ? v0 + a.part_vec : a.nvec;
-  const int64_t dst_rank = t / a.tokens_per_rank;
-  unsigned char *dst = a.out[dst_rank] + (t - dst_rank * a.tokens_per_rank) * a.row_bytes;
-  const int32_t *slots = a.slot + t * K;
-  const float *ws = a.weight + t * K;
-  const unsigned char *rows[K];
+  const uint32_t parts = static_cast<uint32_t>(a.parts);
+  const uint32_t t = blockIdx.x / parts;
+  const int64_t tk = static_cast<int64_t>(t) * K;
+  // Routing status, slots and weights in one batch of scalar loads.  After a
+  // failed routing (which may leave the maps unset) every slot reads as 0
+  // and the row loop is empty, so nothing is read through the maps or
+  // written.  Per-call weights follow their routing column.
+  const int32_t status = route_status_word(a);
+  int32_t s[K];
   float w[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    const int32_t s = slots[j];
-    rows[j] = a.in[s >> kSlotRankShift] + static_cast<int64_t>(s & kSlotRowMask) * a.row_bytes;
-    w[j] = a.wover ? a.wover[t * K + a.col[t * K + j]] : ws[j];
+    s[j] = a.slot[tk + j];
+    w[j] = a.weight[tk + j];
   }
-  const int bs = blockDim.x;
-  for (int64_t i0 = v0 + threadIdx.x; i0 < v1; i0 += static_cast<int64_t>(bs) * CU) {
+  const bool ok = status == 0;
+#pragma unroll
+  for (int j = 0; j < K; ++j) s[j] = ok ? s[j] : 0;
+  if (a.wover && ok) {
+    int32_t c[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) c[j] = a.col[tk + j];
+#pragma unroll
+    for (int j = 0; j < K; ++j) w[j] = a.wover[tk + c[j]];
+  }
+  const uint32_t tpr = static_cast<uint32_t>(a.tokens_per_rank);
+  const uint32_t dst_rank = t / tpr;
+  unsigned char *dst = a.out[dst_rank] + static_cast<int64_t>(t - dst_rank * tpr) * a.row_bytes;
+  const unsigned char *rows[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j)
+    rows[j] = a.in[s[j] >> kSlotRankShift] + static_cast<int64_t>(s[j] & kSlotRowMask) * a.row_bytes;
+  const uint32_t pv = static_cast<uint32_t>(a.part_vec), nv = static_cast<uint32_t>(a.nvec);
+  const uint32_t v0 = (blockIdx.x - t * parts) * pv;
+  const uint32_t v1 = !ok ? v0 : v0 + pv < nv ? v0 + pv : nv;
+  const uint32_t bs = blockDim.x;
+  for (uint32_t i0 = v0 + threadIdx.x; i0 < v1; i0 += bs * CU) {
     v4u z[CU][K];
 #pragma unroll
     for (int u = 0; u < CU; ++u) {
-      const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+      const uint32_t i = i0 + u * bs;
       if (i < v1) {
 #pragma unroll
         for (int j = 0; j < K; ++j)
@@ -166,7 +234,7 @@ __global__ void __launch_bounds__(128) moe_combine_kernel(RowArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < CU; ++u) {
-      const int64_t i = i0 + static_cast<int64_t>(u) * bs;
+      const uint32_t i = i0 + u * bs;
       if (i < v1)
         __builtin_amdgcn_raw_buffer_store_b128(
             combine_vec<K>(z[u], w),
@@ -693,6 +761,19 @@ namespace {
 
 using RowFn = void (*)(RowArgs);
 
+// Dispatch kernel for top-k (nullptr: the any-k kernel).
+RowFn dispatch_for(int k) {
+  switch (k) {
+    case 1: return moe_dispatch_kernel<1>;
+    case 2: return moe_dispatch_kernel<2>;
+    case 4: return moe_dispatch_kernel<4>;
+    case 6: return moe_dispatch_kernel<6>;
+    case 8: return moe_dispatch_kernel<8>;
+    case 16: return moe_dispatch_kernel<16>;
+    default: return nullptr;
+  }
+}
+
 // Combine kernel for top-k and its vectors per lane (k * CU >= 8 loads in
 // flight per lane).
 RowFn combine_for(int k, int *cu) {
@@ -751,7 +832,8 @@ rrb_status launch_rows(const Plan &p, const void *const *in, void *const *out, c
   a.part_vec = a.nvec;
   if (m.dir == RRB_MOE_DISPATCH) {
     if (vec) {
-      kern = moe_dispatch_kernel;
+      kern = dispatch_for(m.topk);
+      if (!kern) kern = moe_dispatch_any_kernel;
       split_row(a, 256);
     } else {
       kern = moe_dispatch_elem_kernel;
