@@ -29,6 +29,37 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
          (static_cast<uint32_t>(f32_to_bf16_rne(hi)) << 16);
 }
 
+// Eight fp32 values to eight bf16 with gfx950's packed conversion
+// (v_cvt_pk_bf16_f32: round to nearest even in the default rounding mode,
+// subnormals kept, the same bits as f32_to_bf16_rne for every value that is
+// not a NaN).  The hardware keeps a NaN's sign and payload, so a wave with a
+// NaN in any lane's eight takes f32_to_bf16_rne instead (the same bits for
+// every other value).  The test is four unordered compares into wave masks,
+// ORed on the scalar unit (predicate 8 is LLVM's FCMP_UNO).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+__device__ __forceinline__ uint4 pack_bf16x8(const float (&a)[8]) {
+  uint4 o;
+  const uint64_t nan = __builtin_amdgcn_fcmpf(a[0], a[1], 8) | __builtin_amdgcn_fcmpf(a[2], a[3], 8) |
+                       __builtin_amdgcn_fcmpf(a[4], a[5], 8) | __builtin_amdgcn_fcmpf(a[6], a[7], 8);
+  if (nan) {
+    o.x = pack_bf16x2(a[0], a[1]);
+    o.y = pack_bf16x2(a[2], a[3]);
+    o.z = pack_bf16x2(a[4], a[5]);
+    o.w = pack_bf16x2(a[6], a[7]);
+  } else {
+    o.x = cvt_pk_bf16(a[0], a[1]);
+    o.y = cvt_pk_bf16(a[2], a[3]);
+    o.z = cvt_pk_bf16(a[4], a[5]);
+    o.w = cvt_pk_bf16(a[6], a[7]);
+  }
+  return o;
+}
+
 // Fixed rank-order fold of 8 bf16 lanes from R sources: fp32 accumulation,
 // one rounding at the end.  The adds are written one per step so the
 // compiler cannot reassociate them (no fast-math anywhere in this library).
@@ -46,12 +77,7 @@ __device__ __forceinline__ uint4 fold_bf16x8(const uint4 (&v)[R]) {
     a[4] = a[4] + bf16_lo(v[r].z); a[5] = a[5] + bf16_hi(v[r].z);
     a[6] = a[6] + bf16_lo(v[r].w); a[7] = a[7] + bf16_hi(v[r].w);
   }
-  uint4 o;
-  o.x = pack_bf16x2(a[0], a[1]);
-  o.y = pack_bf16x2(a[2], a[3]);
-  o.z = pack_bf16x2(a[4], a[5]);
-  o.w = pack_bf16x2(a[6], a[7]);
-  return o;
+  return pack_bf16x8(a);
 }
 
 // Tree-order sum of R fp32 terms held in t[] (overwritten): pairwise, level
@@ -96,12 +122,7 @@ __device__ __forceinline__ uint4 fold_tree_bf16x8(const uint4 (&v)[R]) {
     }
     s[k] = tree_sum<R>(t);
   }
-  uint4 o;
-  o.x = pack_bf16x2(s[0], s[1]);
-  o.y = pack_bf16x2(s[2], s[3]);
-  o.z = pack_bf16x2(s[4], s[5]);
-  o.w = pack_bf16x2(s[6], s[7]);
-  return o;
+  return pack_bf16x8(s);
 }
 
 template <int R>

@@ -168,12 +168,8 @@ __device__ __forceinline__ v4u combine_vec(const v4u (&z)[K], const float (&w)[K
       acc[2 * q + 1] = acc[2 * q + 1] + hi;
     }
   }
-  v4u o;
-  o[0] = pack_bf16x2(acc[0], acc[1]);
-  o[1] = pack_bf16x2(acc[2], acc[3]);
-  o[2] = pack_bf16x2(acc[4], acc[5]);
-  o[3] = pack_bf16x2(acc[6], acc[7]);
-  return o;
+  const uint4 p = pack_bf16x8(acc);
+  return v4u{p.x, p.y, p.z, p.w};
 }
 
 // One workgroup per part of a token row: CU vectors x K rows in flight per

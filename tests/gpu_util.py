@@ -10,6 +10,14 @@ import torch
 DEV = torch.device("cuda", 0)
 
 
+# bf16 bit patterns for special-value tests: zeros, subnormals, ones, the
+# largest finite values, infinities, and NaNs of both signs with and without
+# payload (quiet and signalling).  Every NaN result must come out as 0x7FC0.
+BF16_SPECIALS = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x0002, 0x8003, 0x007F, 0x0080, 0x3F80,
+                          0xBF80, 0x7F7F, 0xFF7F, 0x7F00, 0x4000, 0xC000, 0x3F81, 0xBF81, 0x0100,
+                          0x7F80, 0xFF80, 0x7FC0, 0xFFC0, 0x7FC1, 0x7F81, 0xFF81], dtype=np.uint16)
+
+
 def require_gpu():
     assert torch.cuda.is_available(), "GPU tests need an MI355X (run them with -m gpu where one is present)"
 

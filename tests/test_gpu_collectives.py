@@ -14,8 +14,8 @@ import torch
 
 from oracle import collectives as C, fold
 from reduce_rank_buffers_amd import api, inputs
-from tests.gpu_util import (DEV, assert_bits_equal, empty_like_np, from_dev, oracle_elementwise,
-                            require_gpu, sentinel, to_dev)
+from tests.gpu_util import (BF16_SPECIALS, DEV, assert_bits_equal, empty_like_np, from_dev,
+                            oracle_elementwise, require_gpu, sentinel, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -212,9 +212,7 @@ def test_unaligned_pointers():
 def test_special_values_and_denormals():
     require_gpu()
     R = 8
-    vals = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x3F80, 0xBF80, 0x7F7F,
-                     0xFF7F, 0x7F00, 0x4000, 0xC000, 0x3F81, 0xBF81, 0x0100, 0x7F80, 0xFF80,
-                     0x7FC0], dtype=np.uint16)
+    vals = BF16_SPECIALS
     rng = np.random.default_rng(4)
     n = 8 * 4096
     ins = [vals[rng.integers(0, len(vals), size=n)] for _ in range(R)]

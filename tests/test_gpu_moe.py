@@ -11,7 +11,7 @@ import torch
 
 from oracle import bf16, moe as OM
 from reduce_rank_buffers_amd import api, inputs
-from tests.gpu_util import assert_bits_equal, empty_like_np, from_dev, require_gpu, to_dev
+from tests.gpu_util import BF16_SPECIALS, assert_bits_equal, empty_like_np, from_dev, require_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -125,6 +125,26 @@ def test_combine_no_contraction_and_ascending_expert_order(k, h):
         got, want = _combine_one_token(k, h, order, [1.0] * k, z)
         assert np.all(want == 0x0000)
         assert_bits_equal(got, want, f"combine order k={k} h={h}")
+
+
+@pytest.mark.parametrize("h", [16, 13])
+def test_combine_special_values(h):
+    """Expert rows of zeros, subnormals, infinities and NaNs of both signs
+    with and without payload through the vector (h = 16) and element
+    (h = 13) combine paths: every NaN result is 0x7FC0, the rest match the
+    oracle bit for bit."""
+    require_gpu()
+    T, E, k, R = 64, 16, 4, 8
+    idx, w = inputs.moe_routing(T, E, k)
+    comb = api.MoePlan(R, h, E, idx, w, "combine")
+    rng = np.random.default_rng(7 + h)
+    z_np = [BF16_SPECIALS[rng.integers(0, len(BF16_SPECIALS), size=(n, h))] for n in comb.rows_per_rank]
+    y = [empty_like_np(T // R * h, "bf16", -21555) for _ in range(R)]
+    comb.run([to_dev(a.reshape(-1)) for a in z_np], y)
+    torch.cuda.synchronize()
+    want = OM.combine(z_np, idx, w, E, T // R)
+    for r in range(R):
+        assert_bits_equal(from_dev(y[r]).reshape(-1, h), want[r], f"combine specials rank {r} h={h}")
 
 
 @pytest.mark.parametrize("seed", range(48))

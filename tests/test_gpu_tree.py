@@ -12,8 +12,8 @@ import torch
 
 from oracle import collectives as C, fold
 from reduce_rank_buffers_amd import api, inputs
-from tests.gpu_util import (DEV, assert_bits_equal, empty_like_np, from_dev, oracle_elementwise,
-                            require_gpu, to_dev)
+from tests.gpu_util import (BF16_SPECIALS, DEV, assert_bits_equal, empty_like_np, from_dev,
+                            oracle_elementwise, require_gpu, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -54,6 +54,23 @@ def test_tree_all_reduce_reduce_scatter_reduce(R, n, dtype):
         for q in range(R):
             assert_bits_equal(from_dev(rs[q]), want[q * c:(q + 1) * c], f"tree RS rank {q}")
     assert_bits_equal(from_dev(red[root]), want, "tree Reduce root")
+
+
+@pytest.mark.parametrize("R", [3, 8])
+def test_tree_special_values(R):
+    """Zeros, subnormals, infinities and NaNs of both signs with and without
+    payload through the tree-order vector path (and its tail): every NaN
+    result is 0x7FC0, the rest match the oracle's tree fold bit for bit."""
+    require_gpu()
+    rng = np.random.default_rng(11 + R)
+    n = 8 * 4096 + 5
+    ins_np = [BF16_SPECIALS[rng.integers(0, len(BF16_SPECIALS), size=n)] for _ in range(R)]
+    want = fold.reduce_tree(ins_np, "bf16")
+    outs = [empty_like_np(n, "bf16") for _ in range(R)]
+    api.all_reduce([to_dev(x) for x in ins_np], outs, order="tree")
+    torch.cuda.synchronize()
+    for q in range(R):
+        assert_bits_equal(from_dev(outs[q]), want, f"tree specials rank {q}")
 
 
 def test_tree_collective_matches_layout_oracle():
