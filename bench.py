@@ -8,14 +8,17 @@ plus the same three at fp32, 64 MiB.  Inputs are resident in HBM before the
 timed region.  ``value`` = algorithmic bytes of the whole step (every input
 byte read once, every output byte written once) / step time.
 
-Also reported on the same line (all measured after the timed region):
+Also reported on the same line:
 * ``roofline``: the dominant kernel (the 256 MiB All-Reduce, named as the
   library reports its launch): algorithmic bytes per launch / its mean
-  duration from HIP events on the launch stream, against the 8 TB/s HBM
-  peak; ``serial_bound`` sets it against the fastest Reduce-Scatter and
+  duration from HIP events on the launch stream, recorded around it in the
+  timed steps (the only events there), against the 8 TB/s HBM peak;
+  ``serial_bound`` sets it against the fastest Reduce-Scatter and
   All-Gather of the same run;
-* ``sweep``: per size and collective, the in-step (warm) rate and a cold
-  rate (a 1 GiB scratch read before each call empties the caches);
+* ``sweep``: per size and collective, the in-step (warm) rate from the same
+  number of steps run again after the timed region with events around every
+  collective, and a cold rate (a 1 GiB scratch read before each call empties
+  the caches);
 * ``decode``: the batch-1 decode All-Reduce (8 ranks x 4096 bf16), kernel
   time from events and back-to-back time per call, next to an empty kernel;
 * ``seven``: the seven layout-named collectives at 8 x 16 MiB bf16 (us per
@@ -121,33 +124,48 @@ def main():
                    rrb.bound("all_gather", rs, ag))
            for label, dtype, Sb, ins, ar, rs, ag in cases}
 
+    roof_events = []
+
     def step(record):
+        # record = "roof": events around the roofline kernel only (the timed
+        # steps); record = "all": events around every collective (the
+        # breakdown steps after the timed region).
         for label, *_ in cases:
             op_ar, op_rs, op_ag = ops[label]
-            if record:
+            roof = record == "roof" and label == big[0]
+            if record == "all" or roof:
                 e = [ev() for _ in range(4)]
                 e[0].record()
             op_ar()
-            if record:
+            if roof:
+                e[1].record()
+                roof_events.append(e[:2])
+            if record == "all":
                 e[1].record()
             op_rs()
-            if record:
+            if record == "all":
                 e[2].record()
             op_ag()
-            if record:
+            if record == "all":
                 e[3].record()
                 per_case_events[label].append(e)
 
     for _ in range(args.warmup):
-        step(False)
+        step(None)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(True)
+        step("roof")
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (wall / args.steps) / 1e9
+    # Per-collective breakdown: the same number of steps again, with events
+    # around every collective (outside the timed region: the 24 event
+    # records per step cost about 3% of its time).
+    for _ in range(args.steps):
+        step("all")
+    torch.cuda.synchronize()
 
     sweep = {}
     for label, dtype, Sb, *_ in cases:
@@ -162,7 +180,7 @@ def main():
         }
         sweep[label]["cache_note"] = "fits in the 256 MB Infinity Cache" if Sb * R * 2 <= (256 << 20) else "above the Infinity Cache"
     ar_bytes = alg_bytes(big[2])[0]
-    ar_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in per_case_events[big[0]]]))
+    ar_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in roof_events]))
     achieved = ar_bytes / (ar_ms * 1e-3) / 1e9
 
     # ---- cold-cache timings (outside the timed region) ---------------------
