@@ -96,7 +96,14 @@ def main():
     only = sys.argv[1:]
     if os.path.exists(DST):
         shutil.rmtree(DST)
-    shutil.copytree(SRC, DST, ignore=shutil.ignore_patterns(".git", "_work", "gpurun_out", "__pycache__", "*.log"))
+    # what the CPU suite reads: the oracle, the tests and their fixtures, the
+    # package (with its built library), the header and the pytest settings
+    os.makedirs(DST)
+    for entry in ("oracle", "tests", "reduce_rank_buffers_amd", "include"):
+        shutil.copytree(os.path.join(SRC, entry), os.path.join(DST, entry),
+                        ignore=shutil.ignore_patterns("__pycache__", "*.log"))
+    for entry in ("pytest.ini", "bench.py", "__graft_entry__.py"):
+        shutil.copy2(os.path.join(SRC, entry), DST)
     survivors = []
     for name, f, old, new in M:
         if only and not any(o in name for o in only):
