@@ -534,6 +534,11 @@ __global__ void __launch_bounds__(64) snac_chain_kernel(SnacArgs a) {
     // sources in flight per lane.
     unsigned char *dst_base = a.out + (static_cast<int64_t>(k) * R + r) * a.rank_bytes;
     constexpr int CU = R <= 8 ? 4 : 2;
+    // The speculative first pass holds its loads across the flag wait: two
+    // vectors per lane keep the kernel within 256 VGPRs, two waves per SIMD,
+    // so a chain of 1024 workgroups stays within half the device and takes a
+    // plain launch (four vectors took 310 VGPRs and a cooperative launch).
+    constexpr int CUS = R <= 8 ? 2 : 1;
     int64_t first = v0 + threadIdx.x;  // first vector of the ordinary passes
     if (VAR == kSpeculative) {
       // No top barrier.  One read of the R sources' flags (lanes 0..R-1);
@@ -556,9 +561,9 @@ __global__ void __launch_bounds__(64) snac_chain_kernel(SnacArgs a) {
       // re-read after the wait (a failed sum always has a stale flag; all,
       // should it not)
       const uint32_t late = valid ? 0u : (stale ? stale : kAll);
-      uint4 v[CU][R];
+      uint4 v[CUS][R];
 #pragma unroll
-      for (int u = 0; u < CU; ++u) {
+      for (int u = 0; u < CUS; ++u) {
         const int64_t i = first + static_cast<int64_t>(u) * bs;
         if (i < v1) {
 #pragma unroll
@@ -582,7 +587,7 @@ __global__ void __launch_bounds__(64) snac_chain_kernel(SnacArgs a) {
           for (int q = 0; q < R; ++q) {
             if (late >> q & 1u) {
 #pragma unroll
-              for (int u = 0; u < CU; ++u) {
+              for (int u = 0; u < CUS; ++u) {
                 const int64_t i = first + static_cast<int64_t>(u) * bs;
                 if (i < v1)
                   v[u][q] = load_coherent(rsrc(stage_base + static_cast<int64_t>(q) * a.rank_bytes,
@@ -598,11 +603,11 @@ __global__ void __launch_bounds__(64) snac_chain_kernel(SnacArgs a) {
         break;
       }
 #pragma unroll
-      for (int u = 0; u < CU; ++u) {
+      for (int u = 0; u < CUS; ++u) {
         const int64_t i = first + static_cast<int64_t>(u) * bs;
         if (i < v1) reduce_pass<R, BF16>(v[u], dst_base, a.rank_bytes, i * 16);
       }
-      first += static_cast<int64_t>(bs) * CU;
+      first += static_cast<int64_t>(bs) * CUS;
     } else if (!wait_all<R>(flags_b + s * kFlagStride, stride_rs, ep, a.status, a.spin_limit, lds_ok)) {
       // the top barrier over the R sources' flags of this slice
       ++timeouts;
