@@ -355,7 +355,7 @@ typedef struct rrb_snac_s *rrb_snac_t;
 /* Device-side counters a chain call may accumulate into (zeroed by the
  * caller).  misspec: speculative validations that failed; retries: stale
  * sources re-read after a failed validation (All-Reduce chains: source
- * slices; plan chains: source ranks whose entries were redone), or for
+ * slices; plan chains: source ranks whose entries waited), or for
  * RRB_SNAC_LAMPORT poll rounds that found an untagged word; timeouts:
  * bounded waits that expired; epochs: epochs completed (per rank and slice,
  * summed). */
@@ -402,9 +402,10 @@ rrb_status rrb_snac_allreduce_chain(rrb_snac_t h, int32_t epochs,
  * and sit on 16-byte boundaries, and every rank's input must be a 16-byte
  * multiple (RRB_EUNSUPPORTED otherwise).  flags: 0 (top and bottom barrier),
  * RRB_SNAC_DUAL_BUFFER, RRB_SNAC_DUAL_BUFFER | RRB_SNAC_SPECULATIVE (one
- * read of the workgroup's listed flags, the whole consume once their values
- * have returned, then the reduced check; on a mismatch it waits for the list
- * and redoes only the map entries that read a rank whose flag was stale), or
+ * read of the workgroup's listed flags and the reduced check on their sum;
+ * once their values have returned the consume runs, leaving out the map
+ * entries that read a rank whose flag read stale (copies from it, and every
+ * fold); on a mismatch it waits for the list and then runs those), or
  * RRB_SNAC_GRAPH (one Atom launch per epoch in a cached HIP graph).  Workgroup (r, s) stages slice s of rank r's input and
  * computes piece s of every map entry whose output is rank r; it waits on a
  * list of flags built at create time: the staged slices its pieces read and

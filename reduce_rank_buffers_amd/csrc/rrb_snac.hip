@@ -1035,13 +1035,14 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
     bool ok = true;
     if (VAR == kSpeculative) {
       // One read of the listed flags; once their values have returned, the
-      // whole consume runs, whatever they said.  The reduced check: the flags
-      // must sum to (list length) x epoch (each is epoch or epoch - 2, so the
-      // sum is exact).  On a mismatch the workgroup waits for every listed
-      // flag (the write-after-read guards included) and redoes only the
-      // entries that read a rank whose data flag was stale; the others stand,
-      // their loads having been issued after their sources' flags showed the
-      // epoch.
+      // consume runs.  The reduced check: the flags must sum to (list length)
+      // x epoch (each is epoch or epoch - 2, so the sum is exact).  Entries
+      // that read a rank whose data flag read stale (copies from it, and
+      // every fold) are left out: their sources are known stale, and a fold
+      // run too early would be redone whole.  On a mismatch the workgroup
+      // then waits for every listed flag (the write-after-read guards
+      // included) and runs those entries; the others stand, their loads
+      // having been issued after their sources' flags showed the epoch.
       uint32_t sum = 0, stale = 0;
       for (int i0 = 0; i0 < nw; i0 += bs) {
         const int i = i0 + static_cast<int>(threadIdx.x);
@@ -1061,7 +1062,7 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
       order_after_values();
       const bool valid = sum == static_cast<uint32_t>(nw) * ep;
       if (valid) stale = 0;  // (a valid sum has no stale flag)
-      plan_consume<R, BF16>(a, r, s, stage_base, dst, ents, 0u, false);
+      plan_consume<R, BF16>(a, r, s, stage_base, dst, ents, stale, false);
       if (!valid) {
         ++misspec;
         retries += static_cast<unsigned long long>(__builtin_popcount(stale));
