@@ -982,6 +982,102 @@ __device__ void plan_consume(const PlanChainArgs &a, int r, int s,
   }
 }
 
+// The speculative consume of a workgroup whose work fits one round: the
+// rank's copies at most kCopyU vectors per lane, or its one fold at most CU.
+// Every source is loaded once the flag values have returned.  After a failed
+// sum the workgroup waits for its list and loads the stale ranks' sources
+// again; the current ones' data stays in registers, so the wait overlaps
+// their loads.  Outputs are stored once, after that.  Returns 0 when the work
+// does not fit one round (the caller consumes in two parts around the wait),
+// 1 when done, -1 when a wait ran out.
+template <int R, bool BF16>
+__device__ int plan_consume_spec(const PlanChainArgs &a, int r, int s, const unsigned char *stage_base,
+                                 unsigned char *dst, const PlanEntry *ents, const uint32_t *flags_b,
+                                 const int32_t *wl, int nw, uint32_t ep, bool valid, uint32_t stale) {
+  const int bs = blockDim.x;
+  constexpr int CU = R <= 8 ? 2 : 1;
+  if (a.copy_len[r] > 0) {
+    const int64_t len = a.copy_len[r];
+    const int64_t pl = (len + a.S - 1) / a.S;
+    const int64_t lo = min(len, static_cast<int64_t>(s) * pl);
+    const uint32_t w = static_cast<uint32_t>(min(len, lo + pl) - lo);
+    const uint32_t total = static_cast<uint32_t>(a.cnt[r]) * w;
+    if (total > static_cast<uint32_t>(bs) * kCopyU) return 0;
+    const __amdgpu_buffer_rsrc_t src = rsrc(stage_base, static_cast<int64_t>(R) * a.in_stride);
+    uint4 x[kCopyU];
+    int32_t off[kCopyU];
+    int32_t rank[kCopyU];
+    int64_t at[kCopyU];
+#pragma unroll
+    for (int u = 0; u < kCopyU; ++u) {
+      const uint32_t f = threadIdx.x + static_cast<uint32_t>(u * bs);
+      at[u] = -1;
+      off[u] = 0;
+      rank[u] = 0;
+      if (f < total) {
+        const uint32_t g = f / w;
+        const PlanEntry e = ents[g];
+        const int64_t i = lo + (f - g * w);
+        off[u] = static_cast<int32_t>(e.src_rank * a.in_stride + (e.src_off + i) * 16);
+        rank[u] = e.src_rank;
+        at[u] = (e.dst_off + i) * 16;
+        x[u] = load_coherent(src, off[u]);
+      }
+    }
+    if (!valid) {
+      if (!wait_list(flags_b, wl, nw, ep, a.status, a.spin_limit)) return -1;
+      order_after_values();
+#pragma unroll
+      for (int u = 0; u < kCopyU; ++u)
+        if (at[u] >= 0 && (stale >> rank[u] & 1u)) x[u] = load_coherent(src, off[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyU; ++u)
+      if (at[u] >= 0) *reinterpret_cast<uint4 *>(dst + at[u]) = x[u];
+    return 1;
+  }
+  if (a.cnt[r] != 1) return 0;
+  const PlanEntry e = a.entries[a.first[r]];
+  if (e.src_rank >= 0) return 0;
+  const int64_t pl = (e.len + a.S - 1) / a.S;
+  const int64_t lo = min(e.len, static_cast<int64_t>(s) * pl);
+  const int64_t hi = min(e.len, lo + pl);
+  if (hi - lo > static_cast<int64_t>(bs) * CU) return 0;
+  uint4 v[CU][R];
+#pragma unroll
+  for (int u = 0; u < CU; ++u) {
+    const int64_t i = lo + threadIdx.x + static_cast<int64_t>(u) * bs;
+    if (i < hi) {
+#pragma unroll
+      for (int q = 0; q < R; ++q)
+        v[u][q] = load_coherent(rsrc(stage_base + static_cast<int64_t>(q) * a.in_stride, a.in_stride),
+                                static_cast<int32_t>((e.src_off + i) * 16));
+    }
+  }
+  if (!valid) {
+    if (!wait_list(flags_b, wl, nw, ep, a.status, a.spin_limit)) return -1;
+    order_after_values();
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      if (stale >> q & 1u) {
+#pragma unroll
+        for (int u = 0; u < CU; ++u) {
+          const int64_t i = lo + threadIdx.x + static_cast<int64_t>(u) * bs;
+          if (i < hi)
+            v[u][q] = load_coherent(rsrc(stage_base + static_cast<int64_t>(q) * a.in_stride, a.in_stride),
+                                    static_cast<int32_t>((e.src_off + i) * 16));
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < CU; ++u) {
+    const int64_t i = lo + threadIdx.x + static_cast<int64_t>(u) * bs;
+    if (i < hi) reduce_pass<R, BF16, false>(v[u], dst, a.out_stride, (e.dst_off + i) * 16);
+  }
+  return 1;
+}
+
 template <int R, bool BF16, int VAR>
 __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
   const int r = blockIdx.x / a.S;
@@ -1036,13 +1132,15 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
     if (VAR == kSpeculative) {
       // One read of the listed flags; once their values have returned, the
       // consume runs.  The reduced check: the flags must sum to (list length)
-      // x epoch (each is epoch or epoch - 2, so the sum is exact).  Entries
-      // that read a rank whose data flag read stale (copies from it, and
-      // every fold) are left out: their sources are known stale, and a fold
-      // run too early would be redone whole.  On a mismatch the workgroup
-      // then waits for every listed flag (the write-after-read guards
-      // included) and runs those entries; the others stand, their loads
-      // having been issued after their sources' flags showed the epoch.
+      // x epoch (each is epoch or epoch - 2, so the sum is exact).  Work that
+      // fits one round loads every source at once and, on a mismatch, waits
+      // for every listed flag (the write-after-read guards included) and
+      // loads only the stale ranks' sources again (plan_consume_spec).
+      // Larger work leaves out the entries that read a rank whose data flag
+      // read stale (copies from it, and every fold: a fold run too early
+      // would be redone whole), waits, and then runs those.  Either way the
+      // current sources' loads were issued after their flags showed the
+      // epoch.
       uint32_t sum = 0, stale = 0;
       for (int i0 = 0; i0 < nw; i0 += bs) {
         const int i = i0 + static_cast<int>(threadIdx.x);
@@ -1062,14 +1160,22 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
       order_after_values();
       const bool valid = sum == static_cast<uint32_t>(nw) * ep;
       if (valid) stale = 0;  // (a valid sum has no stale flag)
-      plan_consume<R, BF16>(a, r, s, stage_base, dst, ents, stale, false);
       if (!valid) {
         ++misspec;
         retries += static_cast<unsigned long long>(__builtin_popcount(stale));
-        ok = wait_list(flags_b, wl, nw, ep, a.status, a.spin_limit);
-        if (ok) {
-          order_after_values();
-          if (stale) plan_consume<R, BF16>(a, r, s, stage_base, dst, ents, stale, true);
+      }
+      const int one = plan_consume_spec<R, BF16>(a, r, s, stage_base, dst, ents, flags_b, wl, nw, ep,
+                                                 valid, stale);
+      if (one < 0) {
+        ok = false;
+      } else if (one == 0) {
+        plan_consume<R, BF16>(a, r, s, stage_base, dst, ents, stale, false);
+        if (!valid) {
+          ok = wait_list(flags_b, wl, nw, ep, a.status, a.spin_limit);
+          if (ok) {
+            order_after_values();
+            if (stale) plan_consume<R, BF16>(a, r, s, stage_base, dst, ents, stale, true);
+          }
         }
       }
     } else {
