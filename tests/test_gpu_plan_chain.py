@@ -113,10 +113,12 @@ def test_plan_chain_other_shapes(name, R, n, dtype, slices):
         _run_chain(name, R, n, dtype, variant, E=6, kind=7, slices=slices)
 
 
-@pytest.mark.parametrize("name", ["all_gather", "reduce_scatter", "broadcast"])
+@pytest.mark.parametrize("name", ["all_reduce", "reduce_scatter", "all_gather", "all_to_all",
+                                  "broadcast", "reduce", "gather"])
 def test_plan_chain_staggered_speculation(name):
-    """Late ranks: the speculative consume sees stale flags, retries, and
-    every epoch is still exact."""
+    """Late ranks: the speculative consume sees stale flags, waits, reads the
+    stale ranks' sources again, and every epoch is still exact (16 KiB per
+    rank: every workgroup's work fits one round)."""
     require_gpu()
     R = 8
     st = [r * 64 for r in range(R)]
@@ -124,8 +126,8 @@ def test_plan_chain_staggered_speculation(name):
     stats, _ = _run_chain(name, R, 8 * 1024, "bf16", "speculative", E=24, stagger=stagger, kind=9)
     _say(f"  {name}: misspec {stats[0]} retries {stats[1]}")
     assert stats[0] > 0
-    # retries count the source ranks whose entries were redone after a failed
-    # check (none when only write-after-read guards were stale)
+    # retries count the stale source ranks read after the wait that follows
+    # a failed check (none when only write-after-read guards were stale)
     assert 0 <= stats[1] <= stats[0] * R
     for variant in ("barrier", "dual"):
         _run_chain(name, R, 8 * 1024, "bf16", variant, E=12, stagger=stagger, kind=9)
@@ -174,6 +176,20 @@ def test_plan_chain_large_staggered(name):
     stagger = torch.tensor([r * 64 for r in range(R)], dtype=torch.int32, device=DEV)
     for variant in ("barrier", "dual", "speculative"):
         _run_chain(name, R, 8 * 8192, "bf16", variant, E=16, stagger=stagger, kind=11)
+
+
+@pytest.mark.parametrize("name", ["all_reduce", "all_gather", "reduce_scatter"])
+def test_plan_chain_two_part_speculation_staggered(name):
+    """1 MiB tensors per rank: a workgroup's work takes several rounds, so
+    the speculative consume runs the entries that read only current ranks,
+    waits, then runs the rest; late ranks force that path, every epoch
+    bit-exact."""
+    require_gpu()
+    R = 8
+    stagger = torch.tensor([r * 64 for r in range(R)], dtype=torch.int32, device=DEV)
+    stats, _ = _run_chain(name, R, 8 * 65536, "bf16", "speculative", E=6, stagger=stagger, kind=13)
+    _say(f"  {name}: misspec {stats[0]} retries {stats[1]}")
+    assert stats[0] > 0
 
 
 def test_plan_chain_times_out_cleanly():
