@@ -25,7 +25,9 @@ Also reported on the same line:
   launch replayed from a HIP graph, GB/s, fraction of peak);
 * ``chain``: the decode chain, 64 back-to-back All-Reduces per call for every
   b x h payload (b = 1..64, h = 4096, 8192) and every orchestration variant,
-  us per All-Reduce, and the speculative variant's mis-speculation rate;
+  us per All-Reduce, and the mis-speculation rates (speculative waits for
+  the flags first above 128 KiB per rank; speculative_always speculates at
+  every size);
 * ``moe``: MoE dispatch and combine, 4096 x 7168 bf16, 256 experts over 8
   ranks, top-8 (host-built and device-routed maps);
 * ``cpu_baseline``: the CPU oracle on a bounded sample of the sweep workload.
@@ -426,24 +428,28 @@ def seven_leg(args, torch, rrb, inputs, dev):
     return res
 
 
-CHAIN_VARIANTS = ("barrier", "dual", "speculative", "twoshot", "lamport", "graph")
+CHAIN_VARIANTS = ("barrier", "dual", "speculative", "speculative_always", "twoshot", "lamport", "graph")
 
 
 def chain_leg(args, torch, rrb, inputs, dev, reps=10):
     """The decode chain: for every b x h payload, us per All-Reduce of a
     64-deep chain (median call time / 64) for every variant, and the
-    speculative variant's mis-speculation rate (failed validations per
-    validation: epochs x ranks x slices)."""
+    mis-speculation rates (failed validations per validation: epochs x ranks
+    x slices) of the speculative variant, which waits for the flags first
+    above 128 KiB per rank, and of speculative_always, which speculates at
+    every size."""
     E = 64
     res = {"workload": "64 back-to-back All-Reduces per call, 8 ranks, b x h bf16 N(0,0.02); "
-                       "us per All-Reduce", "cols": list(CHAIN_VARIANTS) + ["spec_misspec_rate"]}
+                       "us per All-Reduce; speculative waits for the flags first above 128 KiB per rank, "
+                       "speculative_always speculates at every size",
+           "cols": list(CHAIN_VARIANTS) + ["spec_misspec_rate", "spec_always_misspec_rate"]}
     for h in (4096, 8192):
         for b in (1, 2, 4, 8, 16, 32, 64):
             n = b * h
             inp = torch.from_numpy(inputs.chain(E, R, n).view(np.int16)).to(dev)
             out = torch.empty_like(inp)
             row = []
-            rate = None
+            rates = {}
             for v in CHAIN_VARIANTS:
                 ch = rrb.SnacChain(R, n, "bf16", v)
                 stats = torch.zeros(4, dtype=torch.int64, device=dev)
@@ -455,12 +461,12 @@ def chain_leg(args, torch, rrb, inputs, dev, reps=10):
                 ms = float(np.median(_events_ms(torch, call, reps)))
                 ch.check()
                 row.append(round(ms * 1e3 / E, 3))
-                if v == "speculative":
+                if v.startswith("speculative"):
                     st = stats.cpu().tolist()
-                    rate = round(st[0] / max(1, st[3]), 3)  # st[3]: epochs x ranks x slices
+                    rates[v] = round(st[0] / max(1, st[3]), 3)  # st[3]: epochs x ranks x slices
                 del call
                 ch.close()
-            res[f"b{b}h{h}"] = row + [rate]
+            res[f"b{b}h{h}"] = row + [rates["speculative"], rates["speculative_always"]]
             del inp, out
     return res
 
@@ -578,7 +584,7 @@ def bench_chain(args, dev):
             inp = torch.from_numpy(inputs.chain(E, R, n).view(np.int16)).to(dev)
             out = torch.empty_like(inp)
             res = {"b": b, "h": h, "payload_bytes": n * 2}
-            for v in ("barrier", "dual", "speculative", "twoshot", "lamport", "graph"):
+            for v in CHAIN_VARIANTS:
                 ch = rrb.SnacChain(R, n, "bf16", v)
                 stats = torch.zeros(4, dtype=torch.int64, device=dev)
                 call = ch.bound(inp, out, stats)  # marshalled once

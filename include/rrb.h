@@ -308,6 +308,13 @@ rrb_status rrb_empty_kernel(rrb_stream_t stream);
  *                              values have returned, so the check holds under
  *                              any order in which the memory system serves
  *                              the loads.
+ *                              All-Reduce chains speculate up to 128 KiB per
+ *                              rank and wait for the flags first above that,
+ *                              as DUAL_BUFFER does: there the chain is
+ *                              bandwidth-bound and the early loads measured
+ *                              slower.  Plan chains speculate at every size.
+ *   | RRB_SNAC_SPEC_ALWAYS     (with SPECULATIVE, All-Reduce chains) speculate
+ *                              at every payload size
  *   RRB_SNAC_TWOSHOT | DUAL    twoshot (SiFAR review, Fig. 6): stage, then each
  *                              rank reduces chunk r of the payload over all
  *                              ranks, then every rank gathers the R reduced
@@ -350,6 +357,7 @@ rrb_status rrb_empty_kernel(rrb_stream_t stream);
 #define RRB_SNAC_TWOSHOT 8u
 #define RRB_SNAC_LAMPORT 16u
 #define RRB_SNAC_COOPERATIVE 32u
+#define RRB_SNAC_SPEC_ALWAYS 64u
 typedef struct rrb_snac_s *rrb_snac_t;
 
 /* Device-side counters a chain call may accumulate into (zeroed by the
@@ -440,8 +448,9 @@ rrb_status rrb_snac_chain(rrb_snac_t h, int32_t epochs, const void *d_in, void *
  * staging buffers, flags and status word in a static device array of 20 MiB
  * per GPU (held until the process ends) instead of caller workspace; no
  * handle, no hipMalloc.  flags: 0, RRB_SNAC_DUAL_BUFFER,
- * RRB_SNAC_DUAL_BUFFER | RRB_SNAC_SPECULATIVE or RRB_SNAC_TWOSHOT |
- * RRB_SNAC_DUAL_BUFFER (each optionally | RRB_SNAC_COOPERATIVE);
+ * RRB_SNAC_DUAL_BUFFER | RRB_SNAC_SPECULATIVE (optionally
+ * | RRB_SNAC_SPEC_ALWAYS) or RRB_SNAC_TWOSHOT | RRB_SNAC_DUAL_BUFFER (each
+ * optionally | RRB_SNAC_COOPERATIVE);
  * RRB_SNAC_GRAPH and RRB_SNAC_LAMPORT return RRB_EUNSUPPORTED.  A chain whose
  * staging and flags exceed the array (8 ranks of up to 1 MiB each fit)
  * returns RRB_EUNSUPPORTED with the bytes it needs.  d_in, d_out, d_stats,

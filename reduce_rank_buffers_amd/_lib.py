@@ -35,6 +35,7 @@ RRB_SNAC_GRAPH = 4
 RRB_SNAC_TWOSHOT = 8
 RRB_SNAC_LAMPORT = 16
 RRB_SNAC_COOPERATIVE = 32
+RRB_SNAC_SPEC_ALWAYS = 64
 
 RRB_MAX_RANKS = 16
 

@@ -434,6 +434,7 @@ class MoeDevicePlan(Plan):
 
 VARIANTS = {"barrier": 0, "dual": L.RRB_SNAC_DUAL_BUFFER,
             "speculative": L.RRB_SNAC_DUAL_BUFFER | L.RRB_SNAC_SPECULATIVE,
+            "speculative_always": L.RRB_SNAC_DUAL_BUFFER | L.RRB_SNAC_SPECULATIVE | L.RRB_SNAC_SPEC_ALWAYS,
             "graph": L.RRB_SNAC_GRAPH,
             "twoshot": L.RRB_SNAC_TWOSHOT | L.RRB_SNAC_DUAL_BUFFER,
             "lamport": L.RRB_SNAC_LAMPORT | L.RRB_SNAC_DUAL_BUFFER}
@@ -532,9 +533,9 @@ def allreduce_chain_noalloc(inp, out, variant="dual", stats=None, spin_limit=0, 
     """`inp.shape[0]` chained All-Reduces of inp [epochs, R, count] into out,
     with the library's static per-GPU scratch instead of a workspace
     (rrb_snac_allreduce_chain_noalloc: no device allocation).  variant:
-    barrier, dual, speculative or twoshot.  Calls that overlap on one GPU
-    race; a wait that ran out shows in stats[2]."""
-    if variant not in ("barrier", "dual", "speculative", "twoshot"):
+    barrier, dual, speculative, speculative_always or twoshot.  Calls that
+    overlap on one GPU race; a wait that ran out shows in stats[2]."""
+    if variant not in ("barrier", "dual", "speculative", "speculative_always", "twoshot"):
         raise ValueError(f"variant {variant!r} has no allocation-free form")
     if not isinstance(inp, torch.Tensor) or inp.dim() != 3:
         raise ValueError("inp: expected a tensor of shape [epochs, R, count]")

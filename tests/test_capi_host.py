@@ -247,6 +247,13 @@ def test_snac_create_validation(librrb):
     lib.rrb_snac_destroy(h)
     assert lib.rrb_snac_create(8, 4096, 0, 4, 0, ctypes.byref(h)) == L.RRB_OK
     lib.rrb_snac_destroy(h)
+    # always-speculate goes with the speculative variant only
+    for f in (L.RRB_SNAC_SPEC_ALWAYS, L.RRB_SNAC_SPEC_ALWAYS | 1, L.RRB_SNAC_SPEC_ALWAYS | 9,
+              L.RRB_SNAC_SPEC_ALWAYS | 17, L.RRB_SNAC_SPEC_ALWAYS | 4):
+        assert lib.rrb_snac_create(8, 4096, 0, f, 0, ctypes.byref(h)) == L.RRB_EINVAL, f
+    assert lib.rrb_snac_create(8, 4096, 0, L.RRB_SNAC_SPEC_ALWAYS | 3, 0, ctypes.byref(h)) == L.RRB_OK
+    lib.rrb_snac_destroy(h)
+    assert lib.rrb_snac_create(8, 4096, 0, 128, 0, ctypes.byref(h)) == L.RRB_EINVAL  # unknown bit
     assert lib.rrb_snac_create(8, 4096, 0, 3, 0, ctypes.byref(h)) == L.RRB_OK
     ws = ctypes.c_size_t()
     assert lib.rrb_snac_workspace(h, ctypes.byref(ws)) == L.RRB_OK
@@ -299,6 +306,9 @@ def test_snac_plan_chain_validation(librrb):
     ragged = api.Plan(8, 8 * 3, "bf16", api.SHARD, api.REPLICATED, "copy")
     assert lib.rrb_snac_create_plan(ragged.handle, 1, 0, ctypes.byref(h)) == L.RRB_EUNSUPPORTED
     assert lib.rrb_snac_create_plan(None, 1, 0, ctypes.byref(h)) == L.RRB_EINVAL
+    # plan chains speculate at every size; the All-Reduce chain's override is refused
+    assert lib.rrb_snac_create_plan(ag.handle, L.RRB_SNAC_SPEC_ALWAYS | 3, 0,
+                                    ctypes.byref(h)) == L.RRB_EUNSUPPORTED
     assert lib.rrb_snac_create_plan(ag.handle, L.RRB_SNAC_COOPERATIVE | L.RRB_SNAC_GRAPH, 0,
                                     ctypes.byref(h)) == L.RRB_EUNSUPPORTED
     assert lib.rrb_snac_create_plan(ag.handle, L.RRB_SNAC_COOPERATIVE | 1, 0,

@@ -23,8 +23,9 @@ from tests.gpu_util import DEV, assert_bits_equal, from_dev, require_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = ["barrier", "dual", "speculative", "twoshot", "lamport", "graph"]
+VARIANTS = ["barrier", "dual", "speculative", "speculative_always", "twoshot", "lamport", "graph"]
 FLAG_VARIANTS = ["barrier", "dual", "speculative", "twoshot", "lamport"]
+SPEC_MAX_BYTES = 128 << 10  # All-Reduce chains speculate up to this payload per rank
 R = 8
 EPOCHS = 64
 
@@ -60,6 +61,8 @@ def test_chain_all_variants_bit_exact(b, h):
         assert st[2] == 0  # no timeouts
         if v != "graph":
             assert st[3] == EPOCHS * R * _slices_of(ch)
+        if v == "speculative" and n * 2 > SPEC_MAX_BYTES:
+            assert st[0] == 0 and st[1] == 0  # waits for the flags first: nothing to validate
         # a second call continues the epoch counter on the same flags
         out2 = torch.empty_like(inp)
         ch.run(inp, out2)
@@ -111,6 +114,29 @@ def test_chain_staggered_ranks(v):
         if v == "lamport":
             _say(f"  poll rounds {s[1]}")
             assert s[1] > 0  # late ranks leave untagged words to poll again
+
+
+@pytest.mark.parametrize("n", [65536, 262144])
+def test_chain_speculation_staggered_large(n):
+    """Speculation forced at 128 KiB and 512 KiB per rank with late ranks: the
+    first pass holds two vectors per lane, the rest of each slice follows in
+    ordinary passes, and failed checks re-read the stale sources."""
+    require_gpu()
+    E = 12
+    ins_np = inputs.chain(E, R, n, kind=81)
+    want = OC.allreduce_chain(ins_np)
+    inp = to_dev(ins_np)
+    stagger = torch.tensor([r * 64 for r in range(R)], dtype=torch.int32, device=DEV)
+    _say(f"stagger speculative_always n={n}")
+    ch = api.SnacChain(R, n, "bf16", "speculative_always")
+    stats = torch.zeros(4, dtype=torch.int64, device=DEV)
+    out = torch.empty_like(inp)
+    ch.run(inp, out, stats=stats, stagger=stagger)
+    ch.check()
+    _check_chain(out, want, f"speculative_always n={n}")
+    s = stats.cpu().tolist()
+    _say(f"  misspec {s[0]} retries {s[1]}")
+    assert s[2] == 0 and s[0] > 0 and s[0] <= s[1] <= s[0] * (R - 1)
 
 
 @pytest.mark.parametrize("slices", [1, 3, 8])
