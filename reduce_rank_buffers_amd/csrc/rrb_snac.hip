@@ -856,8 +856,8 @@ struct PlanChainArgs {
   int64_t slice_vec;         // staging slice length in vectors
   int64_t in_vec[RRB_MAX_RANKS];
   int32_t first[RRB_MAX_RANKS], cnt[RRB_MAX_RANKS];
-  // Vectors per entry when all of a rank's entries are copies of one length
-  // (and there are at most kFlatEntries of them), else 0.
+  // Vectors per entry when all of a rank's entries are copies of one length,
+  // else 0.
   int64_t copy_len[RRB_MAX_RANKS];
   uint32_t epoch0;
   int32_t epochs;
@@ -892,11 +892,12 @@ __device__ bool wait_list(const uint32_t *base, const int32_t *idx, int n, uint3
 // outputs).  stale = 0 with touching = false selects every entry; the
 // speculative consume runs the two halves on either side of its wait.
 //
-// A rank whose entries are all copies of one length (All-Gather, All-to-All,
+// The rank's entries are read from LDS (`ents`, at most kFlatEntries).  A
+// rank whose entries are all copies of one length (All-Gather, All-to-All,
 // Gather) takes its pieces as one flat index range over all lanes, kCopyU
-// vectors per lane in flight, with the entries held in LDS (`ents`): a pass
-// per entry put the entries' round trips one after another, with most lanes
-// idle when a piece is narrower than the workgroup.
+// vectors per lane in flight: a pass per entry put the entries' round trips
+// one after another, with most lanes idle when a piece is narrower than the
+// workgroup.
 constexpr int kFlatEntries = 64;
 
 template <int R, bool BF16>
@@ -937,8 +938,8 @@ __device__ void plan_consume(const PlanChainArgs &a, int r, int s,
     }
     return;
   }
-  for (int g = a.first[r]; g < a.first[r] + a.cnt[r]; ++g) {
-    const PlanEntry e = a.entries[g];
+  for (int g = 0; g < a.cnt[r]; ++g) {
+    const PlanEntry e = ents[g];
     if ((e.src_rank < 0 ? stale != 0 : (stale >> e.src_rank & 1u) != 0) != touching) continue;
     const int64_t pl = (e.len + a.S - 1) / a.S;
     const int64_t lo = min(e.len, static_cast<int64_t>(s) * pl);
@@ -1038,7 +1039,7 @@ __device__ int plan_consume_spec(const PlanChainArgs &a, int r, int s, const uns
     return 1;
   }
   if (a.cnt[r] != 1) return 0;
-  const PlanEntry e = a.entries[a.first[r]];
+  const PlanEntry e = ents[0];
   if (e.src_rank >= 0) return 0;
   const int64_t pl = (e.len + a.S - 1) / a.S;
   const int64_t lo = min(e.len, static_cast<int64_t>(s) * pl);
@@ -1090,11 +1091,11 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
   const int nw = a.wait_off[blockIdx.x + 1] - w0;
   const int32_t *wl = a.wait_idx + w0;
   unsigned long long misspec = 0, retries = 0, timeouts = 0, done_epochs = 0;
+  // The rank's map entries (at most kFlatEntries, checked at plan time),
+  // copied to LDS once, so no epoch waits on a global load for them.
   __shared__ PlanEntry ents[kFlatEntries];
-  if (a.copy_len[r] > 0) {
-    for (int g = threadIdx.x; g < a.cnt[r]; g += bs) ents[g] = a.entries[a.first[r] + g];
-    __syncthreads();
-  }
+  for (int g = threadIdx.x; g < a.cnt[r]; g += bs) ents[g] = a.entries[a.first[r] + g];
+  __syncthreads();
 
   for (int k = 0; k < a.epochs; ++k) {
     const uint32_t ep = a.epoch0 + static_cast<uint32_t>(k);
@@ -1744,8 +1745,14 @@ rrb_status rrb_snac_create_plan(rrb_plan_t plan, uint32_t flags, int32_t slices,
         h->entries.push_back(e);
       }
       h->cnt[r] = static_cast<int32_t>(h->entries.size()) - h->first[r];
-      // Flat consume: copies of one length only, few enough for LDS.
-      bool flat = h->cnt[r] >= 1 && h->cnt[r] <= kFlatEntries;
+      if (h->cnt[r] > kFlatEntries) {
+        const int cnt = h->cnt[r];
+        delete h;
+        return fail(RRB_EUNSUPPORTED, "rank %d has %d map entries; a chain holds at most %d per rank", r,
+                    cnt, kFlatEntries);
+      }
+      // Flat consume: copies of one length only.
+      bool flat = h->cnt[r] >= 1;
       for (int g = h->first[r]; flat && g < h->first[r] + h->cnt[r]; ++g)
         flat = h->entries[g].src_rank >= 0 && h->entries[g].len == h->entries[h->first[r]].len;
       h->copy_len[r] = flat ? h->entries[h->first[r]].len : 0;
