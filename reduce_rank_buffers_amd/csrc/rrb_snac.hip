@@ -1110,21 +1110,8 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
     }
 
     // Stage slice s of rank r's input.
-    const unsigned char *src = a.in + (static_cast<int64_t>(k) * R + r) * a.in_stride;
-    unsigned char *mine = stage_base + static_cast<int64_t>(r) * a.in_stride;
-    for (int64_t i0 = v0 + threadIdx.x; i0 < v1; i0 += static_cast<int64_t>(bs) * kStageU) {
-      v4u x[kStageU];
-#pragma unroll
-      for (int u = 0; u < kStageU; ++u) {
-        const int64_t i = i0 + static_cast<int64_t>(u) * bs;
-        if (i < v1) x[u] = *reinterpret_cast<const v4u *>(src + i * 16);
-      }
-#pragma unroll
-      for (int u = 0; u < kStageU; ++u) {
-        const int64_t i = i0 + static_cast<int64_t>(u) * bs;
-        if (i < v1) store_wt(mine, a.in_stride, i * 16, x[u]);
-      }
-    }
+    stage_slice(a.in + (static_cast<int64_t>(k) * R + r) * a.in_stride,
+                stage_base + static_cast<int64_t>(r) * a.in_stride, a.in_stride, v0, v1);
 
     // Notify.
     notify(flags_b + (static_cast<int64_t>(r) * a.S + s) * kFlagStride, ep);
