@@ -293,11 +293,29 @@ __device__ bool wait_all(const uint32_t *base, int64_t stride_words, uint32_t wa
 // acknowledged and its loads to return (s_waitcnt 0; no L2 write-back is
 // needed, nothing the readers need sits dirty in L2), then thread 0 stores
 // the flag after the workgroup barrier.
+//
+// With SETTLE the workgroup also waits for its own flag store to be
+// acknowledged before it reads other flags.  A flag read issued right behind
+// the store samples memory while the other ranks' flag stores of the same
+// epoch are still on their way, and its value only returns after the store
+// is acknowledged anyway (a wave's memory operations complete in issue
+// order), so it mostly came back stale and was read again.  Measured on
+// MI355X, 8 ranks, 64-epoch All-Reduce chains, us per All-Reduce: dual
+// 8 KiB 1.99 -> 1.95, 128 KiB 2.72 -> 2.43; speculative 8 KiB 1.93 -> 1.80
+// (failed validations 67% -> 14%), 128 KiB 2.78 -> 2.33 (74% -> 1%);
+// barrier 8 KiB 3.09 -> 2.65; twoshot 128 KiB 5.07 -> 4.29.  The plan
+// chains read their wait lists from memory after the flag store, and that
+// load's completion wait already covers the store.
+template <bool SETTLE = true>
 __device__ __forceinline__ void notify(uint32_t *flag, uint32_t ep) {
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __syncthreads();
   if (threadIdx.x == 0) __hip_atomic_store(flag, ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (SETTLE) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  }
 }
 
 // Reduce one pass of this workgroup's slice: R loads in flight per lane, fold
@@ -1114,7 +1132,7 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
                 stage_base + static_cast<int64_t>(r) * a.in_stride, a.in_stride, v0, v1);
 
     // Notify.
-    notify(flags_b + (static_cast<int64_t>(r) * a.S + s) * kFlagStride, ep);
+    notify<false>(flags_b + (static_cast<int64_t>(r) * a.S + s) * kFlagStride, ep);
 
     unsigned char *dst = a.out + (static_cast<int64_t>(k) * R + r) * a.out_stride;
     bool ok = true;
@@ -1177,7 +1195,7 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
     }
     if (VAR == kBarrier) {
       // Bottom barrier: every reader of this workgroup's slice is done.
-      notify(a.done + (static_cast<int64_t>(r) * a.S + s) * kFlagStride, ep);
+      notify<false>(a.done + (static_cast<int64_t>(r) * a.S + s) * kFlagStride, ep);
       if (!wait_list(a.done, wl, nw, ep, a.status, a.spin_limit)) {
         ++timeouts;
         break;
@@ -1592,10 +1610,11 @@ rrb_status launch_ar_chain(rrb_snac_s *h, int32_t epochs, const void *d_in, void
   // Speculation overlaps the loads of the sources that are ready with the
   // wait for the late ones.  That pays while a chain is latency-bound; above
   // kSpecMaxBytes per rank it is bandwidth-bound, and the speculative loads
-  // measured slower than waiting first on MI355X (8 ranks, 64-deep chains:
-  // 256 KiB 3.58 against 3.40 us per All-Reduce, 1 MiB 8.47 against 8.22;
-  // level at 128 KiB, ahead below).  There the speculative variant runs the
-  // dual-buffer kernel: the same buffers and flags, a wait before the loads.
+  // measured slower than waiting first on MI355X (8 ranks, 64-deep chains,
+  // us per All-Reduce: 256 KiB 3.64 against 3.20, 512 KiB 5.50 against 5.31;
+  // ahead at 8-128 KiB, 1.79 against 1.96 at 8 KiB).  There the speculative
+  // variant runs the dual-buffer kernel: the same buffers and flags, a wait
+  // before the loads.
   const bool spec = (h->flags & RRB_SNAC_SPECULATIVE) &&
                     ((h->flags & RRB_SNAC_SPEC_ALWAYS) || a.rank_bytes <= kSpecMaxBytes);
 
