@@ -551,9 +551,14 @@ __global__ void __launch_bounds__(64) snac_chain_kernel(SnacArgs a) {
     notify(flags_b + r * stride_rs + s * kFlagStride, ep);
 
     // Consume: fold the R staged slices in rank order, CU vectors x R
-    // sources in flight per lane.
+    // sources in flight per lane.  Two vectors keep the barrier and dual
+    // kernels at 112 VGPRs, four waves per SIMD, so a chain of 2048
+    // workgroups (256 slices per rank from 512 KiB) stays within half the
+    // device and takes a plain launch; four vectors took 176 VGPRs and a
+    // cooperative launch (dual, 8 ranks, us per All-Reduce: 512 KiB 5.01 ->
+    // 4.68, 2 MiB 14.76 -> 13.98; barrier 5-10% faster from 256 KiB).
     unsigned char *dst_base = a.out + (static_cast<int64_t>(k) * R + r) * a.rank_bytes;
-    constexpr int CU = R <= 8 ? 4 : 2;
+    constexpr int CU = 2;
     // The speculative first pass holds its loads across the flag wait: two
     // vectors per lane keep the kernel within 256 VGPRs, two waves per SIMD,
     // so a chain of 1024 workgroups stays within half the device and takes a
@@ -1258,21 +1263,23 @@ int32_t default_slices(int32_t slices, int64_t nvec, int32_t nranks, uint32_t fl
       }
     } else if (!plan) {
       // Barrier, dual, speculative and twoshot All-Reduce chains: 64 vectors
-      // per workgroup, up to 128 workgroups per rank.  Measured on MI355X, 8
-      // ranks, us per All-Reduce by slices per rank:
-      //   dual     32 KiB   16: 2.71  32: 2.29  64: 2.39
-      //            128 KiB  32: 4.40  64: 3.29  128: 2.84  256: 3.59
-      //            256 KiB  64: 4.99  128: 3.83  256: 3.81
-      //            1 MiB    64: 11.36  128: 8.34  256: 9.86
-      //   twoshot  32 KiB   16: 4.96  32: 4.51  64: 5.01
-      //            128 KiB  64: 5.39  128: 5.14  256: 6.60
-      //            256 KiB  128: 5.81  256: 6.19
-      //            1 MiB    128: 11.13  256: 10.24
-      // (barrier and speculative as dual; 256 per rank for twoshot from 512
-      // KiB won in one sweep and lost in the bench, so it keeps 128).
-      // Before the chains dropped their fences, every extra workgroup added
-      // fence time and 8-32 per rank were best.
-      S = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(128, nvec / 64)));
+      // per workgroup, up to 128 workgroups per rank, and 256 from 512 KiB
+      // per rank.  Measured on MI355X, 8 ranks, us per All-Reduce by slices
+      // per rank (two interleaved runs where two figures are given):
+      //   dual     8 KiB    4: 2.82  8: 2.04  16: 2.11  32: 2.12
+      //            32 KiB   16: 2.59  32: 2.13  64: 2.13  128: 2.37
+      //            128 KiB  64: 2.81  128: 2.47  256: 3.18
+      //            256 KiB  128: 3.33 / 3.47  256: 3.39 / 3.35
+      //            512 KiB  128: 5.42 / 5.27  256: 5.01 / 5.01
+      //            1 MiB    128: 8.67 / 8.36  256: 7.77 / 7.75
+      //   twoshot  512 KiB  128: 7.16 / 7.19  256: 6.67 / 6.70
+      //            1 MiB    128: 10.59 / 10.69  256: 9.02 / 9.06
+      // (barrier and speculative follow dual).  Before the chains dropped
+      // their fences, every extra workgroup added fence time and 8-32 per
+      // rank were best; before the flag store settled (notify), 128 per rank
+      // led at 1 MiB.
+      S = nvec >= 32768 ? 256
+                        : static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(128, nvec / 64)));
     } else {
       // Plan chains: 64 vectors (of the larger of a rank's input and output)
       // per workgroup, up to 64 per rank.  Dual buffer, 8 ranks, 128 KiB
