@@ -466,6 +466,9 @@ def chain_leg(args, torch, rrb, inputs, dev, reps=10):
                     rates[v] = round(st[0] / max(1, st[3]), 3)  # st[3]: epochs x ranks x slices
                 del call
                 ch.close()
+                # every variant's workspace from the same freed block where the
+                # sizes allow, so placement does not differ between variants
+                del ch
             res[f"b{b}h{h}"] = row + [rates["speculative"], rates["speculative_always"]]
             del inp, out
     return res
@@ -600,6 +603,7 @@ def bench_chain(args, dev):
                           "misspec_rate": round(st[0] / max(1, st[3]), 3)}
                 del call
                 ch.close()  # HIP objects released here, not at interpreter exit
+                del ch  # its workspace is free before the next variant allocates
             ops = [rrb.bound("all_reduce", [inp[e, r] for r in range(R)],
                              [out[e, r] for r in range(R)]) for e in range(E)]
 
@@ -647,6 +651,7 @@ def bench_chain(args, dev):
                       "misspec_per_call": round(stats[0].item() / max(5, args.steps), 2)}
             del call
             ch.close()
+            del ch, pin, pout  # freed before the next variant allocates
         plan_rows[name] = res
         log(json.dumps({name: res}))
     print(json.dumps({"metric": "us per All-Reduce in a 64-deep decode chain", "unit": "us",
