@@ -1152,19 +1152,23 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
 
     unsigned char *dst = a.out + (static_cast<int64_t>(k) * R + r) * a.out_stride;
     bool ok = true;
-    if (VAR == kSpeculative) {
+    if (VAR == kSpeculative && a.cnt[r] > 0) {
       // One read of the listed flags; once their values have returned, the
-      // consume runs.  The reduced check: the flags must sum to (list length)
-      // x epoch (each is epoch or epoch - 2, so the sum is exact).  Work that
+      // consume runs.  The reduced check covers the data flags (the slices
+      // this workgroup's pieces read): they must sum to (their count) x
+      // epoch (each is epoch or epoch - 2, so the sum is exact).  Work that
       // fits one round loads every source at once and, on a mismatch, waits
-      // for every listed flag (the write-after-read guards included) and
-      // loads only the stale ranks' sources again (plan_consume_spec).
-      // Larger work leaves out the entries that read a rank whose data flag
-      // read stale (copies from it, and every fold: a fold run too early
-      // would be redone whole), waits, and then runs those.  Either way the
-      // current sources' loads were issued after their flags showed the
-      // epoch.
+      // for every listed flag and loads only the stale ranks' sources again
+      // (plan_consume_spec).  Larger work leaves out the entries that read a
+      // rank whose data flag read stale (copies from it, and every fold: a
+      // fold run too early would be redone whole), waits, and then runs
+      // those.  Either way the current sources' loads were issued after
+      // their flags showed the epoch.  A write-after-read guard that read
+      // stale holds back nothing of this epoch; it is waited for after the
+      // consume, before the next stage.
       uint32_t sum = 0, stale = 0;
+      int ndata = 0;
+      bool guard_late = false;
       for (int i0 = 0; i0 < nw; i0 += bs) {
         const int i = i0 + static_cast<int>(threadIdx.x);
         int32_t w = 0;
@@ -1173,15 +1177,18 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
           w = wl[i];
           f = load_flag_relaxed(flags_b + static_cast<int64_t>(w & kFlagIndexMask) * kFlagStride);
         }
-        sum += lanes_sum(f, min(bs, nw - i0));
+        const bool data = i < nw && !(w & kGuardOnly);
+        sum += lanes_sum(data ? f : 0u, min(bs, nw - i0));
+        ndata += __builtin_popcountll(__ballot(data));
+        guard_late = guard_late || __ballot(i < nw && (w & kGuardOnly) && f != ep) != 0;
         // Lanes holding a stale data flag: their ranks' entries wait.
-        for (uint64_t bad = __ballot(i < nw && f != ep && !(w & kGuardOnly)); bad; bad &= bad - 1) {
+        for (uint64_t bad = __ballot(data && f != ep); bad; bad &= bad - 1) {
           const int l = __builtin_ctzll(bad);
           stale |= 1u << ((__builtin_amdgcn_readlane(w, l) & kFlagIndexMask) / a.S);
         }
       }
       order_after_values();
-      const bool valid = sum == static_cast<uint32_t>(nw) * ep;
+      const bool valid = sum == static_cast<uint32_t>(ndata) * ep;
       if (valid) stale = 0;  // (a valid sum has no stale flag)
       if (!valid) {
         ++misspec;
@@ -1201,7 +1208,10 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
           }
         }
       }
+      // A failed check already waited for the whole list.
+      if (ok && valid && guard_late) ok = wait_list(flags_b, wl, nw, ep, a.status, a.spin_limit);
     } else {
+      // (A speculative workgroup with no map entries only guards: it waits.)
       ok = wait_list(flags_b, wl, nw, ep, a.status, a.spin_limit);
       if (ok) plan_consume<R, BF16>(a, r, s, stage_base, dst, ents, 0u, false);
     }
