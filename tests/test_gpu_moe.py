@@ -142,7 +142,8 @@ def test_combine_special_values(h):
     y = [empty_like_np(T // R * h, "bf16", -21555) for _ in range(R)]
     comb.run([to_dev(a.reshape(-1)) for a in z_np], y)
     torch.cuda.synchronize()
-    want = OM.combine(z_np, idx, w, E, T // R)
+    with np.errstate(invalid="ignore"):  # NaN and infinite inputs on purpose
+        want = OM.combine(z_np, idx, w, E, T // R)
     for r in range(R):
         assert_bits_equal(from_dev(y[r]).reshape(-1, h), want[r], f"combine specials rank {r} h={h}")
 
