@@ -473,7 +473,9 @@ __device__ bool twoshot_epoch(const SnacArgs &a, int r, int s, int k, uint32_t e
   {
     int64_t lo, hi;
     piece_range(a, r, s, lo, hi);
-    constexpr int CU = R <= 8 ? 4 : 2;
+    // Two vectors per lane: 106 VGPRs, four waves per SIMD, so a grid of
+    // 2048 workgroups (256 slices per rank from 512 KiB) launches plainly.
+    constexpr int CU = 2;
     for (int64_t i0 = lo + threadIdx.x; i0 < hi; i0 += static_cast<int64_t>(bs) * CU) {
       uint4 v[CU][R];
 #pragma unroll
@@ -1288,6 +1290,11 @@ int32_t default_slices(int32_t slices, int64_t nvec, int32_t nranks, uint32_t fl
       // led at 1 MiB.
       S = nvec >= 32768 ? 256
                         : static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(128, nvec / 64)));
+      // Speculation held at every size keeps 128 per rank: its kernel (244
+      // VGPRs) fits 1024 workgroups in half the device, not 2048 (512 KiB:
+      // 5.54 us at 128 against 5.72 at 256 cooperatively launched; 1 MiB:
+      // 8.45 against 8.05).
+      if ((flags & RRB_SNAC_SPEC_ALWAYS) && S > 128) S = 128;
     } else {
       // Plan chains: 64 vectors (of the larger of a rank's input and output)
       // per workgroup, up to 64 per rank.  Dual buffer, 8 ranks, 128 KiB
@@ -1352,9 +1359,10 @@ struct rrb_snac_s {
   int64_t in_vec[RRB_MAX_RANKS] = {};
   int32_t first[RRB_MAX_RANKS] = {}, cnt[RRB_MAX_RANKS] = {};
   int64_t copy_len[RRB_MAX_RANKS] = {};
-  // Co-resident capacity (workgroups) of the last persistent kernel launched.
-  const void *cap_fn = nullptr;
-  int64_t cap = 0;
+  // Co-resident capacity (workgroups) of the last two persistent kernels
+  // asked about.
+  const void *cap_fn[2] = {nullptr, nullptr};
+  int64_t cap[2] = {0, 0};
   // RRB_SNAC_GRAPH: one Atom All-Reduce kernel node per epoch, chained in a
   // HIP graph that is cached for the last (in, out, epochs).
   rrb::Plan ar_plan;
@@ -1491,23 +1499,36 @@ rrb_status build_chain_graph(rrb_snac_s *h, int32_t epochs, const void *d_in, vo
 // (or refuses) but costs about 13 us more per call on MI355X.  If other work
 // keeps a plain-launched grid from becoming co-resident, its bounded waits
 // run out and the call reports RRB_ETIMEOUT; it does not hang.
+// Whether a persistent kernel `fn` of the handle's grid (R x S single-wave
+// workgroups) takes a cooperative launch: when the grid exceeds half the
+// device's co-resident capacity for fn (half, as a margin on the occupancy
+// estimate).  The capacities of the last two kernels asked about are kept.
+rrb_status needs_cooperative(rrb_snac_s *h, const void *fn, const char *what, bool *coop) {
+  int slot = h->cap_fn[0] == fn ? 0 : h->cap_fn[1] == fn ? 1 : -1;
+  if (slot < 0) {
+    int dev = 0, cus = 0, per = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, h->bs, 0);
+    if (e != hipSuccess) return fail(RRB_EHIP, "%s occupancy query: %s", what, hipGetErrorString(e));
+    h->cap_fn[1] = h->cap_fn[0];
+    h->cap[1] = h->cap[0];
+    h->cap_fn[0] = fn;
+    h->cap[0] = static_cast<int64_t>(per) * cus;
+    slot = 0;
+  }
+  *coop = 2 * static_cast<int64_t>(h->R) * h->S > h->cap[slot];
+  return RRB_OK;
+}
+
 template <class Args>
 rrb_status launch_persistent(rrb_snac_s *h, const void *fn, Args &a, hipStream_t stream,
                              const char *what) {
   const unsigned grid = static_cast<unsigned>(h->R * h->S);
   bool coop = (h->flags & RRB_SNAC_COOPERATIVE) != 0;
   if (!coop) {
-    if (h->cap_fn != fn) {
-      int dev = 0, cus = 0, per = 0;
-      hipError_t e = hipGetDevice(&dev);
-      if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-      if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, h->bs, 0);
-      if (e != hipSuccess) return fail(RRB_EHIP, "%s occupancy query: %s", what, hipGetErrorString(e));
-      h->cap_fn = fn;
-      h->cap = static_cast<int64_t>(per) * cus;
-    }
-    // Half the capacity, as a margin on the occupancy estimate.
-    coop = 2 * static_cast<int64_t>(grid) > h->cap;
+    const rrb_status st = needs_cooperative(h, fn, what, &coop);
+    if (st != RRB_OK) return st;
   }
   hipError_t e;
   if (coop) {
@@ -1645,10 +1666,22 @@ rrb_status launch_ar_chain(rrb_snac_s *h, int32_t epochs, const void *d_in, void
                     ((h->flags & RRB_SNAC_SPEC_ALWAYS) || a.rank_bytes <= kSpecMaxBytes);
 
   const bool bf16 = h->dtype == RRB_BF16;
-  // Measured on MI355X: payloads up to 16 KiB (slices of one vector per
-  // lane) run 7-8% faster with one vector per lane in flight; from 32 KiB
-  // the two-vector shape is as fast or faster.
-  const bool one = a.nvec <= 1024 && a.slice_vec <= h->bs;
+  // Flag-in-data slices of at most one vector per lane: payloads up to
+  // 16 KiB run 7-8% faster with one vector per lane in flight (measured on
+  // MI355X); at 32-64 KiB the two-vector shape is as fast or faster.  Where
+  // the two-vector instance (172 VGPRs) would need a cooperative launch, the
+  // one-vector instance (85 VGPRs) still launches plainly: 2048 workgroups
+  // at 128 KiB 4.60 -> 4.40 us per All-Reduce, 256 KiB 5.86-5.91 -> 5.53-5.59.
+  bool one = a.nvec <= 1024 && a.slice_vec <= h->bs;
+  if ((h->flags & RRB_SNAC_LAMPORT) && !one && a.slice_vec <= h->bs &&
+      !(h->flags & RRB_SNAC_COOPERATIVE)) {
+    bool coop_two = false;
+    const rrb_status st = needs_cooperative(
+        h, reinterpret_cast<const void *>(bf16 ? snac_for<true, kLamport>(h->R) : snac_for<false, kLamport>(h->R)),
+        "chain", &coop_two);
+    if (st != RRB_OK) return st;
+    one = coop_two;
+  }
   const int var = (h->flags & RRB_SNAC_LAMPORT) ? (one ? kLamportOne : kLamport)
                   : (h->flags & RRB_SNAC_TWOSHOT) ? kTwoshot
                   : spec                              ? kSpeculative

@@ -76,7 +76,7 @@ def _slices_of(ch):
     if ch.variant == "lamport":
         S = max(1, nvec // 64) if nvec < 4096 else min(256, nvec // 32) if nvec <= 16384 else 128
     else:
-        S = 256 if nvec >= 32768 else max(1, min(128, nvec // 64))
+        S = 256 if nvec >= 32768 and ch.variant != "speculative_always" else max(1, min(128, nvec // 64))
     return min(S, 2048 // R, nvec)
 
 
