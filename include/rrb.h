@@ -418,7 +418,7 @@ rrb_status rrb_snac_allreduce_chain(rrb_snac_t h, int32_t epochs,
  * computes piece s of every map entry whose output is rank r; it waits on a
  * list of flags built at create time: the staged slices its pieces read and
  * the workgroups that read its own slice.  slices = 0 gives each workgroup
- * 1 KiB of the larger of a rank's input and output, up to 64 per rank.
+ * 1 KiB of the larger of a rank's input and output, up to 128 per rank.
  * Workspace, bind, check and destroy as for rrb_snac_create.
  */
 rrb_status rrb_snac_create_plan(rrb_plan_t plan, uint32_t flags, int32_t slices,

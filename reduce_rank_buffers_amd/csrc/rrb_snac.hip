@@ -1297,12 +1297,17 @@ int32_t default_slices(int32_t slices, int64_t nvec, int32_t nranks, uint32_t fl
       if ((flags & RRB_SNAC_SPEC_ALWAYS) && S > 128) S = 128;
     } else {
       // Plan chains: 64 vectors (of the larger of a rank's input and output)
-      // per workgroup, up to 64 per rank.  Dual buffer, 8 ranks, 128 KiB
-      // tensor per rank, us per collective at the old default of 8 per rank
-      // against 64: All-Reduce 10.45 -> 3.14, Reduce 10.80 -> 3.26,
-      // Broadcast 4.32 -> 2.45, Reduce-Scatter 4.35 -> 3.35, All-to-All 8.36
-      // -> 7.90, All-Gather 7.14 -> 7.22, Gather 7.13 -> 7.36.
-      S = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(64, nvec / 64)));
+      // per workgroup, up to 128 per rank.  Dual buffer, 8 ranks, us per
+      // collective by slices per rank, measured on MI355X:
+      //   512 KiB tensor  64: All-Reduce 6.91  All-Gather 4.32  All-to-All
+      //                   6.25  Broadcast 4.53  Reduce 6.77  Gather 4.08
+      //                   Reduce-Scatter 4.71
+      //                  128: 5.50  3.40  5.50  3.50  4.88  3.07  4.75
+      //   128 KiB tensor  64: 2.88  2.43  3.26  2.53  3.03  2.44  3.35
+      //                  128: 2.87  2.38  3.25  2.30  2.77  2.42  3.53
+      // (256 per rank was mixed at 512 KiB and slower at 128 KiB; 16 KiB
+      // tensors, 16 per rank, were best or within 0.03 us.)
+      S = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(128, nvec / 64)));
     }
     S = std::min<int32_t>(S, 2048 / nranks);
   }

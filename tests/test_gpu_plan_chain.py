@@ -98,7 +98,7 @@ def ch_slices(ch):
 def _default_slices(ch):
     si, so = ch.strides
     nvec = max(si, so) * ch.esize // 16
-    S = max(1, min(64, nvec // 64))
+    S = max(1, min(128, nvec // 64))
     return min(S, 2048 // ch.nranks, nvec)
 
 
