@@ -931,18 +931,23 @@ __device__ bool wait_list(const uint32_t *base, const int32_t *idx, int n, uint3
 // workgroup.
 constexpr int kFlatEntries = 64;
 
+// A workgroup's piece [lo, hi) of one map entry, in vectors: slice s of the
+// entry's ceil(len / S)-vector pieces.  Computed once per kernel, so no epoch
+// divides.
+struct Piece {
+  int64_t lo, hi;
+};
+
 template <int R, bool BF16>
-__device__ void plan_consume(const PlanChainArgs &a, int r, int s,
-                             const unsigned char *stage_base, unsigned char *dst,
-                             const PlanEntry *ents, uint32_t stale, bool touching) {
+__device__ void plan_consume(const PlanChainArgs &a, int r, const unsigned char *stage_base,
+                             unsigned char *dst, const PlanEntry *ents, const Piece *pieces,
+                             uint32_t stale, bool touching) {
   const int bs = blockDim.x;
   constexpr int CU = R <= 8 ? 2 : 1;
   constexpr int CC = 4;  // copy vectors per lane in flight
   if (a.copy_len[r] > 0) {
-    const int64_t len = a.copy_len[r];
-    const int64_t pl = (len + a.S - 1) / a.S;
-    const int64_t lo = min(len, static_cast<int64_t>(s) * pl);
-    const uint32_t w = static_cast<uint32_t>(min(len, lo + pl) - lo);
+    const int64_t lo = pieces[0].lo;  // every entry has the same piece
+    const uint32_t w = static_cast<uint32_t>(pieces[0].hi - lo);
     const uint32_t total = static_cast<uint32_t>(a.cnt[r]) * w;
     // One descriptor over every rank's staged payload of this buffer.
     const __amdgpu_buffer_rsrc_t src = rsrc(stage_base, static_cast<int64_t>(R) * a.in_stride);
@@ -972,9 +977,8 @@ __device__ void plan_consume(const PlanChainArgs &a, int r, int s,
   for (int g = 0; g < a.cnt[r]; ++g) {
     const PlanEntry e = ents[g];
     if ((e.src_rank < 0 ? stale != 0 : (stale >> e.src_rank & 1u) != 0) != touching) continue;
-    const int64_t pl = (e.len + a.S - 1) / a.S;
-    const int64_t lo = min(e.len, static_cast<int64_t>(s) * pl);
-    const int64_t hi = min(e.len, lo + pl);
+    const int64_t lo = pieces[g].lo;
+    const int64_t hi = pieces[g].hi;
     if (e.src_rank < 0) {
       for (int64_t i0 = lo + threadIdx.x; i0 < hi; i0 += static_cast<int64_t>(bs) * CU) {
         uint4 v[CU][R];
@@ -1024,16 +1028,15 @@ __device__ void plan_consume(const PlanChainArgs &a, int r, int s,
 // does not fit one round (the caller consumes in two parts around the wait),
 // 1 when done, -1 when a wait ran out.
 template <int R, bool BF16>
-__device__ int plan_consume_spec(const PlanChainArgs &a, int r, int s, const unsigned char *stage_base,
-                                 unsigned char *dst, const PlanEntry *ents, const uint32_t *flags_b,
+__device__ int plan_consume_spec(const PlanChainArgs &a, int r, const unsigned char *stage_base,
+                                 unsigned char *dst, const PlanEntry *ents, const Piece *pieces,
+                                 const uint32_t *flags_b,
                                  const int32_t *wl, int nw, uint32_t ep, bool valid, uint32_t stale) {
   const int bs = blockDim.x;
   constexpr int CU = R <= 8 ? 2 : 1;
   if (a.copy_len[r] > 0) {
-    const int64_t len = a.copy_len[r];
-    const int64_t pl = (len + a.S - 1) / a.S;
-    const int64_t lo = min(len, static_cast<int64_t>(s) * pl);
-    const uint32_t w = static_cast<uint32_t>(min(len, lo + pl) - lo);
+    const int64_t lo = pieces[0].lo;  // every entry has the same piece
+    const uint32_t w = static_cast<uint32_t>(pieces[0].hi - lo);
     const uint32_t total = static_cast<uint32_t>(a.cnt[r]) * w;
     if (total > static_cast<uint32_t>(bs) * kCopyU) return 0;
     const __amdgpu_buffer_rsrc_t src = rsrc(stage_base, static_cast<int64_t>(R) * a.in_stride);
@@ -1072,9 +1075,8 @@ __device__ int plan_consume_spec(const PlanChainArgs &a, int r, int s, const uns
   if (a.cnt[r] != 1) return 0;
   const PlanEntry e = ents[0];
   if (e.src_rank >= 0) return 0;
-  const int64_t pl = (e.len + a.S - 1) / a.S;
-  const int64_t lo = min(e.len, static_cast<int64_t>(s) * pl);
-  const int64_t hi = min(e.len, lo + pl);
+  const int64_t lo = pieces[0].lo;
+  const int64_t hi = pieces[0].hi;
   if (hi - lo > static_cast<int64_t>(bs) * CU) return 0;
   uint4 v[CU][R];
 #pragma unroll
@@ -1125,7 +1127,14 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
   // The rank's map entries (at most kFlatEntries, checked at plan time),
   // copied to LDS once, so no epoch waits on a global load for them.
   __shared__ PlanEntry ents[kFlatEntries];
-  for (int g = threadIdx.x; g < a.cnt[r]; g += bs) ents[g] = a.entries[a.first[r] + g];
+  __shared__ Piece pieces[kFlatEntries];
+  for (int g = threadIdx.x; g < a.cnt[r]; g += bs) {
+    const PlanEntry e = a.entries[a.first[r] + g];
+    const int64_t pl = (e.len + a.S - 1) / a.S;
+    const int64_t lo = min(e.len, static_cast<int64_t>(s) * pl);
+    ents[g] = e;
+    pieces[g] = Piece{lo, min(e.len, lo + pl)};
+  }
   __syncthreads();
 
   for (int k = 0; k < a.epochs; ++k) {
@@ -1194,17 +1203,17 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
         ++misspec;
         retries += static_cast<unsigned long long>(__builtin_popcount(stale));
       }
-      const int one = plan_consume_spec<R, BF16>(a, r, s, stage_base, dst, ents, flags_b, wl, nw, ep,
+      const int one = plan_consume_spec<R, BF16>(a, r, stage_base, dst, ents, pieces, flags_b, wl, nw, ep,
                                                  valid, stale);
       if (one < 0) {
         ok = false;
       } else if (one == 0) {
-        plan_consume<R, BF16>(a, r, s, stage_base, dst, ents, stale, false);
+        plan_consume<R, BF16>(a, r, stage_base, dst, ents, pieces, stale, false);
         if (!valid) {
           ok = wait_list(flags_b, wl, nw, ep, a.status, a.spin_limit);
           if (ok) {
             order_after_values();
-            if (stale) plan_consume<R, BF16>(a, r, s, stage_base, dst, ents, stale, true);
+            if (stale) plan_consume<R, BF16>(a, r, stage_base, dst, ents, pieces, stale, true);
           }
         }
       }
@@ -1213,7 +1222,7 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
     } else {
       // (A speculative workgroup with no map entries only guards: it waits.)
       ok = wait_list(flags_b, wl, nw, ep, a.status, a.spin_limit);
-      if (ok) plan_consume<R, BF16>(a, r, s, stage_base, dst, ents, 0u, false);
+      if (ok) plan_consume<R, BF16>(a, r, stage_base, dst, ents, pieces, 0u, false);
     }
     if (!ok) {
       ++timeouts;
