@@ -1021,6 +1021,61 @@ __device__ void plan_consume(const PlanChainArgs &a, int r, const unsigned char 
 
 // The speculative consume of a workgroup whose work fits one round: the
 // rank's copies at most kCopyU vectors per lane, or its one fold at most CU.
+// Its addresses are worked out once per kernel (SpecPrep), so after the flag
+// read only the loads remain: the flag read's ordering barrier keeps every
+// instruction after it, and address work left there lengthened each epoch.
+struct SpecPrep {
+  int kind;  // 0: consume in two parts, 1: flat copies in one round, 2: one fold in one round
+  int32_t off[kCopyU];   // copies: source byte offsets in the staged buffers
+  int32_t rank[kCopyU];  // copies: source ranks
+  int64_t at[kCopyU];    // copies: destination byte offsets, -1 for none
+  int64_t src_off, dst_off, lo, hi;  // fold: the entry and this workgroup's piece
+};
+
+template <int R>
+__device__ __forceinline__ void spec_prepare(const PlanChainArgs &a, int r, const PlanEntry *ents,
+                                             const Piece *pieces, SpecPrep &p) {
+  const int bs = blockDim.x;
+  constexpr int CU = R <= 8 ? 2 : 1;
+  p.kind = 0;
+  p.src_off = p.dst_off = p.lo = p.hi = 0;
+#pragma unroll
+  for (int u = 0; u < kCopyU; ++u) {
+    p.off[u] = 0;
+    p.rank[u] = 0;
+    p.at[u] = -1;
+  }
+  if (a.copy_len[r] > 0) {
+    const int64_t lo = pieces[0].lo;  // every entry has the same piece
+    const uint32_t w = static_cast<uint32_t>(pieces[0].hi - lo);
+    const uint32_t total = static_cast<uint32_t>(a.cnt[r]) * w;
+    if (total > static_cast<uint32_t>(bs) * kCopyU) return;
+    p.kind = 1;
+#pragma unroll
+    for (int u = 0; u < kCopyU; ++u) {
+      const uint32_t f = threadIdx.x + static_cast<uint32_t>(u * bs);
+      if (f < total) {
+        const uint32_t g = f / w;
+        const PlanEntry e = ents[g];
+        const int64_t i = lo + (f - g * w);
+        p.off[u] = static_cast<int32_t>(e.src_rank * a.in_stride + (e.src_off + i) * 16);
+        p.rank[u] = e.src_rank;
+        p.at[u] = (e.dst_off + i) * 16;
+      }
+    }
+    return;
+  }
+  if (a.cnt[r] != 1) return;
+  const PlanEntry e = ents[0];
+  if (e.src_rank >= 0) return;
+  if (pieces[0].hi - pieces[0].lo > static_cast<int64_t>(bs) * CU) return;
+  p.kind = 2;
+  p.src_off = e.src_off;
+  p.dst_off = e.dst_off;
+  p.lo = pieces[0].lo;
+  p.hi = pieces[0].hi;
+}
+
 // Every source is loaded once the flag values have returned.  After a failed
 // sum the workgroup waits for its list and loads the stale ranks' sources
 // again; the current ones' data stays in registers, so the wait overlaps
@@ -1028,65 +1083,39 @@ __device__ void plan_consume(const PlanChainArgs &a, int r, const unsigned char 
 // does not fit one round (the caller consumes in two parts around the wait),
 // 1 when done, -1 when a wait ran out.
 template <int R, bool BF16>
-__device__ int plan_consume_spec(const PlanChainArgs &a, int r, const unsigned char *stage_base,
-                                 unsigned char *dst, const PlanEntry *ents, const Piece *pieces,
-                                 const uint32_t *flags_b,
-                                 const int32_t *wl, int nw, uint32_t ep, bool valid, uint32_t stale) {
+__device__ int plan_consume_spec(const PlanChainArgs &a, const SpecPrep &p, const unsigned char *stage_base,
+                                 unsigned char *dst, const uint32_t *flags_b, const int32_t *wl, int nw,
+                                 uint32_t ep, bool valid, uint32_t stale) {
   const int bs = blockDim.x;
   constexpr int CU = R <= 8 ? 2 : 1;
-  if (a.copy_len[r] > 0) {
-    const int64_t lo = pieces[0].lo;  // every entry has the same piece
-    const uint32_t w = static_cast<uint32_t>(pieces[0].hi - lo);
-    const uint32_t total = static_cast<uint32_t>(a.cnt[r]) * w;
-    if (total > static_cast<uint32_t>(bs) * kCopyU) return 0;
+  if (p.kind == 1) {
     const __amdgpu_buffer_rsrc_t src = rsrc(stage_base, static_cast<int64_t>(R) * a.in_stride);
     uint4 x[kCopyU];
-    int32_t off[kCopyU];
-    int32_t rank[kCopyU];
-    int64_t at[kCopyU];
 #pragma unroll
-    for (int u = 0; u < kCopyU; ++u) {
-      const uint32_t f = threadIdx.x + static_cast<uint32_t>(u * bs);
-      at[u] = -1;
-      off[u] = 0;
-      rank[u] = 0;
-      if (f < total) {
-        const uint32_t g = f / w;
-        const PlanEntry e = ents[g];
-        const int64_t i = lo + (f - g * w);
-        off[u] = static_cast<int32_t>(e.src_rank * a.in_stride + (e.src_off + i) * 16);
-        rank[u] = e.src_rank;
-        at[u] = (e.dst_off + i) * 16;
-        x[u] = load_coherent(src, off[u]);
-      }
-    }
+    for (int u = 0; u < kCopyU; ++u)
+      if (p.at[u] >= 0) x[u] = load_coherent(src, p.off[u]);
     if (!valid) {
       if (!wait_list(flags_b, wl, nw, ep, a.status, a.spin_limit)) return -1;
       order_after_values();
 #pragma unroll
       for (int u = 0; u < kCopyU; ++u)
-        if (at[u] >= 0 && (stale >> rank[u] & 1u)) x[u] = load_coherent(src, off[u]);
+        if (p.at[u] >= 0 && (stale >> p.rank[u] & 1u)) x[u] = load_coherent(src, p.off[u]);
     }
 #pragma unroll
     for (int u = 0; u < kCopyU; ++u)
-      if (at[u] >= 0) *reinterpret_cast<uint4 *>(dst + at[u]) = x[u];
+      if (p.at[u] >= 0) *reinterpret_cast<uint4 *>(dst + p.at[u]) = x[u];
     return 1;
   }
-  if (a.cnt[r] != 1) return 0;
-  const PlanEntry e = ents[0];
-  if (e.src_rank >= 0) return 0;
-  const int64_t lo = pieces[0].lo;
-  const int64_t hi = pieces[0].hi;
-  if (hi - lo > static_cast<int64_t>(bs) * CU) return 0;
+  if (p.kind != 2) return 0;
   uint4 v[CU][R];
 #pragma unroll
   for (int u = 0; u < CU; ++u) {
-    const int64_t i = lo + threadIdx.x + static_cast<int64_t>(u) * bs;
-    if (i < hi) {
+    const int64_t i = p.lo + threadIdx.x + static_cast<int64_t>(u) * bs;
+    if (i < p.hi) {
 #pragma unroll
       for (int q = 0; q < R; ++q)
         v[u][q] = load_coherent(rsrc(stage_base + static_cast<int64_t>(q) * a.in_stride, a.in_stride),
-                                static_cast<int32_t>((e.src_off + i) * 16));
+                                static_cast<int32_t>((p.src_off + i) * 16));
     }
   }
   if (!valid) {
@@ -1097,18 +1126,18 @@ __device__ int plan_consume_spec(const PlanChainArgs &a, int r, const unsigned c
       if (stale >> q & 1u) {
 #pragma unroll
         for (int u = 0; u < CU; ++u) {
-          const int64_t i = lo + threadIdx.x + static_cast<int64_t>(u) * bs;
-          if (i < hi)
+          const int64_t i = p.lo + threadIdx.x + static_cast<int64_t>(u) * bs;
+          if (i < p.hi)
             v[u][q] = load_coherent(rsrc(stage_base + static_cast<int64_t>(q) * a.in_stride, a.in_stride),
-                                    static_cast<int32_t>((e.src_off + i) * 16));
+                                    static_cast<int32_t>((p.src_off + i) * 16));
         }
       }
     }
   }
 #pragma unroll
   for (int u = 0; u < CU; ++u) {
-    const int64_t i = lo + threadIdx.x + static_cast<int64_t>(u) * bs;
-    if (i < hi) reduce_pass<R, BF16, false>(v[u], dst, a.out_stride, (e.dst_off + i) * 16);
+    const int64_t i = p.lo + threadIdx.x + static_cast<int64_t>(u) * bs;
+    if (i < p.hi) reduce_pass<R, BF16, false>(v[u], dst, a.out_stride, (p.dst_off + i) * 16);
   }
   return 1;
 }
@@ -1136,6 +1165,8 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
     pieces[g] = Piece{lo, min(e.len, lo + pl)};
   }
   __syncthreads();
+  SpecPrep prep;
+  if (VAR == kSpeculative) spec_prepare<R>(a, r, ents, pieces, prep);
 
   for (int k = 0; k < a.epochs; ++k) {
     const uint32_t ep = a.epoch0 + static_cast<uint32_t>(k);
@@ -1203,8 +1234,7 @@ __global__ void __launch_bounds__(64) snac_plan_kernel(PlanChainArgs a) {
         ++misspec;
         retries += static_cast<unsigned long long>(__builtin_popcount(stale));
       }
-      const int one = plan_consume_spec<R, BF16>(a, r, stage_base, dst, ents, pieces, flags_b, wl, nw, ep,
-                                                 valid, stale);
+      const int one = plan_consume_spec<R, BF16>(a, prep, stage_base, dst, flags_b, wl, nw, ep, valid, stale);
       if (one < 0) {
         ok = false;
       } else if (one == 0) {
