@@ -345,7 +345,8 @@ rrb_status rrb_empty_kernel(rrb_stream_t stream);
  *                              its bounded waits run out and the call reports
  *                              RRB_ETIMEOUT rather than hang.
  * slices: single-wave workgroups per rank (1..256; 0 = choose from count:
- *         1 KiB of payload per workgroup, up to 128, and 256 from 512 KiB;
+ *         1 KiB of payload per workgroup, up to 128, and 256 from 512 KiB
+ *         (128 with RRB_SNAC_SPEC_ALWAYS);
  *         RRB_SNAC_LAMPORT: 1 KiB per workgroup below 64 KiB, then 512 B per
  *         workgroup up to 256, and 128 above 256 KiB; at most 2048 / nranks).
  *         The grid (nranks x slices) must be co-resident; a cooperative
