@@ -210,6 +210,41 @@ def test_100k_iterations_exact(v):
     _say(f"100k {v}: misspec {s[0]} retries {s[1]} epochs {done}")
 
 
+@pytest.mark.parametrize("v", ["speculative", "lamport"])
+def test_100k_staggered_exact(v):
+    """100k chained All-Reduces with late ranks that change every call
+    (seeded delays of 0-255 sleeps per rank before each stage), so the
+    speculative check fails and retries, and flag-in-data polls find
+    untagged words, throughout; every result bit-exact."""
+    require_gpu()
+    n, pool, per_call, total = 4096, 256, 256, 100_000
+    ins_np = inputs.chain(pool, R, n, kind=82)
+    want = np.stack(OC.allreduce_chain(ins_np))
+    inp = to_dev(ins_np)
+    want_dev = to_dev(np.repeat(want[:, None, :], R, axis=1))
+    ch = api.SnacChain(R, n, "bf16", v)
+    stats = torch.zeros(4, dtype=torch.int64, device=DEV)
+    out = torch.empty_like(inp)
+    rng = np.random.default_rng(83)
+    done = 0
+    while done < total:
+        st = rng.integers(0, 256, size=R).astype(np.int32)
+        stagger = torch.from_numpy(st).to(DEV)
+        ch.run(inp, out, stats=stats, stagger=stagger)
+        if not torch.equal(out, want_dev):
+            ch.check()
+            bad = (out != want_dev).nonzero()
+            raise AssertionError(f"{v} mismatch after {done} epochs, stagger {st.tolist()}: {bad[:5].tolist()}")
+        done += per_call
+        if done % 25600 == 0:
+            _say(f"  {done} staggered epochs exact")
+    ch.check()
+    s = stats.cpu().tolist()
+    _say(f"100k staggered {v}: misspec {s[0]} retries {s[1]}")
+    assert s[2] == 0
+    assert s[1] > 0  # retries (speculative) or poll rounds (flag-in-data) happened
+
+
 @pytest.mark.parametrize("v", ["barrier", "dual", "speculative", "twoshot"])
 def test_many_slices_stress_exact(v):
     """128 KiB payloads take 128 workgroups per rank (1024 in all) for the
