@@ -367,6 +367,83 @@ __global__ void __launch_bounds__(kScanThreads) moe_route_scan_kernel(RouteArgs 
   }
 }
 
+// A token's K routing entries.  They are contiguous: 16-byte loads when K
+// is a multiple of 4 and the caller's arrays are 16-byte aligned.
+template <int K>
+__device__ __forceinline__ void load_topk(const RouteArgs &a, int64_t t, bool live, int32_t (&e)[K],
+                                          float (&w)[K]) {
+  const bool vec = K % 4 == 0 &&
+                   ((reinterpret_cast<uintptr_t>(a.idx) | reinterpret_cast<uintptr_t>(a.w)) & 15u) == 0;
+  if (vec) {
+#pragma unroll
+    for (int v = 0; v < K / 4; ++v) {
+      int4 qi = make_int4(0, 0, 0, 0);
+      float4 qw = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (live) {
+        qi = reinterpret_cast<const int4 *>(a.idx + t * K)[v];
+        qw = reinterpret_cast<const float4 *>(a.w + t * K)[v];
+      }
+      e[4 * v] = qi.x; e[4 * v + 1] = qi.y; e[4 * v + 2] = qi.z; e[4 * v + 3] = qi.w;
+      w[4 * v] = qw.x; w[4 * v + 1] = qw.y; w[4 * v + 2] = qw.z; w[4 * v + 3] = qw.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      e[j] = live ? a.idx[t * K + j] : 0;
+      w[j] = live ? a.w[t * K + j] : 0.f;
+    }
+  }
+}
+
+// Stable exchange sort of a token's entries by expert id (c: the entries'
+// original positions), the swaps taken as selects rather than branches the
+// lanes disagree on.
+template <int K>
+__device__ __forceinline__ void sort_by_expert(int32_t (&e)[K], float (&w)[K], bool (&ok)[K],
+                                               int32_t (&c)[K]) {
+#pragma unroll
+  for (int j = 0; j < K; ++j) c[j] = j;
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+#pragma unroll
+    for (int j = 0; j + 1 < K - i; ++j) {
+      const bool sw = e[j] > e[j + 1];
+      const int32_t e0 = e[j], e1 = e[j + 1];
+      const float w0 = w[j], w1 = w[j + 1];
+      const bool o0 = ok[j], o1 = ok[j + 1];
+      const int32_t c0 = c[j], c1 = c[j + 1];
+      e[j] = sw ? e1 : e0; e[j + 1] = sw ? e0 : e1;
+      w[j] = sw ? w1 : w0; w[j + 1] = sw ? w0 : w1;
+      ok[j] = sw ? o1 : o0; ok[j + 1] = sw ? o0 : o1;
+      c[j] = sw ? c1 : c0; c[j + 1] = sw ? c0 : c1;
+    }
+  }
+}
+
+// A token's slot, weight and column maps.  They are the library's own,
+// 256-byte aligned: 16-byte stores when K is a multiple of 4.
+template <int K>
+__device__ __forceinline__ void store_maps(const RouteArgs &a, int64_t t, const int32_t (&row)[K],
+                                           const float (&wt)[K], const int32_t (&c)[K]) {
+  if (K % 4 == 0) {
+#pragma unroll
+    for (int v = 0; v < K / 4; ++v) {
+      reinterpret_cast<int4 *>(a.slot + t * K)[v] =
+          make_int4(row[4 * v], row[4 * v + 1], row[4 * v + 2], row[4 * v + 3]);
+      reinterpret_cast<float4 *>(a.weight + t * K)[v] =
+          make_float4(wt[4 * v], wt[4 * v + 1], wt[4 * v + 2], wt[4 * v + 3]);
+      reinterpret_cast<int4 *>(a.col + t * K)[v] = make_int4(c[4 * v], c[4 * v + 1], c[4 * v + 2], c[4 * v + 3]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      a.slot[t * K + j] = row[j];
+      a.weight[t * K + j] = wt[j];
+      a.col[t * K + j] = c[j];
+    }
+  }
+}
+
 template <int K>
 __global__ void __launch_bounds__(kRouteBlock) moe_route_slot_kernel(RouteArgs a) {
   constexpr int W = kRouteBlock / 32;
@@ -380,10 +457,9 @@ __global__ void __launch_bounds__(kRouteBlock) moe_route_slot_kernel(RouteArgs a
   float w[K];
   bool ok[K];
   const bool live = t < a.T;
+  load_topk<K>(a, t, live, e, w);
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    e[j] = live ? a.idx[t * K + j] : 0;
-    w[j] = live ? a.w[t * K + j] : 0.f;
     ok[j] = live && e[j] >= 0 && e[j] < a.E;
 #pragma unroll
     for (int j2 = 0; j2 < j; ++j2) ok[j] = ok[j] && e[j2] != e[j];
@@ -400,36 +476,23 @@ __global__ void __launch_bounds__(kRouteBlock) moe_route_slot_kernel(RouteArgs a
   }
   __syncthreads();
   if (!live) return;
-  // Ascending expert id (bubble sort over registers; K is small and static).
+  // Ascending expert id.
   int32_t c[K];
-#pragma unroll
-  for (int j = 0; j < K; ++j) c[j] = j;
-#pragma unroll
-  for (int i = 0; i < K; ++i) {
-#pragma unroll
-    for (int j = 0; j + 1 < K - i; ++j) {
-      if (e[j] > e[j + 1]) {
-        const int32_t te = e[j]; e[j] = e[j + 1]; e[j + 1] = te;
-        const float tw = w[j]; w[j] = w[j + 1]; w[j + 1] = tw;
-        const bool to = ok[j]; ok[j] = ok[j + 1]; ok[j + 1] = to;
-        const int32_t tc = c[j]; c[j] = c[j + 1]; c[j + 1] = tc;
-      }
-    }
-  }
+  sort_by_expert<K>(e, w, ok, c);
+  int32_t row[K];
+  float wt[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    int32_t row = 0;
-    float wt = 0.f;
+    row[j] = 0;
+    wt[j] = 0.f;
     if (ok[j]) {
       const int q = local >> 5;
       const int pos = mpre[e[j] * W + q] + __popc(mask[e[j] * W + q] & ((1u << (local & 31)) - 1u));
-      row = a.expert_off[e[j]] + a.bbase[static_cast<int64_t>(blockIdx.x) * a.E + e[j]] + pos;
-      wt = w[j];
+      row[j] = a.expert_off[e[j]] + a.bbase[static_cast<int64_t>(blockIdx.x) * a.E + e[j]] + pos;
+      wt[j] = w[j];
     }
-    a.slot[t * K + j] = row;
-    a.weight[t * K + j] = wt;
-    a.col[t * K + j] = c[j];
   }
+  store_maps<K>(a, t, row, wt, c);
 }
 
 // Fused routing: one block of kRouteBlock tokens per workgroup, all blocks
@@ -464,29 +527,7 @@ __global__ void __launch_bounds__(kRouteBlock) moe_route_fused_kernel(RouteArgs 
   float w[K];
   bool ok[K];
   int32_t mybad = 0;
-  // A token's K entries are contiguous: 16-byte loads when K is a multiple
-  // of 4 and the caller's arrays are 16-byte aligned.
-  const bool vec = K % 4 == 0 &&
-                   ((reinterpret_cast<uintptr_t>(a.idx) | reinterpret_cast<uintptr_t>(a.w)) & 15u) == 0;
-  if (vec) {
-#pragma unroll
-    for (int v = 0; v < K / 4; ++v) {
-      int4 qi = make_int4(0, 0, 0, 0);
-      float4 qw = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (live) {
-        qi = reinterpret_cast<const int4 *>(a.idx + t * K)[v];
-        qw = reinterpret_cast<const float4 *>(a.w + t * K)[v];
-      }
-      e[4 * v] = qi.x; e[4 * v + 1] = qi.y; e[4 * v + 2] = qi.z; e[4 * v + 3] = qi.w;
-      w[4 * v] = qw.x; w[4 * v + 1] = qw.y; w[4 * v + 2] = qw.z; w[4 * v + 3] = qw.w;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      e[j] = live ? a.idx[t * K + j] : 0;
-      w[j] = live ? a.w[t * K + j] : 0.f;
-    }
-  }
+  load_topk<K>(a, t, live, e, w);
 #pragma unroll
   for (int j = 0; j < K; ++j) {
     const bool in_range = e[j] >= 0 && e[j] < a.E;
@@ -632,25 +673,7 @@ __global__ void __launch_bounds__(kRouteBlock) moe_route_fused_kernel(RouteArgs 
   // Phase 3: this block's slots, experts in ascending id.
   if (!live) return;
   int32_t c[K];
-#pragma unroll
-  for (int j = 0; j < K; ++j) c[j] = j;
-  // Stable exchange sort by expert id, the swaps taken as selects rather
-  // than branches (lanes disagree on them).
-#pragma unroll
-  for (int i = 0; i < K; ++i) {
-#pragma unroll
-    for (int j = 0; j + 1 < K - i; ++j) {
-      const bool sw = e[j] > e[j + 1];
-      const int32_t e0 = e[j], e1 = e[j + 1];
-      const float w0 = w[j], w1 = w[j + 1];
-      const bool o0 = ok[j], o1 = ok[j + 1];
-      const int32_t c0 = c[j], c1 = c[j + 1];
-      e[j] = sw ? e1 : e0; e[j + 1] = sw ? e0 : e1;
-      w[j] = sw ? w1 : w0; w[j + 1] = sw ? w0 : w1;
-      ok[j] = sw ? o1 : o0; ok[j + 1] = sw ? o0 : o1;
-      c[j] = sw ? c1 : c0; c[j + 1] = sw ? c0 : c1;
-    }
-  }
+  sort_by_expert<K>(e, w, ok, c);
   int32_t row[K];
   float wt[K];
 #pragma unroll
@@ -664,23 +687,7 @@ __global__ void __launch_bounds__(kRouteBlock) moe_route_fused_kernel(RouteArgs 
       wt[j] = w[j];
     }
   }
-  // The maps are the library's own, 256-byte aligned: 16-byte stores when K
-  // is a multiple of 4.
-  if (K % 4 == 0) {
-#pragma unroll
-    for (int v = 0; v < K / 4; ++v) {
-      reinterpret_cast<int4 *>(a.slot + t * K)[v] = make_int4(row[4 * v], row[4 * v + 1], row[4 * v + 2], row[4 * v + 3]);
-      reinterpret_cast<float4 *>(a.weight + t * K)[v] = make_float4(wt[4 * v], wt[4 * v + 1], wt[4 * v + 2], wt[4 * v + 3]);
-      reinterpret_cast<int4 *>(a.col + t * K)[v] = make_int4(c[4 * v], c[4 * v + 1], c[4 * v + 2], c[4 * v + 3]);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      a.slot[t * K + j] = row[j];
-      a.weight[t * K + j] = wt[j];
-      a.col[t * K + j] = c[j];
-    }
-  }
+  store_maps<K>(a, t, row, wt, c);
 }
 
 namespace {
