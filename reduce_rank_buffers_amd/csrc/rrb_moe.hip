@@ -273,9 +273,11 @@ __global__ void __launch_bounds__(256) moe_combine_elem_kernel(RowArgs a) {
 // ascending id (tokens ascending within an expert) plus its weight.  Three
 // kernels, all deterministic:
 //   count: per block of kRouteBlock tokens, an LDS histogram of experts;
-//   scan:  per expert, exclusive prefix over blocks; exclusive prefix of the
-//          totals over experts; rank offsets (ranks hold contiguous experts);
-//   slot:  per block, a kRouteBlock-bit token mask per expert in LDS; a
+//   scan:  one workgroup per expert: exclusive prefix of its counts over
+//          blocks, and its total;
+//   slot:  per block, the exclusive prefix of the totals over experts (block
+//          0 also stores it and the rank offsets: ranks hold contiguous
+//          experts); a kRouteBlock-bit token mask per expert in LDS; a
 //          token's position within its expert is the block base plus the
 //          popcount of the mask bits below it.
 // When the token blocks fit on the device at once, one fused kernel does all
@@ -308,63 +310,76 @@ __global__ void moe_fill_kernel(int32_t *p, int64_t n, int32_t v) {
     p[i] = v;
 }
 
-__global__ void __launch_bounds__(kRouteBlock) moe_route_count_kernel(RouteArgs a) {
-  __shared__ int32_t hist[kRouteMaxExperts];
-  for (int e = threadIdx.x; e < a.E; e += blockDim.x) hist[e] = 0;
-  __syncthreads();
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kRouteBlock + threadIdx.x;
-  if (t < a.T) {
-    const int32_t *row = a.idx + t * a.k;
-    for (int j = 0; j < a.k; ++j) {
-      const int32_t e = row[j];
-      if (e < 0 || e >= a.E) {
-        atomicOr(a.status, 1);
-        continue;
-      }
-      bool dup = false;
-      for (int j2 = 0; j2 < j; ++j2) dup = dup || row[j2] == e;
-      if (dup) {
-        atomicOr(a.status, 2);
-        continue;
-      }
-      atomicAdd(&hist[e], 1);
-    }
+// Exclusive prefix of one value per thread over the workgroup's
+// kRouteBlock threads, and their total: a shuffle scan within each wave, then
+// across the waves through part[kRouteBlock / 64] (one workgroup barrier).
+__device__ __forceinline__ int32_t block_exclusive_prefix(int32_t v, int32_t *part, int32_t &total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
   }
+  if (lane == 63) part[wave] = incl;
   __syncthreads();
-  for (int e = threadIdx.x; e < a.E; e += blockDim.x)
-    a.bcounts[static_cast<int64_t>(blockIdx.x) * a.E + e] = hist[e];
+  total = 0;
+#pragma unroll
+  for (int q = 0; q < kRouteBlock / 64; ++q) {
+    if (q < wave) incl += part[q];
+    total += part[q];
+  }
+  return incl - v;
 }
 
-constexpr int kScanThreads = 1024;
+// Exclusive scan of v[0..n) in LDS, in place, by all kRouteBlock threads;
+// returns the total.  Each thread takes a run of consecutive entries.
+__device__ __forceinline__ int32_t lds_exclusive_scan(int32_t *v, int n, int32_t *part) {
+  const int per_thread = (n + kRouteBlock - 1) / kRouteBlock;
+  const int x0 = threadIdx.x * per_thread, x1 = min(n, x0 + per_thread);
+  int32_t sum = 0;
+  for (int x = x0; x < x1; ++x) sum += v[x];
+  int32_t total;
+  int32_t base = block_exclusive_prefix(sum, part, total);
+  for (int x = x0; x < x1; ++x) {
+    const int32_t c = v[x];
+    v[x] = base;
+    base += c;
+  }
+  __syncthreads();
+  return total;
+}
 
-__global__ void __launch_bounds__(kScanThreads) moe_route_scan_kernel(RouteArgs a) {
-  __shared__ int32_t tot[kScanThreads];
-  const int e = threadIdx.x;
-  int32_t run = 0;
-  if (e < a.E) {
-    for (int b = 0; b < a.nblk; ++b) {
-      const int64_t o = static_cast<int64_t>(b) * a.E + e;
-      a.bbase[o] = run;
-      run += a.bcounts[o];
+// One workgroup per expert x: bbase[b][x] = the sum of bcounts[b'][x] over
+// b' < b, and counts[x] = the sum over all blocks.  Each thread takes a run
+// of consecutive blocks, loaded eight at a time.
+__global__ void __launch_bounds__(kRouteBlock) moe_route_scan_kernel(RouteArgs a) {
+  __shared__ int32_t part[kRouteBlock / 64];
+  const int x = blockIdx.x;
+  const int per_thread = (a.nblk + kRouteBlock - 1) / kRouteBlock;
+  const int b0 = threadIdx.x * per_thread, b1 = min(a.nblk, b0 + per_thread);
+  const int32_t *__restrict__ col = a.bcounts + x;
+  int32_t sum = 0;
+  for (int b = b0; b < b1; b += 8) {
+    int32_t c[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c[u] = b + u < b1 ? col[static_cast<int64_t>(b + u) * a.E] : 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += c[u];
+  }
+  int32_t total;
+  int32_t run = block_exclusive_prefix(sum, part, total);
+  for (int b = b0; b < b1; b += 8) {
+    int32_t c[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c[u] = b + u < b1 ? col[static_cast<int64_t>(b + u) * a.E] : 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (b + u < b1) a.bbase[static_cast<int64_t>(b + u) * a.E + x] = run;
+      run += c[u];
     }
-    a.counts[e] = run;
   }
-  tot[e] = e < a.E ? run : 0;
-  __syncthreads();
-  // Inclusive scan over experts (Hillis-Steele), then shift to exclusive.
-  for (int d = 1; d < kScanThreads; d <<= 1) {
-    const int32_t add = e >= d ? tot[e - d] : 0;
-    __syncthreads();
-    tot[e] += add;
-    __syncthreads();
-  }
-  if (e < a.E) a.expert_off[e] = tot[e] - run;
-  __syncthreads();
-  if (e <= a.R) {
-    const int32_t v = e < a.R ? (e * a.per == 0 ? 0 : tot[e * a.per - 1]) : tot[a.E - 1];
-    a.rank_off[e] = v;
-    if (a.user_rank_off) a.user_rank_off[e] = v;
-  }
+  if (threadIdx.x == 0) a.counts[x] = total;
 }
 
 // A token's K routing entries.  They are contiguous: 16-byte loads when K
@@ -393,6 +408,38 @@ __device__ __forceinline__ void load_topk(const RouteArgs &a, int64_t t, bool li
       w[j] = live ? a.w[t * K + j] : 0.f;
     }
   }
+}
+
+// Per block: an LDS histogram of its tokens' valid entries, stored as the
+// block's row of bcounts, and the error bits of its invalid ones.
+template <int K>
+__global__ void __launch_bounds__(kRouteBlock) moe_route_count_kernel(RouteArgs a) {
+  __shared__ int32_t hist[kRouteMaxExperts];
+  __shared__ int32_t bad;
+  for (int x = threadIdx.x; x < a.E; x += blockDim.x) hist[x] = 0;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kRouteBlock + threadIdx.x;
+  const bool live = t < a.T;
+  int32_t e[K];
+  float w[K];
+  load_topk<K>(a, t, live, e, w);
+  int32_t mybad = 0;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const bool in_range = e[j] >= 0 && e[j] < a.E;
+    bool dup = false;
+#pragma unroll
+    for (int j2 = 0; j2 < j; ++j2) dup = dup || e[j2] == e[j];
+    if (live && !in_range) mybad |= 1;
+    if (live && in_range && dup) mybad |= 2;
+    if (live && in_range && !dup) atomicAdd(&hist[e[j]], 1);
+  }
+  if (mybad) atomicOr(&bad, mybad);
+  __syncthreads();
+  if (threadIdx.x == 0 && bad) atomicOr(a.status, bad);
+  for (int x = threadIdx.x; x < a.E; x += blockDim.x)
+    a.bcounts[static_cast<int64_t>(blockIdx.x) * a.E + x] = hist[x];
 }
 
 // Stable exchange sort of a token's entries by expert id (c: the entries'
@@ -449,8 +496,20 @@ __global__ void __launch_bounds__(kRouteBlock) moe_route_slot_kernel(RouteArgs a
   constexpr int W = kRouteBlock / 32;
   __shared__ uint32_t mask[kRouteMaxExperts * W];
   __shared__ uint16_t mpre[kRouteMaxExperts * W];  // tokens in the expert's earlier mask words
+  __shared__ int32_t eoff[kRouteMaxExperts];       // exclusive offsets over experts
+  __shared__ int32_t part[kRouteBlock / 64];
   for (int i = threadIdx.x; i < a.E * W; i += blockDim.x) mask[i] = 0;
+  for (int x = threadIdx.x; x < a.E; x += blockDim.x) eoff[x] = a.counts[x];
   __syncthreads();
+  const int32_t total = lds_exclusive_scan(eoff, a.E, part);
+  if (blockIdx.x == 0) {
+    for (int x = threadIdx.x; x < a.E; x += blockDim.x) a.expert_off[x] = eoff[x];
+    if (static_cast<int>(threadIdx.x) <= a.R) {
+      const int32_t v = static_cast<int>(threadIdx.x) < a.R ? eoff[threadIdx.x * a.per] : total;
+      a.rank_off[threadIdx.x] = v;
+      if (a.user_rank_off) a.user_rank_off[threadIdx.x] = v;
+    }
+  }
   const int local = threadIdx.x;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kRouteBlock + local;
   int32_t e[K];
@@ -488,7 +547,7 @@ __global__ void __launch_bounds__(kRouteBlock) moe_route_slot_kernel(RouteArgs a
     if (ok[j]) {
       const int q = local >> 5;
       const int pos = mpre[e[j] * W + q] + __popc(mask[e[j] * W + q] & ((1u << (local & 31)) - 1u));
-      row[j] = a.expert_off[e[j]] + a.bbase[static_cast<int64_t>(blockIdx.x) * a.E + e[j]] + pos;
+      row[j] = eoff[e[j]] + a.bbase[static_cast<int64_t>(blockIdx.x) * a.E + e[j]] + pos;
       wt[j] = w[j];
     }
   }
@@ -510,7 +569,7 @@ __global__ void __launch_bounds__(kRouteBlock) moe_route_fused_kernel(RouteArgs 
   __shared__ uint16_t mpre[kRouteMaxExperts * W];  // tokens in the expert's earlier mask words
   __shared__ int32_t hist[kRouteMaxExperts];   // counts, then earlier-block prefix
   __shared__ int32_t eoff[kRouteMaxExperts];   // exclusive offsets over experts
-  __shared__ int32_t part[kRouteBlock];
+  __shared__ int32_t part[kRouteBlock / 64];
   __shared__ int32_t bad;
   __shared__ int ok_all;
   const int tid = threadIdx.x;
@@ -617,41 +676,13 @@ __global__ void __launch_bounds__(kRouteBlock) moe_route_fused_kernel(RouteArgs 
     eoff[x] = tot;
   }
   __syncthreads();
-  // Exclusive scan of the totals over experts: each thread sums a run of
-  // consecutive experts, the run sums are scanned within each wave by
-  // shuffles and across the block's waves through LDS, then spread back
-  // (one workgroup barrier instead of two per doubling step: the scan went
-  // from about 2.9 to 0.6 us of the kernel, 256 experts).
-  const int per_thread = (a.E + kRouteBlock - 1) / kRouteBlock;
-  const int x0 = tid * per_thread, x1 = min(a.E, x0 + per_thread);
-  int32_t sum = 0;
-  for (int x = x0; x < x1; ++x) sum += eoff[x];
-  const int lane = tid & 63, wave = tid >> 6;
-  int32_t incl = sum;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int32_t y = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += y;
-  }
-  if (lane == 63) part[wave] = incl;
-  __syncthreads();
-  int32_t total = 0;
-#pragma unroll
-  for (int q = 0; q < kRouteBlock / 64; ++q) {
-    if (q < wave) incl += part[q];
-    total += part[q];
-  }
-  int32_t base = incl - sum;  // exclusive prefix of this thread's run
-  for (int x = x0; x < x1; ++x) {
-    const int32_t c = eoff[x];
-    eoff[x] = base;
-    if (blk == 0) {
-      a.counts[x] = c;
-      a.expert_off[x] = base;
-    }
-    base += c;
-  }
-  __syncthreads();
+  // Exclusive scan of the totals over experts (the shuffle scan went from
+  // about 2.9 to 0.6 us of the kernel against a doubling scan, 256 experts).
+  if (blk == 0)
+    for (int x = tid; x < a.E; x += kRouteBlock) a.counts[x] = eoff[x];
+  const int32_t total = lds_exclusive_scan(eoff, a.E, part);
+  if (blk == 0)
+    for (int x = tid; x < a.E; x += kRouteBlock) a.expert_off[x] = eoff[x];
   for (int x = tid; x < a.E; x += kRouteBlock) a.bbase[static_cast<int64_t>(blk) * a.E + x] = hist[x];
   if (blk == 0) {
     if (tid <= a.R) {
@@ -699,6 +730,19 @@ RouteFn route_fused_for(int k) {
 #define RRB_CASE(n) \
   case n:           \
     return moe_route_fused_kernel<n>;
+    RRB_CASE(1) RRB_CASE(2) RRB_CASE(3) RRB_CASE(4) RRB_CASE(5) RRB_CASE(6) RRB_CASE(7)
+    RRB_CASE(8) RRB_CASE(9) RRB_CASE(10) RRB_CASE(11) RRB_CASE(12) RRB_CASE(13)
+    RRB_CASE(14) RRB_CASE(15) RRB_CASE(16)
+#undef RRB_CASE
+  }
+  return nullptr;
+}
+
+RouteFn route_count_for(int k) {
+  switch (k) {
+#define RRB_CASE(n) \
+  case n:           \
+    return moe_route_count_kernel<n>;
     RRB_CASE(1) RRB_CASE(2) RRB_CASE(3) RRB_CASE(4) RRB_CASE(5) RRB_CASE(6) RRB_CASE(7)
     RRB_CASE(8) RRB_CASE(9) RRB_CASE(10) RRB_CASE(11) RRB_CASE(12) RRB_CASE(13)
     RRB_CASE(14) RRB_CASE(15) RRB_CASE(16)
@@ -800,18 +844,17 @@ rrb_status launch_route(Plan &p, const int32_t *d_idx, const float *d_w, int32_t
   rrb_status st = route_launch_check("route status clear");
   if (st != RRB_OK) return st;
   if (m.tokens > 0) {
-    hipLaunchKernelGGL(moe_route_count_kernel, dim3(static_cast<unsigned>(m.nblk)), dim3(kRouteBlock),
+    hipLaunchKernelGGL(route_count_for(m.topk), dim3(static_cast<unsigned>(m.nblk)), dim3(kRouteBlock),
                        0, s, a);
     if ((st = route_launch_check("route count")) != RRB_OK) return st;
   }
-  hipLaunchKernelGGL(moe_route_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a);
+  hipLaunchKernelGGL(moe_route_scan_kernel, dim3(static_cast<unsigned>(m.experts)), dim3(kRouteBlock), 0, s, a);
   if ((st = route_launch_check("route scan")) != RRB_OK) return st;
-  if (m.tokens > 0) {
-    hipLaunchKernelGGL(route_slot_for(m.topk), dim3(static_cast<unsigned>(m.nblk)), dim3(kRouteBlock),
-                       0, s, a);
-    if ((st = route_launch_check("route slot")) != RRB_OK) return st;
-  }
-  return RRB_OK;
+  // With no tokens, one slot block still stores the (zero) expert and rank
+  // offsets.
+  hipLaunchKernelGGL(route_slot_for(m.topk), dim3(static_cast<unsigned>(m.nblk > 0 ? m.nblk : 1)),
+                     dim3(kRouteBlock), 0, s, a);
+  return route_launch_check("route slot");
 }
 
 namespace {

@@ -203,6 +203,60 @@ def test_device_routing_many_blocks():
     _run(T, h, E, k, R, idx, w, shards)
 
 
+def _distinct_topk(rng, T, E, k, p=None):
+    """T rows of k distinct experts, each drawn from p (uniform if None):
+    rows with a repeat are drawn again until none is left."""
+    idx = rng.choice(E, size=(T, k), p=p).astype(np.int32)
+    while True:
+        s = np.sort(idx, axis=1)
+        bad = np.any(s[:, 1:] == s[:, :-1], axis=1)
+        if not bad.any():
+            return idx
+        idx[bad] = rng.choice(E, size=(int(bad.sum()), k), p=p)
+
+
+def test_device_routing_many_blocks_ragged_skewed():
+    """The three-kernel routing path at the full workload's expert count and
+    top-k: 266,664 tokens = 1041 full routing blocks and a ragged one of 168
+    tokens, 256 experts over 8 ranks, top-8, expert choice skewed (weights
+    1/(i+1)); dispatch arena, rank offsets and combine against the oracle."""
+    require_gpu()
+    T, h, E, k, R = 266664, 8, 256, 8, 8
+    _say(f"device routing three-kernel: T={T} h={h} E={E} k={k} R={R} skewed")
+    rng = np.random.default_rng(93)
+    p = 1.0 / (np.arange(E) + 1.0)
+    idx = _distinct_topk(rng, T, E, k, p / p.sum())
+    w = rng.random((T, k)).astype(np.float32)
+    xa = bf16.rne(rng.standard_normal((T, h)).astype(np.float32))
+    shards = [xa[r * (T // R):(r + 1) * (T // R)] for r in range(R)]
+    _run(T, h, E, k, R, idx, w, shards)
+
+
+def test_device_routing_many_blocks_max_experts():
+    """The three-kernel routing path at the largest expert count and top-k
+    the device routing takes (1024 experts, top-16; 262,144 tokens = 1024
+    blocks): dispatch arena and rank offsets against the oracle.  The weight
+    map goes through the same store as in the top-8 combine test."""
+    require_gpu()
+    T, h, E, k, R = 262144, 2, 1024, 16, 8
+    _say(f"device routing three-kernel: T={T} h={h} E={E} k={k} R={R}")
+    rng = np.random.default_rng(94)
+    idx = _distinct_topk(rng, T, E, k)
+    w = rng.random((T, k)).astype(np.float32)
+    xa = bf16.rne(rng.standard_normal((T, h)).astype(np.float32))
+    shards = [xa[r * (T // R):(r + 1) * (T // R)] for r in range(R)]
+    disp = api.MoeDevicePlan(R, T, h, E, k, "dispatch")
+    offs = torch.zeros(R + 1, dtype=torch.int32, device=DEV)
+    disp.route(torch.from_numpy(idx).to(DEV), torch.from_numpy(w).to(DEV), offs)
+    arena = empty_like_np(T * k * h, "bf16", -21555)
+    disp.run([to_dev(s.reshape(-1)) for s in shards], [arena] + [None] * (R - 1))
+    disp.check()
+    _, counts, offsets, rows = OM.layout(idx, E, R)
+    assert np.array_equal(offs.cpu().numpy(), np.concatenate([[0], np.cumsum(rows)]).astype(np.int32))
+    want = np.concatenate(OM.dispatch(shards, idx, E), axis=0)
+    assert_bits_equal(from_dev(arena).reshape(T * k, h), want, "three-kernel dispatch arena, 1024 experts")
+
+
 @pytest.mark.parametrize("seed", range(32))
 def test_device_routing_random_shapes(seed):
     """Seeded random token counts (one to many blocks of 256, so the fused
