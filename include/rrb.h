@@ -327,7 +327,10 @@ rrb_status rrb_empty_kernel(rrb_stream_t stream);
  *                              tag and readers poll the words themselves
  *                              (staged bytes are 2x the payload);
  *                              stats.retries counts poll rounds that found an
- *                              untagged word
+ *                              untagged word.  On MI355X it leads
+ *                              DUAL_BUFFER up to 32 KiB per rank and trails
+ *                              it from 64 KiB, where polling every word
+ *                              costs more than one flag per slice
  *   RRB_SNAC_GRAPH             (alone) orchestration by kernel boundaries on
  *                              one GPU: one Atom All-Reduce kernel per epoch,
  *                              reading d_in[e] in place and chained in a HIP
