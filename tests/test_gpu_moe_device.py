@@ -257,6 +257,32 @@ def test_device_routing_many_blocks_max_experts():
     assert_bits_equal(from_dev(arena).reshape(T * k, h), want, "three-kernel dispatch arena, 1024 experts")
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_device_routing_many_blocks_random(seed):
+    """Seeded random shapes past the fused routing kernel's co-residency
+    limit (80,000-100,000 tokens, 313-391 blocks with a ragged last one):
+    the three-kernel path at random expert counts, top-k, rank counts,
+    hidden sizes and skew; dispatch arena, rank offsets and combine
+    against the oracle."""
+    require_gpu()
+    rng = np.random.default_rng([9005, seed])
+    R = int(rng.choice([2, 4, 8]))
+    T = R * (int(rng.integers(80000, 100001)) // R)
+    E = min(1024, R * int(rng.choice([1, 4, 16, 64])))
+    k = int(rng.choice([k for k in (1, 2, 3, 5, 8) if k <= E]))
+    h = int(rng.choice([1, 3, 8]))
+    p = None
+    if rng.integers(0, 2):
+        p = 1.0 / (np.arange(E) + 1.0)
+        p = p / p.sum()
+    _say(f"device routing three-kernel random {seed}: T={T} h={h} E={E} k={k} R={R} skew={p is not None}")
+    idx = _distinct_topk(rng, T, E, k, p)
+    w = rng.random((T, k)).astype(np.float32)
+    xa = bf16.rne(rng.standard_normal((T, h)).astype(np.float32))
+    shards = [xa[r * (T // R):(r + 1) * (T // R)] for r in range(R)]
+    _run(T, h, E, k, R, idx, w, shards)
+
+
 @pytest.mark.parametrize("seed", range(32))
 def test_device_routing_random_shapes(seed):
     """Seeded random token counts (one to many blocks of 256, so the fused
