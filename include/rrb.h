@@ -476,6 +476,24 @@ rrb_status rrb_snac_allreduce_chain_noalloc(int32_t nranks, int64_t count, int32
 rrb_status rrb_snac_check(rrb_snac_t h, rrb_stream_t stream);
 void rrb_snac_destroy(rrb_snac_t h);
 
+/* Which ordering this library's SNAC chains were built with.  0 (librrb.so):
+ * no fences -- staged data is written through to the point of coherence,
+ * each flag is stored once the wave's memory operations have completed, and
+ * readers load the data with device-coherent loads issued after the flag
+ * values have returned; this rests on how the hardware completes a wave's
+ * memory operations, below the source-level memory model.  1
+ * (librrb_fenced.so, built from the same sources with RRB_SNAC_FENCES=1):
+ * each flag is published with an agent-scope release store, and a wave that
+ * has seen flags takes an agent-scope acquire fence before it reads the
+ * data they announce or overwrites a buffer they release -- the memory
+ * model's own synchronisation for the notify step (Purlin news page: Stage,
+ * Notify, And Consume; SiFAR review page, Fig. 8, the write-after-read
+ * guard).  The results are bit-identical; the fenced chains are slower.
+ * That build
+ * refuses RRB_SNAC_LAMPORT (RRB_EUNSUPPORTED): the flag-in-data chain's
+ * ordering is per word and has no fenced form.  No device, no errors. */
+int32_t rrb_snac_fenced(void);
+
 #ifdef __cplusplus
 }
 #endif

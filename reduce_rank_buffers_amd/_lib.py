@@ -5,6 +5,10 @@ import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librrb.so")
+# The same library with the SNAC chains built with memory-model release /
+# acquire ordering of their flags (RRB_SNAC_FENCES=1); lib() loads it when the
+# environment sets RRB_FENCED=1.
+LIB_FENCED_PATH = os.path.join(_HERE, "librrb_fenced.so")
 
 RRB_OK = 0
 RRB_EINVAL = -1
@@ -48,7 +52,7 @@ EXPORTS = (
     "rrb_copy", "rrb_reduce", "rrb_plan_launch_info", "rrb_empty_kernel",
     "rrb_snac_create", "rrb_snac_workspace", "rrb_snac_bind", "rrb_snac_allreduce_chain",
     "rrb_snac_create_plan", "rrb_snac_strides", "rrb_snac_chain",
-    "rrb_snac_allreduce_chain_noalloc", "rrb_snac_check", "rrb_snac_destroy",
+    "rrb_snac_allreduce_chain_noalloc", "rrb_snac_check", "rrb_snac_destroy", "rrb_snac_fenced",
 )
 
 
@@ -113,24 +117,50 @@ _SIGS = {
     "rrb_snac_allreduce_chain_noalloc": (_I32, [_I32, _I64, _I32, _U32, _I32, _I32, _P, _P, _P, _U32, _P]),
     "rrb_snac_check": (_I32, [_P, _P]),
     "rrb_snac_destroy": (None, [_P]),
+    "rrb_snac_fenced": (_I32, []),
 }
+_loaded = {}
 
 
-def lib():
-    """The loaded librrb; raises loudly if it was never built."""
-    global _lib
-    if _lib is None:
-        if not os.path.exists(LIB_PATH):
+def _open(path):
+    if path not in _loaded:
+        if not os.path.exists(path):
             raise RuntimeError(
-                f"librrb.so is not built at {LIB_PATH}; run "
+                f"{os.path.basename(path)} is not built at {path}; run "
                 "`python -m reduce_rank_buffers_amd.build` (there is no fallback path)")
-        l = ctypes.CDLL(LIB_PATH)
+        l = ctypes.CDLL(path)
         for name, (res, args) in _SIGS.items():
             fn = getattr(l, name)
             fn.restype = res
             fn.argtypes = args
-        _lib = l
+        _loaded[path] = l
+    return _loaded[path]
+
+
+def lib():
+    """The loaded librrb (librrb_fenced.so if RRB_FENCED=1); raises loudly if
+    it was never built."""
+    global _lib
+    if _lib is None:
+        _lib = _open(LIB_FENCED_PATH if os.environ.get("RRB_FENCED") == "1" else LIB_PATH)
     return _lib
+
+
+def select(fenced):
+    """Make lib() return the fenced-ordering build (True) or the default one
+    (False) from now on, for objects created afterwards; returns the library
+    it replaced (None if none was loaded).  Objects keep the library they
+    were created with."""
+    global _lib
+    prev = _lib
+    _lib = _open(LIB_FENCED_PATH if fenced else LIB_PATH)
+    return prev
+
+
+def restore(prev):
+    """Undo select(): lib() returns `prev` again (or loads afresh if None)."""
+    global _lib
+    _lib = prev
 
 
 def check(status, where):

@@ -2,10 +2,12 @@
 
 ``python -m reduce_rank_buffers_amd.build`` or ``build()`` compiles every
 source under ``csrc/`` with hipcc for gfx950 into
-``reduce_rank_buffers_amd/librrb.so``.  Always recompiles.  The sources are
-compiled to objects in parallel (one hipcc process each) and then linked;
-device code does not call across files, so no relocatable device code is
-needed.
+``reduce_rank_buffers_amd/librrb.so``, and the same library with the chain
+kernels built with RRB_SNAC_FENCES=1 (memory-model release/acquire ordering
+of the SNAC flags) into ``librrb_fenced.so``.  Always recompiles.  The
+sources are compiled to objects in parallel (one hipcc process each) and then
+linked; device code does not call across files, so no relocatable device
+code is needed.
 """
 
 import os
@@ -18,6 +20,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "librrb.so")
+LIB_FENCED = os.path.join(PKG, "librrb_fenced.so")
+FENCED_SOURCE = "rrb_snac.hip"
 SOURCES = ["rrb_capi.cpp", "rrb_plan.cpp", "rrb_atom.hip", "rrb_moe.hip", "rrb_snac.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -46,16 +50,22 @@ def _run(cmd, verbose, what):
 
 def build(verbose=False):
     srcs = SOURCES
+    inc = ["-I", os.path.join(ROOT, "include")]
     with tempfile.TemporaryDirectory(prefix="rrb_build_") as tmp:
         objs = [os.path.join(tmp, s + ".o") for s in srcs]
-        cmds = [[HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-c",
-                 os.path.join(CSRC, s), "-o", o] for s, o in zip(srcs, objs)]
-        workers = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", "0")) or os.cpu_count() or 1))
+        fenced_obj = os.path.join(tmp, FENCED_SOURCE + ".fenced.o")
+        jobs = [([HIPCC, *FLAGS, *inc, "-c", os.path.join(CSRC, s), "-o", o], s) for s, o in zip(srcs, objs)]
+        jobs.append(([HIPCC, *FLAGS, "-DRRB_SNAC_FENCES=1", *inc, "-c", os.path.join(CSRC, FENCED_SOURCE),
+                      "-o", fenced_obj], FENCED_SOURCE + " (fenced)"))
+        workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", "0")) or os.cpu_count() or 1))
         with ThreadPoolExecutor(max_workers=workers) as pool:
-            list(pool.map(lambda cs: _run(cs[0], verbose, cs[1]), zip(cmds, srcs)))
-        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"], verbose,
-             "link")
+            list(pool.map(lambda job: _run(job[0], verbose, job[1]), jobs))
+        fenced_objs = [fenced_obj if s == FENCED_SOURCE else o for s, o in zip(srcs, objs)]
+        for lib, lib_objs in ((LIB, objs), (LIB_FENCED, fenced_objs)):
+            _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *lib_objs, "-o", lib + ".tmp"], verbose,
+                 "link " + os.path.basename(lib))
     os.replace(LIB + ".tmp", LIB)
+    os.replace(LIB_FENCED + ".tmp", LIB_FENCED)
     return LIB
 
 

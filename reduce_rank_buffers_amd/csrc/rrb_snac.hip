@@ -66,6 +66,16 @@
 // same completion wait covers the write-after-read guards: a rank's flag of
 // epoch e + 1 is stored only after its epoch-e loads have returned.
 //
+// This ordering rests on how the hardware completes a wave's memory
+// operations, below the source-level memory model.  Built with
+// RRB_SNAC_FENCES=1 (librrb_fenced.so), the flag-based chains take the
+// memory model's own form instead: each flag is published with an
+// agent-scope release store, and every wave that has seen flags (a wait, or
+// the speculative flag read) takes an agent-scope acquire fence before it
+// touches the data they announce or overwrites a buffer they release.  The
+// kernels are otherwise the same.  The flag-in-data chain, whose ordering is
+// per word, has no fenced form and is refused by that build.
+//
 // Every wait is bounded: a wait that exceeds its poll budget raises a status
 // word that every other wait also watches, so the whole grid drains and the
 // host sees RRB_ETIMEOUT.  The grid must be co-resident: it takes a plain
@@ -89,6 +99,16 @@ constexpr int kMaxSlices = 256;
 constexpr int64_t kSpecMaxBytes = 128 << 10;  // All-Reduce chains speculate up to this payload per rank
 constexpr int64_t kLamportSettleVec = 4096;    // 64 KiB per rank (see lamport_chain_kernel)
 constexpr int kStageU = 8;  // vectors in flight per lane in the stage copy
+
+#ifndef RRB_SNAC_FENCES
+#define RRB_SNAC_FENCES 0
+#endif
+constexpr bool kFences = RRB_SNAC_FENCES != 0;  // memory-model build (see above)
+
+// Fenced build: agent-scope acquire after flags were seen; nothing otherwise.
+__device__ __forceinline__ void acquire_if_fenced() {
+  if constexpr (kFences) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
 
 // kLamportOne: the flag-in-data kernel shaped for slices of at most one
 // vector per lane.
@@ -227,6 +247,7 @@ __device__ __forceinline__ uint32_t load_flag_relaxed(const uint32_t *p) {
 // that must not see data older than a flag is issued only after the flag's
 // value is back; issuing the two together would rest on service order.
 __device__ __forceinline__ void order_after_values() {
+  acquire_if_fenced();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -282,8 +303,9 @@ __device__ bool wait_all(const uint32_t *base, int64_t stride_words, uint32_t wa
     bool mine = true;
     if (threadIdx.x < R) mine = wait_at_least(base + threadIdx.x * stride_words, want, status, limit);
     const bool all = __all(mine) != 0;
-    // No acquire fence: the data that follows is read with device-coherent
-    // loads, issued after the flags were seen.
+    // No acquire fence (but in the fenced build): the data that follows is
+    // read with device-coherent loads, issued after the flags were seen.
+    acquire_if_fenced();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     return all;
   }
@@ -291,6 +313,7 @@ __device__ bool wait_all(const uint32_t *base, int64_t stride_words, uint32_t wa
     ok[threadIdx.x] = wait_at_least(base + threadIdx.x * stride_words, want, status, limit) ? 1 : 0;
   __syncthreads();
   // No acquire fence (as above).
+  acquire_if_fenced();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   bool all = true;
 #pragma unroll
@@ -321,7 +344,12 @@ __device__ __forceinline__ void notify(uint32_t *flag, uint32_t ep) {
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_store(flag, ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) {
+    if constexpr (kFences)
+      __hip_atomic_store(flag, ep, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      __hip_atomic_store(flag, ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   if (SETTLE) {
     __builtin_amdgcn_s_waitcnt(0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -927,6 +955,7 @@ __device__ bool wait_list(const uint32_t *base, const int32_t *idx, int n, uint3
     ok = wait_at_least(base + static_cast<int64_t>(idx[i] & kFlagIndexMask) * kFlagStride, want, status,
                        limit);
   const bool all = __all(ok) != 0;
+  acquire_if_fenced();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   return all;
 }
@@ -1668,6 +1697,8 @@ rrb_status check_ar_chain_args(int32_t nranks, int64_t count, int32_t dtype, uin
   flags &= ~RRB_SNAC_COOPERATIVE;
   if ((flags & RRB_SNAC_LAMPORT) && flags != (RRB_SNAC_LAMPORT | RRB_SNAC_DUAL_BUFFER))
     return fail(RRB_EINVAL, "RRB_SNAC_LAMPORT goes with RRB_SNAC_DUAL_BUFFER only");
+  if (kFences && (flags & RRB_SNAC_LAMPORT))
+    return fail(RRB_EUNSUPPORTED, "the flag-in-data chain has no fenced build");
   if ((flags & RRB_SNAC_TWOSHOT) && flags != (RRB_SNAC_TWOSHOT | RRB_SNAC_DUAL_BUFFER))
     return fail(RRB_EINVAL, "RRB_SNAC_TWOSHOT goes with RRB_SNAC_DUAL_BUFFER only");
   if ((flags & RRB_SNAC_GRAPH) && flags != RRB_SNAC_GRAPH)
@@ -1775,6 +1806,8 @@ rrb_status launch_ar_chain(rrb_snac_s *h, int32_t epochs, const void *d_in, void
 using namespace rrb;
 
 extern "C" {
+
+int32_t rrb_snac_fenced(void) { return kFences ? 1 : 0; }
 
 rrb_status rrb_snac_create(int32_t nranks, int64_t count, int32_t dtype, uint32_t flags,
                            int32_t slices, rrb_snac_t *out) {

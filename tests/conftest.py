@@ -16,7 +16,7 @@ def pytest_configure(config):
 def librrb():
     """The built library; builds it in-tree only if nothing is built yet."""
     from reduce_rank_buffers_amd import _lib
-    if not os.path.exists(_lib.LIB_PATH):
+    if not (os.path.exists(_lib.LIB_PATH) and os.path.exists(_lib.LIB_FENCED_PATH)):
         from reduce_rank_buffers_amd import build
         build.build()
     return _lib.lib()

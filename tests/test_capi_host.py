@@ -31,6 +31,39 @@ def test_exports_every_declared_symbol(librrb):
     assert librrb.rrb_abi_version() == 2
 
 
+def test_fenced_build_exports_reports_and_refuses_flag_in_data(librrb):
+    """librrb_fenced.so (the chains' memory-model ordering) exports the same
+    symbols, reports its ordering, and refuses only the flag-in-data chain,
+    which has no fenced form; the default library reports no fences."""
+    import ctypes
+    fenced = L._open(L.LIB_FENCED_PATH)
+    plain = L._open(L.LIB_PATH)
+    for n in _declared():
+        assert hasattr(fenced, n), n
+    assert fenced.rrb_abi_version() == plain.rrb_abi_version()
+    assert plain.rrb_snac_fenced() == 0 and fenced.rrb_snac_fenced() == 1
+    lam = L.RRB_SNAC_LAMPORT | L.RRB_SNAC_DUAL_BUFFER
+    h = ctypes.c_void_p()
+    assert fenced.rrb_snac_create(8, 4096, 0, lam, 0, ctypes.byref(h)) == L.RRB_EUNSUPPORTED
+    assert b"fenced" in fenced.rrb_last_error()
+    assert plain.rrb_snac_create(8, 4096, 0, lam, 0, ctypes.byref(h)) == L.RRB_OK
+    plain.rrb_snac_destroy(h)
+    for f in (0, L.RRB_SNAC_DUAL_BUFFER, L.RRB_SNAC_DUAL_BUFFER | L.RRB_SNAC_SPECULATIVE,
+              L.RRB_SNAC_DUAL_BUFFER | L.RRB_SNAC_TWOSHOT, L.RRB_SNAC_GRAPH):
+        h = ctypes.c_void_p()
+        assert fenced.rrb_snac_create(8, 4096, 0, f, 0, ctypes.byref(h)) == L.RRB_OK, f
+        fenced.rrb_snac_destroy(h)
+
+
+def test_library_selection_switches_and_restores(librrb):
+    prev = L.select(True)
+    try:
+        assert L.lib().rrb_snac_fenced() == 1
+    finally:
+        L.restore(prev)
+    assert L.lib() is librrb
+
+
 def _apply(segments, ins, in_count, out_count, R, dtype):
     """Interpret a plan's index map on numpy buffers (sentinel-filled outputs)."""
     dt = np.uint16 if dtype == "bf16" else np.float32
