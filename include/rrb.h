@@ -351,7 +351,9 @@ rrb_status rrb_empty_kernel(rrb_stream_t stream);
  *         1 KiB of payload per workgroup, up to 128, and 256 from 512 KiB
  *         (128 with RRB_SNAC_SPEC_ALWAYS);
  *         RRB_SNAC_LAMPORT: 1 KiB per workgroup below 64 KiB, then 512 B per
- *         workgroup up to 256, and 128 above 256 KiB; at most 2048 / nranks).
+ *         workgroup up to 256, and 128 above 256 KiB; the memory-model build
+ *         (rrb_snac_fenced() == 1): 1 KiB per workgroup, up to 16 below
+ *         128 KiB and 32 from there; at most 2048 / nranks).
  *         The grid (nranks x slices) must be co-resident; a cooperative
  *         launch that cannot be fails with RRB_EHIP.
  */
@@ -422,7 +424,8 @@ rrb_status rrb_snac_allreduce_chain(rrb_snac_t h, int32_t epochs,
  * computes piece s of every map entry whose output is rank r; it waits on a
  * list of flags built at create time: the staged slices its pieces read and
  * the workgroups that read its own slice.  slices = 0 gives each workgroup
- * 1 KiB of the larger of a rank's input and output, up to 128 per rank.
+ * 1 KiB of the larger of a rank's input and output, up to 128 per rank (the
+ * memory-model build: up to 16 below 128 KiB and 32 from there).
  * Workspace, bind, check and destroy as for rrb_snac_create.
  */
 rrb_status rrb_snac_create_plan(rrb_plan_t plan, uint32_t flags, int32_t slices,

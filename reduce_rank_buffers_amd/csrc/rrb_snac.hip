@@ -1392,6 +1392,19 @@ int32_t default_slices(int32_t slices, int64_t nvec, int32_t nranks, uint32_t fl
       // tensors, 16 per rank, were best or within 0.03 us.)
       S = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(128, nvec / 64)));
     }
+    if (kFences && !(flags & RRB_SNAC_LAMPORT)) {
+      // The memory-model build writes back and invalidates an XCD's L2 per
+      // workgroup and epoch, so fewer, larger workgroups: 64 vectors each,
+      // up to 16 per rank below 128 KiB and 32 from there.  Measured on
+      // MI355X, 8 ranks, dual, us per All-Reduce by slices per rank:
+      //   8 KiB    4: 2.81  8: 2.50  16: 3.05
+      //   32 KiB   8: 4.01  16: 3.83  32: 4.77
+      //   128 KiB  16: 6.85  32: 6.79  64: 11.9  (128: 21.8)
+      //   512 KiB  16: 21.5  32: 15.4  64: 17.9  (256: 65.9)
+      // (barrier, speculative and twoshot follow dual within 10-30%).
+      S = static_cast<int32_t>(
+          std::max<int64_t>(1, std::min<int64_t>(nvec >= 8192 ? 32 : 16, nvec / 64)));
+    }
     S = std::min<int32_t>(S, 2048 / nranks);
   }
   if (S > nvec) S = static_cast<int32_t>(nvec);

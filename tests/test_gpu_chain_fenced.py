@@ -16,7 +16,7 @@ from oracle import chain as OC
 from reduce_rank_buffers_amd import api, inputs
 from reduce_rank_buffers_amd import _lib as L
 from tests.gpu_util import DEV, require_gpu, to_dev
-from tests.test_gpu_chain import R, _check_chain, _slices_of
+from tests.test_gpu_chain import R, _check_chain
 from tests.test_gpu_plan_chain import _run_chain
 
 pytestmark = pytest.mark.gpu
@@ -26,6 +26,13 @@ FENCED_VARIANTS = ["barrier", "dual", "speculative", "speculative_always", "twos
 
 def _say(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def _fenced_slices(ch):
+    # the fenced build's default slices per rank: 64 vectors per workgroup,
+    # up to 16 below 128 KiB per rank and 32 from there
+    nvec = ch.count * 2 // 16
+    return min(max(1, min(32 if nvec >= 8192 else 16, nvec // 64)), 2048 // R, nvec)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -53,7 +60,7 @@ def test_fenced_chain_variants_bit_exact(b):
         _check_chain(out, want, f"fenced {v} b={b}")
         st = stats.cpu().tolist()
         assert st[2] == 0
-        assert st[3] == E * R * _slices_of(ch)
+        assert st[3] == E * R * _fenced_slices(ch)
         ch.close()
 
 
