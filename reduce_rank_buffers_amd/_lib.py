@@ -163,9 +163,11 @@ def restore(prev):
     _lib = prev
 
 
-def check(status, where):
+def check(status, where, l=None):
+    """Raise RrbError for a failed call; `l` is the library the call went to
+    (default: lib()), whose thread-local last error holds the message."""
     if status != RRB_OK:
-        l = lib()
+        l = lib() if l is None else l
         msg = l.rrb_last_error().decode() or l.rrb_status_string(status).decode()
         raise RrbError(status, where, msg)
     return status

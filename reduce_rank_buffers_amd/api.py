@@ -133,6 +133,9 @@ def _op_code(op):
 class Plan:
     """A layout-naming spec compiled to an index map (rrb_plan_create)."""
 
+    def _check(self, status, where):
+        return L.check(status, where, self._lib)
+
     def __init__(self, nranks, count, dtype, in_layout, out_layout, op):
         spec = L.Spec()
         spec.nranks = int(nranks)
@@ -144,7 +147,7 @@ class Plan:
         spec.reserved = 0
         self._lib = L.lib()
         h = ctypes.c_void_p()
-        L.check(self._lib.rrb_plan_create(ctypes.byref(spec), ctypes.byref(h)), "rrb_plan_create")
+        self._check(self._lib.rrb_plan_create(ctypes.byref(spec), ctypes.byref(h)), "rrb_plan_create")
         self.handle = h
         self.nranks = int(nranks)
         self.op = spec.op
@@ -157,16 +160,16 @@ class Plan:
         ws = ctypes.c_size_t()
         inc = (ctypes.c_int64 * R)()
         outc = (ctypes.c_int64 * R)()
-        L.check(self._lib.rrb_plan_query(self.handle, ctypes.byref(ws), inc, outc), "rrb_plan_query")
+        self._check(self._lib.rrb_plan_query(self.handle, ctypes.byref(ws), inc, outc), "rrb_plan_query")
         self.workspace_bytes = ws.value
         self.in_count = list(inc)
         self.out_count = list(outc)
 
     def segments(self):
         n = ctypes.c_int32()
-        L.check(self._lib.rrb_plan_segments(self.handle, None, 0, ctypes.byref(n)), "rrb_plan_segments")
+        self._check(self._lib.rrb_plan_segments(self.handle, None, 0, ctypes.byref(n)), "rrb_plan_segments")
         arr = (L.Segment * max(1, n.value))()
-        L.check(self._lib.rrb_plan_segments(self.handle, arr, n.value, ctypes.byref(n)),
+        self._check(self._lib.rrb_plan_segments(self.handle, arr, n.value, ctypes.byref(n)),
                 "rrb_plan_segments")
         return [(s.src_rank, s.src_off, s.dst_off, s.len, s.dst_mask) for s in arr[:n.value]]
 
@@ -177,7 +180,7 @@ class Plan:
             self._ws = torch.empty(self.workspace_bytes + 256, dtype=torch.uint8, device=dev)
             base = self._ws.data_ptr()
             aligned = (base + 255) // 256 * 256
-            L.check(self._lib.rrb_plan_bind(self.handle, ctypes.c_void_p(aligned),
+            self._check(self._lib.rrb_plan_bind(self.handle, ctypes.c_void_p(aligned),
                                             self.workspace_bytes, _stream(stream)), "rrb_plan_bind")
         return self
 
@@ -194,7 +197,7 @@ class Plan:
             raise ValueError("weights apply to MoE combine plans only")
         self.check_buffers(ins, outs)
         if self.op == L.RRB_COPY:
-            L.check(self._lib.rrb_copy(self.handle, _ptrs(ins, self.nranks), _ptrs(outs, self.nranks),
+            self._check(self._lib.rrb_copy(self.handle, _ptrs(ins, self.nranks), _ptrs(outs, self.nranks),
                                        _stream(stream)), "rrb_copy")
             return
         wp = None
@@ -204,7 +207,7 @@ class Plan:
                 raise ValueError("weights apply to MoE combine plans only")
             _all_on_gpu(_check_aux(weights, "weights", _F32_TYPES, rows))
             wp = weights.data_ptr()
-        L.check(self._lib.rrb_reduce(self.handle, _ptrs(ins, self.nranks), _ptrs(outs, self.nranks),
+        self._check(self._lib.rrb_reduce(self.handle, _ptrs(ins, self.nranks), _ptrs(outs, self.nranks),
                                      wp, _stream(stream)), "rrb_reduce")
 
     def close(self):
@@ -275,7 +278,7 @@ class Bound:
         st = self._fn(self._h, self._in, self._out,
                       torch.cuda.current_stream().cuda_stream if stream is None else stream.cuda_stream)
         if st:
-            L.check(st, self._name)
+            L.check(st, self._name, self._keep[0]._lib)
 
     def kernels(self):
         """The kernel launches this call issues, as the library names them."""
@@ -343,7 +346,7 @@ def launch_info(p, ins, outs):
     """The launches rrb_copy / rrb_reduce would issue for plan `p` on these
     buffers, as the library names them (nothing is launched)."""
     buf = ctypes.create_string_buffer(1024)
-    L.check(p._lib.rrb_plan_launch_info(p.handle, _ptrs(ins, p.nranks), _ptrs(outs, p.nranks), buf,
+    p._check(p._lib.rrb_plan_launch_info(p.handle, _ptrs(ins, p.nranks), _ptrs(outs, p.nranks), buf,
                                         len(buf)), "rrb_plan_launch_info")
     return buf.value.decode()
 
@@ -365,7 +368,7 @@ class MoePlan(Plan):
         self._lib = L.lib()
         h = ctypes.c_void_p()
         d = L.RRB_MOE_DISPATCH if direction == "dispatch" else L.RRB_MOE_COMBINE
-        L.check(self._lib.rrb_plan_create_rows(int(nranks), int(T), int(hidden), int(experts), int(k),
+        self._check(self._lib.rrb_plan_create_rows(int(nranks), int(T), int(hidden), int(experts), int(k),
                                                idx.ctypes.data, w.ctypes.data, d, ctypes.byref(h)),
                 "rrb_plan_create_rows")
         self.handle = h
@@ -394,7 +397,7 @@ class MoeDevicePlan(Plan):
         self._lib = L.lib()
         h = ctypes.c_void_p()
         d = L.RRB_MOE_DISPATCH if direction == "dispatch" else L.RRB_MOE_COMBINE
-        L.check(self._lib.rrb_plan_create_rows_device(int(nranks), int(tokens), int(hidden),
+        self._check(self._lib.rrb_plan_create_rows_device(int(nranks), int(tokens), int(hidden),
                                                       int(experts), int(topk), d, ctypes.byref(h)),
                 "rrb_plan_create_rows_device")
         self.handle = h
@@ -408,7 +411,7 @@ class MoeDevicePlan(Plan):
         if share is not None:
             self._ws = share._ws
             base = (self._ws.data_ptr() + 255) // 256 * 256
-            L.check(self._lib.rrb_plan_bind(self.handle, ctypes.c_void_p(base), self.workspace_bytes,
+            self._check(self._lib.rrb_plan_bind(self.handle, ctypes.c_void_p(base), self.workspace_bytes,
                                             _stream()), "rrb_plan_bind")
         else:
             self.bind(device)
@@ -421,13 +424,13 @@ class MoeDevicePlan(Plan):
         _all_on_gpu(_check_aux(topk_idx, "topk_idx", (torch.int32,), n) +
                     _check_aux(topk_w, "topk_w", _F32_TYPES, n) +
                     _check_aux(rank_offsets, "rank_offsets", (torch.int32,), self.nranks + 1))
-        L.check(self._lib.rrb_moe_route(
+        self._check(self._lib.rrb_moe_route(
             self.handle, ctypes.c_void_p(topk_idx.data_ptr()), ctypes.c_void_p(topk_w.data_ptr()),
             ctypes.c_void_p(rank_offsets.data_ptr() if rank_offsets is not None else 0),
             _stream(stream)), "rrb_moe_route")
 
     def check(self, stream=None):
-        L.check(self._lib.rrb_moe_route_check(self.handle, _stream(stream)), "rrb_moe_route_check")
+        self._check(self._lib.rrb_moe_route_check(self.handle, _stream(stream)), "rrb_moe_route_check")
 
 
 # ---- SNAC chain -------------------------------------------------------------
@@ -443,12 +446,15 @@ VARIANTS = {"barrier": 0, "dual": L.RRB_SNAC_DUAL_BUFFER,
 class SnacChain:
     """A bound SNAC handle: back-to-back All-Reduces in one persistent kernel."""
 
+    def _check(self, status, where):
+        return L.check(status, where, self._lib)
+
     def __init__(self, nranks, count, dtype="bf16", variant="dual", slices=0, device=None,
                  stream=None, cooperative=False):
         self._lib = L.lib()
         h = ctypes.c_void_p()
         flags = VARIANTS[variant] | (L.RRB_SNAC_COOPERATIVE if cooperative else 0)
-        L.check(self._lib.rrb_snac_create(int(nranks), int(count), _dtype_code(dtype),
+        self._check(self._lib.rrb_snac_create(int(nranks), int(count), _dtype_code(dtype),
                                           flags, int(slices), ctypes.byref(h)),
                 "rrb_snac_create")
         self.handle = h
@@ -458,11 +464,11 @@ class SnacChain:
         self.dtype = _dtype_code(dtype)
         self.strides = (self.count, self.count)  # elements per rank in d_in / d_out
         ws = ctypes.c_size_t()
-        L.check(self._lib.rrb_snac_workspace(h, ctypes.byref(ws)), "rrb_snac_workspace")
+        self._check(self._lib.rrb_snac_workspace(h, ctypes.byref(ws)), "rrb_snac_workspace")
         dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
         self._ws = torch.empty(ws.value + 256, dtype=torch.uint8, device=dev)
         base = (self._ws.data_ptr() + 255) // 256 * 256
-        L.check(self._lib.rrb_snac_bind(h, ctypes.c_void_p(base), ws.value, _stream(stream)),
+        self._check(self._lib.rrb_snac_bind(h, ctypes.c_void_p(base), ws.value, _stream(stream)),
                 "rrb_snac_bind")
 
     def check_buffers(self, inp, out, stats=None, stagger=None):
@@ -485,7 +491,7 @@ class SnacChain:
         """inp, out: [epochs, R, count] device tensors; stats: int64[4] device tensor."""
         self.check_buffers(inp, out, stats, stagger)
         E = inp.shape[0]
-        L.check(self._lib.rrb_snac_allreduce_chain(
+        self._check(self._lib.rrb_snac_allreduce_chain(
             self.handle, int(E), ctypes.c_void_p(inp.data_ptr()), ctypes.c_void_p(out.data_ptr()),
             ctypes.c_void_p(stats.data_ptr() if stats is not None else 0),
             ctypes.c_void_p(stagger.data_ptr() if stagger is not None else 0),
@@ -506,12 +512,12 @@ class SnacChain:
         def call():
             st = fn(*args, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
             if st:
-                L.check(st, "rrb_snac_chain")
+                L.check(st, "rrb_snac_chain", self._lib)
         call.keep = keep
         return call
 
     def check(self, stream=None):
-        L.check(self._lib.rrb_snac_check(self.handle, _stream(stream)), "rrb_snac_check")
+        self._check(self._lib.rrb_snac_check(self.handle, _stream(stream)), "rrb_snac_check")
 
     def close(self):
         """Destroy the library handle now (a graph-mode handle releases its
@@ -574,7 +580,7 @@ class SnacPlanChain(SnacChain):
         self._lib = L.lib()
         h = ctypes.c_void_p()
         flags = PLAN_CHAIN_VARIANTS[variant] | (L.RRB_SNAC_COOPERATIVE if cooperative else 0)
-        L.check(self._lib.rrb_snac_create_plan(plan.handle, flags, int(slices), ctypes.byref(h)),
+        self._check(self._lib.rrb_snac_create_plan(plan.handle, flags, int(slices), ctypes.byref(h)),
                 "rrb_snac_create_plan")
         self.handle = h
         self.nranks = plan.nranks
@@ -582,21 +588,21 @@ class SnacPlanChain(SnacChain):
         self.dtype = plan.dtype
         self.esize = 4 if plan.dtype == L.RRB_F32 else 2
         si, so = ctypes.c_int64(), ctypes.c_int64()
-        L.check(self._lib.rrb_snac_strides(h, ctypes.byref(si), ctypes.byref(so)), "rrb_snac_strides")
+        self._check(self._lib.rrb_snac_strides(h, ctypes.byref(si), ctypes.byref(so)), "rrb_snac_strides")
         self.strides = (si.value // self.esize, so.value // self.esize)
         ws = ctypes.c_size_t()
-        L.check(self._lib.rrb_snac_workspace(h, ctypes.byref(ws)), "rrb_snac_workspace")
+        self._check(self._lib.rrb_snac_workspace(h, ctypes.byref(ws)), "rrb_snac_workspace")
         dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
         self._ws = torch.empty(ws.value + 256, dtype=torch.uint8, device=dev)
         base = (self._ws.data_ptr() + 255) // 256 * 256
-        L.check(self._lib.rrb_snac_bind(h, ctypes.c_void_p(base), ws.value, _stream(stream)),
+        self._check(self._lib.rrb_snac_bind(h, ctypes.c_void_p(base), ws.value, _stream(stream)),
                 "rrb_snac_bind")
 
     def run(self, inp, out, stats=None, stagger=None, spin_limit=0, stream=None):
         """inp: [epochs, R, in_stride], out: [epochs, R, out_stride] device tensors."""
         self.check_buffers(inp, out, stats, stagger)
         E = inp.shape[0]
-        L.check(self._lib.rrb_snac_chain(
+        self._check(self._lib.rrb_snac_chain(
             self.handle, int(E), ctypes.c_void_p(inp.data_ptr()), ctypes.c_void_p(out.data_ptr()),
             ctypes.c_void_p(stats.data_ptr() if stats is not None else 0),
             ctypes.c_void_p(stagger.data_ptr() if stagger is not None else 0),

@@ -44,8 +44,13 @@ def test_fenced_build_exports_reports_and_refuses_flag_in_data(librrb):
     assert plain.rrb_snac_fenced() == 0 and fenced.rrb_snac_fenced() == 1
     lam = L.RRB_SNAC_LAMPORT | L.RRB_SNAC_DUAL_BUFFER
     h = ctypes.c_void_p()
-    assert fenced.rrb_snac_create(8, 4096, 0, lam, 0, ctypes.byref(h)) == L.RRB_EUNSUPPORTED
+    st = fenced.rrb_snac_create(8, 4096, 0, lam, 0, ctypes.byref(h))
+    assert st == L.RRB_EUNSUPPORTED
     assert b"fenced" in fenced.rrb_last_error()
+    # the message comes from the library the call went to, not lib()
+    assert plain.rrb_snac_create(8, 4096, 0, 1 << 20, 0, ctypes.byref(h)) == L.RRB_EINVAL
+    with pytest.raises(L.RrbError, match="fenced"):
+        L.check(st, "rrb_snac_create", fenced)
     assert plain.rrb_snac_create(8, 4096, 0, lam, 0, ctypes.byref(h)) == L.RRB_OK
     plain.rrb_snac_destroy(h)
     for f in (0, L.RRB_SNAC_DUAL_BUFFER, L.RRB_SNAC_DUAL_BUFFER | L.RRB_SNAC_SPECULATIVE,
