@@ -107,7 +107,7 @@ __global__ void __launch_bounds__(256) moe_dispatch_kernel(RowArgs a) {
   }
 }
 
-// Any other k: the same copy with the slots read per store.
+// Top-k above 16: the same copy with the slots read per store.
 __global__ void __launch_bounds__(256) moe_dispatch_any_kernel(RowArgs a) {
   if (route_failed(a)) return;
   const int64_t t = blockIdx.x / a.parts;
@@ -861,29 +861,32 @@ namespace {
 
 using RowFn = void (*)(RowArgs);
 
-// Dispatch kernel for top-k (nullptr: the any-k kernel).
+// Dispatch kernel for top-k up to 16 (nullptr above: the any-k kernel).
 RowFn dispatch_for(int k) {
   switch (k) {
-    case 1: return moe_dispatch_kernel<1>;
-    case 2: return moe_dispatch_kernel<2>;
-    case 4: return moe_dispatch_kernel<4>;
-    case 6: return moe_dispatch_kernel<6>;
-    case 8: return moe_dispatch_kernel<8>;
-    case 16: return moe_dispatch_kernel<16>;
+#define RRB_CASE(n) \
+  case n:           \
+    return moe_dispatch_kernel<n>;
+    RRB_CASE(1) RRB_CASE(2) RRB_CASE(3) RRB_CASE(4) RRB_CASE(5) RRB_CASE(6) RRB_CASE(7)
+    RRB_CASE(8) RRB_CASE(9) RRB_CASE(10) RRB_CASE(11) RRB_CASE(12) RRB_CASE(13)
+    RRB_CASE(14) RRB_CASE(15) RRB_CASE(16)
+#undef RRB_CASE
     default: return nullptr;
   }
 }
 
-// Combine kernel for top-k and its vectors per lane (k * CU >= 8 loads in
-// flight per lane).
+// Combine kernel for top-k up to 16 and its vectors per lane: CU = ceil(8 /
+// k), so k * CU >= 8 loads are in flight per lane.
 RowFn combine_for(int k, int *cu) {
   switch (k) {
-    case 1: *cu = 8; return moe_combine_kernel<1, 8>;
-    case 2: *cu = 4; return moe_combine_kernel<2, 4>;
-    case 4: *cu = 2; return moe_combine_kernel<4, 2>;
-    case 6: *cu = 2; return moe_combine_kernel<6, 2>;
-    case 8: *cu = 1; return moe_combine_kernel<8, 1>;
-    case 16: *cu = 1; return moe_combine_kernel<16, 1>;
+#define RRB_CASE(n)                       \
+  case n:                                 \
+    *cu = (8 + (n) - 1) / (n);            \
+    return moe_combine_kernel<n, (8 + (n) - 1) / (n)>;
+    RRB_CASE(1) RRB_CASE(2) RRB_CASE(3) RRB_CASE(4) RRB_CASE(5) RRB_CASE(6) RRB_CASE(7)
+    RRB_CASE(8) RRB_CASE(9) RRB_CASE(10) RRB_CASE(11) RRB_CASE(12) RRB_CASE(13)
+    RRB_CASE(14) RRB_CASE(15) RRB_CASE(16)
+#undef RRB_CASE
     default: *cu = 0; return nullptr;
   }
 }
