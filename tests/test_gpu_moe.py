@@ -148,6 +148,23 @@ def test_combine_special_values(h):
         assert_bits_equal(from_dev(y[r]).reshape(-1, h), want[r], f"combine specials rank {r} h={h}")
 
 
+@pytest.mark.parametrize("k", range(1, 17))
+def test_moe_every_topk_vector_kernels(k):
+    """Every top-k up to 16 has its own dispatch and combine kernels: full
+    7168-wide rows (several row parts) and a 2392-wide row (299 vectors,
+    a short last part), 64 tokens, 32 experts over 8 ranks."""
+    require_gpu()
+    T, E, R = 64, 32, 8
+    for h in (7168, 2392):
+        rng = np.random.default_rng([9006, k, h])
+        idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+        w = rng.random((T, k)).astype(np.float32)
+        xa = bf16.rne(rng.standard_normal((T, h)).astype(np.float32))
+        shards = [xa[r * (T // R):(r + 1) * (T // R)] for r in range(R)]
+        _say(f"moe top-{k} h={h}")
+        _roundtrip(T, h, E, k, R, idx, w, shards, "seeded")
+
+
 @pytest.mark.parametrize("seed", range(48))
 def test_moe_random_shapes(seed):
     """Seeded random token counts, hidden sizes (vector and element paths, row
