@@ -309,7 +309,9 @@ rrb_status rrb_empty_kernel(rrb_stream_t stream);
  *                              any order in which the memory system serves
  *                              the loads.
  *                              All-Reduce chains speculate up to 128 KiB per
- *                              rank and wait for the flags first above that,
+ *                              rank (8 KiB in the memory-model build, see
+ *                              rrb_snac_fenced) and wait for the flags first
+ *                              above that,
  *                              as DUAL_BUFFER does: there the chain is
  *                              bandwidth-bound and the early loads measured
  *                              slower.  Plan chains speculate at every size.

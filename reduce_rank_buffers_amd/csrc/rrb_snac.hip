@@ -1764,9 +1764,14 @@ rrb_status launch_ar_chain(rrb_snac_s *h, int32_t epochs, const void *d_in, void
   // us per All-Reduce: 256 KiB 3.64 against 3.20, 512 KiB 5.50 against 5.31;
   // ahead at 8-128 KiB, 1.79 against 1.96 at 8 KiB).  There the speculative
   // variant runs the dual-buffer kernel: the same buffers and flags, a wait
-  // before the loads.
+  // before the loads.  The memory-model build pays an acquire fence for the
+  // speculative read and another for a retry, and speculation leads there
+  // only at 8 KiB (64-deep chains, dual against speculative, us per
+  // All-Reduce: 8 KiB 2.36 / 2.28, 16 KiB 3.10 / 3.22, 32 KiB 3.68 / 4.13,
+  // 128 KiB 6.70 / 7.52).
+  const int64_t spec_max = kFences ? int64_t(8) << 10 : kSpecMaxBytes;
   const bool spec = (h->flags & RRB_SNAC_SPECULATIVE) &&
-                    ((h->flags & RRB_SNAC_SPEC_ALWAYS) || a.rank_bytes <= kSpecMaxBytes);
+                    ((h->flags & RRB_SNAC_SPEC_ALWAYS) || a.rank_bytes <= spec_max);
 
   const bool bf16 = h->dtype == RRB_BF16;
   // Flag-in-data slices of at most one vector per lane: payloads up to

@@ -22,6 +22,7 @@ from tests.test_gpu_plan_chain import _run_chain
 pytestmark = pytest.mark.gpu
 
 FENCED_VARIANTS = ["barrier", "dual", "speculative", "speculative_always", "twoshot"]
+FENCED_SPEC_MAX_BYTES = 8 << 10  # that build's All-Reduce chains speculate up to this payload per rank
 
 
 def _say(*a):
@@ -61,6 +62,8 @@ def test_fenced_chain_variants_bit_exact(b):
         st = stats.cpu().tolist()
         assert st[2] == 0
         assert st[3] == E * R * _fenced_slices(ch)
+        if v == "speculative" and n * 2 > FENCED_SPEC_MAX_BYTES:
+            assert st[0] == 0 and st[1] == 0  # waits for the flags first
         ch.close()
 
 
