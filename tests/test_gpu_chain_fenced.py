@@ -124,6 +124,8 @@ def test_fenced_plan_chains(name, variant):
     _say(f"fenced plan chain {name} {variant}")
     stats, ch = _run_chain(name, R, 8 * 1024, "bf16", variant, E=16)
     assert stats[2] == 0
+    if variant == "speculative":
+        assert stats[0] == 0 and stats[1] == 0  # that build's plan chains wait for the flags first
     ch.close()
 
 
