@@ -241,7 +241,41 @@ __global__ void __launch_bounds__(128) moe_combine_kernel(RowArgs a) {
   }
 }
 
-// Any k and any hidden size: one element per lane, k rows folded in order.
+// Top-k above 16: the same combine, one vector per lane, with each row's
+// slot and weight read as the fold reaches it (same terms, same order).
+__global__ void __launch_bounds__(128) moe_combine_any_kernel(RowArgs a) {
+  if (route_failed(a)) return;
+  const int64_t t = blockIdx.x / a.parts;
+  const int64_t tk = t * a.k;
+  const int64_t dst_rank = t / a.tokens_per_rank;
+  unsigned char *dst = a.out[dst_rank] + (t - dst_rank * a.tokens_per_rank) * a.row_bytes;
+  const int64_t v0 = (static_cast<int64_t>(blockIdx.x) - t * a.parts) * a.part_vec;
+  const int64_t v1 = v0 + a.part_vec < a.nvec ? v0 + a.part_vec : a.nvec;
+  for (int64_t i = v0 + threadIdx.x; i < v1; i += blockDim.x) {
+    float acc[8];
+    for (int j = 0; j < a.k; ++j) {
+      const int32_t s = a.slot[tk + j];
+      const float w = a.wover ? a.wover[tk + a.col[tk + j]] : a.weight[tk + j];
+      const v4u z = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(
+          a.in[s >> kSlotRankShift] + static_cast<int64_t>(s & kSlotRowMask) * a.row_bytes + i * 16));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float lo = w * bf16_lo(z[q]);
+        const float hi = w * bf16_hi(z[q]);
+        acc[2 * q] = j == 0 ? lo : acc[2 * q] + lo;
+        acc[2 * q + 1] = j == 0 ? hi : acc[2 * q + 1] + hi;
+      }
+    }
+    const uint4 p = pack_bf16x8(acc);
+    __builtin_amdgcn_raw_buffer_store_b128(
+        v4u{p.x, p.y, p.z, p.w},
+        __builtin_amdgcn_make_buffer_rsrc(dst, static_cast<short>(0), static_cast<int>(a.row_bytes), 0x00020000),
+        static_cast<int32_t>(i * 16), 0, 16);
+  }
+}
+
+// Rows that are not whole, aligned 16-byte vectors, any k: one element per
+// lane, k rows folded in order.
 __global__ void __launch_bounds__(256) moe_combine_elem_kernel(RowArgs a) {
   if (route_failed(a)) return;
   const int64_t t = blockIdx.x;
@@ -943,8 +977,12 @@ rrb_status launch_rows(const Plan &p, const void *const *in, void *const *out, c
     }
   } else {
     int cu = 0;
-    if (vec) kern = combine_for(m.topk, &cu);
-    if (kern) {
+    if (vec) {
+      kern = combine_for(m.topk, &cu);
+      if (!kern) {
+        kern = moe_combine_any_kernel;
+        cu = 1;
+      }
       bs = 128;
       split_row(a, 128LL * cu);
     } else {

@@ -148,6 +148,23 @@ def test_combine_special_values(h):
         assert_bits_equal(from_dev(y[r]).reshape(-1, h), want[r], f"combine specials rank {r} h={h}")
 
 
+@pytest.mark.parametrize("k", [17, 24, 32])
+def test_moe_topk_above_16_vector_kernels(k):
+    """Top-k above 16 (host-built maps only): the vector dispatch that reads
+    slots per store and the vector combine that reads slots and weights per
+    row, on full and ragged row parts; 64 experts over 8 ranks."""
+    require_gpu()
+    T, E, R = 64, 64, 8
+    for h in (7168, 2392):
+        rng = np.random.default_rng([9007, k, h])
+        idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+        w = rng.random((T, k)).astype(np.float32)
+        xa = bf16.rne(rng.standard_normal((T, h)).astype(np.float32))
+        shards = [xa[r * (T // R):(r + 1) * (T // R)] for r in range(R)]
+        _say(f"moe top-{k} h={h}")
+        _roundtrip(T, h, E, k, R, idx, w, shards, "seeded")
+
+
 @pytest.mark.parametrize("k", range(1, 17))
 def test_moe_every_topk_vector_kernels(k):
     """Every top-k up to 16 has its own dispatch and combine kernels: full
@@ -191,7 +208,7 @@ def test_moe_random_shapes(seed):
 
 
 @pytest.mark.parametrize("T,h,E,k,R", [(4096, 7168, 256, 8, 8), (64, 24, 16, 4, 8), (32, 13, 8, 3, 4),
-                                       (16, 8, 16, 16, 2)])
+                                       (16, 8, 16, 16, 2), (64, 2392, 64, 20, 8)])
 def test_combine_per_call_weights(T, h, E, k, R):
     """rrb_reduce's d_weights on a host-built combine plan: weights given in
     the routing arrays' column order replace the plan's for one call (vector
